@@ -1,0 +1,200 @@
+"""Pins of the oracle's GroupedMLP forward and backward.
+
+* Unquantized mode: reduces to a dense Mixtral-style expert FFN computed with
+  torch, and its backward equals torch.autograd in float64 and central finite
+  differences.
+* Quantized mode: which axis each GEMM operand is blocked along is pinned by
+  inputs that are exactly MXFP8-representable along the intended axis and
+  lossy along every other axis; a wrong axis changes the result.
+* Invariants: r_i dr_i = <Y_i, dY_i>, zero rows, empty experts, dY = 0.
+"""
+import numpy as np
+import torch
+
+from oracle import mx_oracle as O
+from tests.test_oracle_codec import exact_block_values
+
+
+def rand_case(rng, M_counts, H, F, wstd=0.1):
+    offsets = np.concatenate([[0], np.cumsum(M_counts)]).astype(np.int64)
+    M, E = int(offsets[-1]), len(M_counts)
+    X = rng.standard_normal((M, H))
+    W1 = rng.standard_normal((E, 2 * F, H)) * wstd
+    W2 = rng.standard_normal((E, H, F)) * wstd
+    r = rng.uniform(0.1, 1.0, M)
+    dY = rng.standard_normal((M, H))
+    return X, W1, W2, r, offsets, dY
+
+
+def torch_mlp(X, W1, W2, r, offsets):
+    """Independent torch formulation (float64) of the unquantized MLP."""
+    F = W2.shape[2]
+    outs = []
+    for e in range(W1.shape[0]):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        x = X[lo:hi]
+        g = x @ W1[e, :F].T
+        u = x @ W1[e, F:].T
+        outs.append((torch.nn.functional.silu(g) * u * r[lo:hi, None])
+                    @ W2[e].T)
+    return torch.cat(outs, 0)
+
+
+def test_fwd_single_expert_dense_ffn():
+    rng = np.random.default_rng(20)
+    X, W1, W2, r, off, _ = rand_case(rng, [37], 64, 32)
+    r[:] = 1.0
+    Y, _ = O.grouped_mlp_fwd(X, W1, W2, r, off, quantize=False)
+    w1, w3 = torch.from_numpy(W1[0, :32]), torch.from_numpy(W1[0, 32:])
+    x = torch.from_numpy(X)
+    ref = (torch.nn.functional.silu(x @ w1.T) * (x @ w3.T)) @ torch.from_numpy(
+        W2[0]).T
+    assert np.allclose(Y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_unquantized_matches_autograd():
+    rng = np.random.default_rng(21)
+    X, W1, W2, r, off, dY = rand_case(rng, [5, 0, 17, 10], 64, 32)
+    Y, saved = O.grouped_mlp_fwd(X, W1, W2, r, off, quantize=False)
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved, quantize=False)
+
+    tX, tW1, tW2, tr = (torch.tensor(a, requires_grad=True)
+                        for a in (X, W1, W2, r))
+    tY = torch_mlp(tX, tW1, tW2, tr, off)
+    assert np.allclose(Y, tY.detach().numpy(), rtol=1e-12, atol=1e-12)
+    (tY * torch.from_numpy(dY)).sum().backward()
+    for name, t in (("dX", tX), ("dW1", tW1), ("dW2", tW2), ("dr", tr)):
+        assert np.allclose(g[name], t.grad.numpy(), rtol=1e-10,
+                           atol=1e-12), name
+    assert not g["dW1"][1].any() and not g["dW2"][1].any()
+
+
+def test_bwd_unquantized_finite_differences():
+    rng = np.random.default_rng(22)
+    X, W1, W2, r, off, dY = rand_case(rng, [6, 9], 32, 32)
+    _, saved = O.grouped_mlp_fwd(X, W1, W2, r, off, quantize=False)
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved, quantize=False)
+
+    def loss(X_, W1_, W2_, r_):
+        return float((O.grouped_mlp_fwd(X_, W1_, W2_, r_, off,
+                                        quantize=False)[0] * dY).sum())
+
+    eps = 1e-6
+    checks = [("dX", 0, (3, 7)), ("dX", 0, (12, 30)), ("dW1", 1, (1, 5, 9)),
+              ("dW1", 1, (0, 40, 3)), ("dW2", 2, (1, 2, 31)), ("dr", 3, (4,)),
+              ("dr", 3, (14,))]
+    args = [X, W1, W2, r]
+    for name, which, idx in checks:
+        p, m = [a.copy() for a in args], [a.copy() for a in args]
+        p[which][idx] += eps
+        m[which][idx] -= eps
+        fd = (loss(*p) - loss(*m)) / (2 * eps)
+        assert abs(fd - g[name][idx]) <= 1e-6 * max(1.0, abs(fd)), name
+
+
+def test_bwd_routing_weight_invariant():
+    rng = np.random.default_rng(23)
+    X, W1, W2, r, off, dY = rand_case(rng, [8, 8, 3], 64, 64)
+    Y, saved = O.grouped_mlp_fwd(X, W1, W2, r, off, quantize=False)
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved, quantize=False)
+    assert np.allclose(r * g["dr"], (Y * dY).sum(axis=1), rtol=1e-10,
+                       atol=1e-12)
+
+
+def test_quantized_zero_rows_empty_experts_zero_dy():
+    rng = np.random.default_rng(24)
+    X, W1, W2, r, off, dY = rand_case(rng, [40, 0, 33], 64, 64)
+    r[5] = 0.0
+    Y, saved = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    assert not Y[5].any()
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved)
+    assert not g["dW1"][1].any() and not g["dW2"][1].any()
+    z = O.grouped_mlp_bwd(np.zeros_like(dY), X, W1, W2, r, off, saved)
+    for name in ("dX", "dW1", "dW2", "dr"):
+        assert not z[name].any(), name
+
+
+def test_quantized_close_to_unquantized():
+    rng = np.random.default_rng(25)
+    X, W1, W2, r, off, dY = rand_case(rng, [64, 29, 0, 100], 128, 64)
+    Yq, sq = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    Yu, su = O.grouped_mlp_fwd(X, W1, W2, r, off, quantize=False)
+    assert O.parity_metrics(Yq, Yu)[0] < 0.15
+    gq = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, sq)
+    gu = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, su, quantize=False)
+    for name in ("dX", "dW1", "dW2", "dr"):
+        assert O.parity_metrics(gq[name], gu[name])[0] < 0.2, name
+
+
+def lossy_elsewhere(rng, shape, axis):
+    """Exactly representable along 32-blocks of ``axis``; exponents jump by
+    up to 40 between neighbouring blocks, so blocking along any other axis
+    loses values."""
+    moved = np.moveaxis(np.zeros(shape), axis, -1)
+    v = exact_block_values(rng, moved.shape, -20, 20)
+    return np.moveaxis(v, -1, axis)
+
+
+def test_fwd_quantization_axes():
+    rng = np.random.default_rng(26)
+    H, F = 64, 64
+    off = np.array([0, 32, 96])
+    X = rng.standard_normal((96, H))
+    W1 = lossy_elsewhere(rng, (2, 2 * F, H), 2)       # exact along H
+    W2 = lossy_elsewhere(rng, (2, H, F), 2)           # exact along F
+    assert not np.array_equal(O.qdq_lastdim(np.swapaxes(W1, 1, 2)),
+                              np.swapaxes(W1, 1, 2))
+    r = rng.uniform(0.2, 1.0, 96)
+    Y, s = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    assert np.array_equal(s["h"], O.grouped_linear(O.qdq_lastdim(X), W1, off))
+    assert np.array_equal(Y, O.grouped_linear(O.qdq_lastdim(s["z"]), W2, off))
+
+
+def test_bwd_dgrad_quantization_axes():
+    rng = np.random.default_rng(27)
+    H, F = 64, 64
+    off = np.array([0, 40, 96])
+    X = rng.standard_normal((96, H))
+    W1 = lossy_elsewhere(rng, (2, 2 * F, H), 1)       # exact along 2F
+    W2 = lossy_elsewhere(rng, (2, H, F), 1)           # exact along H
+    assert not np.array_equal(O.qdq_lastdim(W2), W2)
+    r = rng.uniform(0.2, 1.0, 96)
+    dY = rng.standard_normal((96, H))
+    _, s = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, s)
+    assert np.array_equal(
+        g["dz"], O.grouped_linear(O.qdq_lastdim(dY), W2.transpose(0, 2, 1),
+                                  off))
+    assert np.array_equal(
+        g["dX"], O.grouped_linear(O.qdq_lastdim(g["dh"]),
+                                  W1.transpose(0, 2, 1), off))
+
+
+def test_bwd_wgrad_token_axis():
+    rng = np.random.default_rng(28)
+    H, F = 64, 32
+    off = np.array([0, 64, 160])                      # 32-aligned experts
+    X = lossy_elsewhere(rng, (160, H), 0)              # exact along tokens
+    dY = lossy_elsewhere(rng, (160, H), 0)
+    assert not np.array_equal(O.qdq_lastdim(X), X)
+    W1 = rng.standard_normal((2, 2 * F, H)) * 0.1
+    W2 = rng.standard_normal((2, H, F)) * 0.1
+    r = rng.uniform(0.2, 1.0, 160)
+    _, s = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, s)
+    zt = O.qdq_tokens(s["z"], off)
+    dht = O.qdq_tokens(g["dh"], off)
+    for e in range(2):
+        lo, hi = off[e], off[e + 1]
+        assert np.array_equal(g["dW2"][e], dY[lo:hi].T @ zt[lo:hi])
+        assert np.array_equal(g["dW1"][e], dht[lo:hi].T @ X[lo:hi])
+
+
+def test_parity_metrics_definition():
+    ref = np.array([[3.0, 4.0], [0.0, 0.0]])
+    got = np.array([[3.0, 4.5], [0.0, 0.0]])
+    rel, worst = O.parity_metrics(got, ref)
+    assert abs(rel - 0.1) < 1e-12
+    assert abs(worst - 0.5 / np.sqrt(12.5)) < 1e-12
+    got[1, 0] = 1e-30
+    assert O.parity_metrics(got, ref)[1] == np.inf
