@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the MXFP8 GroupedMLP forward + backward on one MI355X.
+
+Workload (the Mixtral-8x7B expert shape): T=16384 tokens routed top-2
+(M=32768 token-sorted rows), E=8 experts, H=4096, F=14336 (gate-up W1
+[8, 28672, 4096], down W2 [8, 4096, 14336]), Zipf(1.1) expert loads
+[13047, 6087, 3897, 2839, 2221, 1818, 1534, 1325], dY ~ N(0, 1).  Seeded
+synthetic inputs drawn on the GPU; everything stays resident in HBM.
+
+One step = grouped_mlp_fwd + grouped_mlp_bwd: quantization of X, W1, W2 and
+dY (rowwise and columnwise), the fused gate-up/SwiGLU/routing-scale/requant
+GEMM, the down GEMM, the fused dgrad/SwiGLU-backward/dr/requant GEMM, the
+gate-up dgrad GEMM and both weight-gradient GEMMs.
+
+Prints one JSON line: tokens/s (value), TFLOP/s counted as 18*H*F per routed
+row, the dominant kernel's roofline (launch durations from HIP events the
+library records on its stream around each launch), and the FP64 CPU oracle
+timed on a bounded sample as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 / MXFP8 MFMA
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_table(gm, lib):
+    """Per-kernel aggregates of the launch records of the timed region."""
+    n = lib.mx_profile_count()
+    name = ctypes.c_char_p()
+    ms = ctypes.c_float()
+    work = ctypes.c_double()
+    unit = ctypes.c_int32()
+    agg = {}
+    for i in range(n):
+        st = lib.mx_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(work),
+                                ctypes.byref(unit))
+        if st != 0:
+            raise RuntimeError(gm.last_error())
+        a = agg.setdefault(name.value.decode(), {"launches": 0, "ms": 0.0, "work": 0.0,
+                                                 "unit": unit.value})
+        a["launches"] += 1
+        a["ms"] += ms.value
+        a["work"] += work.value
+    return agg
+
+
+def roofline(agg):
+    name, a = max(agg.items(), key=lambda kv: kv[1]["ms"])
+    sec = a["ms"] / 1e3
+    if a["unit"] == 0:
+        achieved = a["work"] / sec / 1e12
+        peak, unit, bound = FP8_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved = a["work"] / sec / 1e9
+        peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
+    return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+            "launches": a["launches"], "avg_launch_ms": round(a["ms"] / a["launches"], 4)}
+
+
+def cpu_baseline(seed, T, M, E, H, F):
+    """The FP64 oracle (as it is) on a bounded sample of the same workload.
+
+    Sample: one expert, full H=4096, a slice of Fs=1024 of the F=14336
+    intermediate units (gate and up rows and the matching W2 columns), run on
+    n=512 and n=1024 rows.  The oracle's time is linear in rows and in F, with
+    a per-expert part (weight quantization) and a per-row part; the two runs
+    give both, and the whole step is extrapolated as
+        (F/Fs) * (E * per_expert + M * per_row).
+    """
+    import numpy as np
+    import torch
+    from oracle import mx_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    Fs, n = 1024, 512
+    g = torch.Generator().manual_seed(seed)
+    bf = lambda *s, std=1.0: (torch.randn(*s, generator=g) * std).to(torch.bfloat16).double().numpy()
+    X, dY = bf(2 * n, H), bf(2 * n, H)
+    W1, W2 = bf(1, 2 * Fs, H, std=0.02), bf(1, H, Fs, std=0.02)
+    r = torch.rand(2 * n, generator=g, dtype=torch.float64).numpy()
+
+    def run(rows):
+        off = np.array([0, rows])
+        t = time.perf_counter()
+        Y, saved = O.grouped_mlp_fwd(X[:rows], W1, W2, r[:rows], off)
+        O.grouped_mlp_bwd(dY[:rows], X[:rows], W1, W2, r[:rows], off, saved)
+        return time.perf_counter() - t
+
+    t1 = run(n)
+    t2 = run(2 * n)
+    per_row = max((t2 - t1) / n, 1e-12)
+    per_expert = max(t1 - n * per_row, 0.0)
+    est = (F / Fs) * (E * per_expert + M * per_row)
+    return {"value": round(T / est, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"FP64 NumPy oracle fwd+bwd on 1 expert, H={H}, F slice {Fs}/{F}, "
+                       f"{n} and {2 * n} rows ({t1:.1f} s + {t2:.1f} s); step time "
+                       f"extrapolated linearly to E={E}, M={M} rows, F={F}: {est:.0f} s"),
+            "est_step_s": round(est, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the expert path is "
+                                   "built and measured on a single MI355X (no collectives); "
+                                   "run with --gpus 1"}))
+        return 2
+    import torch
+    import grouped_gemm_mxfp8_amd as gm
+    from workloads import make_mlp_case
+
+    lib = gm.lib()
+    lib.mx_profile_begin.argtypes = [ctypes.c_int32]
+    lib.mx_profile_get.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                   ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double),
+                                   ctypes.POINTER(ctypes.c_int32)]
+    dev = torch.device("cuda:0")
+    print(f"[bench] device {torch.cuda.get_device_name(dev)}; building inputs", file=sys.stderr,
+          flush=True)
+    case = make_mlp_case("mixtral_fwd_bwd", seed=args.seed, device=dev)
+    M, H, F, E, T = case.M, case.H, case.F, case.E, case.T
+    x, w1, w2, r, off, dy = case.X, case.W1, case.W2, case.r, case.offsets, case.dY
+    fws = torch.empty(gm.fwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+    bws = torch.empty(gm.bwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+
+    def step():
+        y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws)
+        return gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx, ws=bws)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup {i + 1}/{args.warmup}", file=sys.stderr, flush=True)
+
+    if lib.mx_profile_begin(64 * max(args.steps, 1)) != 0:
+        raise RuntimeError(gm.last_error())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    lib.mx_profile_end()
+    print(f"[bench] {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    agg = kernel_table(gm, lib)
+    ms_step = elapsed / args.steps * 1e3
+    tokens_s = T * args.steps / elapsed
+    flops_step = 18.0 * H * F * M
+    tflops = flops_step * args.steps / elapsed / 1e12
+    kernels = {k: {"launches_per_step": v["launches"] / args.steps,
+                   "ms_per_step": round(v["ms"] / args.steps, 4),
+                   ("tflops" if v["unit"] == 0 else "gbs"):
+                       round(v["work"] / (v["ms"] / 1e3) / (1e12 if v["unit"] == 0 else 1e9), 2)}
+               for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["ms"])}
+
+    out = {
+        "metric": "GroupedMLP fwd+bwd tokens/s & TFLOP/s (MXFP8), Mixtral-8x7B expert shape",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "mixtral_fwd_bwd: GroupedMLP fwd+bwd, T=16384 top-2 (M=32768 "
+                               "rows), E=8, H=4096, F=14336, Zipf(1.1) loads",
+                   "T": T, "M": M, "E": E, "H": H, "F": F,
+                   "expert_rows": [int(c) for c in case.counts]},
+        "tflops": round(tflops, 2),
+        "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+        "roofline": roofline(agg),
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.seed, T, M, E, H, F)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

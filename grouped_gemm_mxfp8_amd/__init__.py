@@ -1,0 +1,330 @@
+"""MXFP8 MoE expert path for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libmxmoe.so`` (C ABI in ``include/mxmoe.h``).  The
+functions carry the C names; each one checks tensor dtypes/devices, allocates
+the outputs with torch (device memory only) and passes raw pointers and the
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels: there is no fallback.  If the library is missing, importing the
+functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxmoe.so")
+
+MX_DTYPE_BF16 = 0
+MX_DTYPE_MXFP8 = 1
+TOKEN_ALIGN = 128
+BLOCK = 32
+MX_CTX_H, MX_CTX_XCOL, MX_CTX_ZCOL, MX_CTX_POFF = 0, 1, 2, 3
+MX_WS_ZROW, MX_WS_DHROW, MX_WS_DHCOL = 0, 1, 2
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "mx_last_error": (ctypes.c_char_p, []),
+    "mx_version": (ctypes.c_char_p, []),
+    "mx_padded_rows_bound": (_I64, [_I64, _I32, _I32]),
+    "mxfp8_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _I32, _P, _P, _I64, _P, _P]),
+    "grouped_linear_fwd": (_I32, [_I32, _P, _P, _P, _I32, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
+    "grouped_mlp_fwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P,
+                               _SZ, _P]),
+    "grouped_mlp_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P, _P, _P,
+                               _P, _P, _SZ, _P]),
+    "grouped_mlp_ctx_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "grouped_mlp_fwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "grouped_mlp_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "grouped_mlp_ctx_offset": (_I64, [_I32, _I64, _I64, _I64, _I32]),
+    "grouped_mlp_ws_offset": (_I64, [_I32, _I64, _I64, _I64, _I32]),
+}
+
+
+class MxError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m grouped_gemm_mxfp8_amd._build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().mx_last_error().decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MxError(fn, status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, dtype, name, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def padded_rows_bound(M: int, G: int, align: int = TOKEN_ALIGN) -> int:
+    return int(lib().mx_padded_rows_bound(M, G, align))
+
+
+@dataclasses.dataclass
+class MxTensor:
+    """MXFP8 operand: E4M3 codes (uint8) and E8M0 scales (uint8)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+
+
+def mxfp8_quantize(x: torch.Tensor, rowwise: bool = True, colwise: bool = False,
+                   offsets: Optional[torch.Tensor] = None):
+    """Block-quantize bf16 ``x`` ([R, C] or [batch, R, C]) to MXFP8.
+
+    Returns a dict with ``row`` (MxTensor [.., R, C] / [.., R, C/32]) and/or
+    ``col`` (MxTensor [.., C, ld] / [.., C, ld/32], transposed, token groups
+    padded to 128) and ``padded_offsets`` (int64 [G+1]) when ``offsets`` is
+    given.
+    """
+    _need(x, torch.bfloat16, "x")
+    dev = x.device
+    if x.dim() == 2:
+        batch, (R, C) = 1, x.shape
+        lead = ()
+    elif x.dim() == 3:
+        batch, R, C = x.shape
+        lead = (batch,)
+    else:
+        raise ValueError("x must be 2-D or 3-D")
+    G = 1
+    if offsets is not None:
+        _need(offsets, torch.int64, "offsets", dev)
+        G = offsets.numel() - 1
+    out = {}
+    rc = rs = cc = cs = poff = None
+    ld = 0
+    if rowwise:
+        rc = torch.empty((*lead, R, C), dtype=torch.uint8, device=dev)
+        rs = torch.empty((*lead, R, C // BLOCK), dtype=torch.uint8, device=dev)
+        out["row"] = MxTensor(rc, rs)
+    if colwise:
+        ld = padded_rows_bound(R, G)
+        ld = max(ld, TOKEN_ALIGN)
+        cc = torch.empty((*lead, C, ld), dtype=torch.uint8, device=dev)
+        cs = torch.empty((*lead, C, ld // BLOCK), dtype=torch.uint8, device=dev)
+        out["col"] = MxTensor(cc, cs)
+        if offsets is not None:
+            poff = torch.empty(G + 1, dtype=torch.int64, device=dev)
+            out["padded_offsets"] = poff
+    st = lib().mxfp8_quantize(_ptr(x), batch, R, C, _ptr(rc), _ptr(rs), _ptr(offsets), G,
+                              _ptr(cc), _ptr(cs), ld, _ptr(poff), _stream(dev))
+    _check("mxfp8_quantize", st)
+    return out
+
+
+def grouped_linear_fwd(x, offsets: torch.Tensor, w, row_scale: Optional[torch.Tensor] = None):
+    """GroupedLinear: y[rows of e] = x[rows of e] @ w[e].T for every expert.
+
+    ``x`` bf16 [M, K] and ``w`` bf16 [E, N, K], or both MxTensor (rowwise
+    MXFP8 copies).  Returns bf16 [M, N].
+    """
+    if isinstance(x, MxTensor):
+        if not isinstance(w, MxTensor):
+            raise TypeError("x and w must both be MXFP8 or both bf16")
+        dtype = MX_DTYPE_MXFP8
+        xc, xs, wc, ws = x.codes, x.scales, w.codes, w.scales
+        _need(xc, torch.uint8, "x.codes")
+        dev = xc.device
+        _need(xs, torch.uint8, "x.scales", dev)
+        _need(wc, torch.uint8, "w.codes", dev)
+        _need(ws, torch.uint8, "w.scales", dev)
+        M, K = xc.shape
+        E, N, K2 = wc.shape
+    else:
+        dtype = MX_DTYPE_BF16
+        _need(x, torch.bfloat16, "x")
+        dev = x.device
+        _need(w, torch.bfloat16, "w", dev)
+        xc, xs, wc, ws = x, None, w, None
+        M, K = x.shape
+        E, N, K2 = w.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: x has {K}, w has {K2}")
+    _need(offsets, torch.int64, "offsets", dev)
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must have E+1 entries")
+    if row_scale is not None:
+        _need(row_scale, torch.float32, "row_scale", dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    st = lib().grouped_linear_fwd(dtype, _ptr(xc), _ptr(xs), _ptr(offsets), E, M, _ptr(wc),
+                                  _ptr(ws), N, K, _ptr(row_scale), _ptr(y), _stream(dev))
+    _check("grouped_linear_fwd", st)
+    return y
+
+
+@dataclasses.dataclass
+class MlpCtx:
+    """Saved-for-backward state of grouped_mlp_fwd (opaque device buffer)."""
+    buf: torch.Tensor
+    M: int
+    H: int
+    F: int
+    E: int
+
+    @property
+    def padded_rows(self) -> int:
+        return padded_rows_bound(self.M, self.E)
+
+    def _off(self, which):
+        off = int(lib().grouped_mlp_ctx_offset(which, self.M, self.H, self.F, self.E))
+        if off < 0:
+            raise MxError("grouped_mlp_ctx_offset", 1, last_error())
+        return off
+
+    def h(self) -> torch.Tensor:
+        """Saved gate-up pre-activation, bf16 [M, 2F]."""
+        return _region(self.buf, self._off(MX_CTX_H), (self.M, 2 * self.F), torch.bfloat16)[0]
+
+    def xcol(self) -> MxTensor:
+        """Token-axis MXFP8 copy of X: codes [H, Mp], scales [H, Mp/32]."""
+        return self._mx(MX_CTX_XCOL, (self.H, self.padded_rows))
+
+    def zcol(self) -> MxTensor:
+        """Token-axis MXFP8 copy of z: codes [F, Mp], scales [F, Mp/32]."""
+        return self._mx(MX_CTX_ZCOL, (self.F, self.padded_rows))
+
+    def padded_offsets(self) -> torch.Tensor:
+        return _region(self.buf, self._off(MX_CTX_POFF), (self.E + 1,), torch.int64)[0]
+
+    def _mx(self, which, shape):
+        codes, nxt = _region(self.buf, self._off(which), shape, torch.uint8)
+        scales, _ = _region(self.buf, nxt, (*shape[:-1], shape[-1] // BLOCK), torch.uint8)
+        return MxTensor(codes, scales)
+
+
+def _mlp_check(x, offsets, w1, w2, r):
+    _need(x, torch.bfloat16, "x")
+    dev = x.device
+    _need(offsets, torch.int64, "offsets", dev)
+    _need(w1, torch.bfloat16, "w1", dev)
+    _need(w2, torch.bfloat16, "w2", dev)
+    _need(r, torch.float32, "r", dev)
+    M, H = x.shape
+    E, F2, H1 = w1.shape
+    E2, H2, F = w2.shape
+    if H1 != H or H2 != H or E2 != E or F2 != 2 * F:
+        raise ValueError("shape mismatch: x [M,H], w1 [E,2F,H], w2 [E,H,F]")
+    if r.shape != (M,) or offsets.numel() != E + 1:
+        raise ValueError("r must be [M] and offsets [E+1]")
+    return dev, M, H, F, E
+
+
+def fwd_ws_bytes(M, H, F, E) -> int:
+    return int(lib().grouped_mlp_fwd_ws_bytes(M, H, F, E))
+
+
+def bwd_ws_bytes(M, H, F, E) -> int:
+    return int(lib().grouped_mlp_bwd_ws_bytes(M, H, F, E))
+
+
+def grouped_mlp_fwd(x, offsets, w1, w2, r, ws: Optional[torch.Tensor] = None):
+    """Fused GroupedMLP forward.  Returns (y bf16 [M, H], MlpCtx)."""
+    dev, M, H, F, E = _mlp_check(x, offsets, w1, w2, r)
+    L = lib()
+    nctx = L.grouped_mlp_ctx_bytes(M, H, F, E)
+    nws = L.grouped_mlp_fwd_ws_bytes(M, H, F, E)
+    if nctx == 0 or nws == 0:
+        raise MxError("grouped_mlp_fwd", 2, last_error())
+    ctx = torch.empty(nctx, dtype=torch.uint8, device=dev)
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    st = L.grouped_mlp_fwd(_ptr(x), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
+                           _ptr(y), _ptr(ctx), nctx, _ptr(ws), ws.numel(), _stream(dev))
+    _check("grouped_mlp_fwd", st)
+    return y, MlpCtx(ctx, M, H, F, E)
+
+
+def grouped_mlp_bwd(dy, offsets, w1, w2, r, ctx: MlpCtx, ws: Optional[torch.Tensor] = None):
+    """Fused GroupedMLP backward.  Returns (dx, dw1, dw2, dr)."""
+    dev, M, H, F, E = _mlp_check(dy, offsets, w1, w2, r)
+    if (ctx.M, ctx.H, ctx.F, ctx.E) != (M, H, F, E):
+        raise ValueError("ctx was made for other sizes")
+    L = lib()
+    nws = L.grouped_mlp_bwd_ws_bytes(M, H, F, E)
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    dx = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.empty((E, 2 * F, H), dtype=torch.bfloat16, device=dev)
+    dw2 = torch.empty((E, H, F), dtype=torch.bfloat16, device=dev)
+    dr = torch.empty((M,), dtype=torch.float32, device=dev)
+    st = L.grouped_mlp_bwd(_ptr(dy), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
+                           _ptr(ctx.buf), ctx.buf.numel(), _ptr(dx), _ptr(dw1), _ptr(dw2),
+                           _ptr(dr), _ptr(ws), ws.numel(), _stream(dev))
+    _check("grouped_mlp_bwd", st)
+    return dx, dw1, dw2, dr
+
+
+def _region(buf: torch.Tensor, off: int, shape, dtype):
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return buf[off:off + nbytes].view(dtype).view(*shape), (off + nbytes + 255) // 256 * 256
+
+
+def ws_mx_view(ws: torch.Tensor, which: int, M, H, F, E, shape) -> MxTensor:
+    """MXFP8 tensor inside a forward/backward workspace: codes of ``shape``
+    at the documented offset, scales [.., shape[-1]/32] at the next 256-byte
+    boundary (see include/mxmoe.h)."""
+    off = int(lib().grouped_mlp_ws_offset(which, M, H, F, E))
+    if off < 0:
+        raise MxError("grouped_mlp_ws_offset", 1, last_error())
+    codes, nxt = _region(ws, off, shape, torch.uint8)
+    scales, _ = _region(ws, nxt, (*shape[:-1], shape[-1] // BLOCK), torch.uint8)
+    return MxTensor(codes, scales)
+
+
+__all__ = ["lib", "last_error", "MxError", "MxTensor", "MlpCtx", "mxfp8_quantize",
+           "grouped_linear_fwd", "grouped_mlp_fwd", "grouped_mlp_bwd", "padded_rows_bound",
+           "ws_mx_view", "fwd_ws_bytes", "bwd_ws_bytes"]

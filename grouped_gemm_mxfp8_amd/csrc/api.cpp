@@ -1,0 +1,633 @@
+// C-ABI layer of the MXFP8 MoE expert path: argument validation (host only,
+// before any HIP call), layout of the saved-for-backward context and of the
+// workspaces, and the launch sequence of each entry point on the caller's
+// stream.  Nothing on the compute path allocates, frees or synchronises; only
+// the opt-in launch-timing calls (mx_profile_*) create and wait on events.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/mxmoe.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+mx_status fail(mx_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+mx_status ok() {
+    g_err.clear();
+    return MX_OK;
+}
+
+mx_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(MX_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// ---- launch timing (mx_profile_*) ------------------------------------------
+struct ProfRec {
+    const char* name;
+    double work;
+    int unit;
+    hipEvent_t a, b;
+};
+struct Profiler {
+    bool on = false;
+    int cap = 0;
+    std::vector<hipEvent_t> pool;
+    std::vector<ProfRec> recs;
+    void release() {
+        for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+        pool.clear();
+        recs.clear();
+        cap = 0;
+    }
+};
+thread_local Profiler g_prof;
+
+// Run one launch, bracketed by events when timing is on.
+template <class Fn>
+hipError_t timed(const char* name, double work, int unit, hipStream_t s, Fn&& fn) {
+    Profiler& P = g_prof;
+    if (!P.on || (int)P.recs.size() >= P.cap) return fn();
+    const size_t i = P.recs.size();
+    hipEvent_t a = P.pool[2 * i], b = P.pool[2 * i + 1];
+    (void)hipEventRecord(a, s);
+    const hipError_t e = fn();
+    (void)hipEventRecord(b, s);
+    P.recs.push_back(ProfRec{name, work, unit, a, b});
+    return e;
+}
+
+double quant_bytes(int64_t rows, int64_t C, bool row, bool col) {
+    const double n = (double)rows * (double)C;
+    return 2.0 * n + (row ? n * (1.0 + 1.0 / 32) : 0.0) + (col ? n * (1.0 + 1.0 / 32) : 0.0);
+}
+
+constexpr int64_t kI32Max = 0x7fffffffLL;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carve-out of a buffer into 256-byte aligned regions.
+struct Carver {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t padded_bound(int64_t M, int64_t G, int64_t align) {
+    return (M + G * (align - 1)) / align * align;
+}
+
+// ---- layouts ----------------------------------------------------------------
+struct MlpDims {
+    int64_t M, H, F, E, Mp;
+};
+
+struct CtxLayout {
+    size_t h, xcol, xcol_s, zcol, zcol_s, poff, total;
+};
+CtxLayout ctx_layout(const MlpDims& d) {
+    Carver c;
+    CtxLayout L;
+    L.h = c.take((size_t)d.M * 2 * d.F * 2);
+    L.xcol = c.take((size_t)d.H * d.Mp);
+    L.xcol_s = c.take((size_t)d.H * d.Mp / 32);
+    L.zcol = c.take((size_t)d.F * d.Mp);
+    L.zcol_s = c.take((size_t)d.F * d.Mp / 32);
+    L.poff = c.take((size_t)(d.E + 1) * 8);
+    L.total = c.off;
+    return L;
+}
+
+struct FwdWs {
+    size_t xr, xr_s, w1r, w1r_s, w2r, w2r_s, zr, zr_s, total;
+};
+FwdWs fwd_ws_layout(const MlpDims& d) {
+    Carver c;
+    FwdWs L;
+    L.xr = c.take((size_t)d.M * d.H);
+    L.xr_s = c.take((size_t)d.M * d.H / 32);
+    L.w1r = c.take((size_t)d.E * 2 * d.F * d.H);
+    L.w1r_s = c.take((size_t)d.E * 2 * d.F * d.H / 32);
+    L.w2r = c.take((size_t)d.E * d.H * d.F);
+    L.w2r_s = c.take((size_t)d.E * d.H * d.F / 32);
+    L.zr = c.take((size_t)d.M * d.F);
+    L.zr_s = c.take((size_t)d.M * d.F / 32);
+    L.total = c.off;
+    return L;
+}
+
+int64_t dr_parts(int64_t F) { return (F + 255) / 256 * 2; }
+
+struct BwdWs {
+    size_t dyr, dyr_s, dycol, dycol_s, w2c, w2c_s, w1c, w1c_s, dhr, dhr_s, dhc, dhc_s, drp, total;
+};
+BwdWs bwd_ws_layout(const MlpDims& d) {
+    Carver c;
+    BwdWs L;
+    L.dyr = c.take((size_t)d.M * d.H);
+    L.dyr_s = c.take((size_t)d.M * d.H / 32);
+    L.dycol = c.take((size_t)d.H * d.Mp);
+    L.dycol_s = c.take((size_t)d.H * d.Mp / 32);
+    L.w2c = c.take((size_t)d.E * d.F * d.H);
+    L.w2c_s = c.take((size_t)d.E * d.F * d.H / 32);
+    L.w1c = c.take((size_t)d.E * d.H * 2 * d.F);
+    L.w1c_s = c.take((size_t)d.E * d.H * 2 * d.F / 32);
+    L.dhr = c.take((size_t)d.M * 2 * d.F);
+    L.dhr_s = c.take((size_t)d.M * 2 * d.F / 32);
+    L.dhc = c.take((size_t)2 * d.F * d.Mp);
+    L.dhc_s = c.take((size_t)2 * d.F * d.Mp / 32);
+    L.drp = c.take((size_t)d.M * dr_parts(d.F) * 4);
+    L.total = c.off;
+    return L;
+}
+
+mx_status check_mlp_dims(int64_t M, int64_t H, int64_t F, int32_t E, MlpDims* out) {
+    if (M < 0 || H <= 0 || F <= 0 || E <= 0)
+        return fail(MX_ERR_INVALID_ARG, "bad sizes M=%lld H=%lld F=%lld E=%d", (long long)M,
+                    (long long)H, (long long)F, E);
+    if (E > mx::kMaxGroups)
+        return fail(MX_ERR_UNSUPPORTED, "E=%d exceeds %d experts", E, mx::kMaxGroups);
+    if (H % 128 || F % 128)
+        return fail(MX_ERR_UNSUPPORTED, "H=%lld and F=%lld must be multiples of 128",
+                    (long long)H, (long long)F);
+    const int64_t Mp = padded_bound(M, E, mx::kTokenAlign);
+    const int64_t big = (H > 2 * F ? H : 2 * F);
+    if (2 * F * H > kI32Max || big * Mp > kI32Max || 2 * F * 256 > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "operand too large for 32-bit buffer offsets");
+    if (Mp / 128 > 65535)
+        return fail(MX_ERR_UNSUPPORTED, "M=%lld too large", (long long)M);
+    *out = MlpDims{M, H, F, E, Mp};
+    return MX_OK;
+}
+
+const char* epi_name(mx::Epi e) {
+    switch (e) {
+        case mx::Epi::kStoreBf16: return "mx_gemm<store_bf16>";
+        case mx::Epi::kSwiglu: return "mx_gemm<swiglu_quant>";
+        case mx::Epi::kDSwiglu: return "mx_gemm<dswiglu_quant>";
+    }
+    return "mx_gemm";
+}
+
+hipError_t gemm(const mx::GemmProblem& p, mx::Epi e, double flops, hipStream_t s) {
+    return timed(epi_name(e), flops, MX_WORK_FLOP, s, [&] { return mx::launch_mx_gemm(p, e, s); });
+}
+
+}  // namespace
+
+// ---- misc -------------------------------------------------------------------
+namespace mx {
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const bool cacheable = dev >= 0 && dev < 64;
+    int v = cacheable ? __atomic_load_n(&cache[dev], __ATOMIC_RELAXED) : 0;
+    if (v <= 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        if (cacheable) __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+    }
+    return v;
+}
+}  // namespace mx
+
+extern "C" {
+
+const char* mx_last_error(void) { return g_err.c_str(); }
+
+const char* mx_version(void) { return "mxmoe 0.1 gfx950"; }
+
+int64_t mx_padded_rows_bound(int64_t M, int32_t G, int32_t align) {
+    if (M < 0 || G <= 0 || align <= 0) return -1;
+    return padded_bound(M, G, align);
+}
+
+mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
+                         uint8_t* row_codes, uint8_t* row_scales,
+                         const int64_t* d_offsets, int32_t G,
+                         uint8_t* col_codes, uint8_t* col_scales,
+                         int64_t col_ld, int64_t* d_padded_offsets,
+                         mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!x) return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: x is NULL");
+    if (batch < 1 || R < 0 || C < 0)
+        return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: bad sizes batch=%lld R=%lld C=%lld",
+                    (long long)batch, (long long)R, (long long)C);
+    if (C % 32)
+        return fail(MX_ERR_UNSUPPORTED, "mxfp8_quantize: C=%lld is not a multiple of 32",
+                    (long long)C);
+    const bool want_row = row_codes || row_scales;
+    const bool want_col = col_codes || col_scales;
+    if (want_row && !(row_codes && row_scales))
+        return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: row_codes and row_scales go together");
+    if (want_col && !(col_codes && col_scales))
+        return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: col_codes and col_scales go together");
+    if (!want_row && !want_col)
+        return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: no output requested");
+    if (!aligned(x, 16) || (row_codes && !aligned(row_codes, 16)) ||
+        (col_codes && !aligned(col_codes, 16)))
+        return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: x and codes must be 16-byte aligned");
+    if (d_offsets) {
+        if (batch != 1)
+            return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: row groups need batch == 1");
+        if (G < 1 || G > mx::kMaxGroups)
+            return fail(MX_ERR_UNSUPPORTED, "mxfp8_quantize: G=%d outside [1, %d]", G,
+                        mx::kMaxGroups);
+    }
+    int64_t bound = 0;
+    if (want_col) {
+        bound = d_offsets ? padded_bound(R, G, mx::kTokenAlign)
+                          : padded_bound(R, 1, mx::kTokenAlign);
+        if (col_ld % 128 || col_ld < bound)
+            return fail(MX_ERR_INVALID_ARG,
+                        "mxfp8_quantize: col_ld=%lld must be a multiple of 128 and >= %lld",
+                        (long long)col_ld, (long long)bound);
+        if (d_offsets && !d_padded_offsets)
+            return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: d_padded_offsets is NULL");
+        if (bound / 128 > 65535 || batch > 65535)
+            return fail(MX_ERR_UNSUPPORTED, "mxfp8_quantize: too many rows for one launch");
+    }
+    if (batch * R == 0 || C == 0) {
+        if (want_col && d_offsets)
+            return launched(timed("padded_offsets", 16.0 * (G + 1), MX_WORK_BYTES, s,
+                                  [&] { return mx::launch_padded_offsets(d_offsets, G, d_padded_offsets, s); }),
+                            "padded_offsets");
+        return ok();
+    }
+    const uint16_t* xs = static_cast<const uint16_t*>(x);
+    if (!want_col)
+        return launched(timed("quant_rows", quant_bytes(batch * R, C, true, false), MX_WORK_BYTES,
+                              s,
+                              [&] {
+                                  return mx::launch_quant_rows(xs, batch * R, C, row_codes,
+                                                               row_scales, s);
+                              }),
+                        "quant_rows");
+    if (d_offsets) {
+        hipError_t e = timed("padded_offsets", 16.0 * (G + 1), MX_WORK_BYTES, s, [&] {
+            return mx::launch_padded_offsets(d_offsets, G, d_padded_offsets, s);
+        });
+        if (e != hipSuccess) return launched(e, "padded_offsets");
+    }
+    return launched(timed("quant_tiles", quant_bytes(batch * R, C, want_row, true), MX_WORK_BYTES,
+                          s,
+                          [&] {
+                              return mx::launch_quant_tiles(xs, batch, R, C, d_offsets,
+                                                            d_padded_offsets, d_offsets ? G : 1,
+                                                            bound, row_codes, row_scales,
+                                                            col_codes, col_scales, col_ld, s);
+                          }),
+                    "quant_tiles");
+}
+
+mx_status grouped_linear_fwd(int32_t dtype, const void* x, const uint8_t* x_scales,
+                             const int64_t* d_offsets, int32_t E, int64_t M,
+                             const void* w, const uint8_t* w_scales, int64_t N,
+                             int64_t K, const float* d_row_scale, void* y,
+                             mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!x || !d_offsets || !w || !y)
+        return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: NULL x, offsets, w or y");
+    if (E < 1 || E > mx::kMaxGroups || M < 0 || N <= 0 || K <= 0)
+        return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: bad sizes E=%d M=%lld N=%lld K=%lld",
+                    E, (long long)M, (long long)N, (long long)K);
+    if (!aligned(x, 16) || !aligned(w, 16))
+        return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: x and w must be 16-byte aligned");
+    if (dtype == MX_DTYPE_BF16) {
+        if (x_scales || w_scales)
+            return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: bf16 takes no scales");
+        if (K % 32)
+            return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd: bf16 needs K %% 32 == 0");
+        if ((M + (int64_t)E * 63) / 64 > 65535)
+            return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd: M too large for bf16 path");
+        if (M == 0) return ok();
+        return launched(timed("bf16_grouped", 2.0 * M * N * K, MX_WORK_FLOP, s,
+                              [&] {
+                                  return mx::launch_bf16_grouped(
+                                      static_cast<const uint16_t*>(x), d_offsets, E, M,
+                                      static_cast<const uint16_t*>(w), N, K, d_row_scale,
+                                      static_cast<uint16_t*>(y), s);
+                              }),
+                        "bf16_grouped");
+    }
+    if (dtype != MX_DTYPE_MXFP8)
+        return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: unknown dtype %d", dtype);
+    if (!x_scales || !w_scales)
+        return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: MXFP8 needs x_scales and w_scales");
+    if (K % 128 || N % 32)
+        return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd: MXFP8 needs K %% 128 == 0 and N %% 32 == 0");
+    if (N * K > kI32Max || 256 * K > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd: operand too large");
+    if (M == 0) return ok();
+    mx::GemmProblem p{};
+    p.kgroup = false;
+    p.offs = d_offsets;
+    p.G = E;
+    p.M = M; p.N = N; p.K = K;
+    p.A = mx::MxOperand{static_cast<const uint8_t*>(x), x_scales, K, 0};
+    p.B = mx::MxOperand{static_cast<const uint8_t*>(w), w_scales, K, N};
+    p.C = y; p.ldc = N; p.c_gstride = 0;
+    p.rscale = d_row_scale;
+    return launched(gemm(p, mx::Epi::kStoreBf16, 2.0 * M * N * K, s), "mx_gemm");
+}
+
+size_t grouped_mlp_ctx_bytes(int64_t M, int64_t H, int64_t F, int32_t E) {
+    MlpDims d;
+    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
+    return ctx_layout(d).total;
+}
+size_t grouped_mlp_fwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E) {
+    MlpDims d;
+    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
+    return fwd_ws_layout(d).total;
+}
+size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E) {
+    MlpDims d;
+    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
+    return bwd_ws_layout(d).total;
+}
+
+int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F, int32_t E) {
+    MlpDims d;
+    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return -1;
+    const CtxLayout L = ctx_layout(d);
+    switch (which) {
+        case MX_CTX_H: return (int64_t)L.h;
+        case MX_CTX_XCOL: return (int64_t)L.xcol;
+        case MX_CTX_ZCOL: return (int64_t)L.zcol;
+        case MX_CTX_POFF: return (int64_t)L.poff;
+        default: return -1;
+    }
+}
+
+int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F, int32_t E) {
+    MlpDims d;
+    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return -1;
+    switch (which) {
+        case MX_WS_ZROW: return (int64_t)fwd_ws_layout(d).zr;
+        case MX_WS_DHROW: return (int64_t)bwd_ws_layout(d).dhr;
+        case MX_WS_DHCOL: return (int64_t)bwd_ws_layout(d).dhc;
+        default: return -1;
+    }
+}
+
+mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, int64_t M,
+                          int64_t H, int64_t F, const void* w1, const void* w2,
+                          const float* d_r, void* y, void* ctx, size_t ctx_bytes, void* ws,
+                          size_t ws_bytes, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!x || !d_offsets || !w1 || !w2 || !d_r || !y || !ctx || !ws)
+        return fail(MX_ERR_INVALID_ARG, "grouped_mlp_fwd: NULL argument");
+    MlpDims d;
+    mx_status st = check_mlp_dims(M, H, F, E, &d);
+    if (st != MX_OK) return st;
+    const CtxLayout C = ctx_layout(d);
+    const FwdWs W = fwd_ws_layout(d);
+    if (ctx_bytes < C.total)
+        return fail(MX_ERR_WORKSPACE, "grouped_mlp_fwd: ctx needs %zu bytes, got %zu", C.total,
+                    ctx_bytes);
+    if (ws_bytes < W.total)
+        return fail(MX_ERR_WORKSPACE, "grouped_mlp_fwd: ws needs %zu bytes, got %zu", W.total,
+                    ws_bytes);
+    if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(ctx, kAlign) ||
+        !aligned(ws, kAlign))
+        return fail(MX_ERR_INVALID_ARG,
+                    "grouped_mlp_fwd: tensors must be 16-byte and ctx/ws 256-byte aligned");
+    uint8_t* cb = static_cast<uint8_t*>(ctx);
+    uint8_t* wb = static_cast<uint8_t*>(ws);
+    int64_t* poff = reinterpret_cast<int64_t*>(cb + C.poff);
+    const int64_t M2 = 2 * F;
+    hipError_t e;
+
+    // (1) X: rowwise copy for the gate-up GEMM, token-axis copy saved for dW1
+    e = timed("padded_offsets", 16.0 * (E + 1), MX_WORK_BYTES, s,
+              [&] { return mx::launch_padded_offsets(d_offsets, E, poff, s); });
+    if (e != hipSuccess) return launched(e, "padded_offsets");
+    if (M > 0) {
+        e = timed("quant_tiles", quant_bytes(M, H, true, true), MX_WORK_BYTES, s, [&] {
+            return mx::launch_quant_tiles(static_cast<const uint16_t*>(x), 1, M, H, d_offsets,
+                                          poff, E, d.Mp, wb + W.xr, wb + W.xr_s, cb + C.xcol,
+                                          cb + C.xcol_s, d.Mp, s);
+        });
+        if (e != hipSuccess) return launched(e, "quant_tiles(x)");
+    }
+    // (2) weights: rowwise copies (blocks along H for W1, along F for W2)
+    e = timed("quant_rows", quant_bytes((int64_t)E * M2, H, true, false), MX_WORK_BYTES, s, [&] {
+        return mx::launch_quant_rows(static_cast<const uint16_t*>(w1), (int64_t)E * M2, H,
+                                     wb + W.w1r, wb + W.w1r_s, s);
+    });
+    if (e != hipSuccess) return launched(e, "quant_rows(w1)");
+    e = timed("quant_rows", quant_bytes((int64_t)E * H, F, true, false), MX_WORK_BYTES, s, [&] {
+        return mx::launch_quant_rows(static_cast<const uint16_t*>(w2), (int64_t)E * H, F,
+                                     wb + W.w2r, wb + W.w2r_s, s);
+    });
+    if (e != hipSuccess) return launched(e, "quant_rows(w2)");
+    if (M == 0) return ok();
+
+    // (3) gate-up GEMM with the SwiGLU / routing-scale / requantize epilogue
+    mx::GemmProblem p{};
+    p.kgroup = false;
+    p.offs = d_offsets;
+    p.G = E;
+    p.M = M; p.N = M2; p.K = H;
+    p.A = mx::MxOperand{wb + W.xr, wb + W.xr_s, H, 0};
+    p.B = mx::MxOperand{wb + W.w1r, wb + W.w1r_s, H, M2};
+    p.rscale = d_r;
+    p.F = F;
+    p.h = reinterpret_cast<uint16_t*>(cb + C.h);
+    p.qr = wb + W.zr; p.qrs = wb + W.zr_s; p.ldqr = F;
+    p.qc = cb + C.zcol; p.qcs = cb + C.zcol_s; p.ldqc = d.Mp;
+    p.poff = poff;
+    e = gemm(p, mx::Epi::kSwiglu, 2.0 * M * M2 * H, s);
+    if (e != hipSuccess) return launched(e, "mx_gemm(gate-up)");
+
+    // (4) down projection
+    mx::GemmProblem q{};
+    q.kgroup = false;
+    q.offs = d_offsets;
+    q.G = E;
+    q.M = M; q.N = H; q.K = F;
+    q.A = mx::MxOperand{wb + W.zr, wb + W.zr_s, F, 0};
+    q.B = mx::MxOperand{wb + W.w2r, wb + W.w2r_s, F, H};
+    q.C = y; q.ldc = H;
+    return launched(gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * F, s), "mx_gemm(down)");
+}
+
+mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, int64_t M,
+                          int64_t H, int64_t F, const void* w1, const void* w2,
+                          const float* d_r, const void* ctx, size_t ctx_bytes, void* dx,
+                          void* dw1, void* dw2, float* d_dr, void* ws, size_t ws_bytes,
+                          mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!dy || !d_offsets || !w1 || !w2 || !d_r || !ctx || !dx || !dw1 || !dw2 || !d_dr || !ws)
+        return fail(MX_ERR_INVALID_ARG, "grouped_mlp_bwd: NULL argument");
+    MlpDims d;
+    mx_status st = check_mlp_dims(M, H, F, E, &d);
+    if (st != MX_OK) return st;
+    const CtxLayout C = ctx_layout(d);
+    const BwdWs W = bwd_ws_layout(d);
+    if (ctx_bytes < C.total)
+        return fail(MX_ERR_WORKSPACE, "grouped_mlp_bwd: ctx needs %zu bytes, got %zu", C.total,
+                    ctx_bytes);
+    if (ws_bytes < W.total)
+        return fail(MX_ERR_WORKSPACE, "grouped_mlp_bwd: ws needs %zu bytes, got %zu", W.total,
+                    ws_bytes);
+    if (!aligned(dy, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(ctx, kAlign) ||
+        !aligned(ws, kAlign))
+        return fail(MX_ERR_INVALID_ARG,
+                    "grouped_mlp_bwd: tensors must be 16-byte and ctx/ws 256-byte aligned");
+    const uint8_t* cb = static_cast<const uint8_t*>(ctx);
+    uint8_t* wb = static_cast<uint8_t*>(ws);
+    const int64_t* poff = reinterpret_cast<const int64_t*>(cb + C.poff);
+    const int64_t M2 = 2 * F;
+    const int64_t nparts = dr_parts(F);
+    hipError_t e;
+
+    // (1) dY: rowwise for the data gradient, token-axis for dW2
+    if (M > 0) {
+        e = timed("quant_tiles", quant_bytes(M, H, true, true), MX_WORK_BYTES, s, [&] {
+            return mx::launch_quant_tiles(static_cast<const uint16_t*>(dy), 1, M, H, d_offsets,
+                                          poff, E, d.Mp, wb + W.dyr, wb + W.dyr_s, wb + W.dycol,
+                                          wb + W.dycol_s, d.Mp, s);
+        });
+        if (e != hipSuccess) return launched(e, "quant_tiles(dy)");
+    }
+    // (2) weights: columnwise copies (W2 blocks along H, W1 blocks along 2F)
+    e = timed("quant_tiles", quant_bytes((int64_t)E * H, F, false, true), MX_WORK_BYTES, s, [&] {
+        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w2), E, H, F, nullptr, nullptr,
+                                      1, 0, nullptr, nullptr, wb + W.w2c, wb + W.w2c_s, H, s);
+    });
+    if (e != hipSuccess) return launched(e, "quant_tiles(w2)");
+    e = timed("quant_tiles", quant_bytes((int64_t)E * M2, H, false, true), MX_WORK_BYTES, s, [&] {
+        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w1), E, M2, H, nullptr,
+                                      nullptr, 1, 0, nullptr, nullptr, wb + W.w1c, wb + W.w1c_s,
+                                      M2, s);
+    });
+    if (e != hipSuccess) return launched(e, "quant_tiles(w1)");
+
+    if (M > 0) {
+        // (3) dz = dY W2 with the SwiGLU-backward / dr / requantize epilogue
+        mx::GemmProblem p{};
+        p.kgroup = false;
+        p.offs = d_offsets;
+        p.G = E;
+        p.M = M; p.N = F; p.K = H;
+        p.A = mx::MxOperand{wb + W.dyr, wb + W.dyr_s, H, 0};
+        p.B = mx::MxOperand{wb + W.w2c, wb + W.w2c_s, H, F};
+        p.rscale = d_r;
+        p.F = F;
+        p.h = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(cb + C.h));
+        p.qr = wb + W.dhr; p.qrs = wb + W.dhr_s; p.ldqr = M2;
+        p.qc = wb + W.dhc; p.qcs = wb + W.dhc_s; p.ldqc = d.Mp;
+        p.poff = poff;
+        p.drp = reinterpret_cast<float*>(wb + W.drp); p.lddrp = nparts;
+        e = gemm(p, mx::Epi::kDSwiglu, 2.0 * M * F * H, s);
+        if (e != hipSuccess) return launched(e, "mx_gemm(dgrad-down)");
+        e = timed("dr_reduce", 4.0 * M * (nparts + 1), MX_WORK_BYTES, s, [&] {
+            return mx::launch_dr_reduce(reinterpret_cast<const float*>(wb + W.drp), M, nparts,
+                                        d_dr, s);
+        });
+        if (e != hipSuccess) return launched(e, "dr_reduce");
+
+        // (4) dX = dh W1
+        mx::GemmProblem q{};
+        q.kgroup = false;
+        q.offs = d_offsets;
+        q.G = E;
+        q.M = M; q.N = H; q.K = M2;
+        q.A = mx::MxOperand{wb + W.dhr, wb + W.dhr_s, M2, 0};
+        q.B = mx::MxOperand{wb + W.w1c, wb + W.w1c_s, M2, H};
+        q.C = dx; q.ldc = H;
+        e = gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * M2, s);
+        if (e != hipSuccess) return launched(e, "mx_gemm(dgrad-gate-up)");
+    }
+
+    // (5) weight gradients over each expert's padded token range
+    mx::GemmProblem w{};
+    w.kgroup = true;
+    w.offs = poff;
+    w.G = E;
+    w.M = H; w.N = F;
+    w.A = mx::MxOperand{wb + W.dycol, wb + W.dycol_s, d.Mp, 0};
+    w.B = mx::MxOperand{cb + C.zcol, cb + C.zcol_s, d.Mp, 0};
+    w.C = dw2; w.ldc = F; w.c_gstride = H * F;
+    e = gemm(w, mx::Epi::kStoreBf16, 2.0 * H * F * M, s);
+    if (e != hipSuccess) return launched(e, "mx_gemm(wgrad-down)");
+
+    mx::GemmProblem v{};
+    v.kgroup = true;
+    v.offs = poff;
+    v.G = E;
+    v.M = M2; v.N = H;
+    v.A = mx::MxOperand{wb + W.dhc, wb + W.dhc_s, d.Mp, 0};
+    v.B = mx::MxOperand{cb + C.xcol, cb + C.xcol_s, d.Mp, 0};
+    v.C = dw1; v.ldc = H; v.c_gstride = M2 * H;
+    return launched(gemm(v, mx::Epi::kStoreBf16, 2.0 * M2 * H * M, s), "mx_gemm(wgrad-gate-up)");
+}
+
+mx_status mx_profile_begin(int32_t capacity) {
+    if (capacity < 1 || capacity > (1 << 20))
+        return fail(MX_ERR_INVALID_ARG, "mx_profile_begin: capacity %d outside [1, 2^20]", capacity);
+    Profiler& P = g_prof;
+    P.release();
+    P.pool.resize((size_t)capacity * 2);
+    for (size_t i = 0; i < P.pool.size(); ++i) {
+        if (hipEventCreate(&P.pool[i]) != hipSuccess) {
+            P.pool.resize(i);
+            P.release();
+            return fail(MX_ERR_LAUNCH, "mx_profile_begin: hipEventCreate failed");
+        }
+    }
+    P.recs.reserve((size_t)capacity);
+    P.cap = capacity;
+    P.on = true;
+    return ok();
+}
+
+mx_status mx_profile_end(void) {
+    g_prof.on = false;
+    return ok();
+}
+
+int32_t mx_profile_count(void) { return (int32_t)g_prof.recs.size(); }
+
+mx_status mx_profile_get(int32_t i, const char** name, float* ms, double* work, int32_t* unit) {
+    Profiler& P = g_prof;
+    if (i < 0 || i >= (int32_t)P.recs.size())
+        return fail(MX_ERR_INVALID_ARG, "mx_profile_get: no record %d", i);
+    const ProfRec& r = P.recs[(size_t)i];
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+        return fail(MX_ERR_LAUNCH, "mx_profile_get: event query failed");
+    if (name) *name = r.name;
+    if (ms) *ms = t;
+    if (work) *work = r.work;
+    if (unit) *unit = r.unit;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,580 @@
+// Persistent grouped GEMM on gfx950 block-scaled FP8 MFMA
+// (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 operands, one E8M0 scale per 32
+// values along K on both sides).
+//
+// This one kernel body runs every GEMM of the MoE expert path (GroupedLinear:
+// all experts in one launch driven by per-expert token counts -- German page,
+// the paragraph on fragmented expert execution; the GroupedMLP forward and
+// backward with MXFP8 in both passes -- Portuguese page, third and fourth
+// paragraphs):
+//   * row-grouped  (forward and data gradients): group g owns output rows
+//     [off[g], off[g+1]) and its own B (expert weights); K is shared.
+//   * k-grouped    (weight gradients): group g contracts over its own padded
+//     token range [poff[g], poff[g+1]) and owns its own output matrix.
+// Both operands are K-major MXFP8 (codes [rows][ld], scales [rows][ld/32]);
+// the columnwise (transposed) copies make the data- and weight-gradient GEMMs
+// the same "A . B^T" form.
+//
+// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave
+// 128 x 128 = 8 x 8 MFMA blocks of 16 x 16 with fp32 accumulators; K step 128
+// (one MFMA deep).  Operand tiles are staged through LDS in two buffers with
+// one barrier per K step; 16-byte chunks of each 128-byte LDS row are XOR
+// swizzled by (row & 7) so the fragment reads of 8 neighbouring rows hit
+// distinct banks.  Global reads use buffer resources whose range check
+// returns zeros past the last valid row, which handles ragged expert tails
+// without branches.  The grid is persistent (one workgroup per CU); tiles are
+// walked in bands of 8 M-tiles so that the 32 tiles one XCD runs at a time
+// share 8 A panels and 4 B panels in that XCD's L2, and weight-gradient
+// groups run longest-K first.
+#include "internal.h"
+#include "mx_device.h"
+
+namespace mx {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 128, NTHREADS = 256;
+constexpr int BAND = 8;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, dword format
+
+struct GemmSmem {
+    uint8_t a[2][BM * BK];
+    uint8_t b[2][BN * BK];
+    uint32_t as[2][BM];
+    uint32_t bs[2][BN];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+    const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (int32_t)(bytes < 0 ? 0 : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcWord3);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Tile coordinates are wave-uniform but come from LDS reads; moving them to
+// scalar registers keeps buffer descriptors and LDS-DMA addresses scalar.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ float silu_sig(float a, float& sg) {
+    sg = 1.0f / (1.0f + expf(-a));
+    return a * sg;
+}
+
+// max over the 16 lanes that share (lane >> 4)
+__device__ __forceinline__ uint32_t max16(uint32_t m) {
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+    return m;
+}
+// max over the 4 lanes that share (lane & 15)
+__device__ __forceinline__ uint32_t max4q(uint32_t m) {
+    m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+    return m;
+}
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+
+// Quantize a 32 x 32 unit held as u[ii][jj][v] (ii, jj in {0,1}: 16 x 16
+// MFMA blocks; v: the lane's 4 rows) both rowwise (blocks along columns) and
+// columnwise (blocks along rows), storing codes and scales.
+//   row r(ii,v) = rbase + ii*16 + 4q + v, column c(jj) = cbase + jj*16 + r16.
+//   rowwise: codes at qr[r*ldqr + c], scale qrs[r*(ldqr/32) + cbase/32]
+//   columnwise: codes at qc[c*ldqc + pbase + ii*16 + 4q + v] (pbase = padded
+//   position of rbase), scale qcs[c*(ldqc/32) + pbase/32]
+struct QuantDst {
+    uint8_t* qr; uint8_t* qrs; int64_t ldqr;
+    uint8_t* qc; uint8_t* qcs; int64_t ldqc;
+};
+
+__device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int64_t rbase,
+                                           int64_t cbase, int64_t pbase,
+                                           int rows_valid, int rows_padded,
+                                           const QuantDst& d, int lane) {
+    const int r16 = lane & 15, q = lane >> 4;
+    // rowwise: per (ii, v) amax over the 32 columns (2 blocks x 16 lanes)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            uint32_t m = max(abs_bits(u[ii][0][v]), abs_bits(u[ii][1][v]));
+            m = max16(m);
+            const int rl = ii * 16 + 4 * q + v;       // row within the unit
+            const uint32_t sc = scale_code_from_amax_bits(m);
+            const float inv = inv_scale_from_code(sc);
+            if (rl < rows_valid) {
+                const int64_t r = rbase + rl;
+                uint8_t* dst = d.qr + r * d.ldqr + cbase + r16;
+                dst[0] = (uint8_t)e4m3_encode(u[ii][0][v], inv);
+                dst[16] = (uint8_t)e4m3_encode(u[ii][1][v], inv);
+                if (r16 == 0) d.qrs[r * (d.ldqr / 32) + cbase / 32] = (uint8_t)sc;
+            }
+        }
+    }
+    // columnwise: per jj amax over the 32 rows (2 blocks x 4 q-lanes x 4 v)
+    if (rows_padded <= 0) return;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) m = max(m, abs_bits(u[ii][jj][v]));
+        m = max4q(m);
+        const uint32_t sc = scale_code_from_amax_bits(m);
+        const float inv = inv_scale_from_code(sc);
+        const int64_t c = cbase + jj * 16 + r16;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            if (ii * 16 < rows_padded) {
+                const uint32_t w = e4m3_encode(u[ii][jj][0], inv) |
+                                   (e4m3_encode(u[ii][jj][1], inv) << 8) |
+                                   (e4m3_encode(u[ii][jj][2], inv) << 16) |
+                                   (e4m3_encode(u[ii][jj][3], inv) << 24);
+                *reinterpret_cast<uint32_t*>(d.qc + c * d.ldqc + pbase + ii * 16 + 4 * q) = w;
+            }
+        }
+        if (q == 0) d.qcs[c * (d.ldqc / 32) + pbase / 32] = (uint8_t)sc;
+    }
+}
+
+template <Epi EPI>
+__global__ void __launch_bounds__(NTHREADS, 1)
+mx_gemm_kernel(GemmProblem p) {
+    __shared__ GemmSmem sm;
+    __shared__ int s_prefix[kMaxGroups + 1];
+    __shared__ int s_perm[kMaxGroups];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int G = p.G;
+
+    // output columns per tile: the gate-up tile pairs 128 gate with 128 up
+    // rows of W1 and produces 128 columns of z
+    constexpr int TN_OUT = (EPI == Epi::kSwiglu) ? BN / 2 : BN;
+    const int64_t n_out = (EPI == Epi::kSwiglu) ? p.F : p.N;
+    const int ntn = (int)((n_out + TN_OUT - 1) / TN_OUT);
+    const int mtn_k = (int)((p.M + BM - 1) / BM);     // k-grouped: M tiles
+
+    // ---- tile table: prefix of tile counts per group (wave 0) ----
+    if (wave == 0) {
+        int cnt[16];
+        int local = 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int g = lane * 16 + u;
+            int c = 0;
+            if (g < G) {
+                if (p.kgroup) {
+                    c = mtn_k * ntn;
+                } else {
+                    const int64_t n = p.offs[g + 1] - p.offs[g];
+                    c = n > 0 ? (int)((n + BM - 1) / BM) * ntn : 0;
+                }
+            }
+            cnt[u] = c;
+            local += c;
+        }
+        int incl = local;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        int run = incl - local;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int g = lane * 16 + u;
+            if (g < G) {
+                s_prefix[g] = run;
+                run += cnt[u];
+            }
+        }
+        if (lane == 63) s_prefix[G] = incl;
+    }
+    if (p.kgroup) {
+        // longest contraction first (ties: lower group first)
+        for (int g = tid; g < G; g += NTHREADS) {
+            int rank = g;
+            if (G <= 256) {
+                const int64_t kg = p.offs[g + 1] - p.offs[g];
+                rank = 0;
+                for (int h = 0; h < G; ++h) {
+                    const int64_t kh = p.offs[h + 1] - p.offs[h];
+                    rank += (kh > kg) || (kh == kg && h < g);
+                }
+            }
+            s_perm[rank] = g;
+        }
+    }
+    __syncthreads();
+    const int total = s_prefix[G];
+
+    // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
+    // contiguous run of tiles per round.
+    const int grid = gridDim.x;
+    const int bid = blockIdx.x;
+    const int slot = (grid % 8 == 0) ? (bid % 8) * (grid / 8) + bid / 8 : bid;
+
+    const int swz = r16 & 7;
+
+    for (int t0 = 0; t0 < total; t0 += grid) {
+        const int t = t0 + slot;
+        if (t >= total) break;
+
+        // ---- locate the tile ----
+        int g;
+        int64_t m0, mvalid, n0, klo, K;
+        int local, mtiles;
+        if (p.kgroup) {
+            const int per = mtn_k * ntn;
+            const int gi = t / per;
+            g = s_perm[gi];
+            local = t - gi * per;
+            mtiles = mtn_k;
+        } else {
+            int lo = 0, hi = G - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_prefix[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            g = lo;
+            local = t - s_prefix[g];
+            mtiles = (s_prefix[g + 1] - s_prefix[g]) / ntn;
+        }
+        {
+            const int bandsz = BAND * ntn;
+            const int band = local / bandsz;
+            const int rem = local - band * bandsz;
+            const int bm = min(BAND, mtiles - band * BAND);
+            const int mt = band * BAND + rem % bm;
+            const int nt = rem / bm;
+            n0 = (int64_t)nt * TN_OUT;
+            if (p.kgroup) {
+                m0 = (int64_t)mt * BM;
+                mvalid = min((int64_t)BM, p.M - m0);
+                klo = p.offs[g];
+                K = p.offs[g + 1] - klo;
+            } else {
+                const int64_t lo_row = p.offs[g];
+                m0 = lo_row + (int64_t)mt * BM;
+                mvalid = min((int64_t)BM, p.offs[g + 1] - m0);
+                klo = 0;
+                K = p.K;
+            }
+        }
+        g = uni(g);
+        m0 = uni64(m0);
+        mvalid = uni64(mvalid);
+        n0 = uni64(n0);
+        klo = uni64(klo);
+        K = uni64(K);
+        const int nk = (int)(K / BK);
+
+        // ---- operand descriptors for this tile ----
+        // Range of each descriptor: the last valid row's K range ends the
+        // buffer, so rows past the valid ones read as zeros whether or not the
+        // scalar (K) offset takes part in the range check.
+        const int64_t lda = p.A.ld, ldb = p.B.ld;
+        const int64_t ldas = lda / 32, ldbs = ldb / 32;
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(p.A.codes + m0 * lda + klo, (mvalid - 1) * lda + K);
+        const __amdgpu_buffer_rsrc_t ras =
+            make_rsrc(p.A.scales + m0 * ldas + klo / 32, (mvalid - 1) * ldas + K / 32);
+        // B rows are addressed from brow0: the tile's first row, or for the
+        // gate-up tile the expert's first W1 row (gate and up halves are F
+        // rows apart)
+        const int64_t bg = p.kgroup ? 0 : (int64_t)g * p.B.gstride;
+        const int64_t brow0 = bg + ((EPI == Epi::kSwiglu) ? 0 : n0);
+        const int64_t bvalid = (EPI == Epi::kSwiglu) ? p.N : p.N - n0;
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(p.B.codes + brow0 * ldb + klo, (bvalid - 1) * ldb + K);
+        const __amdgpu_buffer_rsrc_t rbs =
+            make_rsrc(p.B.scales + brow0 * ldbs + klo / 32, (bvalid - 1) * ldbs + K / 32);
+
+        // B row (relative to brow0) staged at tile row b
+        auto brow = [&](int b) -> int64_t {
+            if constexpr (EPI == Epi::kSwiglu) {
+                const int wnb = b >> 7, half = (b >> 6) & 1, c = b & 63;
+                return half * p.F + n0 + wnb * 64 + c;
+            } else {
+                return b;
+            }
+        };
+        // Direct global->LDS loads: one instruction moves 64 lanes x 16 B =
+        // 8 tile rows into 1 KiB of LDS, lane l landing at byte 16*l.  Lane l
+        // therefore fetches row (l >> 3) of the 8 and the logical chunk that
+        // the swizzle places at physical chunk (l & 7).
+        const int dma_row = lane >> 3;
+        const int dma_chunk = (lane & 7) ^ (dma_row & 7);
+        uint32_t aoff[8], boff[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = (wave * 8 + j) * 8 + dma_row;
+            aoff[j] = (uint32_t)(r * lda + dma_chunk * 16);
+            boff[j] = (uint32_t)(brow(r) * ldb + dma_chunk * 16);
+        }
+        const uint32_t asoff = (uint32_t)((wave * 64 + lane) * ldas);
+        const uint32_t bsoff = (uint32_t)(brow(wave * 64 + lane) * ldbs);
+
+        v4f acc[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        auto issue = [&](int st, int ks) {
+            const uint32_t k0 = (uint32_t)ks * BK;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (lds_ptr_t)(&sm.a[st][(wave * 8 + j) * 1024]), 16, aoff[j], k0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (lds_ptr_t)(&sm.b[st][(wave * 8 + j) * 1024]), 16, boff[j], k0, 0, 0);
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr_t)(&sm.as[st][wave * 64]), 4,
+                                                     asoff, k0 / 32, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr_t)(&sm.bs[st][wave * 64]), 4,
+                                                     bsoff, k0 / 32, 0, 0);
+        };
+
+        if (nk > 0) issue(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        for (int ks = 0; ks < nk; ++ks) {
+            const int cur = ks & 1;
+            // ---- fragments of stage cur into registers ----
+            // The scaled 16x16x128 MFMA reads a lane's 32 operand bytes as
+            // two 16-byte runs of K, [16q, 16q+16) and [64+16q, 64+16q+16),
+            // and the scale byte of lane (r, q) as that of K block q of row r
+            // (pinned on the device by per-block scale probes).
+            v8i af[8], bfr[8];
+            int asc[8], bsc[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = wm * 128 + i * 16 + r16;
+                const uint8_t* base = &sm.a[cur][row * BK];
+                const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+                const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+                af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                asc[i] = reinterpret_cast<const uint8_t*>(sm.as[cur])[row * 4 + q];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = wn * 128 + j * 16 + r16;
+                const uint8_t* base = &sm.b[cur][row * BK];
+                const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+                const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+                bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[cur])[row * 4 + q];
+            }
+            // ---- next stage streams in while the MFMAs run ----
+            if (ks + 1 < nk) issue(cur ^ 1, ks + 1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        af[i], bfr[j], acc[i][j], 0, 0, 0, asc[i], 0, bsc[j]);
+            // keep the MFMAs ahead of the wait for the next stage
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+
+        // ---- epilogue ----
+        const int64_t rwave = m0 + wm * 128;          // first row of this wave
+        const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
+
+        if constexpr (EPI == Epi::kStoreBf16) {
+            uint16_t* C = reinterpret_cast<uint16_t*>(p.C) +
+                          (p.kgroup ? (int64_t)g * p.c_gstride : 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int rl = i * 16 + 4 * q + v;
+                    if (rl >= rows_valid_w) continue;
+                    const int64_t row = rwave + rl;
+                    const float sc = p.rscale ? p.rscale[row] : 1.0f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int64_t col = n0 + wn * 128 + j * 16 + r16;
+                        if (col < p.N) C[row * p.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][v] * sc);
+                    }
+                }
+            }
+        } else if constexpr (EPI == Epi::kSwiglu) {
+            // acc[i][j], j < 4: gate; acc[i][j+4]: up, same output column
+            const int64_t F = p.F;
+            const int64_t glo = p.offs[g];
+            const int64_t prow = p.poff[g] + (rwave - glo);       // padded position
+            const int64_t npad = p.poff[g + 1] - p.poff[g];
+            const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
+            const QuantDst d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc};
+            const int64_t cw = n0 + wn * 64;                       // wave's first z column
+#pragma unroll
+            for (int ip = 0; ip < 4; ++ip) {
+                float rr[2][4];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int rl = (2 * ip + ii) * 16 + 4 * q + v;
+                        rr[ii][v] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                    }
+#pragma unroll
+                for (int jp = 0; jp < 2; ++jp) {
+                    float z[2][2][4];
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const int i = 2 * ip + ii, j = 2 * jp + jj;
+                            const int64_t col = cw + j * 16 + r16;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const float a = acc[i][j][v], b = acc[i][j + 4][v];
+                                const int rl = i * 16 + 4 * q + v;
+                                if (rl < rows_valid_w) {
+                                    uint16_t* hr = p.h + (rwave + rl) * 2 * F;
+                                    hr[col] = (uint16_t)f32_to_bf16(a);
+                                    hr[F + col] = (uint16_t)f32_to_bf16(b);
+                                }
+                                float sg;
+                                const float s = silu_sig(a, sg) * b;
+                                z[ii][jj][v] = rr[ii][v] * s;
+                            }
+                        }
+                    quant_unit(z, rwave + 2 * ip * 16, cw + 2 * jp * 16,
+                               prow + 2 * ip * 16, rows_valid_w - 2 * ip * 16,
+                               rows_pad_w - 2 * ip * 16, d, lane);
+                }
+            }
+        } else {   // kDSwiglu
+            const int64_t F = p.F;
+            const int64_t glo = p.offs[g];
+            const int64_t prow = p.poff[g] + (rwave - glo);
+            const int64_t npad = p.poff[g + 1] - p.poff[g];
+            const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
+            const QuantDst dA{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc};
+            const int64_t cw = n0 + wn * 128;
+            const int part = (int)(n0 / BN) * 2 + wn;
+#pragma unroll
+            for (int ip = 0; ip < 4; ++ip) {
+                float rr[2][4], drs[2][4];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int rl = (2 * ip + ii) * 16 + 4 * q + v;
+                        rr[ii][v] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                        drs[ii][v] = 0.0f;
+                    }
+#pragma unroll
+                for (int jp = 0; jp < 4; ++jp) {
+                    float da[2][2][4], db[2][2][4];
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const int i = 2 * ip + ii, j = 2 * jp + jj;
+                            const int64_t col = cw + j * 16 + r16;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int rl = i * 16 + 4 * q + v;
+                                float ga = 0.f, gb = 0.f;
+                                if (rl < rows_valid_w && col < F) {
+                                    const uint16_t* hr = p.h + (rwave + rl) * 2 * F;
+                                    const float a = bf16_to_f32(hr[col]);
+                                    const float b = bf16_to_f32(hr[F + col]);
+                                    const float dz = acc[i][j][v];
+                                    float sg;
+                                    const float sl = silu_sig(a, sg);
+                                    drs[ii][v] += dz * (sl * b);
+                                    const float ds = rr[ii][v] * dz;
+                                    ga = ds * b * sg * (1.0f + a * (1.0f - sg));
+                                    gb = ds * sl;
+                                }
+                                da[ii][jj][v] = ga;
+                                db[ii][jj][v] = gb;
+                            }
+                        }
+                    const int64_t cbase = cw + 2 * jp * 16;
+                    if (cbase < F) {
+                        quant_unit(da, rwave + 2 * ip * 16, cbase, prow + 2 * ip * 16,
+                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, dA, lane);
+                        quant_unit(db, rwave + 2 * ip * 16, F + cbase, prow + 2 * ip * 16,
+                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, dA, lane);
+                    }
+                }
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float s = sum16(drs[ii][v]);
+                        const int rl = (2 * ip + ii) * 16 + 4 * q + v;
+                        if (r16 == 0 && rl < rows_valid_w)
+                            p.drp[(rwave + rl) * p.lddrp + part] = s;
+                    }
+            }
+        }
+        // the next tile's first LDS write must not overtake slow readers
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(256)
+dr_reduce_kernel(const float* __restrict__ drp, int64_t M, int64_t nparts,
+                 float* __restrict__ dr) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M) return;
+    float s = 0.f;
+    for (int64_t j = 0; j < nparts; ++j) s += drp[i * nparts + j];
+    dr[i] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s) {
+    int grid = device_cu_count();
+    grid = grid < 8 ? 8 : grid / 8 * 8;
+    switch (epi) {
+        case Epi::kStoreBf16:
+            hipLaunchKernelGGL(mx_gemm_kernel<Epi::kStoreBf16>, dim3(grid), dim3(NTHREADS), 0, s, p);
+            break;
+        case Epi::kSwiglu:
+            hipLaunchKernelGGL(mx_gemm_kernel<Epi::kSwiglu>, dim3(grid), dim3(NTHREADS), 0, s, p);
+            break;
+        case Epi::kDSwiglu:
+            hipLaunchKernelGGL(mx_gemm_kernel<Epi::kDSwiglu>, dim3(grid), dim3(NTHREADS), 0, s, p);
+            break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dr_reduce(const float* drp, int64_t M, int64_t nparts,
+                            float* dr, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    hipLaunchKernelGGL(dr_reduce_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
+                       drp, M, nparts, dr);
+    return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,79 @@
+// Internal launchers shared by the kernel files and the C-ABI layer.  Every
+// launcher enqueues on `stream`, returns the hipError_t of the launch, and
+// assumes the C-ABI layer has validated its arguments.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+constexpr int kTokenAlign = 128;   // padding of token groups in columnwise copies
+constexpr int kMaxGroups = 1024;   // largest expert count the kernels accept
+
+// ---- quantizer --------------------------------------------------------------
+// Padded offsets of token groups: poff[g] = sum_{j<g} ceil(n_j/128)*128.
+hipError_t launch_padded_offsets(const int64_t* offs, int G, int64_t* poff,
+                                 hipStream_t s);
+// Rowwise copy only, over a flat [rows][C] tensor.
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t C,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Tile pass: rowwise (optional) and columnwise (optional) copies of
+// x[batch][R][C].  Grouped mode (offs != nullptr, batch == 1) needs poff
+// already computed; row_bound is the padded-length bound (multiple of 128).
+hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
+                              int64_t C, const int64_t* offs,
+                              const int64_t* poff, int G, int64_t row_bound,
+                              uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                              uint8_t* cs, int64_t ld, hipStream_t s);
+
+// ---- grouped GEMMs ------------------------------------------------------------
+// Operand of a K-major MXFP8 GEMM: codes [rows][ld], scales [rows][ld/32].
+struct MxOperand {
+    const uint8_t* codes;
+    const uint8_t* scales;
+    int64_t ld;          // bytes between rows of codes (scales: ld/32)
+    int64_t gstride;     // rows between consecutive groups (0: shared)
+};
+
+enum class Epi : int {
+    kStoreBf16 = 0,   // C = acc (* row scale) -> bf16
+    kSwiglu = 1,      // gate-up: h -> bf16, z = r silu(a) b -> MXFP8 row+col
+    kDSwiglu = 2,     // dz -> dr partials, dh = [da|db] -> MXFP8 row+col
+};
+
+struct GemmProblem {
+    // row-grouped (fprop/dgrad): groups split M via offs; B of group g at
+    //   rows g*gstride.  k-grouped (wgrad): groups split K via offs; C of
+    //   group g at c + g*c_gstride; A and B shared.
+    bool kgroup;
+    const int64_t* offs;
+    int G;
+    int64_t M, N, K;            // K unused when kgroup
+    MxOperand A, B;
+    void* C;                    // bf16
+    int64_t ldc, c_gstride;
+    const float* rscale;        // kStoreBf16 and fused: per-row routing weight
+    // fused epilogues
+    int64_t F;
+    uint16_t* h;                // kSwiglu writes, kDSwiglu reads: bf16 [M][2F]
+    uint8_t* qr; uint8_t* qrs; int64_t ldqr;   // rowwise MXFP8 output
+    uint8_t* qc; uint8_t* qcs; int64_t ldqc;   // columnwise MXFP8 output
+    const int64_t* poff;        // padded token offsets of the column copy
+    float* drp; int64_t lddrp;  // kDSwiglu: dr partials [M][lddrp]
+};
+
+hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s);
+
+// Sum of dr partials: dr[i] = sum_j drp[i][j], j ascending.
+hipError_t launch_dr_reduce(const float* drp, int64_t M, int64_t nparts,
+                            float* dr, hipStream_t s);
+
+// BF16 grouped GEMM (row-grouped): y = x w_e^T (* rscale).
+hipError_t launch_bf16_grouped(const uint16_t* x, const int64_t* offs, int G,
+                               int64_t M, const uint16_t* w, int64_t N,
+                               int64_t K, const float* rscale, uint16_t* y,
+                               hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace mx

@@ -1,0 +1,208 @@
+// MXFP8 block quantizer for gfx950: bf16 -> E4M3 codes + E8M0 scales, one
+// scale per 32 values (the MXFP8 paragraphs of the German page and of the
+// Portuguese page's third paragraph).  Memory-bound: each element is read
+// once (2 bytes) and written once or twice (1 byte + 1/32 byte per copy).
+//
+// Two kernels:
+//  * quant_rows_kernel  -- flat rowwise copy.  A lane converts 16 contiguous
+//    values (two 16-byte loads); two neighbouring lanes hold one 32-block and
+//    combine their amax with one lane swap.  Codes leave as one 16-byte store
+//    per lane, so a wave moves 2 KiB in and 1 KiB out contiguously.
+//  * quant_tiles_kernel -- 128-row x 64-column tile per workgroup producing
+//    the rowwise copy (from registers) and the columnwise copy (through LDS)
+//    from one read of the input.  The columnwise copy is transposed
+//    ([C][ld], blocks of 32 rows); row groups (experts) start new blocks and
+//    are padded with zero codes to a multiple of 128 rows, so every tile lies
+//    inside one group.
+#include "internal.h"
+#include "mx_device.h"
+
+namespace mx {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (the source is read exactly once)
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void unpack8(const uint4& u, float* v) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ uint4 encode16(const float* v, float inv) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = e4m3_encode(v[4 * i], inv) | (e4m3_encode(v[4 * i + 1], inv) << 8) |
+               (e4m3_encode(v[4 * i + 2], inv) << 16) |
+               (e4m3_encode(v[4 * i + 3], inv) << 24);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ void __launch_bounds__(1024)
+padded_offsets_kernel(const int64_t* __restrict__ offs, int G,
+                      int64_t* __restrict__ poff) {
+    __shared__ int64_t s[1024];
+    const int t = threadIdx.x;
+    int64_t v = 0;
+    if (t < G) {
+        int64_t n = offs[t + 1] - offs[t];
+        n = n < 0 ? 0 : n;
+        v = (n + kTokenAlign - 1) / kTokenAlign * kTokenAlign;
+    }
+    s[t] = v;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {       // inclusive Hillis-Steele scan
+        int64_t add = t >= d ? s[t - d] : 0;
+        __syncthreads();
+        s[t] += add;
+        __syncthreads();
+    }
+    if (t == 0) poff[0] = 0;
+    if (t < G) poff[t + 1] = s[t];
+}
+
+__global__ void __launch_bounds__(256)
+quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nchunk,
+                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunk; i += stride) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + i * 16);
+        uint4 a = load_stream(src);
+        uint4 b = load_stream(src + 1);
+        float v[16];
+        unpack8(a, v);
+        unpack8(b, v + 8);
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m = max(m, abs_bits(v[j]));
+        // chunks 2k and 2k+1 (one 32-block) sit in neighbouring lanes
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        const uint32_t sc = scale_code_from_amax_bits(m);
+        const float inv = inv_scale_from_code(sc);
+        reinterpret_cast<uint4*>(codes)[i] = encode16(v, inv);
+        if (!(i & 1)) scales[i >> 1] = (uint8_t)sc;
+    }
+}
+
+__global__ void __launch_bounds__(256)
+quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                   const int64_t* __restrict__ offs,
+                   const int64_t* __restrict__ poff, int G,
+                   uint8_t* __restrict__ rc, uint8_t* __restrict__ rs,
+                   uint8_t* __restrict__ cc, uint8_t* __restrict__ cs,
+                   int64_t ld) {
+    __shared__ float tile[128][65];
+    const int64_t b = blockIdx.z;
+    const int64_t p0 = (int64_t)blockIdx.y * 128;   // start in the padded axis
+    int64_t src0, valid;
+    if (offs) {
+        if (p0 >= poff[G]) return;
+        // last group g < G with poff[g] <= p0 (skips empty groups)
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
+        }
+        src0 = offs[lo] + (p0 - poff[lo]);
+        valid = offs[lo + 1] - src0;
+    } else {
+        src0 = p0;
+        valid = R - p0;
+    }
+    valid = valid < 0 ? 0 : (valid > 128 ? 128 : valid);
+
+    const int t = threadIdx.x;
+    const int row = t >> 1, half = t & 1;
+    const int64_t col0 = (int64_t)blockIdx.x * 64;
+    const int64_t cseg = col0 + half * 32;           // this lane's 32 columns
+    const bool live = row < valid && cseg < C;
+
+    float v[32];
+    if (live) {
+        const uint4* src = reinterpret_cast<const uint4*>(
+            x + (b * R + src0 + row) * C + cseg);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) unpack8(load_stream(src + q), v + 8 * q);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = 0.0f;
+    }
+
+    if (rc && live) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) m = max(m, abs_bits(v[j]));
+        const uint32_t sc = scale_code_from_amax_bits(m);
+        const float inv = inv_scale_from_code(sc);
+        uint4* dst = reinterpret_cast<uint4*>(rc + (b * R + src0 + row) * C + cseg);
+        dst[0] = encode16(v, inv);
+        dst[1] = encode16(v + 16, inv);
+        rs[(b * R + src0 + row) * (C / 32) + cseg / 32] = (uint8_t)sc;
+    }
+    if (!cc) return;
+
+#pragma unroll
+    for (int j = 0; j < 32; ++j) tile[row][half * 32 + j] = v[j];
+    __syncthreads();
+
+    const int col = t >> 2, blk = t & 3;
+    if (col0 + col >= C) return;
+    float w[32];
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        w[i] = tile[blk * 32 + i][col];
+        m = max(m, abs_bits(w[i]));
+    }
+    const uint32_t sc = scale_code_from_amax_bits(m);
+    const float inv = inv_scale_from_code(sc);
+    uint4* dst = reinterpret_cast<uint4*>(cc + (b * C + col0 + col) * ld + p0 + blk * 32);
+    dst[0] = encode16(w, inv);
+    dst[1] = encode16(w + 16, inv);
+    cs[(b * C + col0 + col) * (ld / 32) + p0 / 32 + blk] = (uint8_t)sc;
+}
+
+}  // namespace
+
+hipError_t launch_padded_offsets(const int64_t* offs, int G, int64_t* poff,
+                                 hipStream_t s) {
+    hipLaunchKernelGGL(padded_offsets_kernel, dim3(1), dim3(1024), 0, s, offs, G, poff);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t C,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+    const int64_t nchunk = rows * C / 16;
+    if (nchunk == 0) return hipSuccess;
+    int64_t blocks = (nchunk + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 16;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       x, nchunk, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
+                              int64_t C, const int64_t* offs,
+                              const int64_t* poff, int G, int64_t row_bound,
+                              uint8_t* rc, uint8_t* rs, uint8_t* cc,
+                              uint8_t* cs, int64_t ld, hipStream_t s) {
+    const int64_t ytiles = offs ? row_bound / 128 : (R + 127) / 128;
+    if (ytiles == 0 || C == 0 || batch == 0) return hipSuccess;
+    dim3 grid((unsigned)((C + 63) / 64), (unsigned)ytiles, (unsigned)batch);
+    hipLaunchKernelGGL(quant_tiles_kernel, grid, dim3(256), 0, s, x, R, C, offs,
+                       poff, G, rc, rs, cc, cs, ld);
+    return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,231 @@
+/*
+ * mxmoe.h -- C ABI of the MXFP8 MoE expert path for AMD MI355X (gfx950).
+ *
+ * The operations come from the tutorial on MoE training of biological
+ * foundation models (BioNeMo MoE recipe with Transformer Engine), as retold by
+ * "MoE-Training fuer biologische Grundmodelle optimieren" (hyper.ai, German),
+ * "NVIDIA apresenta tecnicas para tornar mais eficiente o treinamento de
+ * modelos biologicos baseados em arquitetura MoE" (conexaotc, Portuguese) and
+ * "NVIDIA optimise l'entrainement MoE des modeles biologiques" (hyper.ai,
+ * French):
+ *   - GroupedLinear: the linear layers of all experts run in one call that is
+ *     handed the number of tokens routed to each expert (German page, the
+ *     paragraph on fragmented expert execution; Portuguese page, third
+ *     paragraph; French page, first improvement).
+ *   - MXFP8: 8 bits per value plus one scale per block of 32 values, with
+ *     16-bit master weights and activations (German page, the paragraph on
+ *     activation memory; Portuguese page, third paragraph; French page,
+ *     second improvement).  Elements are OCP E4M3 (largest finite 448), scales
+ *     E8M0; the scale of a block is 2^(floor(log2(amax)) - 8), elements are
+ *     rounded to nearest even and saturate at +-448.
+ *   - GroupedMLP: gate-up projection, SwiGLU scaled by the routing weight and
+ *     the quantization fused into one forward and one backward pass whose
+ *     intermediates are not materialised as separate tensors (German page, the
+ *     paragraph on the third bottleneck; Portuguese page, third paragraph;
+ *     French page, third improvement).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers named d_* and every tensor pointer are DEVICE pointers on
+ *     the current HIP device.  Sizes are host scalars.  The library never
+ *     allocates, frees or synchronises: every call enqueues kernels on
+ *     `stream` and returns.  The caller owns every buffer.
+ *   - Rows are token-sorted: expert e owns rows [off[e], off[e+1]) of every
+ *     [M, *] tensor; d_offsets is int64 [E+1] with off[0] = 0, off[E] = M,
+ *     non-decreasing (not checked on the device).  Experts may be empty.
+ *   - bf16 tensors are row-major with contiguous rows.  An MXFP8 tensor is a
+ *     pair: codes (uint8 E4M3, same shape as the source, blocks of 32 along the
+ *     last axis) and scales (uint8 E8M0, one per block, [rows][cols/32]).
+ *   - A "columnwise" copy of X[R, C] is stored transposed: codes [C][ld] and
+ *     scales [C][ld/32], blocks of 32 consecutive rows of X.  When X has row
+ *     groups (experts), each group's rows start a new block and the group is
+ *     padded with zero codes to a multiple of MX_TOKEN_ALIGN (128) rows; the
+ *     start of group g in the padded axis is written to d_padded_offsets[g].
+ *   - Errors: host-side validation returns a status and never touches the
+ *     device; mx_last_error() gives the thread's last message.  Kernel launch
+ *     failures return MX_ERR_LAUNCH.  Device-side contract violations (bad
+ *     offsets) are undefined behaviour.
+ *   - Every call is re-entrant; calls on one stream are ordered.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* mx_stream_t; /* same type as hipStream_t */
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad combination */
+    MX_ERR_UNSUPPORTED = 2,  /* size not a multiple the kernels need */
+    MX_ERR_WORKSPACE = 3,    /* ctx or workspace smaller than required */
+    MX_ERR_LAUNCH = 4        /* a HIP launch or query failed */
+} mx_status;
+
+enum { MX_DTYPE_BF16 = 0, MX_DTYPE_MXFP8 = 1 };
+enum { MX_TOKEN_ALIGN = 128, MX_BLOCK = 32 };
+
+/* Last error message of the calling thread ("" if none).  Never NULL. */
+const char* mx_last_error(void);
+
+/* Library version string. */
+const char* mx_version(void);
+
+/* Upper bound of the padded length of G row groups holding M rows in total,
+ * each padded to a multiple of `align`: the leading dimension the caller
+ * allocates for a grouped columnwise copy.  Returns -1 on bad arguments. */
+int64_t mx_padded_rows_bound(int64_t M, int32_t G, int32_t align);
+
+/*
+ * mxfp8_quantize -- block-quantize bf16 to MXFP8 (the MXFP8 paragraphs cited
+ * above: 8-bit values, one scale per 32 values).
+ *
+ *   x            bf16 [batch][R][C], C % 32 == 0.
+ *   row_codes    uint8 [batch][R][C] and row_scales [batch][R][C/32]: the
+ *                rowwise copy (blocks along C).  Both NULL to skip.
+ *   d_offsets    int64 [G+1] row groups of the columnwise copy (batch must be
+ *                1), or NULL: each batch item is one group of R rows.
+ *   col_codes    uint8 [batch][C][col_ld], col_scales [batch][C][col_ld/32]:
+ *                the columnwise copy (blocks along R, restarting at every
+ *                group, groups padded to MX_TOKEN_ALIGN with zero codes).
+ *                Both NULL to skip.  col_ld % 128 == 0 and col_ld must be at
+ *                least mx_padded_rows_bound(R, G, 128) (G = 1 if no groups).
+ *                Columns past the last group's padded end are not written.
+ *   d_padded_offsets  int64 [G+1], written (device) when col_codes is given
+ *                with d_offsets; may be NULL otherwise.
+ * At least one of the two copies must be requested.
+ */
+mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
+                         uint8_t* row_codes, uint8_t* row_scales,
+                         const int64_t* d_offsets, int32_t G,
+                         uint8_t* col_codes, uint8_t* col_scales,
+                         int64_t col_ld, int64_t* d_padded_offsets,
+                         mx_stream_t stream);
+
+/*
+ * grouped_linear_fwd -- GroupedLinear: for every expert e in ONE launch,
+ *   Y[off[e]:off[e+1]] = X[off[e]:off[e+1]] . W[e]^T   (times r[row] if given)
+ * (German page, the paragraph on fragmented expert execution; French page,
+ * first improvement).  Accumulation in fp32, output rounded to bf16 (RNE).
+ *
+ *   dtype MX_DTYPE_BF16:  x bf16 [M][K], w bf16 [E][N][K]; x_scales, w_scales
+ *                         must be NULL.  K % 32 == 0, N % 16 == 0.
+ *   dtype MX_DTYPE_MXFP8: x = E4M3 codes [M][K] with x_scales [M][K/32];
+ *                         w = codes [E][N][K] with w_scales [E][N][K/32]
+ *                         (rowwise copies from mxfp8_quantize).
+ *                         K % 128 == 0, N % 32 == 0.
+ *   d_row_scale  fp32 [M] routing weight applied to each output row, or NULL.
+ *   y            bf16 [M][N].
+ */
+mx_status grouped_linear_fwd(int32_t dtype, const void* x,
+                             const uint8_t* x_scales, const int64_t* d_offsets,
+                             int32_t E, int64_t M, const void* w,
+                             const uint8_t* w_scales, int64_t N, int64_t K,
+                             const float* d_row_scale, void* y,
+                             mx_stream_t stream);
+
+/*
+ * grouped_mlp_fwd -- fused GroupedMLP forward (German page, the paragraph on
+ * the GroupedMLP fusion kernel; Portuguese page, third paragraph; French page,
+ * third improvement), in the order gate-up projection -> SwiGLU -> routing
+ * weight scale -> down projection:
+ *   h = Q(X_e) . Q(W1_e)^T          [rows of e, 2F]   (blocks along H)
+ *   z = r * silu(h[:, :F]) * h[:, F:]                  (fp32, on chip)
+ *   Y_e = Q(z) . Q(W2_e)^T          [rows of e, H]    (blocks along F)
+ *
+ *   x    bf16 [M][H];  w1 bf16 [E][2F][H] (rows [0,F) gate, [F,2F) up);
+ *   w2   bf16 [E][H][F];  d_r fp32 [M];  y bf16 [M][H].
+ *   ctx  saved-for-backward buffer of grouped_mlp_ctx_bytes() bytes, written
+ *        here and read by grouped_mlp_bwd (opaque; 256-byte aligned).
+ *   ws   scratch of grouped_mlp_fwd_ws_bytes() bytes (256-byte aligned).
+ * H % 128 == 0, F % 128 == 0, E in [1, 1024].
+ */
+mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E,
+                          int64_t M, int64_t H, int64_t F, const void* w1,
+                          const void* w2, const float* d_r, void* y,
+                          void* ctx, size_t ctx_bytes, void* ws,
+                          size_t ws_bytes, mx_stream_t stream);
+
+/*
+ * grouped_mlp_bwd -- fused GroupedMLP backward with MXFP8 operands in every
+ * GEMM (Portuguese page, fourth paragraph: MXFP8 active in forward and
+ * backward).  Straight-through quantizers; each GEMM quantizes its operands
+ * along its own contraction axis: rowwise copies feed the data gradients,
+ * columnwise (token-axis) copies the weight gradients.
+ *   dz  = Q(dY_e) . Q(W2_e)          (blocks along H)
+ *   dr  = sum_f dz * s,  s = silu(a) * b, (a, b) = h saved by the forward
+ *   dh  = [r dz b silu'(a) | r dz silu(a)]
+ *   dX  = Q(dh) . Q(W1_e)            (blocks along 2F)
+ *   dW2_e = Q_tok(dY_e)^T . Q_tok(z_e),  dW1_e = Q_tok(dh_e)^T . Q_tok(X_e)
+ * Experts with no rows get dW1_e = dW2_e = 0.
+ *
+ *   dy bf16 [M][H]; outputs dx bf16 [M][H], dw1 bf16 [E][2F][H],
+ *   dw2 bf16 [E][H][F], d_dr fp32 [M].  Same sizes, x-free: the forward's
+ *   ctx holds what is needed.  ws of grouped_mlp_bwd_ws_bytes() bytes.
+ */
+mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E,
+                          int64_t M, int64_t H, int64_t F, const void* w1,
+                          const void* w2, const float* d_r, const void* ctx,
+                          size_t ctx_bytes, void* dx, void* dw1, void* dw2,
+                          float* d_dr, void* ws, size_t ws_bytes,
+                          mx_stream_t stream);
+
+/* Byte sizes of the buffers above (0 on bad arguments). */
+size_t grouped_mlp_ctx_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
+size_t grouped_mlp_fwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
+size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
+
+/*
+ * Views into a forward ctx, for inspection and tests (offsets in bytes from
+ * the ctx base; all regions 256-byte aligned):
+ *   MX_CTX_H        bf16 [M][2F]  gate-up pre-activation h (RNE of fp32)
+ *   MX_CTX_XCOL     X columnwise codes [H][Mp] then scales [H][Mp/32]
+ *   MX_CTX_ZCOL     z columnwise codes [F][Mp] then scales [F][Mp/32]
+ *   MX_CTX_POFF     int64 [E+1] padded token offsets
+ * with Mp = mx_padded_rows_bound(M, E, 128).  In every codes-then-scales
+ * pair here and below, the scales start at the first 256-byte boundary after
+ * the last code byte.  Returns -1 on bad arguments.
+ */
+enum { MX_CTX_H = 0, MX_CTX_XCOL = 1, MX_CTX_ZCOL = 2, MX_CTX_POFF = 3 };
+int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F,
+                               int32_t E);
+
+/*
+ * Views into the forward/backward workspaces, for tests: the rowwise z
+ * (codes [M][F] + scales [M][F/32]) the forward fed its down projection, and
+ * the rowwise and columnwise dh of the backward (codes [M][2F] + scales;
+ * columnwise codes [2F][Mp] + scales).  Returns -1 on bad arguments.
+ */
+enum { MX_WS_ZROW = 0, MX_WS_DHROW = 1, MX_WS_DHCOL = 2 };
+int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F,
+                              int32_t E);
+
+/*
+ * Launch timing (diagnostics; not part of the computation).  Between
+ * mx_profile_begin() and mx_profile_end(), every kernel the library launches
+ * from the calling thread is bracketed by two HIP events recorded on the
+ * launch's stream, up to `capacity` launches (later launches are not timed).
+ * Each record carries the kernel's name and its algorithmic work: floating
+ * point operations for GEMMs (2*M*N*K summed over experts), bytes moved for
+ * memory-bound kernels.  The events are created by mx_profile_begin (the only
+ * call here that allocates) and destroyed by the next mx_profile_begin.
+ *   mx_profile_count  number of records of the last begin/end window.
+ *   mx_profile_get    waits for record i's events, then returns its name
+ *                     (static string), milliseconds, work and unit
+ *                     (MX_WORK_FLOP or MX_WORK_BYTES).
+ */
+enum { MX_WORK_FLOP = 0, MX_WORK_BYTES = 1 };
+mx_status mx_profile_begin(int32_t capacity);
+mx_status mx_profile_end(void);
+int32_t mx_profile_count(void);
+mx_status mx_profile_get(int32_t i, const char** name, float* ms, double* work,
+                         int32_t* unit);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXMOE_H */

@@ -1,0 +1,158 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+the header declares, and rejects bad arguments with the documented status
+before touching the device (no GPU needed: no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxmoe.h")
+
+MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x7f0000001000)       # never dereferenced: validation fails first
+FAKE2 = ctypes.c_void_p(0x7f0000002000)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*?[\s*]+(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for fn in ("mxfp8_quantize", "grouped_linear_fwd", "grouped_mlp_fwd", "grouped_mlp_bwd"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_function(mxlib):
+    missing = [n for n in declared_functions() if not hasattr(mxlib, n)]
+    assert not missing, missing
+
+
+def test_version_and_empty_error(mxlib):
+    assert b"gfx950" in mxlib.mx_version()
+    assert mxlib.mx_last_error() is not None
+
+
+def test_padded_rows_bound_closed_form(mxlib):
+    f = mxlib.mx_padded_rows_bound
+    # sum ceil(n_e/a)*a <= M + G(a-1), rounded down to a multiple of a
+    assert f(0, 1, 128) == 0
+    assert f(1, 1, 128) == 128
+    assert f(128, 1, 128) == 128
+    assert f(129, 1, 128) == 256
+    assert f(32768, 8, 128) == (32768 + 8 * 127) // 128 * 128
+    assert f(-1, 1, 128) == -1 and f(5, 0, 128) == -1
+
+
+def test_padded_bound_dominates_every_split(mxlib):
+    import numpy as np
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        G = int(rng.integers(1, 70))
+        counts = rng.integers(0, 400, G)
+        M = int(counts.sum())
+        padded = int(((counts + 127) // 128 * 128).sum())
+        assert padded <= mxlib.mx_padded_rows_bound(M, G, 128)
+
+
+def test_mlp_sizes(mxlib):
+    M, H, F, E = 32768, 4096, 14336, 8
+    ctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
+    Mp = mxlib.mx_padded_rows_bound(M, E, 128)
+    # h (bf16 [M,2F]) + X and z token-axis copies + scales + padded offsets
+    need = M * 2 * F * 2 + (H + F) * Mp * (1 + 1 / 32)
+    assert need <= ctx <= need + 64 * 256
+    assert mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E) > 0
+    assert mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E) > 0
+    for which in range(4):
+        off = mxlib.grouped_mlp_ctx_offset(which, M, H, F, E)
+        assert 0 <= off < ctx and off % 256 == 0
+    assert mxlib.grouped_mlp_ctx_offset(9, M, H, F, E) == -1
+    # unsupported sizes give 0 / -1
+    assert mxlib.grouped_mlp_ctx_bytes(M, 4000, F, E) == 0
+    assert mxlib.grouped_mlp_ctx_bytes(M, H, F, 0) == 0
+    assert mxlib.grouped_mlp_ctx_offset(0, M, H, 100, E) == -1
+
+
+def _err(mxlib):
+    return mxlib.mx_last_error().decode()
+
+
+def test_quantize_rejects_bad_arguments(mxlib):
+    q = mxlib.mxfp8_quantize
+    # NULL input
+    assert q(None, 1, 64, 64, FAKE, FAKE2, None, 1, None, None, 0, None, None) == MX_ERR_INVALID_ARG
+    assert "NULL" in _err(mxlib)
+    # C not a multiple of 32
+    assert q(FAKE, 1, 64, 48, FAKE, FAKE2, None, 1, None, None, 0, None, None) == MX_ERR_UNSUPPORTED
+    # no output requested
+    assert q(FAKE, 1, 64, 64, None, None, None, 1, None, None, 0, None, None) == MX_ERR_INVALID_ARG
+    # codes without scales
+    assert q(FAKE, 1, 64, 64, FAKE, None, None, 1, None, None, 0, None, None) == MX_ERR_INVALID_ARG
+    # columnwise leading dimension too small / not a multiple of 128
+    assert q(FAKE, 1, 300, 64, None, None, None, 1, FAKE, FAKE2, 128, None, None) == MX_ERR_INVALID_ARG
+    assert q(FAKE, 1, 64, 64, None, None, None, 1, FAKE, FAKE2, 100, None, None) == MX_ERR_INVALID_ARG
+    # grouped columnwise without padded-offsets output
+    assert q(FAKE, 1, 64, 64, None, None, FAKE, 2, FAKE, FAKE2, 384, None, None) == MX_ERR_INVALID_ARG
+    # groups with batch > 1
+    assert q(FAKE, 2, 64, 64, None, None, FAKE, 2, FAKE, FAKE2, 384, FAKE, None) == MX_ERR_INVALID_ARG
+    # too many groups
+    assert q(FAKE, 1, 64, 64, None, None, FAKE, 5000, FAKE, FAKE2, 1 << 20, FAKE, None) == MX_ERR_UNSUPPORTED
+    # misaligned input
+    assert q(ctypes.c_void_p(0x7f0000001001), 1, 64, 64, FAKE, FAKE2, None, 1, None, None, 0,
+             None, None) == MX_ERR_INVALID_ARG
+
+
+def test_grouped_linear_rejects_bad_arguments(mxlib):
+    f = mxlib.grouped_linear_fwd
+    # NULL pointers
+    assert f(0, None, None, FAKE, 4, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
+    # unknown dtype
+    assert f(7, FAKE, None, FAKE, 4, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
+    # bf16 with scales
+    assert f(0, FAKE, FAKE, FAKE, 4, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
+    # bf16 K not a multiple of 32
+    assert f(0, FAKE, None, FAKE, 4, 512, FAKE, None, 256, 100, None, FAKE, None) == MX_ERR_UNSUPPORTED
+    # MXFP8 without scales, K not a multiple of 128
+    assert f(1, FAKE, None, FAKE, 4, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
+    assert f(1, FAKE, FAKE, FAKE, 4, 512, FAKE, FAKE, 256, 96, None, FAKE, None) == MX_ERR_UNSUPPORTED
+    # E out of range, negative M
+    assert f(0, FAKE, None, FAKE, 0, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
+    assert f(0, FAKE, None, FAKE, 4, -1, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
+
+
+def test_grouped_mlp_rejects_bad_arguments(mxlib):
+    fwd, bwd = mxlib.grouped_mlp_fwd, mxlib.grouped_mlp_bwd
+    M, H, F, E = 1024, 256, 256, 4
+    nctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
+    nws = mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E)
+    nbws = mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E)
+    args = lambda **kw: [kw.get("x", FAKE), FAKE, kw.get("E", E), M, kw.get("H", H), F, FAKE,
+                         FAKE, FAKE, FAKE, FAKE, kw.get("nctx", nctx), FAKE, kw.get("nws", nws),
+                         None]
+    assert fwd(*args(x=None)) == MX_ERR_INVALID_ARG
+    assert fwd(*args(H=200)) == MX_ERR_UNSUPPORTED
+    assert fwd(*args(E=0)) == MX_ERR_INVALID_ARG
+    assert fwd(*args(E=2000)) == MX_ERR_UNSUPPORTED
+    assert fwd(*args(nctx=nctx - 1)) == MX_ERR_WORKSPACE
+    assert "ctx" in _err(mxlib)
+    assert fwd(*args(nws=nws - 1)) == MX_ERR_WORKSPACE
+    b = [FAKE, FAKE, E, M, H, F, FAKE, FAKE, FAKE, FAKE, nctx, FAKE, FAKE, FAKE, FAKE, FAKE,
+         nbws - 1, None]
+    assert bwd(*b) == MX_ERR_WORKSPACE
+    b[0] = None
+    assert bwd(*b) == MX_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import grouped_gemm_mxfp8_amd as gm
+    monkeypatch.setattr(gm, "_lib", None)
+    monkeypatch.setattr(gm, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        gm.lib()

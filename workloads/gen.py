@@ -138,8 +138,9 @@ def slot_grid_routing(counts: np.ndarray, T: int, k: int,
 # --------------------------------------------------------------------------
 
 def _randn_bf16(gen, shape, std=1.0):
-    """N(0, std^2) samples drawn in FP32 then rounded to bfloat16."""
-    t = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    """N(0, std^2) samples drawn in FP32 then rounded to bfloat16 (on the
+    generator's device)."""
+    t = torch.randn(*shape, generator=gen, dtype=torch.float32, device=gen.device)
     if std != 1.0:
         t.mul_(std)
     return t.to(torch.bfloat16)
@@ -216,19 +217,24 @@ def make_linear_case(name="tiny_bf16_linear", seed=0, **over) -> LinearCase:
                       counts=counts, token=tok, T=T, k=k)
 
 
-def make_mlp_case(name="mixtral_fwd_bwd", seed=0, with_dy=True,
+def make_mlp_case(name="mixtral_fwd_bwd", seed=0, with_dy=True, device=None,
                   **over) -> MlpCase:
     """Build a GroupedMLP case.  ``over`` overrides config keys, e.g. a
     scaled-down shape for parity tests: make_mlp_case(None, T=300, k=2, E=4,
-    H=256, F=256, routing="counts", counts=[...])."""
+    H=256, F=256, routing="counts", counts=[...]).
+
+    With ``device`` (a GPU), x, W1, W2 and dY are drawn there by a generator
+    of that device seeded with ``seed`` (same distributions, other values than
+    the CPU draw); routing is always drawn on the CPU."""
     cfg = dict(CONFIGS[name]) if name else {}
     cfg.update(over)
     T, k, E, H, F = cfg["T"], cfg["k"], cfg["E"], cfg["H"], cfg["F"]
     M = T * k
     gen = torch.Generator().manual_seed(seed)
-    x = _randn_bf16(gen, (T, H))
-    W1 = _randn_bf16(gen, (E, 2 * F, H), W_STD)
-    W2 = _randn_bf16(gen, (E, H, F), W_STD)
+    tgen = gen if device is None else torch.Generator(device=device).manual_seed(seed)
+    x = _randn_bf16(tgen, (T, H))
+    W1 = _randn_bf16(tgen, (E, 2 * F, H), W_STD)
+    W2 = _randn_bf16(tgen, (E, H, F), W_STD)
     routing = cfg.get("routing", "zipf")
     if routing == "zipf":
         counts = zipf_counts(M, E, cfg.get("zipf_s", 1.1))
@@ -244,7 +250,10 @@ def make_mlp_case(name="mixtral_fwd_bwd", seed=0, with_dy=True,
     else:
         raise ValueError(routing)
     tok, r, counts, offs = sort_by_expert(ids, w, E)
-    dY = _randn_bf16(gen, (M, H)) if with_dy else None
-    return MlpCase(X=x[torch.from_numpy(tok)].contiguous(), W1=W1, W2=W2,
-                   r=torch.from_numpy(r), offsets=torch.from_numpy(offs),
+    dY = _randn_bf16(tgen, (M, H)) if with_dy else None
+    tok_t = torch.from_numpy(tok).to(x.device)
+    r_t, off_t = torch.from_numpy(r), torch.from_numpy(offs)
+    if device is not None:
+        r_t, off_t = r_t.to(device), off_t.to(device)
+    return MlpCase(X=x[tok_t].contiguous(), W1=W1, W2=W2, r=r_t, offsets=off_t,
                    dY=dY, counts=counts, token=tok, T=T, k=k)
