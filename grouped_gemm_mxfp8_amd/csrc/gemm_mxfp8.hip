@@ -26,6 +26,8 @@
 // walked in bands of 8 M-tiles so that the 32 tiles one XCD runs at a time
 // share 8 A panels and 4 B panels in that XCD's L2, and weight-gradient
 // groups run longest-K first.
+#include <utility>
+
 #include "internal.h"
 #include "mx_device.h"
 
@@ -50,6 +52,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>),
+// so that register arrays are only ever indexed by constants.
+template <class Fn, int... I>
+__device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Tile coordinates are wave-uniform but come from LDS reads; moving them to
 // scalar registers keeps buffer descriptors and LDS-DMA addresses scalar.
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -60,7 +73,7 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
 }
 
 __device__ __forceinline__ float silu_sig(float a, float& sg) {
-    sg = 1.0f / (1.0f + expf(-a));
+    sg = __builtin_amdgcn_rcpf(1.0f + __expf(-a));
     return a * sg;
 }
 
@@ -78,6 +91,11 @@ __device__ __forceinline__ uint32_t max4q(uint32_t m) {
     m = max(m, (uint32_t)__shfl_xor((int)m, 32));
     return m;
 }
+__device__ __forceinline__ float sum4q(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
 __device__ __forceinline__ float sum16(float v) {
     v += __shfl_xor(v, 1);
     v += __shfl_xor(v, 2);
@@ -86,66 +104,104 @@ __device__ __forceinline__ float sum16(float v) {
     return v;
 }
 
-// Quantize a 32 x 32 unit held as u[ii][jj][v] (ii, jj in {0,1}: 16 x 16
-// MFMA blocks; v: the lane's 4 rows) both rowwise (blocks along columns) and
-// columnwise (blocks along rows), storing codes and scales.
-//   row r(ii,v) = rbase + ii*16 + 4q + v, column c(jj) = cbase + jj*16 + r16.
-//   rowwise: codes at qr[r*ldqr + c], scale qrs[r*(ldqr/32) + cbase/32]
-//   columnwise: codes at qc[c*ldqc + pbase + ii*16 + 4q + v] (pbase = padded
-//   position of rbase), scale qcs[c*(ldqc/32) + pbase/32]
+// 4 x 4 byte transpose across the 4 lanes that share (lane >> 2): lane u
+// holds bytes B[u][0..3] and receives B[0..3][u].  Two rounds: swap 16-bit
+// halves with lane u^2, then bytes with lane u^1 (DPP quad permutes + v_perm).
+__device__ __forceinline__ uint32_t transpose4x4_bytes(uint32_t x, int u) {
+    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    const uint32_t t = (u & 2) ? __builtin_amdgcn_perm(y, x, 0x03020706u)
+                               : __builtin_amdgcn_perm(y, x, 0x05040100u);
+    const uint32_t w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0xB1, 0xF, 0xF, false);
+    return (u & 1) ? __builtin_amdgcn_perm(w, t, 0x03070105u)
+                   : __builtin_amdgcn_perm(w, t, 0x06020400u);
+}
+
+__device__ __forceinline__ uint32_t pack4_e4m3(const float (&v)[4], float inv) {
+    return e4m3x4(v[0], v[1], v[2], v[3], inv);
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(const float (&v)[4]) {
+    return make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                      f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+}
+
+__device__ __forceinline__ void unpack4_bf16(uint2 w, float (&v)[4]) {
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xffff0000u);
+}
+
+// Destinations of an MXFP8-requantized output: rowwise codes [rows][ldqr]
+// with scales [rows][ldqr/32], and the transposed (token-axis) copy: codes
+// [cols][ldqc] with scales [cols][ldqc/32].
 struct QuantDst {
     uint8_t* qr; uint8_t* qrs; int64_t ldqr;
     uint8_t* qc; uint8_t* qcs; int64_t ldqc;
 };
 
+// Quantize a 32 x 32 unit held as u[ii][jj][v] in the transposed MFMA output
+// layout (lane (r16, q) holds row ii*16 + r16, columns jj*16 + 4q + v), both
+// rowwise (32 consecutive columns of a row) and columnwise (32 consecutive
+// rows of a column), and store codes and scales.
+//   row r = rbase + ii*16 + r16 (stored when r - rbase < rows_valid)
+//   col c = cbase + jj*16 + 4q + v
+//   rowwise: codes qr[r*ldqr + c] (4 per dword), scale qrs[r*(ldqr/32) + cbase/32]
+//   columnwise: codes qc[c*ldqc + pbase + ii*16 + r16], scale
+//     qcs[c*(ldqc/32) + pbase/32]; written when rows_padded > 0 (pbase is the
+//     padded token position of rbase; all 32 rows lie inside the padding).
 __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int64_t rbase,
                                            int64_t cbase, int64_t pbase,
                                            int rows_valid, int rows_padded,
                                            const QuantDst& d, int lane) {
     const int r16 = lane & 15, q = lane >> 4;
-    // rowwise: per (ii, v) amax over the 32 columns (2 blocks x 16 lanes)
+    // rowwise: amax over (jj, v) in-lane, then over the 4 q-lanes
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            uint32_t m = max(abs_bits(u[ii][0][v]), abs_bits(u[ii][1][v]));
-            m = max16(m);
-            const int rl = ii * 16 + 4 * q + v;       // row within the unit
-            const uint32_t sc = scale_code_from_amax_bits(m);
-            const float inv = inv_scale_from_code(sc);
-            if (rl < rows_valid) {
-                const int64_t r = rbase + rl;
-                uint8_t* dst = d.qr + r * d.ldqr + cbase + r16;
-                dst[0] = (uint8_t)e4m3_encode(u[ii][0][v], inv);
-                dst[16] = (uint8_t)e4m3_encode(u[ii][1][v], inv);
-                if (r16 == 0) d.qrs[r * (d.ldqr / 32) + cbase / 32] = (uint8_t)sc;
-            }
-        }
-    }
-    // columnwise: per jj amax over the 32 rows (2 blocks x 4 q-lanes x 4 v)
-    if (rows_padded <= 0) return;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
         uint32_t m = 0;
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int v = 0; v < 4; ++v) m = max(m, abs_bits(u[ii][jj][v]));
         m = max4q(m);
         const uint32_t sc = scale_code_from_amax_bits(m);
         const float inv = inv_scale_from_code(sc);
-        const int64_t c = cbase + jj * 16 + r16;
+        const int rl = ii * 16 + r16;
+        if (rl < rows_valid) {
+            const int64_t r = rbase + rl;
+            uint8_t* dst = d.qr + r * d.ldqr + cbase + 4 * q;
+            *reinterpret_cast<uint32_t*>(dst) = pack4_e4m3(u[ii][0], inv);
+            *reinterpret_cast<uint32_t*>(dst + 16) = pack4_e4m3(u[ii][1], inv);
+            if (q == 0) d.qrs[r * (d.ldqr / 32) + cbase / 32] = (uint8_t)sc;
+        }
+    }
+    if (rows_padded <= 0) return;
+    // columnwise: amax over ii in-lane, then over the 16 r16-lanes
+    const int u4 = r16 & 3, m4 = r16 >> 2;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        float inv[4];
+        uint32_t scv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            uint32_t m = max(abs_bits(u[0][jj][v]), abs_bits(u[1][jj][v]));
+            m = max16(m);
+            scv[v] = scale_code_from_amax_bits(m);
+            inv[v] = inv_scale_from_code(scv[v]);
+        }
+        // this lane's column after the transpose is 4q + u4
+        const int64_t c = cbase + jj * 16 + 4 * q + u4;
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-            if (ii * 16 < rows_padded) {
-                const uint32_t w = e4m3_encode(u[ii][jj][0], inv) |
-                                   (e4m3_encode(u[ii][jj][1], inv) << 8) |
-                                   (e4m3_encode(u[ii][jj][2], inv) << 16) |
-                                   (e4m3_encode(u[ii][jj][3], inv) << 24);
-                *reinterpret_cast<uint32_t*>(d.qc + c * d.ldqc + pbase + ii * 16 + 4 * q) = w;
-            }
+            const uint32_t w = e4m3x4(u[ii][jj][0], u[ii][jj][1], u[ii][jj][2], u[ii][jj][3],
+                                      inv[0], inv[1], inv[2], inv[3]);
+            const uint32_t t = transpose4x4_bytes(w, u4);    // rows 4*m4..4*m4+3
+            *reinterpret_cast<uint32_t*>(d.qc + c * d.ldqc + pbase + ii * 16 + 4 * m4) = t;
         }
-        if (q == 0) d.qcs[c * (d.ldqc / 32) + pbase / 32] = (uint8_t)sc;
+        if (m4 == 0) {
+            const uint32_t sc = u4 == 0 ? scv[0] : u4 == 1 ? scv[1] : u4 == 2 ? scv[2] : scv[3];
+            d.qcs[c * (d.ldqc / 32) + pbase / 32] = (uint8_t)sc;
+        }
     }
 }
 
@@ -391,7 +447,7 @@ mx_gemm_kernel(GemmProblem p) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af[i], bfr[j], acc[i][j], 0, 0, 0, asc[i], 0, bsc[j]);
+                        bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
             // keep the MFMAs ahead of the wait for the next stage
             __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -399,29 +455,34 @@ mx_gemm_kernel(GemmProblem p) {
         }
 
         // ---- epilogue ----
+        // B is the MFMA's first operand, so acc[i][j] holds the transposed
+        // 16 x 16 block: lane (r16, q) has row i*16 + r16 of the wave tile and
+        // its 4 consecutive columns j*16 + 4q + v.
         const int64_t rwave = m0 + wm * 128;          // first row of this wave
         const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
 
         if constexpr (EPI == Epi::kStoreBf16) {
             uint16_t* C = reinterpret_cast<uint16_t*>(p.C) +
                           (p.kgroup ? (int64_t)g * p.c_gstride : 0);
+            const int64_t cw = n0 + wn * 128;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
+                const int rl = i * 16 + r16;
+                if (rl >= rows_valid_w) continue;
+                const int64_t row = rwave + rl;
+                const float sc = p.rscale ? p.rscale[row] : 1.0f;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int rl = i * 16 + 4 * q + v;
-                    if (rl >= rows_valid_w) continue;
-                    const int64_t row = rwave + rl;
-                    const float sc = p.rscale ? p.rscale[row] : 1.0f;
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t col = cw + j * 16 + 4 * q;
+                    if (col >= p.N) continue;
+                    float v4[4];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int64_t col = n0 + wn * 128 + j * 16 + r16;
-                        if (col < p.N) C[row * p.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][v] * sc);
-                    }
+                    for (int v = 0; v < 4; ++v) v4[v] = acc[i][j][v] * sc;
+                    *reinterpret_cast<uint2*>(C + row * p.ldc + col) = pack4_bf16(v4);
                 }
             }
         } else if constexpr (EPI == Epi::kSwiglu) {
-            // acc[i][j], j < 4: gate; acc[i][j+4]: up, same output column
+            // acc[i][j], j < 4: gate; acc[i][j+4]: up, same output columns
             const int64_t F = p.F;
             const int64_t glo = p.offs[g];
             const int64_t prow = p.poff[g] + (rwave - glo);       // padded position
@@ -429,111 +490,110 @@ mx_gemm_kernel(GemmProblem p) {
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
             const QuantDst d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc};
             const int64_t cw = n0 + wn * 64;                       // wave's first z column
+            static_for<4>([&](auto ipc) {
+                constexpr int ip = decltype(ipc)::value;
+                float rr[2];
 #pragma unroll
-            for (int ip = 0; ip < 4; ++ip) {
-                float rr[2][4];
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int rl = (2 * ip + ii) * 16 + 4 * q + v;
-                        rr[ii][v] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
-                    }
-#pragma unroll
-                for (int jp = 0; jp < 2; ++jp) {
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int rl = (2 * ip + ii) * 16 + r16;
+                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                }
+                static_for<2>([&](auto jpc) {
+                    constexpr int jp = decltype(jpc)::value;
                     float z[2][2][4];
 #pragma unroll
-                    for (int ii = 0; ii < 2; ++ii)
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int i = 2 * ip + ii;
+                        const int rl = i * 16 + r16;
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
-                            const int i = 2 * ip + ii, j = 2 * jp + jj;
-                            const int64_t col = cw + j * 16 + r16;
+                            const int j = 2 * jp + jj;
+                            const int64_t col = cw + j * 16 + 4 * q;
+                            float ga[4], ub[4];
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
-                                const float a = acc[i][j][v], b = acc[i][j + 4][v];
-                                const int rl = i * 16 + 4 * q + v;
-                                if (rl < rows_valid_w) {
-                                    uint16_t* hr = p.h + (rwave + rl) * 2 * F;
-                                    hr[col] = (uint16_t)f32_to_bf16(a);
-                                    hr[F + col] = (uint16_t)f32_to_bf16(b);
-                                }
+                                ga[v] = acc[i][j][v];
+                                ub[v] = acc[i][j + 4][v];
+                            }
+                            if (rl < rows_valid_w) {
+                                uint16_t* hr = p.h + (rwave + rl) * 2 * F;
+                                *reinterpret_cast<uint2*>(hr + col) = pack4_bf16(ga);
+                                *reinterpret_cast<uint2*>(hr + F + col) = pack4_bf16(ub);
+                            }
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
                                 float sg;
-                                const float s = silu_sig(a, sg) * b;
-                                z[ii][jj][v] = rr[ii][v] * s;
+                                z[ii][jj][v] = rr[ii] * (silu_sig(ga[v], sg) * ub[v]);
                             }
                         }
-                    quant_unit(z, rwave + 2 * ip * 16, cw + 2 * jp * 16,
-                               prow + 2 * ip * 16, rows_valid_w - 2 * ip * 16,
-                               rows_pad_w - 2 * ip * 16, d, lane);
-                }
-            }
+                    }
+                    quant_unit(z, rwave + 2 * ip * 16, cw + 2 * jp * 16, prow + 2 * ip * 16,
+                               rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, d, lane);
+                });
+            });
         } else {   // kDSwiglu
             const int64_t F = p.F;
             const int64_t glo = p.offs[g];
             const int64_t prow = p.poff[g] + (rwave - glo);
             const int64_t npad = p.poff[g + 1] - p.poff[g];
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
-            const QuantDst dA{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc};
+            const QuantDst d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc};
             const int64_t cw = n0 + wn * 128;
             const int part = (int)(n0 / BN) * 2 + wn;
+            static_for<4>([&](auto ipc) {
+                constexpr int ip = decltype(ipc)::value;
+                float rr[2], drs[2] = {0.f, 0.f};
 #pragma unroll
-            for (int ip = 0; ip < 4; ++ip) {
-                float rr[2][4], drs[2][4];
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int rl = (2 * ip + ii) * 16 + 4 * q + v;
-                        rr[ii][v] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
-                        drs[ii][v] = 0.0f;
-                    }
-#pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int rl = (2 * ip + ii) * 16 + r16;
+                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                }
+                static_for<4>([&](auto jpc) {
+                    constexpr int jp = decltype(jpc)::value;
+                    const int64_t cbase = cw + 2 * jp * 16;
                     float da[2][2][4], db[2][2][4];
 #pragma unroll
-                    for (int ii = 0; ii < 2; ++ii)
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int i = 2 * ip + ii;
+                        const int rl = i * 16 + r16;
+                        const bool rv = rl < rows_valid_w;
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
-                            const int i = 2 * ip + ii, j = 2 * jp + jj;
-                            const int64_t col = cw + j * 16 + r16;
+                            const int j = 2 * jp + jj;
+                            const int64_t col = cw + j * 16 + 4 * q;
+                            float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+                            if (rv && col < F) {
+                                const uint16_t* hr = p.h + (rwave + rl) * 2 * F;
+                                unpack4_bf16(*reinterpret_cast<const uint2*>(hr + col), a);
+                                unpack4_bf16(*reinterpret_cast<const uint2*>(hr + F + col), b);
+                            }
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
-                                const int rl = i * 16 + 4 * q + v;
-                                float ga = 0.f, gb = 0.f;
-                                if (rl < rows_valid_w && col < F) {
-                                    const uint16_t* hr = p.h + (rwave + rl) * 2 * F;
-                                    const float a = bf16_to_f32(hr[col]);
-                                    const float b = bf16_to_f32(hr[F + col]);
-                                    const float dz = acc[i][j][v];
-                                    float sg;
-                                    const float sl = silu_sig(a, sg);
-                                    drs[ii][v] += dz * (sl * b);
-                                    const float ds = rr[ii][v] * dz;
-                                    ga = ds * b * sg * (1.0f + a * (1.0f - sg));
-                                    gb = ds * sl;
-                                }
-                                da[ii][jj][v] = ga;
-                                db[ii][jj][v] = gb;
+                                const float dz = acc[i][j][v];
+                                float sg;
+                                const float sl = silu_sig(a[v], sg);
+                                drs[ii] += dz * (sl * b[v]);
+                                const float ds = rr[ii] * dz;
+                                da[ii][jj][v] = ds * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
+                                db[ii][jj][v] = ds * sl;
                             }
                         }
-                    const int64_t cbase = cw + 2 * jp * 16;
+                    }
                     if (cbase < F) {
                         quant_unit(da, rwave + 2 * ip * 16, cbase, prow + 2 * ip * 16,
-                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, dA, lane);
+                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, d, lane);
                         quant_unit(db, rwave + 2 * ip * 16, F + cbase, prow + 2 * ip * 16,
-                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, dA, lane);
+                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, d, lane);
                     }
+                });
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const float sum = sum4q(drs[ii]);
+                    const int rl = (2 * ip + ii) * 16 + r16;
+                    if (q == 0 && rl < rows_valid_w)
+                        p.drp[(rwave + rl) * p.lddrp + part] = sum;
                 }
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float s = sum16(drs[ii][v]);
-                        const int rl = (2 * ip + ii) * 16 + 4 * q + v;
-                        if (r16 == 0 && rl < rows_valid_w)
-                            p.drp[(rwave + rl) * p.lddrp + part] = s;
-                    }
-            }
+            });
         }
         // the next tile's first LDS write must not overtake slow readers
         __syncthreads();

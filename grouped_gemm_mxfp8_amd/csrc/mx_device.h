@@ -43,22 +43,24 @@ __device__ __forceinline__ float inv_scale_from_code(uint32_t c) {
     return __uint_as_float((254u - c) << 23);
 }
 
-// E4M3 code of a non-negative finite magnitude a (already divided by the
-// block scale), RNE, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_from_mag(float a) {
-    if (a >= 448.0f) return 0x7eu;
-    if (a < 0.015625f)                        // below 2^-6: subnormal grid 2^-9
-        return (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 -> 0x08)
-    uint32_t u = __float_as_uint(a);
-    u += 0x7ffffu + ((u >> 20) & 1u);         // RNE to 3 mantissa bits
-    uint32_t c = (u >> 20) - (120u << 3);     // rebias exponent 127 -> 7
-    return c > 0x7eu ? 0x7eu : c;             // a < 448 never exceeds 0x7E
+// E4M3 codes of four values, each multiplied by its block's 2^-X first (an
+// exact power-of-two scaling), packed into one dword (byte k = value k).
+// The hardware conversion v_cvt_pk_fp8_f32 rounds to nearest even and keeps
+// the sign of values that round to zero; the med3 clamp to +-448 beforehand
+// makes out-of-range values saturate instead of becoming NaN.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float ia,
+                                           float ib, float ic, float id) {
+    a = __builtin_amdgcn_fmed3f(a * ia, 448.0f, -448.0f);
+    b = __builtin_amdgcn_fmed3f(b * ib, 448.0f, -448.0f);
+    c = __builtin_amdgcn_fmed3f(c * ic, 448.0f, -448.0f);
+    d = __builtin_amdgcn_fmed3f(d * id, 448.0f, -448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
 }
 
-// E4M3 code of v * inv_scale with v's sign kept.
-__device__ __forceinline__ uint32_t e4m3_encode(float v, float inv_scale) {
-    uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
-    return s | e4m3_from_mag(__builtin_fabsf(v) * inv_scale);
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float inv) {
+    return e4m3x4(a, b, c, d, inv, inv, inv, inv);
 }
 
 // Max of |v| as fp32 bit pattern (non-negative floats order like integers).

@@ -40,11 +40,8 @@ __device__ __forceinline__ void unpack8(const uint4& u, float* v) {
 __device__ __forceinline__ uint4 encode16(const float* v, float inv) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w[i] = e4m3_encode(v[4 * i], inv) | (e4m3_encode(v[4 * i + 1], inv) << 8) |
-               (e4m3_encode(v[4 * i + 2], inv) << 16) |
-               (e4m3_encode(v[4 * i + 3], inv) << 24);
-    }
+    for (int i = 0; i < 4; ++i)
+        w[i] = e4m3x4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], inv);
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
