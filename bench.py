@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many "
+                         "MiB (read + write), the reference dispatch that scales "
+                         "FETCH_SIZE / WRITE_SIZE counter readings to bytes")
     return ap.parse_args()
 
 
@@ -169,6 +173,15 @@ def main():
     elapsed = time.perf_counter() - t0
     lib.mx_profile_end()
     print(f"[bench] {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {args.copy_calib_mib} MiB done", file=sys.stderr,
+              flush=True)
 
     agg = kernel_table(gm, lib)
     ms_step = elapsed / args.steps * 1e3

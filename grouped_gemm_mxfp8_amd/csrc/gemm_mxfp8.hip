@@ -45,12 +45,51 @@ struct GemmSmem {
     uint32_t bs[2][BN];
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int64_t bytes) {
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (no stride, dword format): base address, byte range
+// (accesses at or past it read as zero).
+__device__ __forceinline__ v4i make_rsrc(const void* p, int64_t bytes) {
     const int32_t n = bytes > 0x7fffffff ? 0x7fffffff : (int32_t)(bytes < 0 ? 0 : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, kRsrcWord3);
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), n, (int)kRsrcWord3};
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Global -> LDS load of 16 (or 4) bytes per lane: lane l's bytes land at LDS
+// address lds + 16*l (4*l).  Issued through inline asm so that the compiler
+// does not track it: the kernel waits for these loads itself with vmcnt.
+// M0 carries the LDS base and is restored afterwards.
+__device__ __forceinline__ void dma_b128(const v4i& rsrc, uint32_t lds, uint32_t voff,
+                                         uint32_t soff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
+__device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t voff,
+                                        uint32_t soff) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, %4 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+        : "memory");
+}
 
 // Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>),
 // so that register arrays are only ever indexed by constants.
@@ -61,6 +100,14 @@ __device__ __forceinline__ void static_for_impl(Fn&& f, std::integer_sequence<in
 template <int N, class Fn>
 __device__ __forceinline__ void static_for(Fn&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Workgroup barrier after this wave's LDS reads and writes have completed;
+// global loads and stores still in flight (including loads into LDS, which
+// the caller waits for with vmcnt) are not waited for.  The memory clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Tile coordinates are wave-uniform but come from LDS reads; moving them to
@@ -347,9 +394,9 @@ mx_gemm_kernel(GemmProblem p) {
         // scalar (K) offset takes part in the range check.
         const int64_t lda = p.A.ld, ldb = p.B.ld;
         const int64_t ldas = lda / 32, ldbs = ldb / 32;
-        const __amdgpu_buffer_rsrc_t ra =
+        const v4i ra =
             make_rsrc(p.A.codes + m0 * lda + klo, (mvalid - 1) * lda + K);
-        const __amdgpu_buffer_rsrc_t ras =
+        const v4i ras =
             make_rsrc(p.A.scales + m0 * ldas + klo / 32, (mvalid - 1) * ldas + K / 32);
         // B rows are addressed from brow0: the tile's first row, or for the
         // gate-up tile the expert's first W1 row (gate and up halves are F
@@ -357,9 +404,9 @@ mx_gemm_kernel(GemmProblem p) {
         const int64_t bg = p.kgroup ? 0 : (int64_t)g * p.B.gstride;
         const int64_t brow0 = bg + ((EPI == Epi::kSwiglu) ? 0 : n0);
         const int64_t bvalid = (EPI == Epi::kSwiglu) ? p.N : p.N - n0;
-        const __amdgpu_buffer_rsrc_t rb =
+        const v4i rb =
             make_rsrc(p.B.codes + brow0 * ldb + klo, (bvalid - 1) * ldb + K);
-        const __amdgpu_buffer_rsrc_t rbs =
+        const v4i rbs =
             make_rsrc(p.B.scales + brow0 * ldbs + klo / 32, (bvalid - 1) * ldbs + K / 32);
 
         // B row (relative to brow0) staged at tile row b
@@ -393,26 +440,40 @@ mx_gemm_kernel(GemmProblem p) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+        // one step's loads: 8 + 8 + 2 instructions per wave (the vmcnt count
+        // the main loop waits on); used for the two steps of the prologue
         auto issue = [&](int st, int ks) {
             const uint32_t k0 = (uint32_t)ks * BK;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    ra, (lds_ptr_t)(&sm.a[st][(wave * 8 + j) * 1024]), 16, aoff[j], k0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rb, (lds_ptr_t)(&sm.b[st][(wave * 8 + j) * 1024]), 16, boff[j], k0, 0, 0);
+                dma_b128(ra, uni(lds_addr(&sm.a[st][(wave * 8 + j) * 1024])), aoff[j], k0);
+                dma_b128(rb, uni(lds_addr(&sm.b[st][(wave * 8 + j) * 1024])), boff[j], k0);
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ras, (lds_ptr_t)(&sm.as[st][wave * 64]), 4,
-                                                     asoff, k0 / 32, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rbs, (lds_ptr_t)(&sm.bs[st][wave * 64]), 4,
-                                                     bsoff, k0 / 32, 0, 0);
+            dma_b32(ras, uni(lds_addr(&sm.as[st][wave * 64])), asoff, k0 / 32);
+            dma_b32(rbs, uni(lds_addr(&sm.bs[st][wave * 64])), bsoff, k0 / 32);
         };
 
+        // Pipeline over two LDS stages with the loads two K steps ahead:
+        // stage (k & 1) holds step k.  Once every wave has step k's fragments
+        // in registers the stage is free, and the 18 load instructions of step
+        // k+2 go into it, spread over the MFMA rows so the vector memory path
+        // (the scarce resource: about 20 bytes per clock per CU) never idles.
+        // The "stage free" barrier sits after the first two MFMA rows so those
+        // rows overlap the tail of the fragment reads.  Barriers fence LDS only
+        // (a workgroup fence would also wait for the loads still in flight);
+        // each wave waits for its own loads with vmcnt.  Past the last step
+        // the loads use a zero-range descriptor: they write zeros into a stage
+        // nobody reads again, which keeps the instruction stream branch-free.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // previous tile's stores
         if (nk > 0) issue(0, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        if (nk > 1) issue(1, 1);
         for (int ks = 0; ks < nk; ++ks) {
             const int cur = ks & 1;
+            if (ks + 1 < nk)
+                asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();                     // step ks has landed for every wave
             // ---- fragments of stage cur into registers ----
             // The scaled 16x16x128 MFMA reads a lane's 32 operand bytes as
             // two 16-byte runs of K, [16q, 16q+16) and [64+16q, 64+16q+16),
@@ -440,19 +501,41 @@ mx_gemm_kernel(GemmProblem p) {
                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[cur])[row * 4 + q];
             }
-            // ---- next stage streams in while the MFMAs run ----
-            if (ks + 1 < nk) issue(cur ^ 1, ks + 1);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
+            const bool more = ks + 2 < nk;
+            const uint32_t k2 = (uint32_t)(ks + 2) * BK;
+            const v4i ra2 = more ? ra : v4i{ra.x, ra.y, 0, ra.w};
+            const v4i rb2 = more ? rb : v4i{rb.x, rb.y, 0, rb.w};
+            const v4i ras2 = more ? ras : v4i{ras.x, ras.y, 0, ras.w};
+            const v4i rbs2 = more ? rbs : v4i{rbs.x, rbs.y, 0, rbs.w};
+            static_for<8>([&](auto jc) {
+                constexpr int j = decltype(jc)::value;
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
-            // keep the MFMAs ahead of the wait for the next stage
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (j == 1) lds_barrier();   // every wave is done with stage cur
+                if constexpr (j >= 2) {
+                    // the 18 loads of step ks+2, three per row over rows 2..7
+                    static_for<3>([&](auto uc) {
+                        constexpr int u = (j - 2) * 3 + decltype(uc)::value;
+                        if constexpr (u < 8)
+                            dma_b128(ra2, uni(lds_addr(&sm.a[cur][(wave * 8 + u) * 1024])),
+                                     aoff[u], k2);
+                        else if constexpr (u < 16)
+                            dma_b128(rb2, uni(lds_addr(&sm.b[cur][(wave * 8 + (u - 8)) * 1024])),
+                                     boff[u - 8], k2);
+                        else if constexpr (u == 16)
+                            dma_b32(ras2, uni(lds_addr(&sm.as[cur][wave * 64])), asoff, k2 / 32);
+                        else
+                            dma_b32(rbs2, uni(lds_addr(&sm.bs[cur][wave * 64])), bsoff, k2 / 32);
+                    });
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
         }
+        // (no barrier needed here: the epilogue does not touch LDS, and every
+        // wave finished reading both stages before the last step's MFMAs)
 
         // ---- epilogue ----
         // B is the MFMA's first operand, so acc[i][j] holds the transposed
@@ -595,8 +678,7 @@ mx_gemm_kernel(GemmProblem p) {
                 }
             });
         }
-        // the next tile's first LDS write must not overtake slow readers
-        __syncthreads();
+
     }
 }
 
