@@ -210,6 +210,7 @@ class MlpCtx:
     H: int
     F: int
     E: int
+    offsets: Optional[torch.Tensor] = None
 
     @property
     def padded_rows(self) -> int:
@@ -222,8 +223,18 @@ class MlpCtx:
         return off
 
     def h(self) -> torch.Tensor:
-        """Saved gate-up pre-activation, bf16 [M, 2F]."""
-        return _region(self.buf, self._off(MX_CTX_H), (self.M, 2 * self.F), torch.bfloat16)[0]
+        """Saved gate-up pre-activation as bf16 [M, 2F], gathered from the
+        library's 16 x 16 blocked layout (see MX_CTX_H in include/mxmoe.h)."""
+        Mp, F = self.padded_rows, self.F
+        raw = _region(self.buf, self._off(MX_CTX_H), (Mp // 16, F // 16, 4, 16, 2, 4),
+                      torch.bfloat16)[0]
+        hp = raw.permute(0, 3, 4, 1, 2, 5).reshape(Mp, 2 * F)
+        poff = self.padded_offsets().cpu().tolist()
+        offs = self.offsets.cpu().tolist()
+        rows = [torch.arange(poff[e], poff[e] + (offs[e + 1] - offs[e]))
+                for e in range(self.E)]
+        idx = torch.cat(rows).to(hp.device) if rows else torch.zeros(0, dtype=torch.int64)
+        return hp.index_select(0, idx)
 
     def xcol(self) -> MxTensor:
         """Token-axis MXFP8 copy of X: codes [H, Mp], scales [H, Mp/32]."""
@@ -282,7 +293,7 @@ def grouped_mlp_fwd(x, offsets, w1, w2, r, ws: Optional[torch.Tensor] = None):
     st = L.grouped_mlp_fwd(_ptr(x), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
                            _ptr(y), _ptr(ctx), nctx, _ptr(ws), ws.numel(), _stream(dev))
     _check("grouped_mlp_fwd", st)
-    return y, MlpCtx(ctx, M, H, F, E)
+    return y, MlpCtx(ctx, M, H, F, E, offsets)
 
 
 def grouped_mlp_bwd(dy, offsets, w1, w2, r, ctx: MlpCtx, ws: Optional[torch.Tensor] = None):

@@ -110,7 +110,7 @@ struct CtxLayout {
 CtxLayout ctx_layout(const MlpDims& d) {
     Carver c;
     CtxLayout L;
-    L.h = c.take((size_t)d.M * 2 * d.F * 2);
+    L.h = c.take((size_t)d.Mp * d.F * 4);     // blocked [Mp/16][F/16] x 1 KiB
     L.xcol = c.take((size_t)d.H * d.Mp);
     L.xcol_s = c.take((size_t)d.H * d.Mp / 32);
     L.zcol = c.take((size_t)d.F * d.Mp);

@@ -124,31 +124,36 @@ __device__ __forceinline__ float silu_sig(float a, float& sg) {
     return a * sg;
 }
 
+// Cross-lane reductions with single VALU ops (no LDS traffic): DPP quad
+// permutes and row rotations within a 16-lane row, v_permlane16/32_swap
+// across rows.  A swap of x with itself returns, per lane, x and the value
+// of the partner lane 16 (32) away in some order, so max/sum of the pair is
+// the pairwise reduction.
+#define MX_DPP(x, ctrl) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x), (ctrl), 0xF, 0xF, false))
+#define MX_DPPF(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xF, 0xF, false))
+
 // max over the 16 lanes that share (lane >> 4)
 __device__ __forceinline__ uint32_t max16(uint32_t m) {
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 4));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+    m = max(m, MX_DPP(m, 0xB1));     // quad_perm [1,0,3,2]
+    m = max(m, MX_DPP(m, 0x4E));     // quad_perm [2,3,0,1]
+    m = max(m, MX_DPP(m, 0x124));    // row_ror:4
+    m = max(m, MX_DPP(m, 0x128));    // row_ror:8
     return m;
 }
 // max over the 4 lanes that share (lane & 15)
 __device__ __forceinline__ uint32_t max4q(uint32_t m) {
-    m = max(m, (uint32_t)__shfl_xor((int)m, 16));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-    return m;
+    auto a = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    m = max(a[0], a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return max(b[0], b[1]);
 }
+// sum over the 4 lanes that share (lane & 15); the pairwise sums are formed
+// in the same order on every lane, so all four lanes hold the same value
 __device__ __forceinline__ float sum4q(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-__device__ __forceinline__ float sum16(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    return v;
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // 4 x 4 byte transpose across the 4 lanes that share (lane >> 2): lane u
@@ -179,30 +184,59 @@ __device__ __forceinline__ void unpack4_bf16(uint2 w, float (&v)[4]) {
     v[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
-// Destinations of an MXFP8-requantized output: rowwise codes [rows][ldqr]
-// with scales [rows][ldqr/32], and the transposed (token-axis) copy: codes
-// [cols][ldqc] with scales [cols][ldqc/32].
-struct QuantDst {
-    uint8_t* qr; uint8_t* qrs; int64_t ldqr;
-    uint8_t* qc; uint8_t* qcs; int64_t ldqc;
+// The gate-up pre-activation h saved for the backward is stored in 16 x 16
+// blocks in the MFMA output layout: block (padded row / 16, column / 16) of
+// the [Mp, F] grid holds 1 KiB, 16 bytes per lane l = (q, r16): the four gate
+// values then the four up values of row r16, columns 4q..4q+3.  Forward and
+// backward tiles share that lane mapping, so both move h with one coalesced
+// 16-byte access per lane per block.  Rows are padded per expert (multiples of
+// 128), so a block never straddles two experts.
+__device__ __forceinline__ uint4* h_block(uint16_t* h, int64_t prow16, int64_t col16,
+                                          int64_t F, int lane) {
+    return reinterpret_cast<uint4*>(h) + ((prow16 / 16) * (F / 16) + col16 / 16) * 64 + lane;
+}
+
+// Requantized outputs (z in the forward, dh in the backward) are staged per
+// wave in LDS and leave as full 16-byte chunks: rowwise codes one 32-row
+// slice at a time, token-axis codes two slices (64 tokens) at a time, token-
+// axis scales once per tile.  A wave's output columns [0, C) map to global
+// columns through colmap (one run of C, or two runs of C/2 at cw and F + cw
+// for dh = [da | db]).
+constexpr int kWaveLds = 33792;                 // sizeof(GemmSmem) / 4 waves
+
+template <int C>
+struct QStage {
+    static constexpr int kRcStride = C + 16;    // 16-byte aligned rows, conflict-free dword writes
+    static constexpr int kCcStride = 80;        // 64 tokens + 16, conflict-free
+    static constexpr int kRc = 0;
+    static constexpr int kRs = kRc + 32 * kRcStride;
+    static constexpr int kCc = kRs + 32 * (C / 32);
+    static constexpr int kCs = kCc + C * kCcStride;
+    static constexpr int kBytes = kCs + C * 4;
+    static_assert(kBytes <= kWaveLds, "staging does not fit the wave's LDS slot");
 };
 
+struct QDest {
+    uint8_t* qr; uint8_t* qrs; int64_t ldqr;    // rowwise codes [rows][ldqr] + scales
+    uint8_t* qc; uint8_t* qcs; int64_t ldqc;    // token-axis codes [cols][ldqc] + scales
+    int64_t cw, F;                              // global column of local column 0; F
+    bool split;                                 // local columns [C/2, C) go to F + cw
+};
+
+template <int C>
+__device__ __forceinline__ int64_t colmap(const QDest& d, int lc) {
+    return (d.split && lc >= C / 2) ? d.F + d.cw + (lc - C / 2) : d.cw + lc;
+}
+
 // Quantize a 32 x 32 unit held as u[ii][jj][v] in the transposed MFMA output
-// layout (lane (r16, q) holds row ii*16 + r16, columns jj*16 + 4q + v), both
-// rowwise (32 consecutive columns of a row) and columnwise (32 consecutive
-// rows of a column), and store codes and scales.
-//   row r = rbase + ii*16 + r16 (stored when r - rbase < rows_valid)
-//   col c = cbase + jj*16 + 4q + v
-//   rowwise: codes qr[r*ldqr + c] (4 per dword), scale qrs[r*(ldqr/32) + cbase/32]
-//   columnwise: codes qc[c*ldqc + pbase + ii*16 + r16], scale
-//     qcs[c*(ldqc/32) + pbase/32]; written when rows_padded > 0 (pbase is the
-//     padded token position of rbase; all 32 rows lie inside the padding).
-__device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int64_t rbase,
-                                           int64_t cbase, int64_t pbase,
-                                           int rows_valid, int rows_padded,
-                                           const QuantDst& d, int lane) {
+// layout (lane (r16, q): row ii*16 + r16 of the slice, columns lc + jj*16 +
+// 4q + v) rowwise (32 consecutive columns) and columnwise (the slice's 32
+// tokens of a column), writing codes and scales into the wave's staging area.
+template <int C>
+__device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, int ip,
+                                           uint8_t* st, int lane) {
+    using S = QStage<C>;
     const int r16 = lane & 15, q = lane >> 4;
-    // rowwise: amax over (jj, v) in-lane, then over the 4 q-lanes
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
         uint32_t m = 0;
@@ -213,17 +247,11 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int64_t rb
         m = max4q(m);
         const uint32_t sc = scale_code_from_amax_bits(m);
         const float inv = inv_scale_from_code(sc);
-        const int rl = ii * 16 + r16;
-        if (rl < rows_valid) {
-            const int64_t r = rbase + rl;
-            uint8_t* dst = d.qr + r * d.ldqr + cbase + 4 * q;
-            *reinterpret_cast<uint32_t*>(dst) = pack4_e4m3(u[ii][0], inv);
-            *reinterpret_cast<uint32_t*>(dst + 16) = pack4_e4m3(u[ii][1], inv);
-            if (q == 0) d.qrs[r * (d.ldqr / 32) + cbase / 32] = (uint8_t)sc;
-        }
+        uint8_t* row = st + S::kRc + (ii * 16 + r16) * S::kRcStride + lc + 4 * q;
+        *reinterpret_cast<uint32_t*>(row) = pack4_e4m3(u[ii][0], inv);
+        *reinterpret_cast<uint32_t*>(row + 16) = pack4_e4m3(u[ii][1], inv);
+        if (q == 0) st[S::kRs + (ii * 16 + r16) * (C / 32) + lc / 32] = (uint8_t)sc;
     }
-    if (rows_padded <= 0) return;
-    // columnwise: amax over ii in-lane, then over the 16 r16-lanes
     const int u4 = r16 & 3, m4 = r16 >> 2;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -236,21 +264,81 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int64_t rb
             scv[v] = scale_code_from_amax_bits(m);
             inv[v] = inv_scale_from_code(scv[v]);
         }
-        // this lane's column after the transpose is 4q + u4
-        const int64_t c = cbase + jj * 16 + 4 * q + u4;
+        const int col = lc + jj * 16 + 4 * q + u4;      // this lane's column after the transpose
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
             const uint32_t w = e4m3x4(u[ii][jj][0], u[ii][jj][1], u[ii][jj][2], u[ii][jj][3],
                                       inv[0], inv[1], inv[2], inv[3]);
-            const uint32_t t = transpose4x4_bytes(w, u4);    // rows 4*m4..4*m4+3
-            *reinterpret_cast<uint32_t*>(d.qc + c * d.ldqc + pbase + ii * 16 + 4 * m4) = t;
+            const uint32_t t = transpose4x4_bytes(w, u4);    // tokens 4*m4 .. 4*m4+3
+            *reinterpret_cast<uint32_t*>(st + S::kCc + col * S::kCcStride + (ip & 1) * 32 +
+                                         ii * 16 + 4 * m4) = t;
         }
         if (m4 == 0) {
             const uint32_t sc = u4 == 0 ? scv[0] : u4 == 1 ? scv[1] : u4 == 2 ? scv[2] : scv[3];
-            d.qcs[c * (d.ldqc / 32) + pbase / 32] = (uint8_t)sc;
+            st[S::kCs + col * 4 + ip] = (uint8_t)sc;
         }
     }
 }
+
+// Rowwise codes and scales of slice ip (rows rbase + ip*32 + [0, 32)) to
+// global memory; rows at or past rows_valid (relative to the wave) are not
+// written.
+template <int C>
+__device__ __forceinline__ void flush_rows(const uint8_t* st, const QDest& d, int64_t rbase,
+                                           int ip, int rows_valid, int lane) {
+    using S = QStage<C>;
+    constexpr int kChunks = 32 * (C / 16);
+#pragma unroll
+    for (int t = 0; t < kChunks / 64; ++t) {
+        const int c = lane + 64 * t;
+        const int row = c / (C / 16), lc = (c % (C / 16)) * 16;
+        if (ip * 32 + row < rows_valid) {
+            const uint4 v = *reinterpret_cast<const uint4*>(st + S::kRc + row * S::kRcStride + lc);
+            *reinterpret_cast<uint4*>(d.qr + (rbase + ip * 32 + row) * d.ldqr + colmap<C>(d, lc)) = v;
+        }
+    }
+    // scales: C/32 bytes per row, in runs of 4 (split) or C/32 (one run)
+    constexpr int kRun = (C / 32) >= 4 ? 4 : C / 32;
+    constexpr int kRuns = 32 * (C / 32) / kRun;
+    for (int c = lane; c < kRuns; c += 64) {
+        const int row = c / ((C / 32) / kRun), blk = (c % ((C / 32) / kRun)) * kRun;
+        if (ip * 32 + row < rows_valid) {
+            uint8_t* dst = d.qrs + (rbase + ip * 32 + row) * (d.ldqr / 32) + colmap<C>(d, blk * 32) / 32;
+            const uint8_t* src = st + S::kRs + row * (C / 32) + blk;
+            if constexpr (kRun == 4)
+                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+            else
+                *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
+        }
+    }
+}
+
+// Token-axis codes of slices 2*pair and 2*pair+1 (64 tokens from pbase +
+// pair*64) to global memory.
+template <int C>
+__device__ __forceinline__ void flush_cols(const uint8_t* st, const QDest& d, int64_t pbase,
+                                           int pair, int lane) {
+    using S = QStage<C>;
+#pragma unroll
+    for (int t = 0; t < C * 4 / 64; ++t) {
+        const int c = lane + 64 * t;
+        const int col = c >> 2, ch = (c & 3) * 16;
+        const uint4 v = *reinterpret_cast<const uint4*>(st + S::kCc + col * S::kCcStride + ch);
+        *reinterpret_cast<uint4*>(d.qc + colmap<C>(d, col) * d.ldqc + pbase + pair * 64 + ch) = v;
+    }
+}
+
+// Token-axis scales of the wave's four slices (one dword per column).
+template <int C>
+__device__ __forceinline__ void flush_col_scales(const uint8_t* st, const QDest& d,
+                                                 int64_t pbase, int lane) {
+    using S = QStage<C>;
+    for (int col = lane; col < C; col += 64)
+        *reinterpret_cast<uint32_t*>(d.qcs + colmap<C>(d, col) * (d.ldqc / 32) + pbase / 32) =
+            *reinterpret_cast<const uint32_t*>(st + S::kCs + col * 4);
+}
+
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <Epi EPI>
 __global__ void __launch_bounds__(NTHREADS, 1)
@@ -534,8 +622,13 @@ mx_gemm_kernel(GemmProblem p) {
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
-        // (no barrier needed here: the epilogue does not touch LDS, and every
-        // wave finished reading both stages before the last step's MFMAs)
+        // The fused epilogues stage their outputs in LDS, which overlaps every
+        // wave's operand stages: wait until the trailing (zero-range) loads of
+        // all waves have landed.  The plain epilogue does not touch LDS.
+        if constexpr (EPI != Epi::kStoreBf16) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+        }
 
         // ---- epilogue ----
         // B is the MFMA's first operand, so acc[i][j] holds the transposed
@@ -571,8 +664,9 @@ mx_gemm_kernel(GemmProblem p) {
             const int64_t prow = p.poff[g] + (rwave - glo);       // padded position
             const int64_t npad = p.poff[g + 1] - p.poff[g];
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
-            const QuantDst d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc};
             const int64_t cw = n0 + wn * 64;                       // wave's first z column
+            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, false};
+            uint8_t* st = reinterpret_cast<uint8_t*>(&sm) + wave * kWaveLds;
             static_for<4>([&](auto ipc) {
                 constexpr int ip = decltype(ipc)::value;
                 float rr[2];
@@ -591,17 +685,16 @@ mx_gemm_kernel(GemmProblem p) {
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             const int j = 2 * jp + jj;
-                            const int64_t col = cw + j * 16 + 4 * q;
                             float ga[4], ub[4];
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
                                 ga[v] = acc[i][j][v];
                                 ub[v] = acc[i][j + 4][v];
                             }
-                            if (rl < rows_valid_w) {
-                                uint16_t* hr = p.h + (rwave + rl) * 2 * F;
-                                *reinterpret_cast<uint2*>(hr + col) = pack4_bf16(ga);
-                                *reinterpret_cast<uint2*>(hr + F + col) = pack4_bf16(ub);
+                            if (rows_pad_w > 0) {
+                                const uint2 g2 = pack4_bf16(ga), u2 = pack4_bf16(ub);
+                                *h_block(p.h, prow + i * 16, cw + j * 16, F, lane) =
+                                    make_uint4(g2.x, g2.y, u2.x, u2.y);
                             }
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
@@ -610,75 +703,108 @@ mx_gemm_kernel(GemmProblem p) {
                             }
                         }
                     }
-                    quant_unit(z, rwave + 2 * ip * 16, cw + 2 * jp * 16, prow + 2 * ip * 16,
-                               rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, d, lane);
+                    quant_unit<64>(z, 2 * jp * 16, ip, st, lane);
                 });
+                lds_wait();
+                flush_rows<64>(st, d, rwave, ip, rows_valid_w, lane);
+                if constexpr (ip & 1) {
+                    if (rows_pad_w > 0) flush_cols<64>(st, d, prow, ip >> 1, lane);
+                }
+                lds_wait();
             });
+            if (rows_pad_w > 0) flush_col_scales<64>(st, d, prow, lane);
         } else {   // kDSwiglu
             const int64_t F = p.F;
             const int64_t glo = p.offs[g];
             const int64_t prow = p.poff[g] + (rwave - glo);
             const int64_t npad = p.poff[g + 1] - p.poff[g];
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
-            const QuantDst d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc};
             const int64_t cw = n0 + wn * 128;
+            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true};
+            uint8_t* st = reinterpret_cast<uint8_t*>(&sm) + wave * kWaveLds;
             const int part = (int)(n0 / BN) * 2 + wn;
-            static_for<4>([&](auto ipc) {
-                constexpr int ip = decltype(ipc)::value;
-                float rr[2], drs[2] = {0.f, 0.f};
+            // h = [a | b] for each 32 x 32 unit (ip, jp) is one 16-byte block
+            // load per lane per 16 x 16 block; the 16 units run in order with
+            // the loads of the next kRing units in flight (a ring of register
+            // buffers).  Loads are unconditional: blocks past F or past the
+            // padded rows read the tile's first block and are masked.
+            constexpr int kRing = 3;
+            uint4 hb[kRing][2][2];
+            const int64_t prow0 = p.poff[g] + (m0 - glo);     // the tile's first block row
+            auto load_unit = [&](auto uc) {
+                constexpr int un = decltype(uc)::value, ip = un / 4, jp = un % 4;
 #pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int rl = (2 * ip + ii) * 16 + r16;
-                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
-                }
-                static_for<4>([&](auto jpc) {
-                    constexpr int jp = decltype(jpc)::value;
-                    const int64_t cbase = cw + 2 * jp * 16;
-                    float da[2][2][4], db[2][2][4];
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int64_t col = cw + (2 * jp + jj) * 16;
+                        const bool in = rows_pad_w > 0 && col < F;
+                        hb[un % kRing][ii][jj] = *h_block(
+                            p.h, in ? prow + (2 * ip + ii) * 16 : prow0, in ? col : 0, F, lane);
+                    }
+            };
+            static_for<kRing>([&](auto uc) { load_unit(uc); });
+            float rr[2], drs[2];
+            static_for<16>([&](auto uc) {
+                constexpr int un = decltype(uc)::value, ip = un / 4, jp = un % 4;
+                if constexpr (jp == 0) {
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
-                        const int i = 2 * ip + ii;
-                        const int rl = i * 16 + r16;
-                        const bool rv = rl < rows_valid_w;
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) {
-                            const int j = 2 * jp + jj;
-                            const int64_t col = cw + j * 16 + 4 * q;
-                            float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
-                            if (rv && col < F) {
-                                const uint16_t* hr = p.h + (rwave + rl) * 2 * F;
-                                unpack4_bf16(*reinterpret_cast<const uint2*>(hr + col), a);
-                                unpack4_bf16(*reinterpret_cast<const uint2*>(hr + F + col), b);
-                            }
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const float dz = acc[i][j][v];
-                                float sg;
-                                const float sl = silu_sig(a[v], sg);
-                                drs[ii] += dz * (sl * b[v]);
-                                const float ds = rr[ii] * dz;
-                                da[ii][jj][v] = ds * b[v] * sg * (1.0f + a[v] * (1.0f - sg));
-                                db[ii][jj][v] = ds * sl;
-                            }
-                        }
+                        const int rl = (2 * ip + ii) * 16 + r16;
+                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                        drs[ii] = 0.f;
                     }
-                    if (cbase < F) {
-                        quant_unit(da, rwave + 2 * ip * 16, cbase, prow + 2 * ip * 16,
-                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, d, lane);
-                        quant_unit(db, rwave + 2 * ip * 16, F + cbase, prow + 2 * ip * 16,
-                                   rows_valid_w - 2 * ip * 16, rows_pad_w - 2 * ip * 16, d, lane);
-                    }
-                });
+                }
+                float da[2][2][4], db[2][2][4];
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
-                    const float sum = sum4q(drs[ii]);
-                    const int rl = (2 * ip + ii) * 16 + r16;
-                    if (q == 0 && rl < rows_valid_w)
-                        p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                    const int i = 2 * ip + ii;
+                    const bool rv = i * 16 + r16 < rows_valid_w;
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int j = 2 * jp + jj;
+                        const bool ok = rv && (cw + j * 16 + 4 * q) < F;
+                        float a[4], b[4];
+                        const uint4 hv = hb[un % kRing][ii][jj];
+                        unpack4_bf16(make_uint2(hv.x, hv.y), a);
+                        unpack4_bf16(make_uint2(hv.z, hv.w), b);
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float av = ok ? a[v] : 0.f, bv = ok ? b[v] : 0.f;
+                            const float dz = ok ? acc[i][j][v] : 0.f;
+                            float sg;
+                            const float sl = silu_sig(av, sg);
+                            drs[ii] += dz * (sl * bv);
+                            const float ds = rr[ii] * dz;
+                            da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
+                            db[ii][jj][v] = ds * sl;
+                        }
+                    }
+                }
+                if constexpr (un + kRing < 16) load_unit(std::integral_constant<int, un + kRing>{});
+                quant_unit<256>(da, 2 * jp * 16, ip, st, lane);
+                quant_unit<256>(db, 128 + 2 * jp * 16, ip, st, lane);
+                if constexpr (jp == 3) {
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const float sum = sum4q(drs[ii]);
+                        const int rl = (2 * ip + ii) * 16 + r16;
+                        if (q == 0 && rl < rows_valid_w)
+                            p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                    }
+                    // the wave's 128 columns are all below F or all at or past it
+                    lds_wait();
+                    if (cw < F) flush_rows<256>(st, d, rwave, ip, rows_valid_w, lane);
+                    if constexpr (ip & 1) {
+                        if (cw < F && rows_pad_w > 0) flush_cols<256>(st, d, prow, ip >> 1, lane);
+                    }
+                    lds_wait();
                 }
             });
+            if (cw < F && rows_pad_w > 0) flush_col_scales<256>(st, d, prow, lane);
         }
-
+        // the next tile's loads overwrite other waves' staging areas
+        if constexpr (EPI != Epi::kStoreBf16) lds_barrier();
     }
 }
 

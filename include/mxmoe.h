@@ -182,7 +182,12 @@ size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
 /*
  * Views into a forward ctx, for inspection and tests (offsets in bytes from
  * the ctx base; all regions 256-byte aligned):
- *   MX_CTX_H        bf16 [M][2F]  gate-up pre-activation h (RNE of fp32)
+ *   MX_CTX_H        gate-up pre-activation h (bf16, RNE of fp32) in 16 x 16
+ *                   blocks: block (pr/16, c/16), pr = padded row (expert e's
+ *                   row off[e]+t sits at padded row poff[e]+t), c in [0, F),
+ *                   is 1 KiB at byte ((pr/16)*(F/16) + c/16)*1024; within it
+ *                   lane l = 16*q + r holds 16 bytes: gate h[pr+r][c+4q+v] for
+ *                   v = 0..3, then up h[pr+r][F+c+4q+v].  Mp*F*4 bytes.
  *   MX_CTX_XCOL     X columnwise codes [H][Mp] then scales [H][Mp/32]
  *   MX_CTX_ZCOL     z columnwise codes [F][Mp] then scales [F][Mp/32]
  *   MX_CTX_POFF     int64 [E+1] padded token offsets

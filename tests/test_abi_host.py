@@ -65,8 +65,9 @@ def test_mlp_sizes(mxlib):
     M, H, F, E = 32768, 4096, 14336, 8
     ctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
     Mp = mxlib.mx_padded_rows_bound(M, E, 128)
-    # h (bf16 [M,2F]) + X and z token-axis copies + scales + padded offsets
-    need = M * 2 * F * 2 + (H + F) * Mp * (1 + 1 / 32)
+    # h (bf16, 16x16 blocks over padded rows: Mp*F*4 bytes) + X and z token-axis
+    # copies + scales + padded offsets
+    need = Mp * F * 4 + (H + F) * Mp * (1 + 1 / 32)
     assert need <= ctx <= need + 64 * 256
     assert mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E) > 0
     assert mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E) > 0
