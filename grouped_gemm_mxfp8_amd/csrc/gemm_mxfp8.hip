@@ -191,29 +191,44 @@ __device__ __forceinline__ void unpack4_bf16(uint2 w, float (&v)[4]) {
 // backward tiles share that lane mapping, so both move h with one coalesced
 // 16-byte access per lane per block.  Rows are padded per expert (multiples of
 // 128), so a block never straddles two experts.
+// The block's base is wave-uniform; the lane adds a 32-bit offset.
 __device__ __forceinline__ uint4* h_block(uint16_t* h, int64_t prow16, int64_t col16,
                                           int64_t F, int lane) {
-    return reinterpret_cast<uint4*>(h) + ((prow16 / 16) * (F / 16) + col16 / 16) * 64 + lane;
+    uint8_t* const blk = reinterpret_cast<uint8_t*>(h) + ((prow16 >> 4) * (F >> 4) + (col16 >> 4)) * 1024;
+    return reinterpret_cast<uint4*>(blk + (uint32_t)(lane * 16));
 }
 
 // Requantized outputs (z in the forward, dh in the backward) are staged per
 // wave in LDS and leave as full 16-byte chunks: rowwise codes one 32-row
-// slice at a time, token-axis codes two slices (64 tokens) at a time, token-
-// axis scales once per tile.  A wave's output columns [0, C) map to global
-// columns through colmap (one run of C, or two runs of C/2 at cw and F + cw
-// for dh = [da | db]).
-constexpr int kWaveLds = 33792;                 // sizeof(GemmSmem) / 4 waves
-
+// slice at a time, token-axis codes kTok tokens (one or two slices) at a
+// time, token-axis scales once per tile.  A wave's output columns [0, C) map
+// to global columns through colmap (one run of C, or two runs of C/2 at cw
+// and F + cw for dh = [da | db]).  The backward (C = 256) flushes token-axis
+// codes every slice so that its LDS slot also holds the h ring.
 template <int C>
 struct QStage {
+    static constexpr int kTok = C >= 256 ? 32 : 64;   // tokens per token-axis flush
     static constexpr int kRcStride = C + 16;    // 16-byte aligned rows, conflict-free dword writes
-    static constexpr int kCcStride = 80;        // 64 tokens + 16, conflict-free
+    static constexpr int kCcStride = kTok + 16;
     static constexpr int kRc = 0;
     static constexpr int kRs = kRc + 32 * kRcStride;
     static constexpr int kCc = kRs + 32 * (C / 32);
     static constexpr int kCs = kCc + C * kCcStride;
     static constexpr int kBytes = kCs + C * 4;
-    static_assert(kBytes <= kWaveLds, "staging does not fit the wave's LDS slot");
+};
+
+// LDS of one workgroup: the operand stages of the main loop, reused by the
+// fused epilogues as four per-wave slots.  The backward's slot adds a ring of
+// four h units (4 x 4 KiB) after its staging area.
+constexpr int kHRing = 4 * 4 * 1024;
+template <Epi EPI>
+struct Slot {
+    static constexpr int kBytes = EPI == Epi::kDSwiglu ? QStage<256>::kBytes + kHRing
+                                                       : (int)sizeof(GemmSmem) / 4;
+    static constexpr int kSmem = 4 * kBytes > (int)sizeof(GemmSmem) ? 4 * kBytes
+                                                                     : (int)sizeof(GemmSmem);
+    static_assert(EPI != Epi::kSwiglu || QStage<64>::kBytes <= kBytes, "staging fits the slot");
+    static_assert(kBytes % 16 == 0 && QStage<256>::kBytes % 16 == 0, "16-byte aligned regions");
 };
 
 struct QDest {
@@ -270,8 +285,8 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
             const uint32_t w = e4m3x4(u[ii][jj][0], u[ii][jj][1], u[ii][jj][2], u[ii][jj][3],
                                       inv[0], inv[1], inv[2], inv[3]);
             const uint32_t t = transpose4x4_bytes(w, u4);    // tokens 4*m4 .. 4*m4+3
-            *reinterpret_cast<uint32_t*>(st + S::kCc + col * S::kCcStride + (ip & 1) * 32 +
-                                         ii * 16 + 4 * m4) = t;
+            *reinterpret_cast<uint32_t*>(st + S::kCc + col * S::kCcStride +
+                                         (ip % (S::kTok / 32)) * 32 + ii * 16 + 4 * m4) = t;
         }
         if (m4 == 0) {
             const uint32_t sc = u4 == 0 ? scv[0] : u4 == 1 ? scv[1] : u4 == 2 ? scv[2] : scv[3];
@@ -280,6 +295,10 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
     }
 }
 
+// The flushes address global memory as a wave-uniform base (scalar
+// registers) plus one 32-bit per-lane offset that is the same for every pass,
+// so each store is a single instruction with no per-lane 64-bit arithmetic.
+
 // Rowwise codes and scales of slice ip (rows rbase + ip*32 + [0, 32)) to
 // global memory; rows at or past rows_valid (relative to the wave) are not
 // written.
@@ -287,44 +306,57 @@ template <int C>
 __device__ __forceinline__ void flush_rows(const uint8_t* st, const QDest& d, int64_t rbase,
                                            int ip, int rows_valid, int lane) {
     using S = QStage<C>;
-    constexpr int kChunks = 32 * (C / 16);
+    constexpr int kCpr = C / 16;                  // 16-byte chunks per row
+    constexpr int kRpp = 64 / kCpr;               // rows per pass of 64 lanes
+    const int rl = lane / kCpr, lc = (lane % kCpr) * 16;
+    const uint32_t coff = (d.split && lc >= C / 2) ? (uint32_t)(d.F - C / 2 + lc) : (uint32_t)lc;
+    const uint32_t loff = (uint32_t)rl * (uint32_t)d.ldqr + coff;
+    uint8_t* const base = d.qr + (rbase + ip * 32) * d.ldqr + d.cw;
 #pragma unroll
-    for (int t = 0; t < kChunks / 64; ++t) {
-        const int c = lane + 64 * t;
-        const int row = c / (C / 16), lc = (c % (C / 16)) * 16;
-        if (ip * 32 + row < rows_valid) {
-            const uint4 v = *reinterpret_cast<const uint4*>(st + S::kRc + row * S::kRcStride + lc);
-            *reinterpret_cast<uint4*>(d.qr + (rbase + ip * 32 + row) * d.ldqr + colmap<C>(d, lc)) = v;
+    for (int t = 0; t < 32 / kRpp; ++t) {
+        if (ip * 32 + t * kRpp + rl < rows_valid) {
+            const uint4 v = *reinterpret_cast<const uint4*>(
+                st + S::kRc + (t * kRpp + rl) * S::kRcStride + lc);
+            *reinterpret_cast<uint4*>(base + (int64_t)(t * kRpp) * d.ldqr + loff) = v;
         }
     }
-    // scales: C/32 bytes per row, in runs of 4 (split) or C/32 (one run)
-    constexpr int kRun = (C / 32) >= 4 ? 4 : C / 32;
-    constexpr int kRuns = 32 * (C / 32) / kRun;
-    for (int c = lane; c < kRuns; c += 64) {
-        const int row = c / ((C / 32) / kRun), blk = (c % ((C / 32) / kRun)) * kRun;
-        if (ip * 32 + row < rows_valid) {
-            uint8_t* dst = d.qrs + (rbase + ip * 32 + row) * (d.ldqr / 32) + colmap<C>(d, blk * 32) / 32;
-            const uint8_t* src = st + S::kRs + row * (C / 32) + blk;
-            if constexpr (kRun == 4)
-                *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
-            else
-                *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
-        }
+    // scales: C/32 bytes per row; a split row is two runs of C/64 bytes
+    constexpr int kRun = C >= 128 ? 4 : C / 32;
+    constexpr int kRunsPerRow = (C / 32) / kRun;
+    static_assert(32 * kRunsPerRow <= 64, "one pass covers the slice's scale runs");
+    const int srow = lane / kRunsPerRow, sblk = (lane % kRunsPerRow) * kRun;
+    const int64_t lds = d.ldqr / 32;
+    if (srow < 32 && ip * 32 + srow < rows_valid) {
+        const uint32_t soff = (uint32_t)srow * (uint32_t)lds +
+                              ((d.split && sblk >= C / 64) ? (uint32_t)((d.F - C / 2) / 32 + sblk)
+                                                           : (uint32_t)sblk);
+        uint8_t* const sbase = d.qrs + (rbase + ip * 32) * lds + d.cw / 32;
+        const uint8_t* src = st + S::kRs + srow * (C / 32) + sblk;
+        if constexpr (kRun == 4)
+            *reinterpret_cast<uint32_t*>(sbase + soff) = *reinterpret_cast<const uint32_t*>(src);
+        else
+            *reinterpret_cast<uint16_t*>(sbase + soff) = *reinterpret_cast<const uint16_t*>(src);
     }
 }
 
-// Token-axis codes of slices 2*pair and 2*pair+1 (64 tokens from pbase +
-// pair*64) to global memory.
+// Token-axis codes of the staged kTok tokens (padded positions tok0 ..
+// tok0 + kTok - 1) to global memory: pass t moves kCpp columns.
 template <int C>
-__device__ __forceinline__ void flush_cols(const uint8_t* st, const QDest& d, int64_t pbase,
-                                           int pair, int lane) {
+__device__ __forceinline__ void flush_cols(const uint8_t* st, const QDest& d, int64_t tok0,
+                                           int lane) {
     using S = QStage<C>;
+    constexpr int kCh = S::kTok / 16;             // 16-byte chunks per column
+    constexpr int kCpp = 64 / kCh;                // columns per pass
+    const int cl = lane / kCh, ch = (lane % kCh) * 16;
+    const uint32_t loff = (uint32_t)cl * (uint32_t)d.ldqc + (uint32_t)ch;
 #pragma unroll
-    for (int t = 0; t < C * 4 / 64; ++t) {
-        const int c = lane + 64 * t;
-        const int col = c >> 2, ch = (c & 3) * 16;
-        const uint4 v = *reinterpret_cast<const uint4*>(st + S::kCc + col * S::kCcStride + ch);
-        *reinterpret_cast<uint4*>(d.qc + colmap<C>(d, col) * d.ldqc + pbase + pair * 64 + ch) = v;
+    for (int t = 0; t < C / kCpp; ++t) {
+        const int64_t gcol = (d.split && t * kCpp >= C / 2) ? d.F + d.cw + t * kCpp - C / 2
+                                                            : d.cw + t * kCpp;
+        uint8_t* const base = d.qc + gcol * d.ldqc + tok0;
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            st + S::kCc + (t * kCpp + cl) * S::kCcStride + ch);
+        *reinterpret_cast<uint4*>(base + loff) = v;
     }
 }
 
@@ -333,9 +365,44 @@ template <int C>
 __device__ __forceinline__ void flush_col_scales(const uint8_t* st, const QDest& d,
                                                  int64_t pbase, int lane) {
     using S = QStage<C>;
-    for (int col = lane; col < C; col += 64)
-        *reinterpret_cast<uint32_t*>(d.qcs + colmap<C>(d, col) * (d.ldqc / 32) + pbase / 32) =
-            *reinterpret_cast<const uint32_t*>(st + S::kCs + col * 4);
+    const int64_t lds = d.ldqc / 32;
+    const uint32_t loff = (uint32_t)lane * (uint32_t)lds;
+#pragma unroll
+    for (int k = 0; k < (C + 63) / 64; ++k) {
+        if (k * 64 + lane < C) {
+            const int64_t gcol = (d.split && k * 64 >= C / 2) ? d.F + d.cw + k * 64 - C / 2
+                                                              : d.cw + k * 64;
+            uint8_t* const base = d.qcs + gcol * lds + pbase / 32;
+            *reinterpret_cast<uint32_t*>(base + loff) =
+                *reinterpret_cast<const uint32_t*>(st + S::kCs + (k * 64 + lane) * 4);
+        }
+    }
+}
+
+// The 2 x 2 accumulator blocks of unit (ip, jp): rows 2ip, 2ip+1 and columns
+// J0, J0 + 1, for a wave-uniform runtime ip.  The fused epilogues loop over the
+// wave's four 32-row slices at run time so that their code stays small enough
+// for the instruction cache; one uniform branch per slice keeps the
+// accumulator registers indexed by constants, and the empty asm in each
+// branch stops the compiler from turning the branches into selects (which
+// would read every candidate out of the accumulators at once).
+template <int J0>
+__device__ __forceinline__ void pick_unit(const v4f (&acc)[8][8], int ip, float (&u)[2][2][4]) {
+    static_for<4>([&](auto c) {
+        constexpr int k = decltype(c)::value;
+        if (ip == k) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = acc[2 * k + ii][J0 + jj][v];
+                        asm volatile("" : "+v"(x));
+                        u[ii][jj][v] = x;
+                    }
+        }
+    });
 }
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -343,15 +410,15 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 template <Epi EPI>
 __global__ void __launch_bounds__(NTHREADS, 1)
 mx_gemm_kernel(GemmProblem p) {
-    __shared__ GemmSmem sm;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Slot<EPI>::kSmem];
+    GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem);
     __shared__ int s_prefix[kMaxGroups + 1];
     __shared__ int s_perm[kMaxGroups];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int lane_id = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int r16 = lane & 15, q = lane >> 4;
     const int G = p.G;
 
     // output columns per tile: the gate-up tile pairs 128 gate with 128 up
@@ -367,7 +434,7 @@ mx_gemm_kernel(GemmProblem p) {
         int local = 0;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int g = lane * 16 + u;
+            const int g = lane_id * 16 + u;
             int c = 0;
             if (g < G) {
                 if (p.kgroup) {
@@ -384,18 +451,18 @@ mx_gemm_kernel(GemmProblem p) {
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
+            if (lane_id >= d) incl += o;
         }
         int run = incl - local;
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int g = lane * 16 + u;
+            const int g = lane_id * 16 + u;
             if (g < G) {
                 s_prefix[g] = run;
                 run += cnt[u];
             }
         }
-        if (lane == 63) s_prefix[G] = incl;
+        if (lane_id == 63) s_prefix[G] = incl;
     }
     if (p.kgroup) {
         // longest contraction first (ties: lower group first)
@@ -421,11 +488,16 @@ mx_gemm_kernel(GemmProblem p) {
     const int bid = blockIdx.x;
     const int slot = (grid % 8 == 0) ? (bid % 8) * (grid / 8) + bid / 8 : bid;
 
-    const int swz = r16 & 7;
-
     for (int t0 = 0; t0 < total; t0 += grid) {
         const int t = t0 + slot;
         if (t >= total) break;
+        // Per-lane offsets are derived per tile from an opaque copy of the
+        // lane index: hoisted out of the tile loop they would stay live
+        // through the epilogue, which needs every register it can get.
+        int lane = lane_id;
+        asm volatile("" : "+v"(lane));
+        const int r16 = lane & 15, q = lane >> 4;
+        const int swz = r16 & 7;
 
         // ---- locate the tile ----
         int g;
@@ -666,9 +738,16 @@ mx_gemm_kernel(GemmProblem p) {
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
             const int64_t cw = n0 + wn * 64;                       // wave's first z column
             const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, false};
-            uint8_t* st = reinterpret_cast<uint8_t*>(&sm) + wave * kWaveLds;
-            static_for<4>([&](auto ipc) {
-                constexpr int ip = decltype(ipc)::value;
+            uint8_t* st = smem + wave * Slot<EPI>::kBytes;
+#pragma nounroll
+            for (int ip = 0; ip < 4; ++ip) {
+                // Lane-derived values are re-derived from an opaque copy of the
+                // lane index in every slice: hoisted out of the tile loop they
+                // would stay live through the main loop and crowd out the
+                // accumulators.
+                int lane = lane_id;
+                asm volatile("" : "+v"(lane));
+                const int r16 = lane & 15, q = lane >> 4;
                 float rr[2];
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
@@ -677,29 +756,24 @@ mx_gemm_kernel(GemmProblem p) {
                 }
                 static_for<2>([&](auto jpc) {
                     constexpr int jp = decltype(jpc)::value;
-                    float z[2][2][4];
+                    float gu[2][2][4], uu[2][2][4], z[2][2][4];
+                    pick_unit<2 * jp>(acc, ip, gu);
+                    pick_unit<2 * jp + 4>(acc, ip, uu);
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const int i = 2 * ip + ii;
-                        const int rl = i * 16 + r16;
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             const int j = 2 * jp + jj;
-                            float ga[4], ub[4];
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                ga[v] = acc[i][j][v];
-                                ub[v] = acc[i][j + 4][v];
-                            }
                             if (rows_pad_w > 0) {
-                                const uint2 g2 = pack4_bf16(ga), u2 = pack4_bf16(ub);
+                                const uint2 g2 = pack4_bf16(gu[ii][jj]), u2 = pack4_bf16(uu[ii][jj]);
                                 *h_block(p.h, prow + i * 16, cw + j * 16, F, lane) =
                                     make_uint4(g2.x, g2.y, u2.x, u2.y);
                             }
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
                                 float sg;
-                                z[ii][jj][v] = rr[ii] * (silu_sig(ga[v], sg) * ub[v]);
+                                z[ii][jj][v] = rr[ii] * (silu_sig(gu[ii][jj][v], sg) * uu[ii][jj][v]);
                             }
                         }
                     }
@@ -707,11 +781,9 @@ mx_gemm_kernel(GemmProblem p) {
                 });
                 lds_wait();
                 flush_rows<64>(st, d, rwave, ip, rows_valid_w, lane);
-                if constexpr (ip & 1) {
-                    if (rows_pad_w > 0) flush_cols<64>(st, d, prow, ip >> 1, lane);
-                }
+                if ((ip & 1) && rows_pad_w > 0) flush_cols<64>(st, d, prow + (ip >> 1) * 64, lane);
                 lds_wait();
-            });
+            }
             if (rows_pad_w > 0) flush_col_scales<64>(st, d, prow, lane);
         } else {   // kDSwiglu
             const int64_t F = p.F;
@@ -721,89 +793,109 @@ mx_gemm_kernel(GemmProblem p) {
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
             const int64_t cw = n0 + wn * 128;
             const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true};
-            uint8_t* st = reinterpret_cast<uint8_t*>(&sm) + wave * kWaveLds;
+            uint8_t* st = smem + wave * Slot<EPI>::kBytes;
             const int part = (int)(n0 / BN) * 2 + wn;
-            // h = [a | b] for each 32 x 32 unit (ip, jp) is one 16-byte block
-            // load per lane per 16 x 16 block; the 16 units run in order with
-            // the loads of the next kRing units in flight (a ring of register
-            // buffers).  Loads are unconditional: blocks past F or past the
-            // padded rows read the tile's first block and are masked.
-            constexpr int kRing = 3;
-            uint4 hb[kRing][2][2];
-            const int64_t prow0 = p.poff[g] + (m0 - glo);     // the tile's first block row
-            auto load_unit = [&](auto uc) {
-                constexpr int un = decltype(uc)::value, ip = un / 4, jp = un % 4;
+            // h = [a | b] of unit (ip, jp) (32 rows x 32 columns) is four 1 KiB
+            // blocks, each moved by one global->LDS load into the unit's buffer
+            // of the ring.  While slice ip is processed, unit jp's buffer is
+            // refilled with unit (ip + 1, jp), so each load has a whole slice
+            // to land.  Blocks past F, past the padded rows or past the last
+            // slice use a zero-range descriptor (zeros, never read).  The wait
+            // before a unit is vmcnt(12): the three other units' loads (12
+            // instructions) always follow it, and anything else issued after
+            // it only makes the wait stricter.
+            uint8_t* const ring = st + QStage<256>::kBytes;
+            auto dma_unit = [&](int ipn, auto jpc, int lane) {
+                constexpr int jp = decltype(jpc)::value;
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
                     for (int jj = 0; jj < 2; ++jj) {
                         const int64_t col = cw + (2 * jp + jj) * 16;
-                        const bool in = rows_pad_w > 0 && col < F;
-                        hb[un % kRing][ii][jj] = *h_block(
-                            p.h, in ? prow + (2 * ip + ii) * 16 : prow0, in ? col : 0, F, lane);
+                        const bool in = rows_pad_w > 0 && col < F && ipn < 4;
+                        const uint8_t* blk = reinterpret_cast<const uint8_t*>(p.h) +
+                            (((prow >> 4) + 2 * ipn + ii) * (F >> 4) + (col >> 4)) * 1024;
+                        const v4i rs = make_rsrc(in ? blk : reinterpret_cast<const uint8_t*>(p.h),
+                                                 in ? 1024 : 0);
+                        dma_b128(rs, uni(lds_addr(ring + ((jp * 2 + ii) * 2 + jj) * 1024)),
+                                 (uint32_t)lane * 16, 0);
                     }
             };
-            static_for<kRing>([&](auto uc) { load_unit(uc); });
-            float rr[2], drs[2];
-            static_for<16>([&](auto uc) {
-                constexpr int un = decltype(uc)::value, ip = un / 4, jp = un % 4;
-                if constexpr (jp == 0) {
-#pragma unroll
-                    for (int ii = 0; ii < 2; ++ii) {
-                        const int rl = (2 * ip + ii) * 16 + r16;
-                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
-                        drs[ii] = 0.f;
-                    }
-                }
-                float da[2][2][4], db[2][2][4];
+            static_for<4>([&](auto jpc) { dma_unit(0, jpc, lane); });
+#pragma nounroll
+            for (int ip = 0; ip < 4; ++ip) {
+                // Lane-derived values are re-derived from an opaque copy of the
+                // lane index in every slice: hoisted out of the tile loop they
+                // would stay live through the main loop and crowd out the
+                // accumulators.
+                int lane = lane_id;
+                asm volatile("" : "+v"(lane));
+                const int r16 = lane & 15, q = lane >> 4;
+                float rr[2], drs[2];
 #pragma unroll
                 for (int ii = 0; ii < 2; ++ii) {
-                    const int i = 2 * ip + ii;
-                    const bool rv = i * 16 + r16 < rows_valid_w;
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        const int j = 2 * jp + jj;
-                        const bool ok = rv && (cw + j * 16 + 4 * q) < F;
-                        float a[4], b[4];
-                        const uint4 hv = hb[un % kRing][ii][jj];
-                        unpack4_bf16(make_uint2(hv.x, hv.y), a);
-                        unpack4_bf16(make_uint2(hv.z, hv.w), b);
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const float av = ok ? a[v] : 0.f, bv = ok ? b[v] : 0.f;
-                            const float dz = ok ? acc[i][j][v] : 0.f;
-                            float sg;
-                            const float sl = silu_sig(av, sg);
-                            drs[ii] += dz * (sl * bv);
-                            const float ds = rr[ii] * dz;
-                            da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
-                            db[ii][jj][v] = ds * sl;
-                        }
-                    }
+                    const int rl = (2 * ip + ii) * 16 + r16;
+                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                    drs[ii] = 0.f;
                 }
-                if constexpr (un + kRing < 16) load_unit(std::integral_constant<int, un + kRing>{});
-                quant_unit<256>(da, 2 * jp * 16, ip, st, lane);
-                quant_unit<256>(db, 128 + 2 * jp * 16, ip, st, lane);
-                if constexpr (jp == 3) {
+                static_for<4>([&](auto jpc) {
+                    constexpr int jp = decltype(jpc)::value;
+                    float dzu[2][2][4], da[2][2][4], db[2][2][4];
+                    uint4 hb[2][2];
+                    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj)
+                            hb[ii][jj] = *reinterpret_cast<const uint4*>(
+                                ring + ((jp * 2 + ii) * 2 + jj) * 1024 + lane * 16);
+                    lds_wait();                 // the buffer is free for the next slice's unit
+                    dma_unit(ip + 1, jpc, lane);
+                    pick_unit<2 * jp>(acc, ip, dzu);
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
-                        const float sum = sum4q(drs[ii]);
-                        const int rl = (2 * ip + ii) * 16 + r16;
-                        if (q == 0 && rl < rows_valid_w)
-                            p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                        const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const int j = 2 * jp + jj;
+                            const bool ok = rv && (cw + j * 16 + 4 * q) < F;
+                            float a[4], b[4];
+                            const uint4 hv = hb[ii][jj];
+                            unpack4_bf16(make_uint2(hv.x, hv.y), a);
+                            unpack4_bf16(make_uint2(hv.z, hv.w), b);
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const float av = ok ? a[v] : 0.f, bv = ok ? b[v] : 0.f;
+                                const float dz = ok ? dzu[ii][jj][v] : 0.f;
+                                float sg;
+                                const float sl_ = silu_sig(av, sg);
+                                drs[ii] += dz * (sl_ * bv);
+                                const float ds = rr[ii] * dz;
+                                da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
+                                db[ii][jj][v] = ds * sl_;
+                            }
+                        }
                     }
-                    // the wave's 128 columns are all below F or all at or past it
-                    lds_wait();
-                    if (cw < F) flush_rows<256>(st, d, rwave, ip, rows_valid_w, lane);
-                    if constexpr (ip & 1) {
-                        if (cw < F && rows_pad_w > 0) flush_cols<256>(st, d, prow, ip >> 1, lane);
-                    }
-                    lds_wait();
+                    quant_unit<256>(da, 2 * jp * 16, ip, st, lane);
+                    quant_unit<256>(db, 128 + 2 * jp * 16, ip, st, lane);
+                });
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const float sum = sum4q(drs[ii]);
+                    const int rl = (2 * ip + ii) * 16 + r16;
+                    if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
                 }
-            });
+                // the wave's 128 columns are all below F or all at or past it
+                lds_wait();
+                if (cw < F) flush_rows<256>(st, d, rwave, ip, rows_valid_w, lane);
+                if (cw < F && rows_pad_w > 0) flush_cols<256>(st, d, prow + ip * 32, lane);
+                lds_wait();
+            }
             if (cw < F && rows_pad_w > 0) flush_col_scales<256>(st, d, prow, lane);
         }
-        // the next tile's loads overwrite other waves' staging areas
+        // the next tile's loads overwrite other waves' staging areas (and the
+        // backward's trailing ring loads must land before they do)
+        if constexpr (EPI == Epi::kDSwiglu) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if constexpr (EPI != Epi::kStoreBf16) lds_barrier();
     }
 }
