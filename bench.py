@@ -71,6 +71,38 @@ def kernel_table(gm, lib):
     return agg
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mixtral_fwd_bwd_hbm_traffic.json")
+
+
+def kernel_sources_sha256():
+    """Hash of the library's device and host sources, to tell whether the
+    kernels have changed since the counter record was taken."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "grouped_gemm_mxfp8_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    record (FETCH_SIZE and WRITE_SIZE passes, scaled by a 1 GiB copy), or
+    None when there is no record or the sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_sources_sha256():
+        return None
+    ent = rec.get("per_launch", {}).get(kernel)
+    return None if ent is None else int(round(ent["bytes"]))
+
+
 def roofline(agg):
     name, a = max(agg.items(), key=lambda kv: kv[1]["ms"])
     sec = a["ms"] / 1e3
@@ -81,7 +113,8 @@ def roofline(agg):
         achieved = a["work"] / sec / 1e9
         peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(name),
+            "traffic_unit": "HBM bytes per launch",
             "launches": a["launches"], "avg_launch_ms": round(a["ms"] / a["launches"], 4)}
 
 
