@@ -251,6 +251,8 @@ mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
     if (!aligned(x, 16) || (row_codes && !aligned(row_codes, 16)) ||
         (col_codes && !aligned(col_codes, 16)))
         return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: x and codes must be 16-byte aligned");
+    if ((row_scales && !aligned(row_scales, 4)) || (col_scales && !aligned(col_scales, 4)))
+        return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: scales must be 4-byte aligned");
     if (d_offsets) {
         if (batch != 1)
             return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: row groups need batch == 1");

@@ -9,8 +9,8 @@
 //    combine their amax with one lane swap.  Codes leave as one 16-byte store
 //    per lane, so a wave moves 2 KiB in and 1 KiB out contiguously.
 //  * quant_tiles_kernel -- 128-row x 64-column tile per workgroup producing
-//    the rowwise copy (from registers) and the columnwise copy (through LDS)
-//    from one read of the input.  The columnwise copy is transposed
+//    the rowwise copy (from registers) and the columnwise copy (through an
+//    LDS transpose of bf16 row pairs) from one read of the input.  The columnwise copy is transposed
 //    ([C][ld], blocks of 32 rows); row groups (experts) start new blocks and
 //    are padded with zero codes to a multiple of 128 rows, so every tile lies
 //    inside one group.
@@ -91,6 +91,20 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nchunk,
     }
 }
 
+// DPP helpers: lane i of a quad reads lane (pattern) of the same quad
+#define MXQ_DPP(x, ctrl) ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x), (ctrl), 0xF, 0xF, false))
+
+__device__ __forceinline__ uint2 encode8(const float* v, float inv) {
+    return make_uint2(e4m3x4(v[0], v[1], v[2], v[3], inv), e4m3x4(v[4], v[5], v[6], v[7], inv));
+}
+
+// 128 rows x 64 columns per workgroup of 256 lanes.  Loads: lane t reads the
+// 16-byte chunk (t & 7) of row pair (t >> 3), so every load instruction moves
+// eight full 128-byte row segments.  Rowwise blocks of 32 columns are four
+// neighbouring lanes (a DPP quad).  The columnwise copy goes through an LDS
+// tile that holds bf16 row pairs transposed, [column][row pair] with a row
+// stride of 65 dwords: both the writes (eight columns x eight row pairs per
+// instruction) and the reads (16 columns x 4 blocks) hit 64 distinct banks.
 __global__ void __launch_bounds__(256)
 quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                    const int64_t* __restrict__ offs,
@@ -98,9 +112,10 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                    uint8_t* __restrict__ rc, uint8_t* __restrict__ rs,
                    uint8_t* __restrict__ cc, uint8_t* __restrict__ cs,
                    int64_t ld) {
-    __shared__ float tile[128][65];
+    constexpr int kStride = 65;                      // dwords per column of the tile
+    __shared__ uint32_t tile[64 * kStride];
     const int64_t b = blockIdx.z;
-    const int64_t p0 = (int64_t)blockIdx.y * 128;   // start in the padded axis
+    const int64_t p0 = (int64_t)blockIdx.y * 128;    // start in the padded axis
     int64_t src0, valid;
     if (offs) {
         if (p0 >= poff[G]) return;
@@ -119,54 +134,87 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
     valid = valid < 0 ? 0 : (valid > 128 ? 128 : valid);
 
     const int t = threadIdx.x;
-    const int row = t >> 1, half = t & 1;
+    const int c8 = t & 7, rp = t >> 3;
     const int64_t col0 = (int64_t)blockIdx.x * 64;
-    const int64_t cseg = col0 + half * 32;           // this lane's 32 columns
-    const bool live = row < valid && cseg < C;
+    const int64_t ccol = col0 + c8 * 8;               // this lane's 8 columns
+    const bool colok = ccol < C;                      // C % 32 == 0: whole chunk in or out
+    const uint16_t* xb = x + (b * R + src0) * C + ccol;
 
-    float v[32];
-    if (live) {
-        const uint4* src = reinterpret_cast<const uint4*>(
-            x + (b * R + src0 + row) * C + cseg);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) unpack8(load_stream(src + q), v + 8 * q);
-    } else {
+    for (int it = 0; it < 2; ++it) {
+        const int r0 = it * 64 + 2 * rp;
+        uint4 w[2];
+        float v[2][8];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) v[j] = 0.0f;
-    }
-
-    if (rc && live) {
-        uint32_t m = 0;
+        for (int h = 0; h < 2; ++h) {
+            const bool live = colok && r0 + h < valid;
+            w[h] = live ? load_stream(reinterpret_cast<const uint4*>(xb + (int64_t)(r0 + h) * C))
+                        : make_uint4(0, 0, 0, 0);
+            unpack8(w[h], v[h]);
+        }
+        if (rc) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) m = max(m, abs_bits(v[j]));
-        const uint32_t sc = scale_code_from_amax_bits(m);
-        const float inv = inv_scale_from_code(sc);
-        uint4* dst = reinterpret_cast<uint4*>(rc + (b * R + src0 + row) * C + cseg);
-        dst[0] = encode16(v, inv);
-        dst[1] = encode16(v + 16, inv);
-        rs[(b * R + src0 + row) * (C / 32) + cseg / 32] = (uint8_t)sc;
+            for (int h = 0; h < 2; ++h) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m = max(m, abs_bits(v[h][j]));
+                m = max(m, MXQ_DPP(m, 0xB1));         // quad_perm [1,0,3,2]
+                m = max(m, MXQ_DPP(m, 0x4E));         // quad_perm [2,3,0,1]
+                const uint32_t sc = scale_code_from_amax_bits(m);
+                const uint32_t sc_hi = MXQ_DPP(sc, 0x104);   // row_shl:4 -- the next block's
+                const int64_t row = b * R + src0 + r0 + h;
+                if (colok && r0 + h < valid) {
+                    *reinterpret_cast<uint2*>(rc + row * C + ccol) = encode8(v[h], inv_scale_from_code(sc));
+                    if (c8 == 0) {
+                        // the row's two scale bytes; one 16-bit store when aligned
+                        uint8_t* d = rs + row * (C / 32) + col0 / 32;
+                        const bool two = col0 + 64 <= C;
+                        if (two && !((C / 32) & 1)) {
+                            *reinterpret_cast<uint16_t*>(d) = (uint16_t)(sc | (sc_hi << 8));
+                        } else {
+                            d[0] = (uint8_t)sc;
+                            if (two) d[1] = (uint8_t)sc_hi;
+                        }
+                    }
+                }
+            }
+        }
+        if (cc) {
+            const uint32_t a4[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+            const uint32_t b4[4] = {w[1].x, w[1].y, w[1].z, w[1].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tile[(c8 * 8 + 2 * i) * kStride + it * 32 + rp] = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);
+                tile[(c8 * 8 + 2 * i + 1) * kStride + it * 32 + rp] = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);
+            }
+        }
     }
     if (!cc) return;
-
-#pragma unroll
-    for (int j = 0; j < 32; ++j) tile[row][half * 32 + j] = v[j];
     __syncthreads();
 
     const int col = t >> 2, blk = t & 3;
-    if (col0 + col >= C) return;
-    float w[32];
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t d = tile[col * kStride + blk * 16 + i];
+        v[2 * i] = __uint_as_float(d << 16);
+        v[2 * i + 1] = __uint_as_float(d & 0xffff0000u);
+    }
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        w[i] = tile[blk * 32 + i][col];
-        m = max(m, abs_bits(w[i]));
-    }
+    for (int i = 0; i < 32; ++i) m = max(m, abs_bits(v[i]));
     const uint32_t sc = scale_code_from_amax_bits(m);
     const float inv = inv_scale_from_code(sc);
-    uint4* dst = reinterpret_cast<uint4*>(cc + (b * C + col0 + col) * ld + p0 + blk * 32);
-    dst[0] = encode16(w, inv);
-    dst[1] = encode16(w + 16, inv);
-    cs[(b * C + col0 + col) * (ld / 32) + p0 / 32 + blk] = (uint8_t)sc;
+    // the four blocks of a column sit in one quad: gather their scales
+    const uint32_t s1 = MXQ_DPP(sc, 0x55), s2 = MXQ_DPP(sc, 0xAA), s3 = MXQ_DPP(sc, 0xFF);
+    if (col0 + col >= C) return;
+    const int64_t crow = b * C + col0 + col;
+    uint4* dst = reinterpret_cast<uint4*>(cc + crow * ld + p0 + blk * 32);
+    dst[0] = encode16(v, inv);
+    dst[1] = encode16(v + 16, inv);
+    if (blk == 0)
+        *reinterpret_cast<uint32_t*>(cs + crow * (ld / 32) + p0 / 32) =
+            sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
 }
 
 }  // namespace

@@ -97,7 +97,9 @@ int64_t mx_padded_rows_bound(int64_t M, int32_t G, int32_t align);
  *                Columns past the last group's padded end are not written.
  *   d_padded_offsets  int64 [G+1], written (device) when col_codes is given
  *                with d_offsets; may be NULL otherwise.
- * At least one of the two copies must be requested.
+ * At least one of the two copies must be requested.  x and the code buffers
+ * must be 16-byte aligned, the scale buffers 4-byte aligned
+ * (MX_ERR_INVALID_ARG otherwise).
  */
 mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
                          uint8_t* row_codes, uint8_t* row_scales,

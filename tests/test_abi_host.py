@@ -108,6 +108,12 @@ def test_quantize_rejects_bad_arguments(mxlib):
     # misaligned input
     assert q(ctypes.c_void_p(0x7f0000001001), 1, 64, 64, FAKE, FAKE2, None, 1, None, None, 0,
              None, None) == MX_ERR_INVALID_ARG
+    # misaligned scales
+    assert q(FAKE, 1, 64, 64, FAKE, ctypes.c_void_p(0x7f0000002002), None, 1, None, None, 0,
+             None, None) == MX_ERR_INVALID_ARG
+    assert "scales" in _err(mxlib)
+    assert q(FAKE, 1, 64, 64, None, None, None, 1, FAKE, ctypes.c_void_p(0x7f0000002001), 128,
+             None, None) == MX_ERR_INVALID_ARG
 
 
 def test_grouped_linear_rejects_bad_arguments(mxlib):

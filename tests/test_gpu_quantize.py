@@ -104,6 +104,25 @@ def test_grouped_token_axis(dev, counts):
     assert np.array_equal(out["row"].scales.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("R,C", [(200, 96), (1, 32), (129, 224), (256, 64)])
+def test_tile_pass_ragged_shapes(dev, R, C):
+    """One tile pass (rowwise + token-axis) on shapes with a ragged last row
+    tile, a half-used last column tile and an odd number of scale blocks."""
+    rng = np.random.default_rng(R * 1000 + C)
+    xf = rng.standard_normal((R, C)) * np.exp(rng.uniform(-6, 6, (R, 1)))
+    x = torch.from_numpy(xf.astype(np.float32)).to(torch.bfloat16).to(dev)
+    out = gm.mxfp8_quantize(x, rowwise=True, colwise=True)
+    torch.cuda.synchronize()
+    x64 = to64(x)
+    rc, rs = O.quantize_lastdim(x64)
+    assert np.array_equal(out["row"].codes.cpu().numpy(), rc)
+    assert np.array_equal(out["row"].scales.cpu().numpy(), rs)
+    codes, scales, poff = O.quantize_tokens(x64, np.array([0, R]), align=128)
+    n = int(poff[-1])
+    assert np.array_equal(out["col"].codes.cpu().numpy()[:, :n], codes)
+    assert np.array_equal(out["col"].scales.cpu().numpy()[:, : n // 32], scales)
+
+
 def test_batched_columnwise_weights(dev):
     rng = np.random.default_rng(7)
     E, R, C = 3, 384, 160
