@@ -237,20 +237,20 @@ class MlpCtx:
         return hp.index_select(0, idx)
 
     def xcol(self) -> MxTensor:
-        """Token-axis MXFP8 copy of X: codes [H, Mp], scales [H, Mp/32]."""
+        """Token-axis MXFP8 copy of X: codes [H, Mp], scales [H, Mp/32]
+        (row-major copy of the tiled scales)."""
         return self._mx(MX_CTX_XCOL, (self.H, self.padded_rows))
 
     def zcol(self) -> MxTensor:
-        """Token-axis MXFP8 copy of z: codes [F, Mp], scales [F, Mp/32]."""
+        """Token-axis MXFP8 copy of z: codes [F, Mp], scales [F, Mp/32]
+        (row-major copy of the tiled scales)."""
         return self._mx(MX_CTX_ZCOL, (self.F, self.padded_rows))
 
     def padded_offsets(self) -> torch.Tensor:
         return _region(self.buf, self._off(MX_CTX_POFF), (self.E + 1,), torch.int64)[0]
 
     def _mx(self, which, shape):
-        codes, nxt = _region(self.buf, self._off(which), shape, torch.uint8)
-        scales, _ = _region(self.buf, nxt, (*shape[:-1], shape[-1] // BLOCK), torch.uint8)
-        return MxTensor(codes, scales)
+        return _tiled_mx_view(self.buf, self._off(which), shape)
 
 
 def _mlp_check(x, offsets, w1, w2, r):
@@ -324,16 +324,27 @@ def _region(buf: torch.Tensor, off: int, shape, dtype):
     return buf[off:off + nbytes].view(dtype).view(*shape), (off + nbytes + 255) // 256 * 256
 
 
+def _tiled_mx_view(buf: torch.Tensor, off: int, shape) -> MxTensor:
+    """Codes [R, Kp] at ``off`` and the K-step tiled scales after them (the
+    library's internal layout, see include/mxmoe.h), returned as row-major
+    scales [R, Kp/32] (a gathered copy; codes are a view)."""
+    R, Kp = shape
+    codes, nxt = _region(buf, off, shape, torch.uint8)
+    groups = (R + 31) // 32
+    raw, _ = _region(buf, nxt, (groups, Kp // 128, 32, 4), torch.uint8)
+    scales = raw.permute(0, 2, 1, 3).reshape(groups * 32, Kp // BLOCK)[:R]
+    return MxTensor(codes, scales)
+
+
 def ws_mx_view(ws: torch.Tensor, which: int, M, H, F, E, shape) -> MxTensor:
     """MXFP8 tensor inside a forward/backward workspace: codes of ``shape``
-    at the documented offset, scales [.., shape[-1]/32] at the next 256-byte
-    boundary (see include/mxmoe.h)."""
+    [R, Kp] at the documented offset, scales at the next 256-byte boundary in
+    the K-step tiled layout, returned row-major [R, Kp/32] (see
+    include/mxmoe.h)."""
     off = int(lib().grouped_mlp_ws_offset(which, M, H, F, E))
     if off < 0:
         raise MxError("grouped_mlp_ws_offset", 1, last_error())
-    codes, nxt = _region(ws, off, shape, torch.uint8)
-    scales, _ = _region(ws, nxt, (*shape[:-1], shape[-1] // BLOCK), torch.uint8)
-    return MxTensor(codes, scales)
+    return _tiled_mx_view(ws, off, shape)
 
 
 __all__ = ["lib", "last_error", "MxError", "MxTensor", "MlpCtx", "mxfp8_quantize",

@@ -127,13 +127,13 @@ FwdWs fwd_ws_layout(const MlpDims& d) {
     Carver c;
     FwdWs L;
     L.xr = c.take((size_t)d.M * d.H);
-    L.xr_s = c.take((size_t)d.M * d.H / 32);
+    L.xr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
     L.w1r = c.take((size_t)d.E * 2 * d.F * d.H);
     L.w1r_s = c.take((size_t)d.E * 2 * d.F * d.H / 32);
     L.w2r = c.take((size_t)d.E * d.H * d.F);
     L.w2r_s = c.take((size_t)d.E * d.H * d.F / 32);
     L.zr = c.take((size_t)d.M * d.F);
-    L.zr_s = c.take((size_t)d.M * d.F / 32);
+    L.zr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.F));
     L.total = c.off;
     return L;
 }
@@ -147,7 +147,7 @@ BwdWs bwd_ws_layout(const MlpDims& d) {
     Carver c;
     BwdWs L;
     L.dyr = c.take((size_t)d.M * d.H);
-    L.dyr_s = c.take((size_t)d.M * d.H / 32);
+    L.dyr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
     L.dycol = c.take((size_t)d.H * d.Mp);
     L.dycol_s = c.take((size_t)d.H * d.Mp / 32);
     L.w2c = c.take((size_t)d.E * d.F * d.H);
@@ -155,7 +155,7 @@ BwdWs bwd_ws_layout(const MlpDims& d) {
     L.w1c = c.take((size_t)d.E * d.H * 2 * d.F);
     L.w1c_s = c.take((size_t)d.E * d.H * 2 * d.F / 32);
     L.dhr = c.take((size_t)d.M * 2 * d.F);
-    L.dhr_s = c.take((size_t)d.M * 2 * d.F / 32);
+    L.dhr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, 2 * d.F));
     L.dhc = c.take((size_t)2 * d.F * d.Mp);
     L.dhc_s = c.take((size_t)2 * d.F * d.Mp / 32);
     L.drp = c.take((size_t)d.M * dr_parts(d.F) * 4);
@@ -286,7 +286,7 @@ mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
                               s,
                               [&] {
                                   return mx::launch_quant_rows(xs, batch * R, C, row_codes,
-                                                               row_scales, s);
+                                                               row_scales, false, s);
                               }),
                         "quant_rows");
     if (d_offsets) {
@@ -301,7 +301,8 @@ mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
                               return mx::launch_quant_tiles(xs, batch, R, C, d_offsets,
                                                             d_padded_offsets, d_offsets ? G : 1,
                                                             bound, row_codes, row_scales,
-                                                            col_codes, col_scales, col_ld, s);
+                                                            col_codes, col_scales, col_ld, false,
+                                                            s);
                           }),
                     "quant_tiles");
 }
@@ -433,19 +434,19 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, in
         e = timed("quant_tiles", quant_bytes(M, H, true, true), MX_WORK_BYTES, s, [&] {
             return mx::launch_quant_tiles(static_cast<const uint16_t*>(x), 1, M, H, d_offsets,
                                           poff, E, d.Mp, wb + W.xr, wb + W.xr_s, cb + C.xcol,
-                                          cb + C.xcol_s, d.Mp, s);
+                                          cb + C.xcol_s, d.Mp, true, s);
         });
         if (e != hipSuccess) return launched(e, "quant_tiles(x)");
     }
     // (2) weights: rowwise copies (blocks along H for W1, along F for W2)
     e = timed("quant_rows", quant_bytes((int64_t)E * M2, H, true, false), MX_WORK_BYTES, s, [&] {
         return mx::launch_quant_rows(static_cast<const uint16_t*>(w1), (int64_t)E * M2, H,
-                                     wb + W.w1r, wb + W.w1r_s, s);
+                                     wb + W.w1r, wb + W.w1r_s, true, s);
     });
     if (e != hipSuccess) return launched(e, "quant_rows(w1)");
     e = timed("quant_rows", quant_bytes((int64_t)E * H, F, true, false), MX_WORK_BYTES, s, [&] {
         return mx::launch_quant_rows(static_cast<const uint16_t*>(w2), (int64_t)E * H, F,
-                                     wb + W.w2r, wb + W.w2r_s, s);
+                                     wb + W.w2r, wb + W.w2r_s, true, s);
     });
     if (e != hipSuccess) return launched(e, "quant_rows(w2)");
     if (M == 0) return ok();
@@ -456,13 +457,14 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, in
     p.offs = d_offsets;
     p.G = E;
     p.M = M; p.N = M2; p.K = H;
-    p.A = mx::MxOperand{wb + W.xr, wb + W.xr_s, H, 0};
-    p.B = mx::MxOperand{wb + W.w1r, wb + W.w1r_s, H, M2};
+    p.A = mx::MxOperand{wb + W.xr, wb + W.xr_s, H, 0, true};
+    p.B = mx::MxOperand{wb + W.w1r, wb + W.w1r_s, H, M2, true};
     p.rscale = d_r;
     p.F = F;
     p.h = reinterpret_cast<uint16_t*>(cb + C.h);
     p.qr = wb + W.zr; p.qrs = wb + W.zr_s; p.ldqr = F;
     p.qc = cb + C.zcol; p.qcs = cb + C.zcol_s; p.ldqc = d.Mp;
+    p.qtiled = true;
     p.poff = poff;
     e = gemm(p, mx::Epi::kSwiglu, 2.0 * M * M2 * H, s);
     if (e != hipSuccess) return launched(e, "mx_gemm(gate-up)");
@@ -473,8 +475,8 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, in
     q.offs = d_offsets;
     q.G = E;
     q.M = M; q.N = H; q.K = F;
-    q.A = mx::MxOperand{wb + W.zr, wb + W.zr_s, F, 0};
-    q.B = mx::MxOperand{wb + W.w2r, wb + W.w2r_s, F, H};
+    q.A = mx::MxOperand{wb + W.zr, wb + W.zr_s, F, 0, true};
+    q.B = mx::MxOperand{wb + W.w2r, wb + W.w2r_s, F, H, true};
     q.C = y; q.ldc = H;
     return launched(gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * F, s), "mx_gemm(down)");
 }
@@ -514,20 +516,21 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         e = timed("quant_tiles", quant_bytes(M, H, true, true), MX_WORK_BYTES, s, [&] {
             return mx::launch_quant_tiles(static_cast<const uint16_t*>(dy), 1, M, H, d_offsets,
                                           poff, E, d.Mp, wb + W.dyr, wb + W.dyr_s, wb + W.dycol,
-                                          wb + W.dycol_s, d.Mp, s);
+                                          wb + W.dycol_s, d.Mp, true, s);
         });
         if (e != hipSuccess) return launched(e, "quant_tiles(dy)");
     }
     // (2) weights: columnwise copies (W2 blocks along H, W1 blocks along 2F)
     e = timed("quant_tiles", quant_bytes((int64_t)E * H, F, false, true), MX_WORK_BYTES, s, [&] {
         return mx::launch_quant_tiles(static_cast<const uint16_t*>(w2), E, H, F, nullptr, nullptr,
-                                      1, 0, nullptr, nullptr, wb + W.w2c, wb + W.w2c_s, H, s);
+                                      1, 0, nullptr, nullptr, wb + W.w2c, wb + W.w2c_s, H, true,
+                                      s);
     });
     if (e != hipSuccess) return launched(e, "quant_tiles(w2)");
     e = timed("quant_tiles", quant_bytes((int64_t)E * M2, H, false, true), MX_WORK_BYTES, s, [&] {
         return mx::launch_quant_tiles(static_cast<const uint16_t*>(w1), E, M2, H, nullptr,
                                       nullptr, 1, 0, nullptr, nullptr, wb + W.w1c, wb + W.w1c_s,
-                                      M2, s);
+                                      M2, true, s);
     });
     if (e != hipSuccess) return launched(e, "quant_tiles(w1)");
 
@@ -538,13 +541,14 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         p.offs = d_offsets;
         p.G = E;
         p.M = M; p.N = F; p.K = H;
-        p.A = mx::MxOperand{wb + W.dyr, wb + W.dyr_s, H, 0};
-        p.B = mx::MxOperand{wb + W.w2c, wb + W.w2c_s, H, F};
+        p.A = mx::MxOperand{wb + W.dyr, wb + W.dyr_s, H, 0, true};
+        p.B = mx::MxOperand{wb + W.w2c, wb + W.w2c_s, H, F, true};
         p.rscale = d_r;
         p.F = F;
         p.h = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(cb + C.h));
         p.qr = wb + W.dhr; p.qrs = wb + W.dhr_s; p.ldqr = M2;
         p.qc = wb + W.dhc; p.qcs = wb + W.dhc_s; p.ldqc = d.Mp;
+        p.qtiled = true;
         p.poff = poff;
         p.drp = reinterpret_cast<float*>(wb + W.drp); p.lddrp = nparts;
         e = gemm(p, mx::Epi::kDSwiglu, 2.0 * M * F * H, s);
@@ -561,8 +565,8 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         q.offs = d_offsets;
         q.G = E;
         q.M = M; q.N = H; q.K = M2;
-        q.A = mx::MxOperand{wb + W.dhr, wb + W.dhr_s, M2, 0};
-        q.B = mx::MxOperand{wb + W.w1c, wb + W.w1c_s, M2, H};
+        q.A = mx::MxOperand{wb + W.dhr, wb + W.dhr_s, M2, 0, true};
+        q.B = mx::MxOperand{wb + W.w1c, wb + W.w1c_s, M2, H, true};
         q.C = dx; q.ldc = H;
         e = gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * M2, s);
         if (e != hipSuccess) return launched(e, "mx_gemm(dgrad-gate-up)");
@@ -574,8 +578,8 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
     w.offs = poff;
     w.G = E;
     w.M = H; w.N = F;
-    w.A = mx::MxOperand{wb + W.dycol, wb + W.dycol_s, d.Mp, 0};
-    w.B = mx::MxOperand{cb + C.zcol, cb + C.zcol_s, d.Mp, 0};
+    w.A = mx::MxOperand{wb + W.dycol, wb + W.dycol_s, d.Mp, 0, true};
+    w.B = mx::MxOperand{cb + C.zcol, cb + C.zcol_s, d.Mp, 0, true};
     w.C = dw2; w.ldc = F; w.c_gstride = H * F;
     e = gemm(w, mx::Epi::kStoreBf16, 2.0 * H * F * M, s);
     if (e != hipSuccess) return launched(e, "mx_gemm(wgrad-down)");
@@ -585,8 +589,8 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
     v.offs = poff;
     v.G = E;
     v.M = M2; v.N = H;
-    v.A = mx::MxOperand{wb + W.dhc, wb + W.dhc_s, d.Mp, 0};
-    v.B = mx::MxOperand{cb + C.xcol, cb + C.xcol_s, d.Mp, 0};
+    v.A = mx::MxOperand{wb + W.dhc, wb + W.dhc_s, d.Mp, 0, true};
+    v.B = mx::MxOperand{cb + C.xcol, cb + C.xcol_s, d.Mp, 0, true};
     v.C = dw1; v.ldc = H; v.c_gstride = M2 * H;
     return launched(gemm(v, mx::Epi::kStoreBf16, 2.0 * M2 * H * M, s), "mx_gemm(wgrad-gate-up)");
 }

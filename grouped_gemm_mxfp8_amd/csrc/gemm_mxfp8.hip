@@ -55,6 +55,28 @@ __device__ __forceinline__ v4i make_rsrc(const void* p, int64_t bytes) {
     return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), n, (int)kRsrcWord3};
 }
 
+// Scale source of one operand for one tile: descriptor, this lane's offset
+// (its row), and the scalar offset of K step ks = s0 + ks * sstep.  Row-major
+// scales put the tile's K range in the descriptor; K-step tiled scales (one
+// 128-byte line per 32 rows and K step) start the descriptor at the row group
+// of the first row and reach the step through the scalar offset.
+struct ScaleSrc {
+    v4i rsrc;
+    uint32_t voff, s0, sstep;
+};
+__device__ __forceinline__ ScaleSrc scale_src(const uint8_t* scales, int64_t ld, bool tiled,
+                                              int64_t row0, int64_t rvalid, int64_t lane_row,
+                                              int64_t klo, int64_t K) {
+    if (!tiled) {
+        const int64_t lds = ld / 32;
+        return {make_rsrc(scales + row0 * lds + klo / 32, (rvalid - 1) * lds + K / 32),
+                (uint32_t)(lane_row * lds), 0u, 4u};
+    }
+    const int64_t r0 = row0 & 31, last = r0 + rvalid - 1, rel = r0 + lane_row;
+    return {make_rsrc(scales + (row0 >> 5) * ld, ((last >> 5) + 1) * ld),
+            (uint32_t)((rel >> 5) * ld + (rel & 31) * 4), (uint32_t)(klo >> 7) * 128u, 128u};
+}
+
 // LDS byte address of a __shared__ location.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -236,6 +258,7 @@ struct QDest {
     uint8_t* qc; uint8_t* qcs; int64_t ldqc;    // token-axis codes [cols][ldqc] + scales
     int64_t cw, F;                              // global column of local column 0; F
     bool split;                                 // local columns [C/2, C) go to F + cw
+    bool tiled;                                 // K-step tiled scales (Kp = ldqr / ldqc)
 };
 
 template <int C>
@@ -327,15 +350,22 @@ __device__ __forceinline__ void flush_rows(const uint8_t* st, const QDest& d, in
     const int srow = lane / kRunsPerRow, sblk = (lane % kRunsPerRow) * kRun;
     const int64_t lds = d.ldqr / 32;
     if (srow < 32 && ip * 32 + srow < rows_valid) {
-        const uint32_t soff = (uint32_t)srow * (uint32_t)lds +
-                              ((d.split && sblk >= C / 64) ? (uint32_t)((d.F - C / 2) / 32 + sblk)
-                                                           : (uint32_t)sblk);
-        uint8_t* const sbase = d.qrs + (rbase + ip * 32) * lds + d.cw / 32;
+        const int64_t kb = (d.split && sblk >= C / 64) ? (d.F + d.cw) / 32 + (sblk - C / 64)
+                                                       : d.cw / 32 + sblk;
+        uint8_t* dst;
+        if (d.tiled) {
+            dst = d.qrs + tiled_scale_offset(rbase + ip * 32 + srow, kb, d.ldqr);
+        } else {
+            const uint32_t soff = (uint32_t)srow * (uint32_t)lds +
+                                  ((d.split && sblk >= C / 64) ? (uint32_t)((d.F - C / 2) / 32 + sblk)
+                                                               : (uint32_t)sblk);
+            dst = d.qrs + (rbase + ip * 32) * lds + d.cw / 32 + soff;
+        }
         const uint8_t* src = st + S::kRs + srow * (C / 32) + sblk;
         if constexpr (kRun == 4)
-            *reinterpret_cast<uint32_t*>(sbase + soff) = *reinterpret_cast<const uint32_t*>(src);
+            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
         else
-            *reinterpret_cast<uint16_t*>(sbase + soff) = *reinterpret_cast<const uint16_t*>(src);
+            *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(src);
     }
 }
 
@@ -372,8 +402,9 @@ __device__ __forceinline__ void flush_col_scales(const uint8_t* st, const QDest&
         if (k * 64 + lane < C) {
             const int64_t gcol = (d.split && k * 64 >= C / 2) ? d.F + d.cw + k * 64 - C / 2
                                                               : d.cw + k * 64;
-            uint8_t* const base = d.qcs + gcol * lds + pbase / 32;
-            *reinterpret_cast<uint32_t*>(base + loff) =
+            uint8_t* const dst = d.tiled ? d.qcs + tiled_scale_offset(gcol + lane, pbase / 32, d.ldqc)
+                                         : d.qcs + gcol * lds + pbase / 32 + loff;
+            *reinterpret_cast<uint32_t*>(dst) =
                 *reinterpret_cast<const uint32_t*>(st + S::kCs + (k * 64 + lane) * 4);
         }
     }
@@ -553,11 +584,8 @@ mx_gemm_kernel(GemmProblem p) {
         // buffer, so rows past the valid ones read as zeros whether or not the
         // scalar (K) offset takes part in the range check.
         const int64_t lda = p.A.ld, ldb = p.B.ld;
-        const int64_t ldas = lda / 32, ldbs = ldb / 32;
         const v4i ra =
             make_rsrc(p.A.codes + m0 * lda + klo, (mvalid - 1) * lda + K);
-        const v4i ras =
-            make_rsrc(p.A.scales + m0 * ldas + klo / 32, (mvalid - 1) * ldas + K / 32);
         // B rows are addressed from brow0: the tile's first row, or for the
         // gate-up tile the expert's first W1 row (gate and up halves are F
         // rows apart)
@@ -566,8 +594,6 @@ mx_gemm_kernel(GemmProblem p) {
         const int64_t bvalid = (EPI == Epi::kSwiglu) ? p.N : p.N - n0;
         const v4i rb =
             make_rsrc(p.B.codes + brow0 * ldb + klo, (bvalid - 1) * ldb + K);
-        const v4i rbs =
-            make_rsrc(p.B.scales + brow0 * ldbs + klo / 32, (bvalid - 1) * ldbs + K / 32);
 
         // B row (relative to brow0) staged at tile row b
         auto brow = [&](int b) -> int64_t {
@@ -591,8 +617,11 @@ mx_gemm_kernel(GemmProblem p) {
             aoff[j] = (uint32_t)(r * lda + dma_chunk * 16);
             boff[j] = (uint32_t)(brow(r) * ldb + dma_chunk * 16);
         }
-        const uint32_t asoff = (uint32_t)((wave * 64 + lane) * ldas);
-        const uint32_t bsoff = (uint32_t)(brow(wave * 64 + lane) * ldbs);
+        const ScaleSrc sa = scale_src(p.A.scales, lda, p.A.tiled, m0, mvalid, wave * 64 + lane,
+                                      klo, K);
+        const ScaleSrc sb = scale_src(p.B.scales, ldb, p.B.tiled, brow0, bvalid,
+                                      brow(wave * 64 + lane), klo, K);
+        const v4i ras = sa.rsrc, rbs = sb.rsrc;
 
         v4f acc[8][8];
 #pragma unroll
@@ -609,8 +638,8 @@ mx_gemm_kernel(GemmProblem p) {
                 dma_b128(ra, uni(lds_addr(&sm.a[st][(wave * 8 + j) * 1024])), aoff[j], k0);
                 dma_b128(rb, uni(lds_addr(&sm.b[st][(wave * 8 + j) * 1024])), boff[j], k0);
             }
-            dma_b32(ras, uni(lds_addr(&sm.as[st][wave * 64])), asoff, k0 / 32);
-            dma_b32(rbs, uni(lds_addr(&sm.bs[st][wave * 64])), bsoff, k0 / 32);
+            dma_b32(ras, uni(lds_addr(&sm.as[st][wave * 64])), sa.voff, sa.s0 + ks * sa.sstep);
+            dma_b32(rbs, uni(lds_addr(&sm.bs[st][wave * 64])), sb.voff, sb.s0 + ks * sb.sstep);
         };
 
         // Pipeline over two LDS stages with the loads two K steps ahead:
@@ -686,9 +715,11 @@ mx_gemm_kernel(GemmProblem p) {
                             dma_b128(rb2, uni(lds_addr(&sm.b[cur][(wave * 8 + (u - 8)) * 1024])),
                                      boff[u - 8], k2);
                         else if constexpr (u == 16)
-                            dma_b32(ras2, uni(lds_addr(&sm.as[cur][wave * 64])), asoff, k2 / 32);
+                            dma_b32(ras2, uni(lds_addr(&sm.as[cur][wave * 64])), sa.voff,
+                                    sa.s0 + (ks + 2) * sa.sstep);
                         else
-                            dma_b32(rbs2, uni(lds_addr(&sm.bs[cur][wave * 64])), bsoff, k2 / 32);
+                            dma_b32(rbs2, uni(lds_addr(&sm.bs[cur][wave * 64])), sb.voff,
+                                    sb.s0 + (ks + 2) * sb.sstep);
                     });
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -737,7 +768,7 @@ mx_gemm_kernel(GemmProblem p) {
             const int64_t npad = p.poff[g + 1] - p.poff[g];
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
             const int64_t cw = n0 + wn * 64;                       // wave's first z column
-            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, false};
+            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, false, p.qtiled};
             uint8_t* st = smem + wave * Slot<EPI>::kBytes;
 #pragma nounroll
             for (int ip = 0; ip < 4; ++ip) {
@@ -792,7 +823,7 @@ mx_gemm_kernel(GemmProblem p) {
             const int64_t npad = p.poff[g + 1] - p.poff[g];
             const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
             const int64_t cw = n0 + wn * 128;
-            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true};
+            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true, p.qtiled};
             uint8_t* st = smem + wave * Slot<EPI>::kBytes;
             const int part = (int)(n0 / BN) * 2 + wn;
             // h = [a | b] of unit (ip, jp) (32 rows x 32 columns) is four 1 KiB

@@ -10,29 +10,51 @@ namespace mx {
 constexpr int kTokenAlign = 128;   // padding of token groups in columnwise copies
 constexpr int kMaxGroups = 1024;   // largest expert count the kernels accept
 
+// Scale layouts of a K-major MXFP8 operand with rows r and Kp codes per row
+// (one E8M0 scale per 32 codes, block kb = k / 32):
+//  * row-major:     byte r * (Kp / 32) + kb.
+//  * K-step tiled:  the 4 scales of one GEMM K step (128 codes) of 32
+//    consecutive rows form one 128-byte line, so a K step of a 256-row tile
+//    reads 8 lines instead of 256:
+//      byte ((r / 32) * (Kp / 128) + kb / 4) * 128 + (r % 32) * 4 + kb % 4,
+//    Kp % 128 == 0, rows padded to a multiple of 32 (scales of padding rows
+//    are never used: they only reach output rows that are not stored).
+__host__ __device__ inline int64_t tiled_scale_offset(int64_t r, int64_t kb, int64_t Kp) {
+    return ((r >> 5) * (Kp >> 7) + (kb >> 2)) * 128 + (r & 31) * 4 + (kb & 3);
+}
+inline int64_t tiled_scale_bytes(int64_t rows, int64_t Kp) {
+    return (rows + 31) / 32 * 32 * (Kp / 32);
+}
+
 // ---- quantizer --------------------------------------------------------------
 // Padded offsets of token groups: poff[g] = sum_{j<g} ceil(n_j/128)*128.
 hipError_t launch_padded_offsets(const int64_t* offs, int G, int64_t* poff,
                                  hipStream_t s);
-// Rowwise copy only, over a flat [rows][C] tensor.
+// Rowwise copy only, over a flat [rows][C] tensor (tiled: K-step tiled
+// scales, C % 128 == 0).
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t C,
-                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+                             uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t s);
 // Tile pass: rowwise (optional) and columnwise (optional) copies of
 // x[batch][R][C].  Grouped mode (offs != nullptr, batch == 1) needs poff
 // already computed; row_bound is the padded-length bound (multiple of 128).
+// tiled: both copies get K-step tiled scales (rowwise: rows = batch*R, Kp = C,
+// needs C % 128 == 0 and R % 32 == 0 when batch > 1; columnwise: rows =
+// batch*C, Kp = ld).
 hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
                               int64_t C, const int64_t* offs,
                               const int64_t* poff, int G, int64_t row_bound,
                               uint8_t* rc, uint8_t* rs, uint8_t* cc,
-                              uint8_t* cs, int64_t ld, hipStream_t s);
+                              uint8_t* cs, int64_t ld, bool tiled, hipStream_t s);
 
 // ---- grouped GEMMs ------------------------------------------------------------
-// Operand of a K-major MXFP8 GEMM: codes [rows][ld], scales [rows][ld/32].
+// Operand of a K-major MXFP8 GEMM: codes [rows][ld], scales row-major
+// [rows][ld/32] or K-step tiled (Kp = ld).
 struct MxOperand {
     const uint8_t* codes;
     const uint8_t* scales;
-    int64_t ld;          // bytes between rows of codes (scales: ld/32)
+    int64_t ld;          // bytes between rows of codes
     int64_t gstride;     // rows between consecutive groups (0: shared)
+    bool tiled = false;  // scale layout
 };
 
 enum class Epi : int {
@@ -58,6 +80,7 @@ struct GemmProblem {
     uint16_t* h;                // kSwiglu writes, kDSwiglu reads: bf16 [M][2F]
     uint8_t* qr; uint8_t* qrs; int64_t ldqr;   // rowwise MXFP8 output
     uint8_t* qc; uint8_t* qcs; int64_t ldqc;   // columnwise MXFP8 output
+    bool qtiled;                // fused outputs: K-step tiled scales
     const int64_t* poff;        // padded token offsets of the column copy
     float* drp; int64_t lddrp;  // kDSwiglu: dr partials [M][lddrp]
 };

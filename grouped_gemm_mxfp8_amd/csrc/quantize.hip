@@ -69,7 +69,7 @@ padded_offsets_kernel(const int64_t* __restrict__ offs, int G,
 }
 
 __global__ void __launch_bounds__(256)
-quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nchunk,
+quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nchunk, int64_t C, bool tiled,
                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nchunk; i += stride) {
@@ -87,7 +87,10 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nchunk,
         const uint32_t sc = scale_code_from_amax_bits(m);
         const float inv = inv_scale_from_code(sc);
         reinterpret_cast<uint4*>(codes)[i] = encode16(v, inv);
-        if (!(i & 1)) scales[i >> 1] = (uint8_t)sc;
+        if (!(i & 1)) {
+            const int64_t blk = i >> 1, bpr = C / 32;       // block index, blocks per row
+            scales[tiled ? tiled_scale_offset(blk / bpr, blk % bpr, C) : blk] = (uint8_t)sc;
+        }
     }
 }
 
@@ -111,7 +114,7 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                    const int64_t* __restrict__ poff, int G,
                    uint8_t* __restrict__ rc, uint8_t* __restrict__ rs,
                    uint8_t* __restrict__ cc, uint8_t* __restrict__ cs,
-                   int64_t ld) {
+                   int64_t ld, bool tiled) {
     constexpr int kStride = 65;                      // dwords per column of the tile
     __shared__ uint32_t tile[64 * kStride];
     const int64_t b = blockIdx.z;
@@ -167,9 +170,11 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                     *reinterpret_cast<uint2*>(rc + row * C + ccol) = encode8(v[h], inv_scale_from_code(sc));
                     if (c8 == 0) {
                         // the row's two scale bytes; one 16-bit store when aligned
-                        uint8_t* d = rs + row * (C / 32) + col0 / 32;
+                        // (always in the tiled layout: col0 / 32 is even)
+                        uint8_t* d = rs + (tiled ? tiled_scale_offset(row, col0 / 32, C)
+                                                 : row * (C / 32) + col0 / 32);
                         const bool two = col0 + 64 <= C;
-                        if (two && !((C / 32) & 1)) {
+                        if (two && (tiled || !((C / 32) & 1))) {
                             *reinterpret_cast<uint16_t*>(d) = (uint16_t)(sc | (sc_hi << 8));
                         } else {
                             d[0] = (uint8_t)sc;
@@ -213,7 +218,8 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
     dst[0] = encode16(v, inv);
     dst[1] = encode16(v + 16, inv);
     if (blk == 0)
-        *reinterpret_cast<uint32_t*>(cs + crow * (ld / 32) + p0 / 32) =
+        *reinterpret_cast<uint32_t*>(cs + (tiled ? tiled_scale_offset(crow, p0 / 32, ld)
+                                                 : crow * (ld / 32) + p0 / 32)) =
             sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
 }
 
@@ -226,14 +232,14 @@ hipError_t launch_padded_offsets(const int64_t* offs, int G, int64_t* poff,
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t C,
-                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                             uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t s) {
     const int64_t nchunk = rows * C / 16;
     if (nchunk == 0) return hipSuccess;
     int64_t blocks = (nchunk + 255) / 256;
     const int64_t cap = (int64_t)device_cu_count() * 16;
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       x, nchunk, codes, scales);
+                       x, nchunk, C, tiled, codes, scales);
     return hipGetLastError();
 }
 
@@ -241,12 +247,12 @@ hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
                               int64_t C, const int64_t* offs,
                               const int64_t* poff, int G, int64_t row_bound,
                               uint8_t* rc, uint8_t* rs, uint8_t* cc,
-                              uint8_t* cs, int64_t ld, hipStream_t s) {
+                              uint8_t* cs, int64_t ld, bool tiled, hipStream_t s) {
     const int64_t ytiles = offs ? row_bound / 128 : (R + 127) / 128;
     if (ytiles == 0 || C == 0 || batch == 0) return hipSuccess;
     dim3 grid((unsigned)((C + 63) / 64), (unsigned)ytiles, (unsigned)batch);
     hipLaunchKernelGGL(quant_tiles_kernel, grid, dim3(256), 0, s, x, R, C, offs,
-                       poff, G, rc, rs, cc, cs, ld);
+                       poff, G, rc, rs, cc, cs, ld, tiled);
     return hipGetLastError();
 }
 

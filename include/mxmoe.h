@@ -190,12 +190,15 @@ size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
  *                   is 1 KiB at byte ((pr/16)*(F/16) + c/16)*1024; within it
  *                   lane l = 16*q + r holds 16 bytes: gate h[pr+r][c+4q+v] for
  *                   v = 0..3, then up h[pr+r][F+c+4q+v].  Mp*F*4 bytes.
- *   MX_CTX_XCOL     X columnwise codes [H][Mp] then scales [H][Mp/32]
- *   MX_CTX_ZCOL     z columnwise codes [F][Mp] then scales [F][Mp/32]
+ *   MX_CTX_XCOL     X columnwise codes [H][Mp] then scales
+ *   MX_CTX_ZCOL     z columnwise codes [F][Mp] then scales
  *   MX_CTX_POFF     int64 [E+1] padded token offsets
  * with Mp = mx_padded_rows_bound(M, E, 128).  In every codes-then-scales
  * pair here and below, the scales start at the first 256-byte boundary after
- * the last code byte.  Returns -1 on bad arguments.
+ * the last code byte, and (unlike the public entry points' row-major scales)
+ * are K-step tiled: for codes [R][Kp], the scale of row r and block kb (codes
+ * kb*32 .. kb*32+31) is byte ((r/32)*(Kp/128) + kb/4)*128 + (r%32)*4 + kb%4,
+ * with R rounded up to a multiple of 32.  Returns -1 on bad arguments.
  */
 enum { MX_CTX_H = 0, MX_CTX_XCOL = 1, MX_CTX_ZCOL = 2, MX_CTX_POFF = 3 };
 int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F,
@@ -203,8 +206,8 @@ int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F,
 
 /*
  * Views into the forward/backward workspaces, for tests: the rowwise z
- * (codes [M][F] + scales [M][F/32]) the forward fed its down projection, and
- * the rowwise and columnwise dh of the backward (codes [M][2F] + scales;
+ * (codes [M][F] + K-step tiled scales) the forward fed its down projection,
+ * and the rowwise and columnwise dh of the backward (codes [M][2F] + scales;
  * columnwise codes [2F][Mp] + scales).  Returns -1 on bad arguments.
  */
 enum { MX_WS_ZROW = 0, MX_WS_DHROW = 1, MX_WS_DHCOL = 2 };
