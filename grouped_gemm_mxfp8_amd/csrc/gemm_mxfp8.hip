@@ -85,32 +85,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Global -> LDS load of 16 (or 4) bytes per lane: lane l's bytes land at LDS
 // address lds + 16*l (4*l).  Issued through inline asm so that the compiler
 // does not track it: the kernel waits for these loads itself with vmcnt.
-// M0 carries the LDS base and is restored afterwards.
+// M0 carries the LDS base (declared clobbered: no other instruction in these
+// kernels reads M0); one wait state separates the M0 write from the load.
 __device__ __forceinline__ void dma_b128(const v4i& rsrc, uint32_t lds, uint32_t voff,
                                          uint32_t soff) {
-    uint32_t saved;
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
+        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
         : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-        : "memory");
+        : "memory", "m0");
 }
 __device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t voff,
                                         uint32_t soff) {
-    uint32_t saved;
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
+        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dword %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
+        "buffer_load_dword %1, %2, %3 offen lds"
+        :
         : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-        : "memory");
+        : "memory", "m0");
 }
 
 // Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>),
@@ -629,98 +624,118 @@ mx_gemm_kernel(GemmProblem p) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        // one step's loads: 8 + 8 + 2 instructions per wave (the vmcnt count
-        // the main loop waits on); used for the two steps of the prologue
-        auto issue = [&](int st, int ks) {
+        // One K step's loads: 8 + 8 + 2 instructions per wave into stage st
+        // (u < 8: A rows, u < 16: B rows, 16: A scales, 17: B scales).  Steps
+        // at or past nk use zero-range descriptors: they write zeros into a
+        // stage nobody reads, so every step issues the same instructions and
+        // the vmcnt counts below hold without branches.
+        auto dma_u = [&](auto uc, int st, int ks) {
+            constexpr int u = decltype(uc)::value;
+            const bool live = ks < nk;
             const uint32_t k0 = (uint32_t)ks * BK;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                dma_b128(ra, uni(lds_addr(&sm.a[st][(wave * 8 + j) * 1024])), aoff[j], k0);
-                dma_b128(rb, uni(lds_addr(&sm.b[st][(wave * 8 + j) * 1024])), boff[j], k0);
+            if constexpr (u < 8) {
+                const v4i r = live ? ra : v4i{ra.x, ra.y, 0, ra.w};
+                dma_b128(r, uni(lds_addr(&sm.a[st][(wave * 8 + u) * 1024])), aoff[u], k0);
+            } else if constexpr (u < 16) {
+                const v4i r = live ? rb : v4i{rb.x, rb.y, 0, rb.w};
+                dma_b128(r, uni(lds_addr(&sm.b[st][(wave * 8 + (u - 8)) * 1024])), boff[u - 8], k0);
+            } else if constexpr (u == 16) {
+                const v4i r = live ? ras : v4i{ras.x, ras.y, 0, ras.w};
+                dma_b32(r, uni(lds_addr(&sm.as[st][wave * 64])), sa.voff, sa.s0 + ks * sa.sstep);
+            } else {
+                const v4i r = live ? rbs : v4i{rbs.x, rbs.y, 0, rbs.w};
+                dma_b32(r, uni(lds_addr(&sm.bs[st][wave * 64])), sb.voff, sb.s0 + ks * sb.sstep);
             }
-            dma_b32(ras, uni(lds_addr(&sm.as[st][wave * 64])), sa.voff, sa.s0 + ks * sa.sstep);
-            dma_b32(rbs, uni(lds_addr(&sm.bs[st][wave * 64])), sb.voff, sb.s0 + ks * sb.sstep);
         };
 
-        // Pipeline over two LDS stages with the loads two K steps ahead:
-        // stage (k & 1) holds step k.  Once every wave has step k's fragments
-        // in registers the stage is free, and the 18 load instructions of step
-        // k+2 go into it, spread over the MFMA rows so the vector memory path
-        // (the scarce resource: about 20 bytes per clock per CU) never idles.
-        // The "stage free" barrier sits after the first two MFMA rows so those
-        // rows overlap the tail of the fragment reads.  Barriers fence LDS only
-        // (a workgroup fence would also wait for the loads still in flight);
-        // each wave waits for its own loads with vmcnt.  Past the last step
-        // the loads use a zero-range descriptor: they write zeros into a stage
-        // nobody reads again, which keeps the instruction stream branch-free.
+        // Fragments of stage st into registers.  The scaled 16x16x128 MFMA
+        // reads a lane's 32 operand bytes as two 16-byte runs of K, [16q,
+        // 16q+16) and [64+16q, 64+16q+16), and the scale byte of lane (r, q)
+        // as that of K block q of row r (pinned on the device by per-block
+        // scale probes).
+        v8i af[8], bfr[8];
+        int asc[8], bsc[8];
+        auto read_a = [&](auto ic, int st) {
+            constexpr int i = decltype(ic)::value;
+            const int row = wm * 128 + i * 16 + r16;
+            const uint8_t* base = &sm.a[st][row * BK];
+            const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+            const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+            af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            asc[i] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
+        };
+        auto read_b = [&](auto jc, int st) {
+            constexpr int j = decltype(jc)::value;
+            const int row = wn * 128 + j * 16 + r16;
+            const uint8_t* base = &sm.b[st][row * BK];
+            const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+            const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+            bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
+        };
+        auto mfma = [&](auto ic, auto jc) {
+            constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
+        };
+
+        // Software pipeline over two LDS stages (stage k & 1 holds step k):
+        //  * S1 (start of step k): every wave has step k's fragments in
+        //    registers, so stage k is free; the 18 loads of step k+2 go into
+        //    it, 12 spread over pass A and 6 over pass B.
+        //  * pass A: MFMA rows 0..3 over the 8 columns.
+        //  * S2: vmcnt(12) -- this wave's loads of step k+1 have landed (only
+        //    the 12 pass-A loads of step k+2 may still be in flight) -- then a
+        //    barrier, after which stage k+1 is complete for every wave.  The
+        //    next step's A rows 0..3 are read into the registers pass A freed.
+        //  * pass B: MFMA rows 4..7; after column j the next step's B
+        //    fragment j is read, and in the last column each A row i is read
+        //    as soon as its last MFMA has issued.
+        // So the LDS reads overlap the MFMAs and use no extra registers, and
+        // each load has about one and a half steps to land.  Barriers fence
+        // LDS only (a workgroup fence would also wait for loads in flight).
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // previous tile's stores
-        if (nk > 0) issue(0, 0);
-        if (nk > 1) issue(1, 1);
+        static_for<18>([&](auto uc) { dma_u(uc, 0, 0); });
+        static_for<18>([&](auto uc) { dma_u(uc, 1, 1); });
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // step 0 (this wave)
+        lds_barrier();                                      // step 0 (every wave)
+        static_for<8>([&](auto ic) { read_a(ic, 0); });
+        static_for<8>([&](auto jc) { read_b(jc, 0); });
         for (int ks = 0; ks < nk; ++ks) {
-            const int cur = ks & 1;
-            if (ks + 1 < nk)
-                asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();                     // step ks has landed for every wave
-            // ---- fragments of stage cur into registers ----
-            // The scaled 16x16x128 MFMA reads a lane's 32 operand bytes as
-            // two 16-byte runs of K, [16q, 16q+16) and [64+16q, 64+16q+16),
-            // and the scale byte of lane (r, q) as that of K block q of row r
-            // (pinned on the device by per-block scale probes).
-            v8i af[8], bfr[8];
-            int asc[8], bsc[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int row = wm * 128 + i * 16 + r16;
-                const uint8_t* base = &sm.a[cur][row * BK];
-                const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-                const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
-                af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                asc[i] = reinterpret_cast<const uint8_t*>(sm.as[cur])[row * 4 + q];
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int row = wn * 128 + j * 16 + r16;
-                const uint8_t* base = &sm.b[cur][row * BK];
-                const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-                const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
-                bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[cur])[row * 4 + q];
-            }
-            const bool more = ks + 2 < nk;
-            const uint32_t k2 = (uint32_t)(ks + 2) * BK;
-            const v4i ra2 = more ? ra : v4i{ra.x, ra.y, 0, ra.w};
-            const v4i rb2 = more ? rb : v4i{rb.x, rb.y, 0, rb.w};
-            const v4i ras2 = more ? ras : v4i{ras.x, ras.y, 0, ras.w};
-            const v4i rbs2 = more ? rbs : v4i{rbs.x, rbs.y, 0, rbs.w};
-            static_for<8>([&](auto jc) {
+            const int cur = ks & 1, nxt = cur ^ 1;
+            lds_barrier();                                  // S1: stage cur is free
+            static_for<8>([&](auto jc) {                    // pass A
                 constexpr int j = decltype(jc)::value;
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
+                static_for<4>([&](auto ic) { mfma(ic, jc); });
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (j == 1) lds_barrier();   // every wave is done with stage cur
-                if constexpr (j >= 2) {
-                    // the 18 loads of step ks+2, three per row over rows 2..7
-                    static_for<3>([&](auto uc) {
-                        constexpr int u = (j - 2) * 3 + decltype(uc)::value;
-                        if constexpr (u < 8)
-                            dma_b128(ra2, uni(lds_addr(&sm.a[cur][(wave * 8 + u) * 1024])),
-                                     aoff[u], k2);
-                        else if constexpr (u < 16)
-                            dma_b128(rb2, uni(lds_addr(&sm.b[cur][(wave * 8 + (u - 8)) * 1024])),
-                                     boff[u - 8], k2);
-                        else if constexpr (u == 16)
-                            dma_b32(ras2, uni(lds_addr(&sm.as[cur][wave * 64])), sa.voff,
-                                    sa.s0 + (ks + 2) * sa.sstep);
-                        else
-                            dma_b32(rbs2, uni(lds_addr(&sm.bs[cur][wave * 64])), sb.voff,
-                                    sb.s0 + (ks + 2) * sb.sstep);
+                if constexpr (j < 6) {
+                    dma_u(std::integral_constant<int, 2 * j>{}, cur, ks + 2);
+                    dma_u(std::integral_constant<int, 2 * j + 1>{}, cur, ks + 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+            lds_barrier();                                  // S2: stage nxt complete
+            static_for<4>([&](auto ic) { read_a(ic, nxt); });
+            static_for<8>([&](auto jc) {                    // pass B
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j < 7) {
+                    static_for<4>([&](auto ic) {
+                        mfma(std::integral_constant<int, decltype(ic)::value + 4>{}, jc);
                     });
+                    __builtin_amdgcn_sched_barrier(0);
+                    read_b(jc, nxt);
+                    if constexpr (j < 6) dma_u(std::integral_constant<int, 12 + j>{}, cur, ks + 2);
+                } else {
+                    static_for<4>([&](auto ic) {
+                        constexpr int i = decltype(ic)::value + 4;
+                        mfma(std::integral_constant<int, i>{}, jc);
+                        __builtin_amdgcn_sched_barrier(0);
+                        read_a(std::integral_constant<int, i>{}, nxt);
+                    });
+                    read_b(jc, nxt);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
