@@ -696,7 +696,10 @@ mx_gemm_kernel(GemmProblem p) {
         // So the LDS reads overlap the MFMAs and use no extra registers, and
         // each load has about one and a half steps to land.  Barriers fence
         // LDS only (a workgroup fence would also wait for loads in flight).
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // previous tile's stores
+        // The previous tile's output stores may still be in flight: loads
+        // complete in order among themselves, so the vmcnt waits below stay
+        // sufficient with older stores outstanding (they only make them
+        // stricter), and the stores drain under this tile's first steps.
         static_for<18>([&](auto uc) { dma_u(uc, 0, 0); });
         static_for<18>([&](auto uc) { dma_u(uc, 1, 1); });
         asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // step 0 (this wave)
@@ -759,20 +762,33 @@ mx_gemm_kernel(GemmProblem p) {
             uint16_t* C = reinterpret_cast<uint16_t*>(p.C) +
                           (p.kgroup ? (int64_t)g * p.c_gstride : 0);
             const int64_t cw = n0 + wn * 128;
+            // Lanes q and q^1 (16 lanes apart) hold the same row; one
+            // v_permlane16_swap per dword gives the even lane 8 consecutive
+            // columns of block 2jp and the odd lane 8 of block 2jp+1, so each
+            // row leaves as 64 contiguous bytes in 16-byte stores.  A block
+            // pair (32 columns) is wholly inside or outside N (N % 32 == 0).
+            const int codd = q & 1;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int rl = i * 16 + r16;
-                if (rl >= rows_valid_w) continue;
-                const int64_t row = rwave + rl;
+                const bool rok = rl < rows_valid_w;
+                const int64_t row = rwave + (rok ? rl : 0);
                 const float sc = p.rscale ? p.rscale[row] : 1.0f;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int64_t col = cw + j * 16 + 4 * q;
-                    if (col >= p.N) continue;
-                    float v4[4];
+                for (int jp = 0; jp < 4; ++jp) {
+                    float va[4], vb[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) v4[v] = acc[i][j][v] * sc;
-                    *reinterpret_cast<uint2*>(C + row * p.ldc + col) = pack4_bf16(v4);
+                    for (int v = 0; v < 4; ++v) {
+                        va[v] = acc[i][2 * jp][v] * sc;
+                        vb[v] = acc[i][2 * jp + 1][v] * sc;
+                    }
+                    const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
+                    const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+                    const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+                    const int64_t col = cw + (2 * jp + codd) * 16 + 4 * (q & 2);
+                    if (rok && cw + 2 * jp * 16 < p.N)
+                        *reinterpret_cast<uint4*>(C + row * p.ldc + col) =
+                            make_uint4(x[0], y[0], x[1], y[1]);
                 }
             }
         } else if constexpr (EPI == Epi::kSwiglu) {
@@ -845,11 +861,8 @@ mx_gemm_kernel(GemmProblem p) {
             // blocks, each moved by one global->LDS load into the unit's buffer
             // of the ring.  While slice ip is processed, unit jp's buffer is
             // refilled with unit (ip + 1, jp), so each load has a whole slice
-            // to land.  Blocks past F, past the padded rows or past the last
-            // slice use a zero-range descriptor (zeros, never read).  The wait
-            // before a unit is vmcnt(12): the three other units' loads (12
-            // instructions) always follow it, and anything else issued after
-            // it only makes the wait stricter.
+            // to land.  Blocks past F or past the padded rows use a zero-range
+            // descriptor (zeros, masked); the last slice loads nothing.
             uint8_t* const ring = st + QStage<256>::kBytes;
             auto dma_unit = [&](int ipn, auto jpc, int lane) {
                 constexpr int jp = decltype(jpc)::value;
@@ -888,7 +901,16 @@ mx_gemm_kernel(GemmProblem p) {
                     constexpr int jp = decltype(jpc)::value;
                     float dzu[2][2][4], da[2][2][4], db[2][2][4];
                     uint4 hb[2][2];
-                    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+                    // this unit's ring loads: 12 younger ring loads follow them,
+                    // except in the last slice, which issues none
+                    if (ip < 3) {
+                        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+                    } else {
+                        if constexpr (jp == 0) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+                        if constexpr (jp == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                        if constexpr (jp == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                        if constexpr (jp == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    }
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -896,7 +918,7 @@ mx_gemm_kernel(GemmProblem p) {
                             hb[ii][jj] = *reinterpret_cast<const uint4*>(
                                 ring + ((jp * 2 + ii) * 2 + jj) * 1024 + lane * 16);
                     lds_wait();                 // the buffer is free for the next slice's unit
-                    dma_unit(ip + 1, jpc, lane);
+                    if (ip < 3) dma_unit(ip + 1, jpc, lane);
                     pick_unit<2 * jp>(acc, ip, dzu);
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
@@ -939,9 +961,7 @@ mx_gemm_kernel(GemmProblem p) {
             }
             if (cw < F && rows_pad_w > 0) flush_col_scales<256>(st, d, prow, lane);
         }
-        // the next tile's loads overwrite other waves' staging areas (and the
-        // backward's trailing ring loads must land before they do)
-        if constexpr (EPI == Epi::kDSwiglu) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the next tile's loads overwrite other waves' staging areas
         if constexpr (EPI != Epi::kStoreBf16) lds_barrier();
     }
 }
