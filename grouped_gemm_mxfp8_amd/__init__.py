@@ -23,7 +23,7 @@ MX_DTYPE_BF16 = 0
 MX_DTYPE_MXFP8 = 1
 TOKEN_ALIGN = 128
 BLOCK = 32
-MX_CTX_H, MX_CTX_XCOL, MX_CTX_ZCOL, MX_CTX_POFF = 0, 1, 2, 3
+MX_CTX_H, MX_CTX_XCOL, MX_CTX_ZCOL, MX_CTX_POFF, MX_CTX_W1COL, MX_CTX_W2COL = 0, 1, 2, 3, 4, 5
 MX_WS_ZROW, MX_WS_DHROW, MX_WS_DHCOL = 0, 1, 2
 
 _lib = None
@@ -245,6 +245,15 @@ class MlpCtx:
         """Token-axis MXFP8 copy of z: codes [F, Mp], scales [F, Mp/32]
         (row-major copy of the tiled scales)."""
         return self._mx(MX_CTX_ZCOL, (self.F, self.padded_rows))
+
+    def w1col(self) -> MxTensor:
+        """Columnwise MXFP8 copy of W1 made by the forward: codes [E*H, 2F]
+        (row e*H + k is column k of expert e's W1), scales [E*H, 2F/32]."""
+        return self._mx(MX_CTX_W1COL, (self.E * self.H, 2 * self.F))
+
+    def w2col(self) -> MxTensor:
+        """Columnwise MXFP8 copy of W2: codes [E*F, H], scales [E*F, H/32]."""
+        return self._mx(MX_CTX_W2COL, (self.E * self.F, self.H))
 
     def padded_offsets(self) -> torch.Tensor:
         return _region(self.buf, self._off(MX_CTX_POFF), (self.E + 1,), torch.int64)[0]

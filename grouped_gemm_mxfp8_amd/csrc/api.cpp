@@ -105,7 +105,7 @@ struct MlpDims {
 };
 
 struct CtxLayout {
-    size_t h, xcol, xcol_s, zcol, zcol_s, poff, total;
+    size_t h, xcol, xcol_s, zcol, zcol_s, poff, w1c, w1c_s, w2c, w2c_s, total;
 };
 CtxLayout ctx_layout(const MlpDims& d) {
     Carver c;
@@ -116,6 +116,12 @@ CtxLayout ctx_layout(const MlpDims& d) {
     L.zcol = c.take((size_t)d.F * d.Mp);
     L.zcol_s = c.take((size_t)d.F * d.Mp / 32);
     L.poff = c.take((size_t)(d.E + 1) * 8);
+    // columnwise weight copies made by the forward's weight pass, for the
+    // data-gradient GEMMs of the backward
+    L.w1c = c.take((size_t)d.E * d.H * 2 * d.F);
+    L.w1c_s = c.take((size_t)d.E * d.H * 2 * d.F / 32);
+    L.w2c = c.take((size_t)d.E * d.F * d.H);
+    L.w2c_s = c.take((size_t)d.E * d.F * d.H / 32);
     L.total = c.off;
     return L;
 }
@@ -141,7 +147,7 @@ FwdWs fwd_ws_layout(const MlpDims& d) {
 int64_t dr_parts(int64_t F) { return (F + 255) / 256 * 2; }
 
 struct BwdWs {
-    size_t dyr, dyr_s, dycol, dycol_s, w2c, w2c_s, w1c, w1c_s, dhr, dhr_s, dhc, dhc_s, drp, total;
+    size_t dyr, dyr_s, dycol, dycol_s, dhr, dhr_s, dhc, dhc_s, drp, total;
 };
 BwdWs bwd_ws_layout(const MlpDims& d) {
     Carver c;
@@ -150,10 +156,6 @@ BwdWs bwd_ws_layout(const MlpDims& d) {
     L.dyr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
     L.dycol = c.take((size_t)d.H * d.Mp);
     L.dycol_s = c.take((size_t)d.H * d.Mp / 32);
-    L.w2c = c.take((size_t)d.E * d.F * d.H);
-    L.w2c_s = c.take((size_t)d.E * d.F * d.H / 32);
-    L.w1c = c.take((size_t)d.E * d.H * 2 * d.F);
-    L.w1c_s = c.take((size_t)d.E * d.H * 2 * d.F / 32);
     L.dhr = c.take((size_t)d.M * 2 * d.F);
     L.dhr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, 2 * d.F));
     L.dhc = c.take((size_t)2 * d.F * d.Mp);
@@ -383,6 +385,8 @@ int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F, i
         case MX_CTX_XCOL: return (int64_t)L.xcol;
         case MX_CTX_ZCOL: return (int64_t)L.zcol;
         case MX_CTX_POFF: return (int64_t)L.poff;
+        case MX_CTX_W1COL: return (int64_t)L.w1c;
+        case MX_CTX_W2COL: return (int64_t)L.w2c;
         default: return -1;
     }
 }
@@ -438,17 +442,21 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, in
         });
         if (e != hipSuccess) return launched(e, "quant_tiles(x)");
     }
-    // (2) weights: rowwise copies (blocks along H for W1, along F for W2)
-    e = timed("quant_rows", quant_bytes((int64_t)E * M2, H, true, false), MX_WORK_BYTES, s, [&] {
-        return mx::launch_quant_rows(static_cast<const uint16_t*>(w1), (int64_t)E * M2, H,
-                                     wb + W.w1r, wb + W.w1r_s, true, s);
+    // (2) weights, one pass each: rowwise copies for the forward GEMMs (W1
+    // blocks along H, W2 along F) and the columnwise copies the backward's
+    // data gradients use (W1 blocks along 2F, W2 along H), saved in ctx
+    e = timed("quant_tiles", quant_bytes((int64_t)E * M2, H, true, true), MX_WORK_BYTES, s, [&] {
+        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w1), E, M2, H, nullptr,
+                                      nullptr, 1, 0, wb + W.w1r, wb + W.w1r_s, cb + C.w1c,
+                                      cb + C.w1c_s, M2, true, s);
     });
-    if (e != hipSuccess) return launched(e, "quant_rows(w1)");
-    e = timed("quant_rows", quant_bytes((int64_t)E * H, F, true, false), MX_WORK_BYTES, s, [&] {
-        return mx::launch_quant_rows(static_cast<const uint16_t*>(w2), (int64_t)E * H, F,
-                                     wb + W.w2r, wb + W.w2r_s, true, s);
+    if (e != hipSuccess) return launched(e, "quant_tiles(w1)");
+    e = timed("quant_tiles", quant_bytes((int64_t)E * H, F, true, true), MX_WORK_BYTES, s, [&] {
+        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w2), E, H, F, nullptr, nullptr,
+                                      1, 0, wb + W.w2r, wb + W.w2r_s, cb + C.w2c, cb + C.w2c_s, H,
+                                      true, s);
     });
-    if (e != hipSuccess) return launched(e, "quant_rows(w2)");
+    if (e != hipSuccess) return launched(e, "quant_tiles(w2)");
     if (M == 0) return ok();
 
     // (3) gate-up GEMM with the SwiGLU / routing-scale / requantize epilogue
@@ -520,19 +528,7 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         });
         if (e != hipSuccess) return launched(e, "quant_tiles(dy)");
     }
-    // (2) weights: columnwise copies (W2 blocks along H, W1 blocks along 2F)
-    e = timed("quant_tiles", quant_bytes((int64_t)E * H, F, false, true), MX_WORK_BYTES, s, [&] {
-        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w2), E, H, F, nullptr, nullptr,
-                                      1, 0, nullptr, nullptr, wb + W.w2c, wb + W.w2c_s, H, true,
-                                      s);
-    });
-    if (e != hipSuccess) return launched(e, "quant_tiles(w2)");
-    e = timed("quant_tiles", quant_bytes((int64_t)E * M2, H, false, true), MX_WORK_BYTES, s, [&] {
-        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w1), E, M2, H, nullptr,
-                                      nullptr, 1, 0, nullptr, nullptr, wb + W.w1c, wb + W.w1c_s,
-                                      M2, true, s);
-    });
-    if (e != hipSuccess) return launched(e, "quant_tiles(w1)");
+    // (2) the weights' columnwise copies were made by the forward (ctx)
 
     if (M > 0) {
         // (3) dz = dY W2 with the SwiGLU-backward / dr / requantize epilogue
@@ -542,7 +538,7 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         p.G = E;
         p.M = M; p.N = F; p.K = H;
         p.A = mx::MxOperand{wb + W.dyr, wb + W.dyr_s, H, 0, true};
-        p.B = mx::MxOperand{wb + W.w2c, wb + W.w2c_s, H, F, true};
+        p.B = mx::MxOperand{cb + C.w2c, cb + C.w2c_s, H, F, true};
         p.rscale = d_r;
         p.F = F;
         p.h = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(cb + C.h));
@@ -566,7 +562,7 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         q.G = E;
         q.M = M; q.N = H; q.K = M2;
         q.A = mx::MxOperand{wb + W.dhr, wb + W.dhr_s, M2, 0, true};
-        q.B = mx::MxOperand{wb + W.w1c, wb + W.w1c_s, M2, H, true};
+        q.B = mx::MxOperand{cb + C.w1c, cb + C.w1c_s, M2, H, true};
         q.C = dx; q.ldc = H;
         e = gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * M2, s);
         if (e != hipSuccess) return launched(e, "mx_gemm(dgrad-gate-up)");

@@ -167,7 +167,10 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E,
  *
  *   dy bf16 [M][H]; outputs dx bf16 [M][H], dw1 bf16 [E][2F][H],
  *   dw2 bf16 [E][H][F], d_dr fp32 [M].  Same sizes, x-free: the forward's
- *   ctx holds what is needed.  ws of grouped_mlp_bwd_ws_bytes() bytes.
+ *   ctx holds what is needed, including the quantized columnwise copies of
+ *   w1 and w2 made by the forward (w1 and w2 must be the tensors given to
+ *   the forward that wrote ctx; the backward only checks them for NULL and
+ *   alignment).  ws of grouped_mlp_bwd_ws_bytes() bytes.
  */
 mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E,
                           int64_t M, int64_t H, int64_t F, const void* w1,
@@ -193,6 +196,8 @@ size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
  *   MX_CTX_XCOL     X columnwise codes [H][Mp] then scales
  *   MX_CTX_ZCOL     z columnwise codes [F][Mp] then scales
  *   MX_CTX_POFF     int64 [E+1] padded token offsets
+ *   MX_CTX_W1COL    W1 columnwise codes [E*H][2F] (blocks along 2F) + scales
+ *   MX_CTX_W2COL    W2 columnwise codes [E*F][H] (blocks along H) + scales
  * with Mp = mx_padded_rows_bound(M, E, 128).  In every codes-then-scales
  * pair here and below, the scales start at the first 256-byte boundary after
  * the last code byte, and (unlike the public entry points' row-major scales)
@@ -200,7 +205,8 @@ size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
  * kb*32 .. kb*32+31) is byte ((r/32)*(Kp/128) + kb/4)*128 + (r%32)*4 + kb%4,
  * with R rounded up to a multiple of 32.  Returns -1 on bad arguments.
  */
-enum { MX_CTX_H = 0, MX_CTX_XCOL = 1, MX_CTX_ZCOL = 2, MX_CTX_POFF = 3 };
+enum { MX_CTX_H = 0, MX_CTX_XCOL = 1, MX_CTX_ZCOL = 2, MX_CTX_POFF = 3, MX_CTX_W1COL = 4,
+       MX_CTX_W2COL = 5 };
 int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F,
                                int32_t E);
 

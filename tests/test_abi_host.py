@@ -66,12 +66,12 @@ def test_mlp_sizes(mxlib):
     ctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
     Mp = mxlib.mx_padded_rows_bound(M, E, 128)
     # h (bf16, 16x16 blocks over padded rows: Mp*F*4 bytes) + X and z token-axis
-    # copies + scales + padded offsets
-    need = Mp * F * 4 + (H + F) * Mp * (1 + 1 / 32)
+    # copies + scales + padded offsets + the weights' columnwise copies + scales
+    need = Mp * F * 4 + (H + F) * Mp * (1 + 1 / 32) + E * (2 * F * H + F * H) * (1 + 1 / 32)
     assert need <= ctx <= need + 64 * 256
     assert mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E) > 0
     assert mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E) > 0
-    for which in range(4):
+    for which in range(6):
         off = mxlib.grouped_mlp_ctx_offset(which, M, H, F, E)
         assert 0 <= off < ctx and off % 256 == 0
     assert mxlib.grouped_mlp_ctx_offset(9, M, H, F, E) == -1

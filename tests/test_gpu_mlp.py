@@ -110,6 +110,12 @@ def run_case(dev, case):
     assert np.array_equal(ctx.xcol().scales.cpu().numpy()[:, : n // 32], xs_o)
     rep.rate("zcol flips", np.mean(ctx.zcol().codes.cpu().numpy()[:, :n]
                                    != O.quantize_tokens(z_ref, off_np)[0]), FLIP_MAX)
+    # the weights' columnwise copies the forward saved for the backward:
+    # blocks along 2F (W1) and along H (W2), bit-exact
+    for got, w64 in ((ctx.w1col(), W164), (ctx.w2col(), W264)):
+        c_ref, s_ref = O.quantize_lastdim(w64.transpose(0, 2, 1))
+        assert np.array_equal(got.codes.cpu().numpy(), c_ref.reshape(-1, c_ref.shape[-1]))
+        assert np.array_equal(got.scales.cpu().numpy(), s_ref.reshape(-1, s_ref.shape[-1]))
 
     # ---- backward, stage by stage (on the GPU's own saved h and codes) ----
     dz_ref = O.grouped_linear(O.qdq_lastdim(dY64), O.qdq_lastdim(W264.transpose(0, 2, 1)),
