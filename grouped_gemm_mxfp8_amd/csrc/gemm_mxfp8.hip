@@ -920,21 +920,23 @@ mx_gemm_kernel(GemmProblem p) {
                     lds_wait();                 // the buffer is free for the next slice's unit
                     if (ip < 3) dma_unit(ip + 1, jpc, lane);
                     pick_unit<2 * jp>(acc, ip, dzu);
+                    // No masking: rows past the expert's end have dz = 0 (their
+                    // A rows read as zeros) and h = 0 (padded rows of the
+                    // forward), and a wave's columns are all below F or all
+                    // past it (dz = 0, h loads of zero range), so every
+                    // output below is 0 where it is not stored.
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
-                        const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
-                            const int j = 2 * jp + jj;
-                            const bool ok = rv && (cw + j * 16 + 4 * q) < F;
                             float a[4], b[4];
                             const uint4 hv = hb[ii][jj];
                             unpack4_bf16(make_uint2(hv.x, hv.y), a);
                             unpack4_bf16(make_uint2(hv.z, hv.w), b);
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
-                                const float av = ok ? a[v] : 0.f, bv = ok ? b[v] : 0.f;
-                                const float dz = ok ? dzu[ii][jj][v] : 0.f;
+                                const float av = a[v], bv = b[v];
+                                const float dz = dzu[ii][jj][v];
                                 float sg;
                                 const float sl_ = silu_sig(av, sg);
                                 drs[ii] += dz * (sl_ * bv);

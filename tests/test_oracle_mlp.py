@@ -198,3 +198,35 @@ def test_parity_metrics_definition():
     assert abs(worst - 0.5 / np.sqrt(12.5)) < 1e-12
     got[1, 0] = 1e-30
     assert O.parity_metrics(got, ref)[1] == np.inf
+
+
+def test_single_expert_slices_equal_the_full_computation():
+    """The full-size GPU tests compare against the oracle run on one expert
+    alone, or on a subset of one expert's rows: pin that this equals the
+    corresponding slice of the oracle run on all experts (weight gradients
+    only for whole experts)."""
+    from tests._oracle_workers import expert_reference
+    rng = np.random.default_rng(11)
+    counts = [70, 0, 129, 33]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    M, H, F, E = int(off[-1]), 64, 96, len(counts)
+    bf = lambda *s, std=1.0: O.round_bf16(rng.standard_normal(s) * std)
+    X, dY = bf(M, H), bf(M, H)
+    W1, W2 = bf(E, 2 * F, H, std=0.05), bf(E, H, F, std=0.05)
+    r = rng.uniform(0.1, 1.0, M)
+    Y, saved = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved)
+    # equal up to fp64 summation order (BLAS may block a sub-problem differently)
+    same = lambda a, b: np.testing.assert_allclose(a, b, rtol=1e-10,
+                                                   atol=1e-12 * max(1.0, np.abs(b).max()))
+    for e in (0, 2, 3):
+        lo, hi = off[e], off[e + 1]
+        Ye, dXe, dre, dW1e, dW2e = expert_reference(X[lo:hi], W1[e], W2[e], r[lo:hi], dY[lo:hi])
+        same(Ye, Y[lo:hi]); same(dXe, g["dX"][lo:hi]); same(dre, g["dr"][lo:hi])
+        same(dW1e, g["dW1"][e]); same(dW2e, g["dW2"][e])
+    # a row subset of expert 2 (rows 0..4, 64..69, 120..128): row-local outputs
+    lo = off[2]
+    rows = np.r_[0:5, 64:70, 120:129]
+    Ys, dXs, drs, _, _ = expert_reference(X[lo + rows], W1[2], W2[2], r[lo + rows],
+                                          dY[lo + rows])
+    same(Ys, Y[lo + rows]); same(dXs, g["dX"][lo + rows]); same(drs, g["dr"][lo + rows])
