@@ -287,15 +287,19 @@ def bwd_ws_bytes(M, H, F, E) -> int:
     return int(lib().grouped_mlp_bwd_ws_bytes(M, H, F, E))
 
 
-def grouped_mlp_fwd(x, offsets, w1, w2, r, ws: Optional[torch.Tensor] = None):
-    """Fused GroupedMLP forward.  Returns (y bf16 [M, H], MlpCtx)."""
+def grouped_mlp_fwd(x, offsets, w1, w2, r, ws: Optional[torch.Tensor] = None,
+                    ctx_buf: Optional[torch.Tensor] = None):
+    """Fused GroupedMLP forward.  Returns (y bf16 [M, H], MlpCtx).  ``ws`` and
+    ``ctx_buf`` are optional caller-owned uint8 buffers (allocated when
+    missing or too small)."""
     dev, M, H, F, E = _mlp_check(x, offsets, w1, w2, r)
     L = lib()
     nctx = L.grouped_mlp_ctx_bytes(M, H, F, E)
     nws = L.grouped_mlp_fwd_ws_bytes(M, H, F, E)
     if nctx == 0 or nws == 0:
         raise MxError("grouped_mlp_fwd", 2, last_error())
-    ctx = torch.empty(nctx, dtype=torch.uint8, device=dev)
+    ctx = ctx_buf if ctx_buf is not None and ctx_buf.numel() >= nctx else \
+        torch.empty(nctx, dtype=torch.uint8, device=dev)
     if ws is None or ws.numel() < nws:
         ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)

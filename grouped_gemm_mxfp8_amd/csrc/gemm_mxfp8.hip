@@ -821,12 +821,23 @@ mx_gemm_kernel(GemmProblem p) {
                     float gu[2][2][4], uu[2][2][4], z[2][2][4];
                     pick_unit<2 * jp>(acc, ip, gu);
                     pick_unit<2 * jp + 4>(acc, ip, uu);
+                    // Rows past the expert's valid rows are selected to 0 (h
+                    // and z): the padded rows take part in the token-axis
+                    // blocks, and rows past M read never-written scale bytes
+                    // (the tiled layout pads rows to 32), so their
+                    // accumulators may be anything, NaN included.
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const int i = 2 * ip + ii;
+                        const bool rv = i * 16 + r16 < rows_valid_w;
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             const int j = 2 * jp + jj;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                gu[ii][jj][v] = rv ? gu[ii][jj][v] : 0.f;
+                                uu[ii][jj][v] = rv ? uu[ii][jj][v] : 0.f;
+                            }
                             if (rows_pad_w > 0) {
                                 const uint2 g2 = pack4_bf16(gu[ii][jj]), u2 = pack4_bf16(uu[ii][jj]);
                                 *h_block(p.h, prow + i * 16, cw + j * 16, F, lane) =
@@ -920,13 +931,16 @@ mx_gemm_kernel(GemmProblem p) {
                     lds_wait();                 // the buffer is free for the next slice's unit
                     if (ip < 3) dma_unit(ip + 1, jpc, lane);
                     pick_unit<2 * jp>(acc, ip, dzu);
-                    // No masking: rows past the expert's end have dz = 0 (their
-                    // A rows read as zeros) and h = 0 (padded rows of the
-                    // forward), and a wave's columns are all below F or all
-                    // past it (dz = 0, h loads of zero range), so every
-                    // output below is 0 where it is not stored.
+                    // Rows past the expert's valid rows get dz = 0 by a select
+                    // (rows past M read never-written scale bytes, so their
+                    // accumulators may be anything, NaN included); their h is
+                    // 0 (the forward stores 0 there), so da = db = 0 in the
+                    // token-axis blocks they share with valid rows.  A wave's
+                    // columns are all below F or all past it (dz = 0 from
+                    // zero-filled B rows, h loads of zero range).
 #pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
+                        const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
 #pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             float a[4], b[4];
@@ -936,7 +950,7 @@ mx_gemm_kernel(GemmProblem p) {
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
                                 const float av = a[v], bv = b[v];
-                                const float dz = dzu[ii][jj][v];
+                                const float dz = rv ? dzu[ii][jj][v] : 0.f;
                                 float sg;
                                 const float sl_ = silu_sig(av, sg);
                                 drs[ii] += dz * (sl_ * bv);

@@ -63,9 +63,13 @@ def _run_full(dev, case, samples):
     with ProcessPoolExecutor(max_workers=min(len(jobs), 4), mp_context=ctx_mp) as pool:
         futs = [pool.submit(expert_reference, *args) for *_, args in jobs]
         print(f"full size M={M} H={H} F={F} E={E}: running the library", flush=True)
-        fws = torch.empty(gm.fwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
-        bws = torch.empty(gm.bwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
-        y, ctx = gm.grouped_mlp_fwd(case.X, case.offsets, case.W1, case.W2, case.r, ws=fws)
+        # buffers start as 0xFF bytes: nothing unwritten may reach a result
+        fws = torch.full((gm.fwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
+        bws = torch.full((gm.bwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
+        cbuf = torch.full((gm.lib().grouped_mlp_ctx_bytes(M, H, F, E),), 255,
+                          dtype=torch.uint8, device=dev)
+        y, ctx = gm.grouped_mlp_fwd(case.X, case.offsets, case.W1, case.W2, case.r, ws=fws,
+                                    ctx_buf=cbuf)
         dx, dw1, dw2, dr = gm.grouped_mlp_bwd(case.dY, case.offsets, case.W1, case.W2, case.r,
                                               ctx, ws=bws)
         torch.cuda.synchronize()

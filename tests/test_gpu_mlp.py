@@ -81,9 +81,13 @@ def run_case(dev, case):
     poff = O.padded_offsets(off_np)
     x, w1, w2 = case.X.to(dev), case.W1.to(dev), case.W2.to(dev)
     r, off, dy = case.r.to(dev), case.offsets.to(dev), case.dY.to(dev)
-    fws = torch.empty(gm.fwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
-    bws = torch.empty(gm.bwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
-    y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws)
+    # Workspaces and ctx start as 0xFF bytes (E8M0 NaN scales, E4M3 NaN
+    # codes): anything the library reads without having written it shows.
+    fws = torch.full((gm.fwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
+    bws = torch.full((gm.bwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
+    cbuf = torch.full((gm.lib().grouped_mlp_ctx_bytes(M, H, F, E),), 255, dtype=torch.uint8,
+                      device=dev)
+    y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, ctx_buf=cbuf)
     dx, dw1, dw2, dr = gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx, ws=bws)
     torch.cuda.synchronize()
     print(f"case M={M} H={H} F={F} E={E} counts={list(case.counts)}", flush=True)
