@@ -709,37 +709,32 @@ mx_gemm_kernel(GemmProblem p) {
         for (int ks = 0; ks < nk; ++ks) {
             const int cur = ks & 1, nxt = cur ^ 1;
             lds_barrier();                                  // S1: stage cur is free
-            static_for<8>([&](auto jc) {                    // pass A
-                constexpr int j = decltype(jc)::value;
-                static_for<4>([&](auto ic) { mfma(ic, jc); });
+            // Pass A: one MFMA per slot (column j = s / 4, row i = s % 4), the
+            // 12 pass-A loads after slots 1, 4, 6 of every 8, so each
+            // MFMA's execution hides the instructions issued after it.
+            static_for<32>([&](auto sc) {
+                constexpr int s = decltype(sc)::value, r = s % 8, g = s / 8;
+                mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{});
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (j < 6) {
-                    dma_u(std::integral_constant<int, 2 * j>{}, cur, ks + 2);
-                    dma_u(std::integral_constant<int, 2 * j + 1>{}, cur, ks + 2);
-                }
+                constexpr int u = r == 1 ? 3 * g : r == 4 ? 3 * g + 1 : r == 6 ? 3 * g + 2 : -1;
+                if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
                 __builtin_amdgcn_sched_barrier(0);
             });
             asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
             lds_barrier();                                  // S2: stage nxt complete
-            static_for<4>([&](auto ic) { read_a(ic, nxt); });
-            static_for<8>([&](auto jc) {                    // pass B
-                constexpr int j = decltype(jc)::value;
-                if constexpr (j < 7) {
-                    static_for<4>([&](auto ic) {
-                        mfma(std::integral_constant<int, decltype(ic)::value + 4>{}, jc);
-                    });
-                    __builtin_amdgcn_sched_barrier(0);
-                    read_b(jc, nxt);
-                    if constexpr (j < 6) dma_u(std::integral_constant<int, 12 + j>{}, cur, ks + 2);
-                } else {
-                    static_for<4>([&](auto ic) {
-                        constexpr int i = decltype(ic)::value + 4;
-                        mfma(std::integral_constant<int, i>{}, jc);
-                        __builtin_amdgcn_sched_barrier(0);
-                        read_a(std::integral_constant<int, i>{}, nxt);
-                    });
-                    read_b(jc, nxt);
-                }
+            // Pass B: slots s (column j = s / 4, row i = 4 + s % 4); the next
+            // step's A rows 0..3 after slots 0..3, B column j after slot
+            // 4j+3, A row i (4..7) right after its last MFMA (slots 28..31),
+            // the 6 pass-B loads after slots 5, 9, 13, 17, 21, 25.
+            static_for<32>([&](auto sc) {
+                constexpr int s = decltype(sc)::value, j = s / 4, i = 4 + s % 4;
+                mfma(std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (s < 4) read_a(std::integral_constant<int, s>{}, nxt);
+                if constexpr (s >= 28) read_a(std::integral_constant<int, i>{}, nxt);
+                if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
+                if constexpr (s >= 5 && s <= 25 && s % 4 == 1)
+                    dma_u(std::integral_constant<int, 12 + (s - 5) / 4>{}, cur, ks + 2);
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
