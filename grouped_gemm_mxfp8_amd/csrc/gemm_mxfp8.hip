@@ -283,7 +283,9 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
         uint8_t* row = st + S::kRc + (ii * 16 + r16) * S::kRcStride + lc + 4 * q;
         *reinterpret_cast<uint32_t*>(row) = pack4_e4m3(u[ii][0], inv);
         *reinterpret_cast<uint32_t*>(row + 16) = pack4_e4m3(u[ii][1], inv);
-        if (q == 0) st[S::kRs + (ii * 16 + r16) * (C / 32) + lc / 32] = (uint8_t)sc;
+        // the 4 lanes of a row hold the same code and all store it: no
+        // divergent branch to split the unit's code for the scheduler
+        st[S::kRs + (ii * 16 + r16) * (C / 32) + lc / 32] = (uint8_t)sc;
     }
     const int u4 = r16 & 3, m4 = r16 >> 2;
 #pragma unroll
@@ -306,10 +308,10 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
             *reinterpret_cast<uint32_t*>(st + S::kCc + col * S::kCcStride +
                                          (ip % (S::kTok / 32)) * 32 + ii * 16 + 4 * m4) = t;
         }
-        if (m4 == 0) {
-            const uint32_t sc = u4 == 0 ? scv[0] : u4 == 1 ? scv[1] : u4 == 2 ? scv[2] : scv[3];
-            st[S::kCs + col * 4 + ip] = (uint8_t)sc;
-        }
+        // the 4 lanes of a column (m4 = 0..3) store the same code, picked
+        // from the four with a byte extract rather than a branch
+        const uint32_t sc4 = scv[0] | (scv[1] << 8) | (scv[2] << 16) | (scv[3] << 24);
+        st[S::kCs + col * 4 + ip] = (uint8_t)(sc4 >> (8 * u4));
     }
 }
 
