@@ -321,8 +321,10 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
 
 // Rowwise codes and scales of slice ip (rows rbase + ip*32 + [0, 32)) to
 // global memory; rows at or past rows_valid (relative to the wave) are not
-// written.
-template <int C>
+// written.  NT: nontemporal code stores (measured: faster for the forward's
+// z copies, slower for the backward's dh copies, whose epilogue waits on
+// vmcnt while its stores are in flight).
+template <int C, bool NT>
 __device__ __forceinline__ void flush_rows(const uint8_t* st, const QDest& d, int64_t rbase,
                                            int ip, int rows_valid, int lane) {
     using S = QStage<C>;
@@ -337,7 +339,9 @@ __device__ __forceinline__ void flush_rows(const uint8_t* st, const QDest& d, in
         if (ip * 32 + t * kRpp + rl < rows_valid) {
             const uint4 v = *reinterpret_cast<const uint4*>(
                 st + S::kRc + (t * kRpp + rl) * S::kRcStride + lc);
-            *reinterpret_cast<uint4*>(base + (int64_t)(t * kRpp) * d.ldqr + loff) = v;
+            uint8_t* const dst = base + (int64_t)(t * kRpp) * d.ldqr + loff;
+            if constexpr (NT) store_nt(dst, v);
+            else *reinterpret_cast<uint4*>(dst) = v;
         }
     }
     // scales: C/32 bytes per row; a split row is two runs of C/64 bytes
@@ -367,8 +371,9 @@ __device__ __forceinline__ void flush_rows(const uint8_t* st, const QDest& d, in
 }
 
 // Token-axis codes of the staged kTok tokens (padded positions tok0 ..
-// tok0 + kTok - 1) to global memory: pass t moves kCpp columns.
-template <int C>
+// tok0 + kTok - 1) to global memory: pass t moves kCpp columns.  NT as for
+// flush_rows.
+template <int C, bool NT>
 __device__ __forceinline__ void flush_cols(const uint8_t* st, const QDest& d, int64_t tok0,
                                            int lane) {
     using S = QStage<C>;
@@ -383,7 +388,8 @@ __device__ __forceinline__ void flush_cols(const uint8_t* st, const QDest& d, in
         uint8_t* const base = d.qc + gcol * d.ldqc + tok0;
         const uint4 v = *reinterpret_cast<const uint4*>(
             st + S::kCc + (t * kCpp + cl) * S::kCcStride + ch);
-        *reinterpret_cast<uint4*>(base + loff) = v;
+        if constexpr (NT) store_nt(base + loff, v);
+        else *reinterpret_cast<uint4*>(base + loff) = v;
     }
 }
 
@@ -784,8 +790,7 @@ mx_gemm_kernel(GemmProblem p) {
                     const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
                     const int64_t col = cw + (2 * jp + codd) * 16 + 4 * (q & 2);
                     if (rok && cw + 2 * jp * 16 < p.N)
-                        *reinterpret_cast<uint4*>(C + row * p.ldc + col) =
-                            make_uint4(x[0], y[0], x[1], y[1]);
+                        store_nt(C + row * p.ldc + col, make_uint4(x[0], y[0], x[1], y[1]));
                 }
             }
         } else if constexpr (EPI == Epi::kSwiglu) {
@@ -837,8 +842,8 @@ mx_gemm_kernel(GemmProblem p) {
                             }
                             if (rows_pad_w > 0) {
                                 const uint2 g2 = pack4_bf16(gu[ii][jj]), u2 = pack4_bf16(uu[ii][jj]);
-                                *h_block(p.h, prow + i * 16, cw + j * 16, F, lane) =
-                                    make_uint4(g2.x, g2.y, u2.x, u2.y);
+                                store_nt(h_block(p.h, prow + i * 16, cw + j * 16, F, lane),
+                                         make_uint4(g2.x, g2.y, u2.x, u2.y));
                             }
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
@@ -850,8 +855,8 @@ mx_gemm_kernel(GemmProblem p) {
                     quant_unit<64>(z, 2 * jp * 16, ip, st, lane);
                 });
                 lds_wait();
-                flush_rows<64>(st, d, rwave, ip, rows_valid_w, lane);
-                if ((ip & 1) && rows_pad_w > 0) flush_cols<64>(st, d, prow + (ip >> 1) * 64, lane);
+                flush_rows<64, true>(st, d, rwave, ip, rows_valid_w, lane);
+                if ((ip & 1) && rows_pad_w > 0) flush_cols<64, true>(st, d, prow + (ip >> 1) * 64, lane);
                 lds_wait();
             }
             if (rows_pad_w > 0) flush_col_scales<64>(st, d, prow, lane);
@@ -968,8 +973,8 @@ mx_gemm_kernel(GemmProblem p) {
                 }
                 // the wave's 128 columns are all below F or all at or past it
                 lds_wait();
-                if (cw < F) flush_rows<256>(st, d, rwave, ip, rows_valid_w, lane);
-                if (cw < F && rows_pad_w > 0) flush_cols<256>(st, d, prow + ip * 32, lane);
+                if (cw < F) flush_rows<256, false>(st, d, rwave, ip, rows_valid_w, lane);
+                if (cw < F && rows_pad_w > 0) flush_cols<256, false>(st, d, prow + ip * 32, lane);
                 lds_wait();
             }
             if (cw < F && rows_pad_w > 0) flush_col_scales<256>(st, d, prow, lane);

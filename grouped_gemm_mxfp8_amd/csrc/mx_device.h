@@ -63,6 +63,18 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, f
     return e4m3x4(a, b, c, d, inv, inv, inv, inv);
 }
 
+// Streaming stores: the output is read by a later kernel, never again by
+// this one, so the nontemporal hint keeps it from displacing lines that the
+// running kernels re-read from the caches.
+__device__ __forceinline__ void store_nt(void* p, uint4 v) {
+    typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store((u32x4_nt){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_nt*>(p));
+}
+__device__ __forceinline__ void store_nt(void* p, uint2 v) {
+    typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store((u32x2_nt){v.x, v.y}, reinterpret_cast<u32x2_nt*>(p));
+}
+
 // Max of |v| as fp32 bit pattern (non-negative floats order like integers).
 __device__ __forceinline__ uint32_t abs_bits(float v) {
     return __float_as_uint(v) & 0x7fffffffu;

@@ -86,7 +86,7 @@ quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nchunk, int64_t C, boo
         m = max(m, (uint32_t)__shfl_xor((int)m, 1));
         const uint32_t sc = scale_code_from_amax_bits(m);
         const float inv = inv_scale_from_code(sc);
-        reinterpret_cast<uint4*>(codes)[i] = encode16(v, inv);
+        store_nt(reinterpret_cast<uint4*>(codes) + i, encode16(v, inv));
         if (!(i & 1)) {
             const int64_t blk = i >> 1, bpr = C / 32;       // block index, blocks per row
             scales[tiled ? tiled_scale_offset(blk / bpr, blk % bpr, C) : blk] = (uint8_t)sc;
@@ -167,7 +167,7 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                 const uint32_t sc_hi = MXQ_DPP(sc, 0x104);   // row_shl:4 -- the next block's
                 const int64_t row = b * R + src0 + r0 + h;
                 if (colok && r0 + h < valid) {
-                    *reinterpret_cast<uint2*>(rc + row * C + ccol) = encode8(v[h], inv_scale_from_code(sc));
+                    store_nt(rc + row * C + ccol, encode8(v[h], inv_scale_from_code(sc)));
                     if (c8 == 0) {
                         // the row's two scale bytes; one 16-bit store when aligned
                         // (always in the tiled layout: col0 / 32 is even)
@@ -215,8 +215,8 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
     if (col0 + col >= C) return;
     const int64_t crow = b * C + col0 + col;
     uint4* dst = reinterpret_cast<uint4*>(cc + crow * ld + p0 + blk * 32);
-    dst[0] = encode16(v, inv);
-    dst[1] = encode16(v + 16, inv);
+    store_nt(dst, encode16(v, inv));
+    store_nt(dst + 1, encode16(v + 16, inv));
     if (blk == 0)
         *reinterpret_cast<uint32_t*>(cs + (tiled ? tiled_scale_offset(crow, p0 / 32, ld)
                                                  : crow * (ld / 32) + p0 / 32)) =
