@@ -190,8 +190,7 @@ __device__ __forceinline__ uint32_t pack4_e4m3(const float (&v)[4], float inv) {
 }
 
 __device__ __forceinline__ uint2 pack4_bf16(const float (&v)[4]) {
-    return make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
-                      f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+    return make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
 }
 
 __device__ __forceinline__ void unpack4_bf16(uint2 w, float (&v)[4]) {

@@ -21,12 +21,17 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
     return __uint_as_float(b << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even (NaN stays NaN): gfx950 converts two
+// values in one v_cvt_pk_bf16_f32 (equal, for every non-NaN fp32 pattern, to
+// the integer rounding u + 0x7fff + ((u >> 16) & 1), checked exhaustively on
+// the device).  bf16x2 packs a in the low and b in the high half.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return bf16x2(f, 0.0f) & 0xffffu;
 }
 
 // E8M0 scale code of a block from the bit pattern of its (non-negative,
