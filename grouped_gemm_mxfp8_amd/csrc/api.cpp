@@ -250,6 +250,9 @@ mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
         return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: col_codes and col_scales go together");
     if (!want_row && !want_col)
         return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: no output requested");
+    if (want_col && 256 * C > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "mxfp8_quantize: C=%lld too large for 32-bit tile offsets",
+                    (long long)C);
     if (!aligned(x, 16) || (row_codes && !aligned(row_codes, 16)) ||
         (col_codes && !aligned(col_codes, 16)))
         return fail(MX_ERR_INVALID_ARG, "mxfp8_quantize: x and codes must be 16-byte aligned");

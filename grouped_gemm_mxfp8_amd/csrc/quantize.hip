@@ -27,6 +27,12 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same through a buffer descriptor: offsets at or past the range read
+// zeros, so a masked load needs no branch.
+__device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2 /* nt */);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ void unpack8(const uint4& u, float* v) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -141,8 +147,24 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
     const int64_t col0 = (int64_t)blockIdx.x * 64;
     const int64_t ccol = col0 + c8 * 8;               // this lane's 8 columns
     const bool colok = ccol < C;                      // C % 32 == 0: whole chunk in or out
-    const uint16_t* xb = x + (b * R + src0) * C + ccol;
+    // the tile's valid rows as one buffer: rows at or past `valid` and
+    // columns past C read as zeros (the caller keeps 256 * C below 2^31, so
+    // the byte offsets fit 32 bits)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x + (b * R + src0) * C), (short)0, (int)(valid * C * 2), 0x00020000);
 
+    // All four row loads first, without branches: issued back to back, they
+    // are in flight together instead of each pair waiting behind the previous
+    // pair's stores.
+    uint4 wl[2][2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = it * 64 + 2 * rp + h;
+            const uint32_t off = colok ? ((uint32_t)r * (uint32_t)C + (uint32_t)ccol) * 2u : 0x7ffffff0u;
+            wl[it][h] = load_stream(xr, off);
+        }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int r0 = it * 64 + 2 * rp;
@@ -150,9 +172,7 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
         float v[2][8];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const bool live = colok && r0 + h < valid;
-            w[h] = live ? load_stream(reinterpret_cast<const uint4*>(xb + (int64_t)(r0 + h) * C))
-                        : make_uint4(0, 0, 0, 0);
+            w[h] = wl[it][h];
             unpack8(w[h], v[h]);
         }
         if (rc) {

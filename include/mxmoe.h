@@ -99,7 +99,8 @@ int64_t mx_padded_rows_bound(int64_t M, int32_t G, int32_t align);
  *                with d_offsets; may be NULL otherwise.
  * At least one of the two copies must be requested.  x and the code buffers
  * must be 16-byte aligned, the scale buffers 4-byte aligned
- * (MX_ERR_INVALID_ARG otherwise).
+ * (MX_ERR_INVALID_ARG otherwise).  With the columnwise copy, 256 * C must be
+ * below 2^31 (MX_ERR_UNSUPPORTED otherwise: 32-bit tile offsets).
  */
 mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
                          uint8_t* row_codes, uint8_t* row_scales,
