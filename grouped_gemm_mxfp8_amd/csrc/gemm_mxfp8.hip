@@ -185,10 +185,6 @@ __device__ __forceinline__ uint32_t transpose4x4_bytes(uint32_t x, int u) {
                    : __builtin_amdgcn_perm(w, t, 0x06020400u);
 }
 
-__device__ __forceinline__ uint32_t pack4_e4m3(const float (&v)[4], float inv) {
-    return e4m3x4(v[0], v[1], v[2], v[3], inv);
-}
-
 __device__ __forceinline__ uint2 pack4_bf16(const float (&v)[4]) {
     return make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
 }
@@ -278,10 +274,12 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
             for (int v = 0; v < 4; ++v) m = max(m, abs_bits(u[ii][jj][v]));
         m = max4q(m);
         const uint32_t sc = scale_code_from_amax_bits(m);
-        const float inv = inv_scale_from_code(sc);
+        const float scl = scale_from_code(sc), lim = e4m3_limit_from_code(sc);
         uint8_t* row = st + S::kRc + (ii * 16 + r16) * S::kRcStride + lc + 4 * q;
-        *reinterpret_cast<uint32_t*>(row) = pack4_e4m3(u[ii][0], inv);
-        *reinterpret_cast<uint32_t*>(row + 16) = pack4_e4m3(u[ii][1], inv);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+            *reinterpret_cast<uint32_t*>(row + 16 * jj) = e4m3x4_scaled(
+                u[ii][jj][0], u[ii][jj][1], u[ii][jj][2], u[ii][jj][3], lim, scl);
         // the 4 lanes of a row hold the same code and all store it: no
         // divergent branch to split the unit's code for the scheduler
         st[S::kRs + (ii * 16 + r16) * (C / 32) + lc / 32] = (uint8_t)sc;
@@ -289,21 +287,27 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
     const int u4 = r16 & 3, m4 = r16 >> 2;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-        float inv[4];
         uint32_t scv[4];
+        // column v's two rows (ii = 0, 1) share its scale: one scaled
+        // conversion per column, byte pairs (ii0, ii1) regrouped by row below
+        uint32_t pr[2] = {0u, 0u};
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             uint32_t m = max(abs_bits(u[0][jj][v]), abs_bits(u[1][jj][v]));
             m = max16(m);
             scv[v] = scale_code_from_amax_bits(m);
-            inv[v] = inv_scale_from_code(scv[v]);
+            pr[v >> 1] = e4m3x2_scaled(pr[v >> 1], u[0][jj][v], u[1][jj][v],
+                                       e4m3_limit_from_code(scv[v]), scale_from_code(scv[v]),
+                                       (v & 1) != 0);
         }
+        // pr[0] = [v0 of ii0, v0 of ii1, v1 of ii0, v1 of ii1], pr[1] likewise
+        // for v2, v3; row ii's dword holds its v0..v3
+        const uint32_t wrow[2] = {__builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u),
+                                  __builtin_amdgcn_perm(pr[1], pr[0], 0x07050301u)};
         const int col = lc + jj * 16 + 4 * q + u4;      // this lane's column after the transpose
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
-            const uint32_t w = e4m3x4(u[ii][jj][0], u[ii][jj][1], u[ii][jj][2], u[ii][jj][3],
-                                      inv[0], inv[1], inv[2], inv[3]);
-            const uint32_t t = transpose4x4_bytes(w, u4);    // tokens 4*m4 .. 4*m4+3
+            const uint32_t t = transpose4x4_bytes(wrow[ii], u4);    // tokens 4*m4 .. 4*m4+3
             *reinterpret_cast<uint32_t*>(st + S::kCc + col * S::kCcStride +
                                          (ip % (S::kTok / 32)) * 32 + ii * 16 + 4 * m4) = t;
         }

@@ -68,6 +68,39 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, f
     return e4m3x4(a, b, c, d, inv, inv, inv, inv);
 }
 
+// The block scale 2^X = 2^(c - 127) of E8M0 code c (c = 0 gives the fp32
+// subnormal 2^-127; these kernels keep fp32 denormals).
+__device__ __forceinline__ float scale_from_code(uint32_t c) {
+    return __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), (int)c);
+}
+// 448 * 2^X for code c: 1.75 * 2^(c - 119), a normal number for every c.
+__device__ __forceinline__ float e4m3_limit_from_code(uint32_t c) {
+    return __uint_as_float(((c + 8u) << 23) | 0x600000u);
+}
+
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+// E4M3 codes of a and b divided by a block scale, in the low (hi = false) or
+// high half of old: v_cvt_scalef32_pk_fp8_f32 divides by the scale (exact, a
+// power of two) and rounds to nearest even but does not saturate, so the
+// values are clamped to +-lim = +-448 * scale first.  Equal, code for code, to
+// clamping x * 2^-X to +-448 and converting (checked on the device over every
+// finite bf16 pattern and random fp32 values at scale exponents from -127 to
+// 30).
+__device__ __forceinline__ uint32_t e4m3x2_scaled(uint32_t old, float a, float b, float lim,
+                                                  float scale, bool hi) {
+    a = __builtin_amdgcn_fmed3f(a, lim, -lim);
+    b = __builtin_amdgcn_fmed3f(b, lim, -lim);
+    const v2s16 o = __builtin_bit_cast(v2s16, old);
+    const v2s16 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, false);
+    return __builtin_bit_cast(uint32_t, r);
+}
+// Four values of one block: bytes a, b, c, d.
+__device__ __forceinline__ uint32_t e4m3x4_scaled(float a, float b, float c, float d, float lim,
+                                                  float scale) {
+    return e4m3x2_scaled(e4m3x2_scaled(0u, a, b, lim, scale, false), c, d, lim, scale, true);
+}
+
 // Streaming stores: the output is read by a later kernel, never again by
 // this one, so the nontemporal hint keeps it from displacing lines that the
 // running kernels re-read from the caches.
