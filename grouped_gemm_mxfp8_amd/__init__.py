@@ -41,6 +41,8 @@ _SIGS = {
     "grouped_linear_fwd": (_I32, [_I32, _P, _P, _P, _I32, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
     "grouped_mlp_fwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P,
                                _SZ, _P]),
+    "grouped_mlp_fwd_ex": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P,
+                                  _SZ, ctypes.c_uint32, _P]),
     "grouped_mlp_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P, _P, _P,
                                _P, _P, _SZ, _P]),
     "grouped_mlp_ctx_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
@@ -288,23 +290,29 @@ def bwd_ws_bytes(M, H, F, E) -> int:
 
 
 def grouped_mlp_fwd(x, offsets, w1, w2, r, ws: Optional[torch.Tensor] = None,
-                    ctx_buf: Optional[torch.Tensor] = None):
+                    ctx_buf: Optional[torch.Tensor] = None, reuse_weights: bool = False):
     """Fused GroupedMLP forward.  Returns (y bf16 [M, H], MlpCtx).  ``ws`` and
     ``ctx_buf`` are optional caller-owned uint8 buffers (allocated when
-    missing or too small)."""
+    missing or too small).  ``reuse_weights``: use the MXFP8 weight copies an
+    earlier call with the same weights left in ``ws`` and ``ctx_buf`` (both
+    must then be given) instead of quantizing w1 and w2 again."""
     dev, M, H, F, E = _mlp_check(x, offsets, w1, w2, r)
     L = lib()
     nctx = L.grouped_mlp_ctx_bytes(M, H, F, E)
     nws = L.grouped_mlp_fwd_ws_bytes(M, H, F, E)
     if nctx == 0 or nws == 0:
         raise MxError("grouped_mlp_fwd", 2, last_error())
+    if reuse_weights and (ws is None or ctx_buf is None or ws.numel() < nws
+                          or ctx_buf.numel() < nctx):
+        raise ValueError("reuse_weights needs the ws and ctx_buf of the earlier call")
     ctx = ctx_buf if ctx_buf is not None and ctx_buf.numel() >= nctx else \
         torch.empty(nctx, dtype=torch.uint8, device=dev)
     if ws is None or ws.numel() < nws:
         ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-    st = L.grouped_mlp_fwd(_ptr(x), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
-                           _ptr(y), _ptr(ctx), nctx, _ptr(ws), ws.numel(), _stream(dev))
+    st = L.grouped_mlp_fwd_ex(_ptr(x), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
+                              _ptr(y), _ptr(ctx), ctx.numel(), _ptr(ws), ws.numel(),
+                              1 if reuse_weights else 0, _stream(dev))
     _check("grouped_mlp_fwd", st)
     return y, MlpCtx(ctx, M, H, F, E, offsets)
 

@@ -110,18 +110,19 @@ struct CtxLayout {
 CtxLayout ctx_layout(const MlpDims& d) {
     Carver c;
     CtxLayout L;
+    // columnwise weight copies made by the forward's weight pass, for the
+    // data-gradient GEMMs of the backward; first, so that their offsets do
+    // not depend on M (a forward that reuses them may have another M)
+    L.w1c = c.take((size_t)d.E * d.H * 2 * d.F);
+    L.w1c_s = c.take((size_t)d.E * d.H * 2 * d.F / 32);
+    L.w2c = c.take((size_t)d.E * d.F * d.H);
+    L.w2c_s = c.take((size_t)d.E * d.F * d.H / 32);
     L.h = c.take((size_t)d.Mp * d.F * 4);     // blocked [Mp/16][F/16] x 1 KiB
     L.xcol = c.take((size_t)d.H * d.Mp);
     L.xcol_s = c.take((size_t)d.H * d.Mp / 32);
     L.zcol = c.take((size_t)d.F * d.Mp);
     L.zcol_s = c.take((size_t)d.F * d.Mp / 32);
     L.poff = c.take((size_t)(d.E + 1) * 8);
-    // columnwise weight copies made by the forward's weight pass, for the
-    // data-gradient GEMMs of the backward
-    L.w1c = c.take((size_t)d.E * d.H * 2 * d.F);
-    L.w1c_s = c.take((size_t)d.E * d.H * 2 * d.F / 32);
-    L.w2c = c.take((size_t)d.E * d.F * d.H);
-    L.w2c_s = c.take((size_t)d.E * d.F * d.H / 32);
     L.total = c.off;
     return L;
 }
@@ -132,12 +133,13 @@ struct FwdWs {
 FwdWs fwd_ws_layout(const MlpDims& d) {
     Carver c;
     FwdWs L;
-    L.xr = c.take((size_t)d.M * d.H);
-    L.xr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
+    // rowwise weight copies first (offsets independent of M, see ctx_layout)
     L.w1r = c.take((size_t)d.E * 2 * d.F * d.H);
     L.w1r_s = c.take((size_t)d.E * 2 * d.F * d.H / 32);
     L.w2r = c.take((size_t)d.E * d.H * d.F);
     L.w2r_s = c.take((size_t)d.E * d.H * d.F / 32);
+    L.xr = c.take((size_t)d.M * d.H);
+    L.xr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
     L.zr = c.take((size_t)d.M * d.F);
     L.zr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.F));
     L.total = c.off;
@@ -409,8 +411,19 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, in
                           int64_t H, int64_t F, const void* w1, const void* w2,
                           const float* d_r, void* y, void* ctx, size_t ctx_bytes, void* ws,
                           size_t ws_bytes, mx_stream_t stream) {
+    return grouped_mlp_fwd_ex(x, d_offsets, E, M, H, F, w1, w2, d_r, y, ctx, ctx_bytes, ws,
+                              ws_bytes, 0u, stream);
+}
+
+mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E, int64_t M,
+                             int64_t H, int64_t F, const void* w1, const void* w2,
+                             const float* d_r, void* y, void* ctx, size_t ctx_bytes, void* ws,
+                             size_t ws_bytes, uint32_t flags, mx_stream_t stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (!x || !d_offsets || !w1 || !w2 || !d_r || !y || !ctx || !ws)
+    const bool reuse = (flags & MX_FWD_REUSE_WEIGHTS) != 0;
+    if (flags & ~(uint32_t)MX_FWD_REUSE_WEIGHTS)
+        return fail(MX_ERR_INVALID_ARG, "grouped_mlp_fwd: unknown flags 0x%x", flags);
+    if (!x || !d_offsets || (!reuse && (!w1 || !w2)) || !d_r || !y || !ctx || !ws)
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_fwd: NULL argument");
     MlpDims d;
     mx_status st = check_mlp_dims(M, H, F, E, &d);
@@ -427,6 +440,7 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, in
         !aligned(ws, kAlign))
         return fail(MX_ERR_INVALID_ARG,
                     "grouped_mlp_fwd: tensors must be 16-byte and ctx/ws 256-byte aligned");
+    // with reuse the weight copies in ws and ctx are the previous call's
     uint8_t* cb = static_cast<uint8_t*>(ctx);
     uint8_t* wb = static_cast<uint8_t*>(ws);
     int64_t* poff = reinterpret_cast<int64_t*>(cb + C.poff);
@@ -447,19 +461,26 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, in
     }
     // (2) weights, one pass each: rowwise copies for the forward GEMMs (W1
     // blocks along H, W2 along F) and the columnwise copies the backward's
-    // data gradients use (W1 blocks along 2F, W2 along H), saved in ctx
-    e = timed("quant_tiles", quant_bytes((int64_t)E * M2, H, true, true), MX_WORK_BYTES, s, [&] {
-        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w1), E, M2, H, nullptr,
-                                      nullptr, 1, 0, wb + W.w1r, wb + W.w1r_s, cb + C.w1c,
-                                      cb + C.w1c_s, M2, true, s);
-    });
-    if (e != hipSuccess) return launched(e, "quant_tiles(w1)");
-    e = timed("quant_tiles", quant_bytes((int64_t)E * H, F, true, true), MX_WORK_BYTES, s, [&] {
-        return mx::launch_quant_tiles(static_cast<const uint16_t*>(w2), E, H, F, nullptr, nullptr,
-                                      1, 0, wb + W.w2r, wb + W.w2r_s, cb + C.w2c, cb + C.w2c_s, H,
-                                      true, s);
-    });
-    if (e != hipSuccess) return launched(e, "quant_tiles(w2)");
+    // data gradients use (W1 blocks along 2F, W2 along H), saved in ctx.
+    // Skipped when the caller reuses the copies of an earlier call.
+    if (!reuse) {
+        e = timed("quant_tiles", quant_bytes((int64_t)E * M2, H, true, true), MX_WORK_BYTES, s,
+                  [&] {
+                      return mx::launch_quant_tiles(static_cast<const uint16_t*>(w1), E, M2, H,
+                                                    nullptr, nullptr, 1, 0, wb + W.w1r,
+                                                    wb + W.w1r_s, cb + C.w1c, cb + C.w1c_s, M2,
+                                                    true, s);
+                  });
+        if (e != hipSuccess) return launched(e, "quant_tiles(w1)");
+        e = timed("quant_tiles", quant_bytes((int64_t)E * H, F, true, true), MX_WORK_BYTES, s,
+                  [&] {
+                      return mx::launch_quant_tiles(static_cast<const uint16_t*>(w2), E, H, F,
+                                                    nullptr, nullptr, 1, 0, wb + W.w2r,
+                                                    wb + W.w2r_s, cb + C.w2c, cb + C.w2c_s, H,
+                                                    true, s);
+                  });
+        if (e != hipSuccess) return launched(e, "quant_tiles(w2)");
+    }
     if (M == 0) return ok();
 
     // (3) gate-up GEMM with the SwiGLU / routing-scale / requantize epilogue

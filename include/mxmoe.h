@@ -154,6 +154,29 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E,
                           size_t ws_bytes, mx_stream_t stream);
 
 /*
+ * grouped_mlp_fwd_ex -- grouped_mlp_fwd with flags (0: same as
+ * grouped_mlp_fwd).
+ *
+ * MX_FWD_REUSE_WEIGHTS: skip quantizing the weights and use the MXFP8 copies
+ * that an earlier forward with the same w1, w2, E, H and F left in this ctx
+ * (columnwise copies) and this ws (rowwise copies): the caching of weight
+ * quantization across micro-batches that the 16-bit master weights allow
+ * while they do not change (German page, the paragraph on quantization
+ * between 16-bit master weights and the 8-bit path).  The weight regions sit
+ * at the start of ctx and ws, so M may differ from that earlier call.  w1
+ * and w2 are not read and may be NULL.  The caller guarantees that the
+ * weights have not changed and that nothing else has written those regions
+ * (grouped_mlp_bwd only reads them); with any other contents the results are
+ * undefined, not an error.  Unknown flag bits: MX_ERR_INVALID_ARG.
+ */
+#define MX_FWD_REUSE_WEIGHTS 1u
+mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
+                             int64_t M, int64_t H, int64_t F, const void* w1,
+                             const void* w2, const float* d_r, void* y,
+                             void* ctx, size_t ctx_bytes, void* ws,
+                             size_t ws_bytes, uint32_t flags, mx_stream_t stream);
+
+/*
  * grouped_mlp_bwd -- fused GroupedMLP backward with MXFP8 operands in every
  * GEMM (Portuguese page, fourth paragraph: MXFP8 active in forward and
  * backward).  Straight-through quantizers; each GEMM quantizes its operands

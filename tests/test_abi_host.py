@@ -157,6 +157,29 @@ def test_grouped_mlp_rejects_bad_arguments(mxlib):
     assert bwd(*b) == MX_ERR_INVALID_ARG
 
 
+def test_grouped_mlp_fwd_ex_checks_flags_and_weights(mxlib):
+    """The flags entry point validates on the host: unknown flag bits, weights
+    required unless reused, workspace sizes (no GPU call is reached)."""
+    fwd = mxlib.grouped_mlp_fwd_ex
+    M, H, F, E = 1024, 256, 256, 4
+    nctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
+    nws = mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E)
+    args = lambda flags, w=FAKE, n=nctx: [FAKE, FAKE, E, M, H, F, w, w, FAKE, FAKE, FAKE, n,
+                                          FAKE, nws, flags, None]
+    assert fwd(*args(2)) == MX_ERR_INVALID_ARG
+    assert "flags" in _err(mxlib)
+    assert fwd(*args(0, w=None)) == MX_ERR_INVALID_ARG
+    assert fwd(*args(1, w=None, n=nctx - 1)) == MX_ERR_WORKSPACE
+
+
+def test_weight_regions_do_not_move_with_m(mxlib):
+    """Reused weight copies sit at offsets that do not depend on M."""
+    H, F, E = 256, 512, 4
+    for which in (4, 5):     # the ctx regions of the weights' columnwise copies
+        offs = {mxlib.grouped_mlp_ctx_offset(which, M, H, F, E) for M in (0, 100, 4096, 9999)}
+        assert len(offs) == 1 and offs.pop() >= 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import grouped_gemm_mxfp8_amd as gm
     monkeypatch.setattr(gm, "_lib", None)

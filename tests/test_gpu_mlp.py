@@ -233,3 +233,37 @@ def test_mlp_zero_dy_gives_zero_gradients(dev):
     torch.cuda.synchronize()
     for t in (dx, dw1, dw2, dr):
         assert not t.any()
+
+
+def test_mlp_reuse_weights_matches_fresh_quantization(dev):
+    """A forward that reuses the weight copies an earlier forward left in its
+    ws and ctx (another batch with another M, same weights) gives the same
+    bits as a forward that quantizes the weights itself, and so does the
+    backward that follows it."""
+    H, F = 256, 384
+    a = small_case([300, 0, 257, 143], H, F, seed=11)
+    b = small_case([110, 40, 0, 78], H, F, seed=12)
+    E = a.E
+    w1, w2 = a.W1.to(dev), a.W2.to(dev)
+    Mx = max(a.M, b.M)
+    fws = torch.full((gm.fwd_ws_bytes(Mx, H, F, E),), 255, dtype=torch.uint8, device=dev)
+    cbuf = torch.full((gm.lib().grouped_mlp_ctx_bytes(Mx, H, F, E),), 255, dtype=torch.uint8,
+                      device=dev)
+    gm.grouped_mlp_fwd(a.X.to(dev), a.offsets.to(dev), w1, w2, a.r.to(dev), ws=fws,
+                       ctx_buf=cbuf)
+    xb, offb, rb, dyb = b.X.to(dev), b.offsets.to(dev), b.r.to(dev), b.dY.to(dev)
+    y_re, ctx_re = gm.grouped_mlp_fwd(xb, offb, w1, w2, rb, ws=fws, ctx_buf=cbuf,
+                                      reuse_weights=True)
+    g_re = gm.grouped_mlp_bwd(dyb, offb, w1, w2, rb, ctx_re)
+    y_fr, ctx_fr = gm.grouped_mlp_fwd(xb, offb, w1, w2, rb)
+    g_fr = gm.grouped_mlp_bwd(dyb, offb, w1, w2, rb, ctx_fr)
+    torch.cuda.synchronize()
+    n = int(O.padded_offsets(b.offsets.numpy())[-1])
+    assert torch.equal(y_re, y_fr)
+    assert torch.equal(ctx_re.h(), ctx_fr.h())
+    for get in (lambda c: c.xcol(), lambda c: c.zcol()):
+        u, v = get(ctx_re), get(ctx_fr)
+        assert torch.equal(u.codes[:, :n], v.codes[:, :n])
+        assert torch.equal(u.scales[:, : n // 32], v.scales[:, : n // 32])
+    for u, v in zip(g_re, g_fr):
+        assert torch.equal(u, v)
