@@ -46,6 +46,12 @@ _SIGS = {
     "grouped_mlp_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P, _P, _P,
                                _P, _P, _SZ, _P]),
     "grouped_mlp_ctx_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "moe_route_ws_bytes": (_SZ, [_I64, _I32, _I32]),
+    "moe_route_plan": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_quantize": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _P, _P, _I64,
+                                    _P, _P]),
+    "moe_combine": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P]),
+    "moe_combine_bwd": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P, _I64, _P, _P, _P]),
     "grouped_mlp_fwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
     "grouped_mlp_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
     "grouped_mlp_ctx_offset": (_I64, [_I32, _I64, _I64, _I64, _I32]),
@@ -368,6 +374,108 @@ def ws_mx_view(ws: torch.Tensor, which: int, M, H, F, E, shape) -> MxTensor:
     return _tiled_mx_view(ws, off, shape)
 
 
+# ---- routing around the expert path ------------------------------------------
+
+def route_plan(ids: torch.Tensor, E: int, w: Optional[torch.Tensor] = None):
+    """Sorted-row plan of a top-k routing ``ids`` int32 [T, k] over E experts.
+
+    Returns (offsets int64 [E+1], row_of int32 [T, k], tok_of int32 [T*k],
+    r_sorted fp32 [T*k] or None): rows sorted stably by (expert, token, slot);
+    ``r_sorted`` holds ``w`` (fp32 [T, k]) in row order."""
+    _need(ids, torch.int32, "ids")
+    dev = ids.device
+    if ids.dim() != 2:
+        raise ValueError("ids must be [T, k]")
+    T, k = ids.shape
+    if w is not None:
+        _need(w, torch.float32, "w", dev)
+        if tuple(w.shape) != (T, k):
+            raise ValueError("w must match ids")
+    L = lib()
+    nws = L.moe_route_ws_bytes(T, k, E)
+    if nws == 0:
+        raise MxError("moe_route_plan", 1, "bad sizes")
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int64, device=dev)
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tok_of = torch.empty(T * k, dtype=torch.int32, device=dev)
+    r_sorted = torch.empty(T * k, dtype=torch.float32, device=dev) if w is not None else None
+    st = L.moe_route_plan(_ptr(ids), T, k, E, _ptr(w), _ptr(offsets), _ptr(row_of), _ptr(tok_of),
+                          _ptr(r_sorted), _ptr(ws), nws, _stream(dev))
+    _check("moe_route_plan", st)
+    return offsets, row_of, tok_of, r_sorted
+
+
+def permute_quantize(x: torch.Tensor, tok_of: torch.Tensor, offsets: torch.Tensor, M: int,
+                     rowwise: bool = True, colwise: bool = True):
+    """MXFP8 copies of the sorted rows x[tok_of[row]] (x bf16 [T, H]), made
+    straight from token order; same outputs as ``mxfp8_quantize`` of the
+    sorted rows with ``offsets``: dict with ``row``, ``col`` and
+    ``padded_offsets``."""
+    _need(x, torch.bfloat16, "x")
+    dev = x.device
+    _need(tok_of, torch.int32, "tok_of", dev)
+    _need(offsets, torch.int64, "offsets", dev)
+    T, H = x.shape
+    E = offsets.numel() - 1
+    out = {}
+    rc = rs = cc = cs = None
+    ld = 0
+    if rowwise:
+        rc = torch.empty((M, H), dtype=torch.uint8, device=dev)
+        rs = torch.empty((M, H // BLOCK), dtype=torch.uint8, device=dev)
+        out["row"] = MxTensor(rc, rs)
+    if colwise:
+        ld = max(padded_rows_bound(M, E), TOKEN_ALIGN)
+        cc = torch.empty((H, ld), dtype=torch.uint8, device=dev)
+        cs = torch.empty((H, ld // BLOCK), dtype=torch.uint8, device=dev)
+        out["col"] = MxTensor(cc, cs)
+    poff = torch.empty(E + 1, dtype=torch.int64, device=dev)
+    out["padded_offsets"] = poff
+    st = lib().moe_permute_quantize(_ptr(x), T, H, _ptr(tok_of), M, _ptr(offsets), E, _ptr(rc),
+                                    _ptr(rs), _ptr(cc), _ptr(cs), ld, _ptr(poff), _stream(dev))
+    _check("moe_permute_quantize", st)
+    return out
+
+
+def combine(y: torch.Tensor, row_of: torch.Tensor, w: Optional[torch.Tensor] = None):
+    """out bf16 [T, H] = sum_j c[t, j] * y[row_of[t, j]], c = w or 1."""
+    _need(y, torch.bfloat16, "y")
+    dev = y.device
+    _need(row_of, torch.int32, "row_of", dev)
+    if w is not None:
+        _need(w, torch.float32, "w", dev)
+    M, H = y.shape
+    T, k = row_of.shape
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    st = lib().moe_combine(_ptr(y), M, H, _ptr(row_of), T, k, _ptr(w), _ptr(out), _stream(dev))
+    _check("moe_combine", st)
+    return out
+
+
+def combine_bwd(dout: torch.Tensor, row_of: torch.Tensor, M: int,
+                w: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None):
+    """Backward of ``combine``: (dy bf16 [M, H], dw fp32 [T, k] or None).
+    Unweighted it is the token -> sorted-row permute of ``dout``."""
+    _need(dout, torch.bfloat16, "dout")
+    dev = dout.device
+    _need(row_of, torch.int32, "row_of", dev)
+    T, H = dout.shape
+    k = row_of.shape[1]
+    if w is not None:
+        _need(w, torch.float32, "w", dev)
+    if y is not None:
+        _need(y, torch.bfloat16, "y", dev)
+    dy = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev) if (w is not None and
+                                                                  y is not None) else None
+    st = lib().moe_combine_bwd(_ptr(dout), T, H, k, _ptr(row_of), _ptr(w), _ptr(y), M, _ptr(dy),
+                               _ptr(dw), _stream(dev))
+    _check("moe_combine_bwd", st)
+    return dy, dw
+
+
 __all__ = ["lib", "last_error", "MxError", "MxTensor", "MlpCtx", "mxfp8_quantize",
            "grouped_linear_fwd", "grouped_mlp_fwd", "grouped_mlp_bwd", "padded_rows_bound",
-           "ws_mx_view", "fwd_ws_bytes", "bwd_ws_bytes"]
+           "ws_mx_view", "fwd_ws_bytes", "bwd_ws_bytes", "route_plan", "permute_quantize",
+           "combine", "combine_bwd"]

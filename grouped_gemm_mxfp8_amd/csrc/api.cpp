@@ -615,6 +615,139 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
     return launched(gemm(v, mx::Epi::kStoreBf16, 2.0 * M2 * H * M, s), "mx_gemm(wgrad-gate-up)");
 }
 
+// ---- routing: sorted-row plan, permute + quantize, combine --------------------
+size_t moe_route_ws_bytes(int64_t T, int32_t k, int32_t E) {
+    if (T < 0 || k < 1 || E < 1 || E > mx::kMaxGroups) return 0;
+    const int64_t n = mx::route_chunks(T * k);
+    return (size_t)(n > 0 ? n : 1) * (size_t)E * 4;
+}
+
+mx_status moe_route_plan(const int32_t* d_ids, int64_t T, int32_t k, int32_t E, const float* d_w,
+                         int64_t* d_offsets, int32_t* d_row_of, int32_t* d_tok_of,
+                         float* d_r_sorted, void* ws, size_t ws_bytes, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (T < 0 || k < 1 || k > 64 || E < 1)
+        return fail(MX_ERR_INVALID_ARG, "moe_route_plan: bad sizes T=%lld k=%d E=%d",
+                    (long long)T, k, E);
+    if (E > mx::kMaxGroups)
+        return fail(MX_ERR_UNSUPPORTED, "moe_route_plan: E=%d exceeds %d", E, mx::kMaxGroups);
+    if (T * k > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "moe_route_plan: T*k=%lld rows exceed int32",
+                    (long long)(T * k));
+    if (!d_offsets || !ws || (T > 0 && (!d_ids || !d_row_of || !d_tok_of)))
+        return fail(MX_ERR_INVALID_ARG, "moe_route_plan: NULL argument");
+    if ((d_w == nullptr) != (d_r_sorted == nullptr))
+        return fail(MX_ERR_INVALID_ARG, "moe_route_plan: d_w and d_r_sorted go together");
+    if (ws_bytes < moe_route_ws_bytes(T, k, E))
+        return fail(MX_ERR_WORKSPACE, "moe_route_plan: ws needs %zu bytes, got %zu",
+                    moe_route_ws_bytes(T, k, E), ws_bytes);
+    if (!aligned(ws, 4))
+        return fail(MX_ERR_INVALID_ARG, "moe_route_plan: ws must be 4-byte aligned");
+    return launched(timed("route_plan", 16.0 * T * k, MX_WORK_BYTES, s,
+                          [&] {
+                              return mx::launch_route_plan(d_ids, T, k, E, d_w, d_offsets,
+                                                           d_row_of, d_tok_of, d_r_sorted,
+                                                           static_cast<int32_t*>(ws), s);
+                          }),
+                    "route_plan");
+}
+
+mx_status moe_permute_quantize(const void* x, int64_t T, int64_t H, const int32_t* d_tok_of,
+                               int64_t M, const int64_t* d_offsets, int32_t E,
+                               uint8_t* row_codes, uint8_t* row_scales, uint8_t* col_codes,
+                               uint8_t* col_scales, int64_t col_ld, int64_t* d_padded_offsets,
+                               mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!x || !d_tok_of || !d_offsets || !d_padded_offsets)
+        return fail(MX_ERR_INVALID_ARG, "moe_permute_quantize: NULL argument");
+    if (T < 0 || M < 0 || H <= 0 || E < 1)
+        return fail(MX_ERR_INVALID_ARG, "moe_permute_quantize: bad sizes T=%lld M=%lld H=%lld E=%d",
+                    (long long)T, (long long)M, (long long)H, E);
+    if (E > mx::kMaxGroups || H % 32)
+        return fail(MX_ERR_UNSUPPORTED, "moe_permute_quantize: E=%d or H=%lld unsupported", E,
+                    (long long)H);
+    if (T * H * 2 > kI32Max || 256 * H > kI32Max || M > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "moe_permute_quantize: too large for 32-bit offsets");
+    const bool want_row = row_codes || row_scales, want_col = col_codes || col_scales;
+    if (want_row && !(row_codes && row_scales))
+        return fail(MX_ERR_INVALID_ARG, "moe_permute_quantize: row_codes and row_scales go together");
+    if (want_col && !(col_codes && col_scales))
+        return fail(MX_ERR_INVALID_ARG, "moe_permute_quantize: col_codes and col_scales go together");
+    if (!want_row && !want_col)
+        return fail(MX_ERR_INVALID_ARG, "moe_permute_quantize: no output requested");
+    if (!aligned(x, 16) || (row_codes && !aligned(row_codes, 16)) ||
+        (col_codes && !aligned(col_codes, 16)) || (row_scales && !aligned(row_scales, 4)) ||
+        (col_scales && !aligned(col_scales, 4)))
+        return fail(MX_ERR_INVALID_ARG,
+                    "moe_permute_quantize: x and codes 16-byte, scales 4-byte aligned");
+    const int64_t bound = padded_bound(M, E, mx::kTokenAlign);
+    const int64_t ld = want_col ? col_ld : bound;
+    if (want_col && (col_ld % 128 || col_ld < bound))
+        return fail(MX_ERR_INVALID_ARG,
+                    "moe_permute_quantize: col_ld=%lld must be a multiple of 128 and >= %lld",
+                    (long long)col_ld, (long long)bound);
+    if (bound / 128 > 65535)
+        return fail(MX_ERR_UNSUPPORTED, "moe_permute_quantize: too many rows for one launch");
+    hipError_t e = timed("padded_offsets", 16.0 * (E + 1), MX_WORK_BYTES, s, [&] {
+        return mx::launch_padded_offsets(d_offsets, E, d_padded_offsets, s);
+    });
+    if (e != hipSuccess) return launched(e, "padded_offsets");
+    if (M == 0) return ok();
+    return launched(timed("quant_tiles", quant_bytes(M, H, want_row, want_col), MX_WORK_BYTES, s,
+                          [&] {
+                              return mx::launch_quant_tiles(
+                                  static_cast<const uint16_t*>(x), 1, M, H, d_offsets,
+                                  d_padded_offsets, E, bound, row_codes, row_scales, col_codes,
+                                  col_scales, ld, false, s, d_tok_of, T);
+                          }),
+                    "quant_tiles(permute)");
+}
+
+mx_status moe_combine(const void* y, int64_t M, int64_t H, const int32_t* d_row_of, int64_t T,
+                      int32_t k, const float* d_w, void* out, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (T < 0 || M < 0 || H <= 0 || k < 1)
+        return fail(MX_ERR_INVALID_ARG, "moe_combine: bad sizes");
+    if (H % 8)
+        return fail(MX_ERR_UNSUPPORTED, "moe_combine: H=%lld is not a multiple of 8", (long long)H);
+    if (T > 0 && (!y || !d_row_of || !out))
+        return fail(MX_ERR_INVALID_ARG, "moe_combine: NULL argument");
+    if (!aligned(y, 16) || !aligned(out, 16))
+        return fail(MX_ERR_INVALID_ARG, "moe_combine: y and out must be 16-byte aligned");
+    return launched(timed("combine", 2.0 * H * (T * k + T), MX_WORK_BYTES, s,
+                          [&] {
+                              return mx::launch_combine(static_cast<const uint16_t*>(y), d_row_of,
+                                                        d_w, T, k, H, M,
+                                                        static_cast<uint16_t*>(out), s);
+                          }),
+                    "combine");
+}
+
+mx_status moe_combine_bwd(const void* dout, int64_t T, int64_t H, int32_t k,
+                          const int32_t* d_row_of, const float* d_w, const void* y, int64_t M,
+                          void* dy, float* d_dw, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (T < 0 || M < 0 || H <= 0 || k < 1)
+        return fail(MX_ERR_INVALID_ARG, "moe_combine_bwd: bad sizes");
+    if (H % 8)
+        return fail(MX_ERR_UNSUPPORTED, "moe_combine_bwd: H=%lld is not a multiple of 8",
+                    (long long)H);
+    if (T > 0 && (!dout || !d_row_of || !dy))
+        return fail(MX_ERR_INVALID_ARG, "moe_combine_bwd: NULL argument");
+    if (d_dw && (!d_w || !y))
+        return fail(MX_ERR_INVALID_ARG, "moe_combine_bwd: d_dw needs d_w and y");
+    if (!aligned(dout, 16) || !aligned(dy, 16) || !aligned(y, 16))
+        return fail(MX_ERR_INVALID_ARG, "moe_combine_bwd: dout, y and dy must be 16-byte aligned");
+    return launched(timed("combine_bwd", 2.0 * H * (T * k + T), MX_WORK_BYTES, s,
+                          [&] {
+                              return mx::launch_combine_bwd(
+                                  static_cast<const uint16_t*>(dout), d_row_of, d_w,
+                                  static_cast<const uint16_t*>(y), T, k, H, M,
+                                  static_cast<uint16_t*>(dy), d_dw, s);
+                          }),
+                    "combine_bwd");
+}
+
 mx_status mx_profile_begin(int32_t capacity) {
     if (capacity < 1 || capacity > (1 << 20))
         return fail(MX_ERR_INVALID_ARG, "mx_profile_begin: capacity %d outside [1, 2^20]", capacity);

@@ -42,11 +42,14 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t C,
 // tiled: both copies get K-step tiled scales (rowwise: rows = batch*R, Kp = C,
 // needs C % 128 == 0 and R % 32 == 0 when batch > 1; columnwise: rows =
 // batch*C, Kp = ld).
+// gather (optional, batch == 1): row i of the tiled tensor is source row
+// gather[i] of x (src_rows rows; negative entries read as zeros).
 hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
                               int64_t C, const int64_t* offs,
                               const int64_t* poff, int G, int64_t row_bound,
                               uint8_t* rc, uint8_t* rs, uint8_t* cc,
-                              uint8_t* cs, int64_t ld, bool tiled, hipStream_t s);
+                              uint8_t* cs, int64_t ld, bool tiled, hipStream_t s,
+                              const int32_t* gather = nullptr, int64_t src_rows = 0);
 
 // ---- grouped GEMMs ------------------------------------------------------------
 // Operand of a K-major MXFP8 GEMM: codes [rows][ld], scales row-major
@@ -98,6 +101,24 @@ hipError_t launch_bf16_grouped(const uint16_t* x, const int64_t* offs, int G,
                                int64_t M, const uint16_t* w, int64_t N,
                                int64_t K, const float* rscale, uint16_t* y,
                                hipStream_t s);
+
+// ---- routing: sorted-row plan, combine ---------------------------------------
+// Plan of a top-k routing ids [T][k] (values in [0, E); others are skipped:
+// row_of = -1 and no row): offsets [E+1], row_of [T*k], tok_of [M], and
+// r_sorted [M] = w of each row when w is given.  hist: route_chunks(T*k) * E
+// int32 of scratch.
+int64_t route_chunks(int64_t n);
+hipError_t launch_route_plan(const int32_t* ids, int64_t T, int k, int E, const float* w,
+                             int64_t* offsets, int32_t* row_of, int32_t* tok_of,
+                             float* r_sorted, int32_t* hist, hipStream_t s);
+// out [T][H] = sum_j c_tj y[row_of[t][j]] (c = w, or 1 when w is null); H % 8 == 0.
+hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float* w, int64_t T,
+                          int k, int64_t H, int64_t M, uint16_t* out, hipStream_t s);
+// dy[row_of[t][j]] = c_tj dout[t]; dw [T][k] = <dout[t], y[row_of[t][j]]> when
+// dw is given (y then needed).
+hipError_t launch_combine_bwd(const uint16_t* dout, const int32_t* row_of, const float* w,
+                              const uint16_t* y, int64_t T, int k, int64_t H, int64_t M,
+                              uint16_t* dy, float* dw, hipStream_t s);
 
 int device_cu_count();
 

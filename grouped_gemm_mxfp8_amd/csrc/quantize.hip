@@ -120,7 +120,8 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                    const int64_t* __restrict__ poff, int G,
                    uint8_t* __restrict__ rc, uint8_t* __restrict__ rs,
                    uint8_t* __restrict__ cc, uint8_t* __restrict__ cs,
-                   int64_t ld, bool tiled) {
+                   int64_t ld, bool tiled, const int32_t* __restrict__ gather,
+                   int64_t src_rows) {
     constexpr int kStride = 65;                      // dwords per column of the tile
     __shared__ uint32_t tile[64 * kStride];
     const int64_t b = blockIdx.z;
@@ -149,9 +150,14 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
     const bool colok = ccol < C;                      // C % 32 == 0: whole chunk in or out
     // the tile's valid rows as one buffer: rows at or past `valid` and
     // columns past C read as zeros (the caller keeps 256 * C below 2^31, so
-    // the byte offsets fit 32 bits)
-    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(x + (b * R + src0) * C), (short)0, (int)(valid * C * 2), 0x00020000);
+    // the byte offsets fit 32 bits).  With a gather map, row r of the
+    // tile is source row gather[src0 + r] of x (src_rows rows, whose bytes
+    // the caller keeps below 2^31).
+    const __amdgpu_buffer_rsrc_t xr = gather
+        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0,
+                                            (int)(src_rows * C * 2), 0x00020000)
+        : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (b * R + src0) * C),
+                                            (short)0, (int)(valid * C * 2), 0x00020000);
 
     // All four row loads first, without branches: issued back to back, they
     // are in flight together instead of each pair waiting behind the previous
@@ -162,7 +168,14 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int r = it * 64 + 2 * rp + h;
-            const uint32_t off = colok ? ((uint32_t)r * (uint32_t)C + (uint32_t)ccol) * 2u : 0x7ffffff0u;
+            uint32_t off;
+            if (gather) {
+                const int32_t sr = r < valid ? gather[src0 + r] : -1;
+                off = colok && sr >= 0 && sr < src_rows
+                          ? ((uint32_t)sr * (uint32_t)C + (uint32_t)ccol) * 2u : 0x7ffffff0u;
+            } else {
+                off = colok ? ((uint32_t)r * (uint32_t)C + (uint32_t)ccol) * 2u : 0x7ffffff0u;
+            }
             wl[it][h] = load_stream(xr, off);
         }
 #pragma unroll
@@ -267,12 +280,13 @@ hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
                               int64_t C, const int64_t* offs,
                               const int64_t* poff, int G, int64_t row_bound,
                               uint8_t* rc, uint8_t* rs, uint8_t* cc,
-                              uint8_t* cs, int64_t ld, bool tiled, hipStream_t s) {
+                              uint8_t* cs, int64_t ld, bool tiled, hipStream_t s,
+                              const int32_t* gather, int64_t src_rows) {
     const int64_t ytiles = offs ? row_bound / 128 : (R + 127) / 128;
     if (ytiles == 0 || C == 0 || batch == 0) return hipSuccess;
     dim3 grid((unsigned)((C + 63) / 64), (unsigned)ytiles, (unsigned)batch);
     hipLaunchKernelGGL(quant_tiles_kernel, grid, dim3(256), 0, s, x, R, C, offs,
-                       poff, G, rc, rs, cc, cs, ld, tiled);
+                       poff, G, rc, rs, cc, cs, ld, tiled, gather, src_rows);
     return hipGetLastError();
 }
 

@@ -245,6 +245,70 @@ int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F,
                               int32_t E);
 
 /*
+ * Routing around the expert path: the sorted-row plan of a top-k routing,
+ * the permute that gathers token rows into that order (fused with MXFP8
+ * quantization), and the combine back to token order with its backward.
+ * The German page's paragraph on GroupedLinear: the caller hands over the
+ * number of tokens per expert and the expert inputs are gathered into one
+ * grouped call; the Portuguese page, third paragraph: routing weights send
+ * each token to its experts.  Rows are sorted stably by (expert, token,
+ * slot); the combine is out[t] = sum_j c[t][j] * Y[row_of[t][j]] with c = w
+ * or, when the expert path already applied the routing weights (as the
+ * GroupedMLP does), c = 1.  No host synchronisation; deterministic.
+ *
+ * moe_route_ws_bytes -- scratch bytes moe_route_plan needs (0 on bad sizes).
+ *
+ * moe_route_plan
+ *   d_ids       int32 [T][k], expert of token t's slot j, in [0, E).  Slots
+ *               with other values are not routed: row_of = -1, no row.
+ *   d_w         fp32 [T][k] routing weights, or NULL.
+ *   d_offsets   int64 [E+1] out: expert e owns sorted rows
+ *               [offsets[e], offsets[e+1]); offsets[E] = routed slots M.
+ *   d_row_of    int32 [T][k] out: sorted row of each slot.
+ *   d_tok_of    int32 [T*k] out: token of each sorted row (first M entries).
+ *   d_r_sorted  fp32 [T*k] out: w of each sorted row; NULL iff d_w is NULL.
+ *   ws          moe_route_ws_bytes(T, k, E) bytes, 4-byte aligned.
+ *   1 <= k <= 64, 1 <= E <= 1024 (MX_ERR_UNSUPPORTED above), T*k < 2^31.
+ *
+ * moe_permute_quantize -- MXFP8 copies of the sorted rows X[tok_of[row]]
+ *   straight from the token-order x, as mxfp8_quantize makes them from
+ *   already sorted rows (row-major scales): rowwise codes [M][H] + scales
+ *   [M][H/32], columnwise codes [H][col_ld] + scales [H][col_ld/32] with
+ *   every expert padded to MX_TOKEN_ALIGN zero tokens; either copy may be
+ *   skipped (both pointers NULL).  x bf16 [T][H]; d_offsets from
+ *   moe_route_plan; M = the routed rows (T*k when every slot is routed);
+ *   d_padded_offsets int64 [E+1] out.  H % 32 == 0, T*H*2 and 256*H below
+ *   2^31; alignment as mxfp8_quantize.
+ *
+ * moe_combine -- out bf16 [T][H] = sum_j c[t][j] * y[row_of[t][j]] in fp32,
+ *   j ascending, rounded once to bf16; y bf16 [M][H]; d_w NULL for c = 1.
+ *   Unrouted slots contribute nothing.  H % 8 == 0; y, out 16-byte aligned.
+ *
+ * moe_combine_bwd -- dy bf16 [M][H]: dy[row_of[t][j]] = c[t][j] * dout[t]
+ *   (with d_w NULL an exact copy: the token -> sorted-row permute of dout);
+ *   d_dw fp32 [T][k] (or NULL): <dout[t], y[row_of[t][j]]>, needs d_w and y
+ *   bf16 [M][H].  Rows that no slot maps to are not written.
+ */
+size_t moe_route_ws_bytes(int64_t T, int32_t k, int32_t E);
+mx_status moe_route_plan(const int32_t* d_ids, int64_t T, int32_t k, int32_t E,
+                         const float* d_w, int64_t* d_offsets, int32_t* d_row_of,
+                         int32_t* d_tok_of, float* d_r_sorted, void* ws,
+                         size_t ws_bytes, mx_stream_t stream);
+mx_status moe_permute_quantize(const void* x, int64_t T, int64_t H,
+                               const int32_t* d_tok_of, int64_t M,
+                               const int64_t* d_offsets, int32_t E,
+                               uint8_t* row_codes, uint8_t* row_scales,
+                               uint8_t* col_codes, uint8_t* col_scales,
+                               int64_t col_ld, int64_t* d_padded_offsets,
+                               mx_stream_t stream);
+mx_status moe_combine(const void* y, int64_t M, int64_t H, const int32_t* d_row_of,
+                      int64_t T, int32_t k, const float* d_w, void* out,
+                      mx_stream_t stream);
+mx_status moe_combine_bwd(const void* dout, int64_t T, int64_t H, int32_t k,
+                          const int32_t* d_row_of, const float* d_w, const void* y,
+                          int64_t M, void* dy, float* d_dw, mx_stream_t stream);
+
+/*
  * Launch timing (diagnostics; not part of the computation).  Between
  * mx_profile_begin() and mx_profile_end(), every kernel the library launches
  * from the calling thread is bracketed by two HIP events recorded on the
