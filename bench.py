@@ -18,7 +18,9 @@ library records on its stream around each launch), and the FP64 CPU oracle
 timed on a bounded sample as a reported baseline.  A second figure,
 "weights_cached", times the same step with the forward reusing the MXFP8
 weight copies of an earlier forward (as across the micro-batches of one
-optimizer step); the headline always quantizes the weights.
+optimizer step); the headline always quantizes the weights.  "routing"
+times the steps around the expert path at the same shape (sorted-row plan,
+permute fused with quantization, combine and its backward), not in the step.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -165,6 +167,49 @@ def cpu_baseline(seed, T, M, E, H, F):
             "est_step_s": round(est, 1)}
 
 
+def routing_figures(gm, case, dev, reps):
+    """The steps around the expert path at the same shape (not part of the
+    step): the sorted-row plan of the top-2 routing, the permute of the token
+    rows fused with both MXFP8 copies, the unweighted combine back to token
+    order and its backward (the token -> sorted-row permute of a gradient).
+    Algorithmic bytes per call: every row read and written once."""
+    import numpy as np
+    import torch
+    T, k, E, H = case.T, case.k, case.E, case.H
+    M = case.M
+    expert_of_row = np.repeat(np.arange(E), case.counts)
+    order = np.lexsort((expert_of_row, case.token))          # rows by (token, expert)
+    ids = torch.from_numpy(expert_of_row[order].reshape(T, k).astype(np.int32)).to(dev)
+    first = np.zeros(T, dtype=np.int64)
+    first[case.token[::-1]] = np.arange(M)[::-1]             # a sorted row of every token
+    x_tok = case.X[torch.from_numpy(first).to(dev)].contiguous()
+    y = case.dY
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            out = f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps, out
+
+    ms_plan, (offs, row_of, tok_of, _) = timed(lambda: gm.route_plan(ids, E))
+    ms_pq, _ = timed(lambda: gm.permute_quantize(x_tok, tok_of, offs, M))
+    ms_c, _ = timed(lambda: gm.combine(y, row_of))
+    ms_cb, _ = timed(lambda: gm.combine_bwd(x_tok, row_of, M))
+    fig = lambda ms, nbytes: {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
+                              "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3)}
+    return {
+        "route_plan_ms": round(ms_plan, 4),
+        "permute_quantize": fig(ms_pq, M * H * 2 + 2 * M * H * (1 + 1 / 32)),
+        "combine": fig(ms_c, M * H * 2 + T * H * 2),
+        "combine_bwd": fig(ms_cb, M * H * 2 * 2),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -242,6 +287,8 @@ def main():
           file=sys.stderr, flush=True)
     del cbuf
 
+    routing = routing_figures(gm, case, dev, reps=max(args.steps, 3))
+
     ms_step = elapsed / args.steps * 1e3
     tokens_s = T * args.steps / elapsed
     flops_step = 18.0 * H * F * M
@@ -273,6 +320,7 @@ def main():
         "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
         "roofline": roofline(agg),
         "kernels": kernels,
+        "routing": routing,
         "weights_cached": {
             "ms_per_step": round(elapsed_cached / args.steps * 1e3, 4),
             "tokens_per_s": round(T * args.steps / elapsed_cached, 1),

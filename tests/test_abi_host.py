@@ -180,6 +180,47 @@ def test_weight_regions_do_not_move_with_m(mxlib):
         assert len(offs) == 1 and offs.pop() >= 0
 
 
+def test_routing_entry_points_reject_bad_arguments(mxlib):
+    """Host-side validation of the routing entry points (no GPU call is
+    reached)."""
+    assert mxlib.moe_route_ws_bytes(100, 2, 8) == 1 * 8 * 4
+    assert mxlib.moe_route_ws_bytes(1000, 2, 8) == 8 * 8 * 4     # ceil(2000/256) chunks
+    assert mxlib.moe_route_ws_bytes(10, 0, 8) == 0
+    assert mxlib.moe_route_ws_bytes(10, 2, 2000) == 0
+    plan = mxlib.moe_route_plan
+    nws = mxlib.moe_route_ws_bytes(100, 2, 8)
+    base = [FAKE, 100, 2, 8, None, FAKE, FAKE, FAKE, None, FAKE, nws, None]
+    a = list(base); a[3] = 2000
+    assert plan(*a) == MX_ERR_UNSUPPORTED
+    a = list(base); a[2] = 0
+    assert plan(*a) == MX_ERR_INVALID_ARG
+    a = list(base); a[4] = FAKE                     # weights without their sorted copy
+    assert plan(*a) == MX_ERR_INVALID_ARG
+    assert "go together" in _err(mxlib)
+    a = list(base); a[10] = nws - 1
+    assert plan(*a) == MX_ERR_WORKSPACE
+    a = list(base); a[0] = None
+    assert plan(*a) == MX_ERR_INVALID_ARG
+    pq = mxlib.moe_permute_quantize
+    args = [FAKE, 100, 256, FAKE, 200, FAKE, 8, FAKE, FAKE, None, None, 0, FAKE, None]
+    a = list(args); a[2] = 100                      # H not a multiple of 32
+    assert pq(*a) == MX_ERR_UNSUPPORTED
+    a = list(args); a[7] = None                     # row codes without scales
+    assert pq(*a) == MX_ERR_INVALID_ARG
+    a = list(args); a[12] = None
+    assert pq(*a) == MX_ERR_INVALID_ARG
+    a = list(args); a[1] = 1 << 20; a[2] = 4096     # T*H*2 past 2^31
+    assert pq(*a) == MX_ERR_UNSUPPORTED
+    a = list(args); a[9] = FAKE; a[10] = FAKE; a[11] = 64   # col_ld not a multiple of 128
+    assert pq(*a) == MX_ERR_INVALID_ARG
+    comb = mxlib.moe_combine
+    assert comb(FAKE, 200, 100, FAKE, 100, 2, None, FAKE, None) == MX_ERR_UNSUPPORTED
+    assert comb(None, 200, 128, FAKE, 100, 2, None, FAKE, None) == MX_ERR_INVALID_ARG
+    bwd = mxlib.moe_combine_bwd
+    assert bwd(FAKE, 100, 128, 2, FAKE, None, None, 200, FAKE, FAKE, None) == MX_ERR_INVALID_ARG
+    assert "needs" in _err(mxlib)
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     import grouped_gemm_mxfp8_amd as gm
     monkeypatch.setattr(gm, "_lib", None)
