@@ -24,6 +24,10 @@ design notes of the repository):
 * R-combine  out[t] = sum_j c[t, j] * Y[row_of[t, j]] with c = w (the routing
              weights) when the expert path did not apply them, or c = 1 when it
              did (the GroupedMLP scales z by r); j ascending.
+* R-router   token t's experts are its k largest logits, taken one at a time
+             (the largest remaining, the lower expert index among equal
+             values), and its routing weights are the softmax of those k
+             logits.
 * R-bwd      the combine's backward: dY[row_of[t, j]] = c[t, j] * dout[t], and
              for the weighted combine dw[t, j] = <dout[t], Y[row_of[t, j]]>.
              Gathering token rows into sorted order (the permute) is the same
@@ -37,6 +41,31 @@ Functions with no independent pin: none (see tests/test_oracle_moe_route.py).
 from __future__ import annotations
 
 import numpy as np
+
+
+def router_topk_softmax(logits, k):
+    """Top-k experts of every token and the softmax of their logits (R-router).
+
+    logits [T, E].  Returns ids int64 [T, k] (selection order) and w float64
+    [T, k].
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    T, E = logits.shape
+    ids = np.zeros((T, k), dtype=np.int64)
+    w = np.zeros((T, k))
+    for t in range(T):
+        taken = [False] * E
+        for j in range(k):
+            best = -1
+            for e in range(E):
+                if not taken[e] and (best < 0 or logits[t, e] > logits[t, best]):
+                    best = e                      # strictly larger: ties keep the lower index
+            taken[best] = True
+            ids[t, j] = best
+        sel = logits[t, ids[t]]
+        ex = np.exp(sel - sel.max())
+        w[t] = ex / ex.sum()
+    return ids, w
 
 
 def route_plan(ids, E):

@@ -135,3 +135,34 @@ def test_permute_is_the_unweighted_combine_backward():
     _, row_of, tok_of = R.route_plan(ids, E)
     dy, _ = R.combine_bwd(x, row_of)
     assert np.array_equal(dy, R.permute_rows(x, tok_of))
+
+
+def test_router_selection_matches_stable_sort():
+    """Selection pass by pass equals a stable descending sort (ties to the
+    lower index), including heavy ties."""
+    rng = np.random.default_rng(17)
+    for T, E, k in [(30, 8, 2), (20, 16, 5), (10, 4, 4), (15, 64, 8)]:
+        logits = np.round(rng.standard_normal((T, E)) * 2) / 2      # many equal values
+        ids, w = R.router_topk_softmax(logits, k)
+        ref = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref)
+
+
+def test_router_weights_closed_forms():
+    rng = np.random.default_rng(19)
+    logits = rng.standard_normal((40, 12))
+    ids, w = R.router_topk_softmax(logits, 3)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(np.diff(w, axis=1) <= 0)                    # selection order = weight order
+    _, w2 = R.router_topk_softmax(logits + 7.25, 3)           # shift invariance
+    assert np.allclose(w, w2, rtol=0, atol=1e-15)
+    # two equal selected logits split evenly; k = 1 gives weight 1
+    ids1, w1 = R.router_topk_softmax(np.array([[0.5, 2.0, 2.0, -1.0]]), 2)
+    assert ids1.tolist() == [[1, 2]] and np.allclose(w1, [[0.5, 0.5]])
+    _, wk1 = R.router_topk_softmax(logits, 1)
+    assert np.all(wk1 == 1.0)
+    # k = E: the full softmax over the row (sorted)
+    full = np.exp(logits - logits.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    idsE, wE = R.router_topk_softmax(logits, 12)
+    assert np.allclose(wE, np.take_along_axis(full, idsE, axis=1), rtol=0, atol=1e-15)
