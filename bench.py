@@ -19,7 +19,7 @@ timed on a bounded sample as a reported baseline.  A second figure,
 "weights_cached", times the same step with the forward reusing the MXFP8
 weight copies of an earlier forward (as across the micro-batches of one
 optimizer step); the headline always quantizes the weights.  "routing"
-times the steps around the expert path at the same shape (sorted-row plan,
+times the steps around the expert path at the same shape (router, sorted-row plan,
 permute fused with quantization, combine and its backward), not in the step.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -169,7 +169,8 @@ def cpu_baseline(seed, T, M, E, H, F):
 
 def routing_figures(gm, case, dev, reps):
     """The steps around the expert path at the same shape (not part of the
-    step): the sorted-row plan of the top-2 routing, the permute of the token
+    step): the router (top-2 of fp32 logits and their softmax), the
+    sorted-row plan of the top-2 routing, the permute of the token
     rows fused with both MXFP8 copies, the unweighted combine back to token
     order and its backward (the token -> sorted-row permute of a gradient).
     Algorithmic bytes per call: every row read and written once."""
@@ -196,6 +197,9 @@ def routing_figures(gm, case, dev, reps):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps, out
 
+    logits = torch.randn((T, E), dtype=torch.float32, device=dev,
+                         generator=torch.Generator(device=dev).manual_seed(3))
+    ms_router, _ = timed(lambda: gm.router(logits, k))
     ms_plan, (offs, row_of, tok_of, _) = timed(lambda: gm.route_plan(ids, E))
     ms_pq, _ = timed(lambda: gm.permute_quantize(x_tok, tok_of, offs, M))
     ms_c, _ = timed(lambda: gm.combine(y, row_of))
@@ -203,6 +207,7 @@ def routing_figures(gm, case, dev, reps):
     fig = lambda ms, nbytes: {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1),
                               "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 3)}
     return {
+        "router": fig(ms_router, T * E * 4 + T * k * 8),
         "route_plan_ms": round(ms_plan, 4),
         "permute_quantize": fig(ms_pq, M * H * 2 + 2 * M * H * (1 + 1 / 32)),
         "combine": fig(ms_c, M * H * 2 + T * H * 2),

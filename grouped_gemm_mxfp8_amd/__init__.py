@@ -46,6 +46,7 @@ _SIGS = {
     "grouped_mlp_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P, _P, _P,
                                _P, _P, _SZ, _P]),
     "grouped_mlp_ctx_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "moe_router": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_route_ws_bytes": (_SZ, [_I64, _I32, _I32]),
     "moe_route_plan": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_quantize": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _P, _P, _I64,
@@ -376,6 +377,19 @@ def ws_mx_view(ws: torch.Tensor, which: int, M, H, F, E, shape) -> MxTensor:
 
 # ---- routing around the expert path ------------------------------------------
 
+def router(logits: torch.Tensor, k: int):
+    """Top-k experts of every token (lower index among equal logits) and the
+    softmax of their logits: (ids int32 [T, k], w fp32 [T, k])."""
+    _need(logits, torch.float32, "logits")
+    dev = logits.device
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    st = lib().moe_router(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(dev))
+    _check("moe_router", st)
+    return ids, w
+
+
 def route_plan(ids: torch.Tensor, E: int, w: Optional[torch.Tensor] = None):
     """Sorted-row plan of a top-k routing ``ids`` int32 [T, k] over E experts.
 
@@ -477,5 +491,5 @@ def combine_bwd(dout: torch.Tensor, row_of: torch.Tensor, M: int,
 
 __all__ = ["lib", "last_error", "MxError", "MxTensor", "MlpCtx", "mxfp8_quantize",
            "grouped_linear_fwd", "grouped_mlp_fwd", "grouped_mlp_bwd", "padded_rows_bound",
-           "ws_mx_view", "fwd_ws_bytes", "bwd_ws_bytes", "route_plan", "permute_quantize",
+           "ws_mx_view", "fwd_ws_bytes", "bwd_ws_bytes", "router", "route_plan", "permute_quantize",
            "combine", "combine_bwd"]

@@ -615,7 +615,23 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
     return launched(gemm(v, mx::Epi::kStoreBf16, 2.0 * M2 * H * M, s), "mx_gemm(wgrad-gate-up)");
 }
 
-// ---- routing: sorted-row plan, permute + quantize, combine --------------------
+// ---- routing: router, sorted-row plan, permute + quantize, combine ------------
+mx_status moe_router(const float* d_logits, int64_t T, int32_t E, int32_t k, int32_t* d_ids,
+                     float* d_w, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (T < 0 || E < 1 || k < 1 || k > E)
+        return fail(MX_ERR_INVALID_ARG, "moe_router: bad sizes T=%lld E=%d k=%d", (long long)T,
+                    E, k);
+    if (E > mx::kMaxGroups || k > 64)
+        return fail(MX_ERR_UNSUPPORTED, "moe_router: E=%d or k=%d unsupported", E, k);
+    if (T * k > kI32Max) return fail(MX_ERR_UNSUPPORTED, "moe_router: T*k above 2^31-1");
+    if (T > 0 && (!d_logits || !d_ids || !d_w))
+        return fail(MX_ERR_INVALID_ARG, "moe_router: NULL argument");
+    return launched(timed("router", 4.0 * T * E + 8.0 * T * k, MX_WORK_BYTES, s,
+                          [&] { return mx::launch_router(d_logits, T, E, k, d_ids, d_w, s); }),
+                    "router");
+}
+
 size_t moe_route_ws_bytes(int64_t T, int32_t k, int32_t E) {
     if (T < 0 || k < 1 || E < 1 || E > mx::kMaxGroups) return 0;
     const int64_t n = mx::route_chunks(T * k);

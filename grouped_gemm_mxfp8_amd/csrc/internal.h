@@ -108,6 +108,10 @@ hipError_t launch_bf16_grouped(const uint16_t* x, const int64_t* offs, int G,
 // r_sorted [M] = w of each row when w is given.  hist: route_chunks(T*k) * E
 // int32 of scratch.
 int64_t route_chunks(int64_t n);
+// Top-k of logits [T][E] (E <= kMaxGroups, 1 <= k <= min(E, 64)) and the
+// softmax of the k selected: ids [T][k] in selection order, w [T][k].
+hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
+                         hipStream_t s);
 hipError_t launch_route_plan(const int32_t* ids, int64_t T, int k, int E, const float* w,
                              int64_t* offsets, int32_t* row_of, int32_t* tok_of,
                              float* r_sorted, int32_t* hist, hipStream_t s);

@@ -5,6 +5,10 @@
 // back to token order with its backward (the Portuguese page, third
 // paragraph: routing weights send each token to its experts).
 //
+// Router: one wave per token picks its k largest logits one at a time (a
+// wave-wide arg-max over the lanes' remaining logits, the lower expert index
+// among equal values) and turns them into the softmax weights.
+//
 // Plan: three launches, no host synchronisation and no global atomics.
 //  * route_hist: one workgroup per chunk of 256 routing slots counts its
 //    slots per expert (LDS counters).
@@ -25,6 +29,67 @@ namespace mx {
 namespace {
 
 constexpr int kChunk = 256;   // routing slots per workgroup in the plan
+constexpr int kRouterPer = kMaxGroups / 64;   // logits per lane in the router
+
+// (v, i) before (v', i'): larger value, or equal value and lower index
+__device__ __forceinline__ bool better(float v, int i, float v2, int i2) {
+    return v > v2 || (v == v2 && i < i2);
+}
+
+__global__ void __launch_bounds__(256)
+router_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
+              int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;                             // the whole wave
+    float v[kRouterPer];
+#pragma unroll
+    for (int i = 0; i < kRouterPer; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? logits[t * E + e] : 0.f;
+    }
+    uint32_t taken = 0;
+    float my_v = 0.f;
+    int my_i = 0;
+    for (int p = 0; p < k; ++p) {
+        // this lane's best remaining logit (its experts ascend with i)
+        float bv = 0.f;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kRouterPer; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !(taken >> i & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
+                bv = v[i];
+                bi = e;
+            }
+        }
+        // wave-wide best: a strict total order, so every lane ends with it
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            const float ov = __shfl_xor(bv, d);
+            const int oi = __shfl_xor(bi, d);
+            if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (lane == p) {
+            my_v = bv;
+            my_i = bi;
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    }
+    // softmax of the k selected logits (lane p holds selection p; lane 0 the max)
+    const float m = __shfl(my_v, 0);
+    const float ex = lane < k ? expf(my_v - m) : 0.f;
+    float s = ex;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d);
+    if (lane < k) {
+        ids[t * k + lane] = my_i;
+        w[t * k + lane] = ex / s;
+    }
+}
 
 __global__ void __launch_bounds__(kChunk)
 route_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ hist) {
@@ -184,6 +249,14 @@ combine_dw_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict_
 }  // namespace
 
 int64_t route_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
+
+hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
+                         hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(router_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, logits, T, E,
+                       k, ids, w);
+    return hipGetLastError();
+}
 
 hipError_t launch_route_plan(const int32_t* ids, int64_t T, int k, int E, const float* w,
                              int64_t* offsets, int32_t* row_of, int32_t* tok_of,

@@ -256,6 +256,12 @@ int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F,
  * or, when the expert path already applied the routing weights (as the
  * GroupedMLP does), c = 1.  No host synchronisation; deterministic.
  *
+ * moe_router -- the router: token t's experts d_ids int32 [T][k] are its k
+ *   largest logits (d_logits fp32 [T][E], finite), taken one at a time (the
+ *   lower expert index among equal values), and d_w fp32 [T][k] the softmax
+ *   of those k logits.  1 <= k <= min(E, 64), E <= 1024 (MX_ERR_UNSUPPORTED
+ *   above 64 or 1024).
+ *
  * moe_route_ws_bytes -- scratch bytes moe_route_plan needs (0 on bad sizes).
  *
  * moe_route_plan
@@ -289,6 +295,8 @@ int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F,
  *   d_dw fp32 [T][k] (or NULL): <dout[t], y[row_of[t][j]]>, needs d_w and y
  *   bf16 [M][H].  Rows that no slot maps to are not written.
  */
+mx_status moe_router(const float* d_logits, int64_t T, int32_t E, int32_t k,
+                     int32_t* d_ids, float* d_w, mx_stream_t stream);
 size_t moe_route_ws_bytes(int64_t T, int32_t k, int32_t E);
 mx_status moe_route_plan(const int32_t* d_ids, int64_t T, int32_t k, int32_t E,
                          const float* d_w, int64_t* d_offsets, int32_t* d_row_of,

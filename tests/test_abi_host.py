@@ -219,6 +219,14 @@ def test_routing_entry_points_reject_bad_arguments(mxlib):
     bwd = mxlib.moe_combine_bwd
     assert bwd(FAKE, 100, 128, 2, FAKE, None, None, 200, FAKE, FAKE, None) == MX_ERR_INVALID_ARG
     assert "needs" in _err(mxlib)
+    rt = mxlib.moe_router
+    assert rt(FAKE, 100, 8, 0, FAKE, FAKE, None) == MX_ERR_INVALID_ARG       # k = 0
+    assert rt(FAKE, 100, 8, 9, FAKE, FAKE, None) == MX_ERR_INVALID_ARG       # k > E
+    assert rt(FAKE, 100, 2000, 2, FAKE, FAKE, None) == MX_ERR_UNSUPPORTED    # E > 1024
+    assert rt(FAKE, 100, 128, 65, FAKE, FAKE, None) == MX_ERR_UNSUPPORTED    # k > 64
+    assert rt(FAKE, 1 << 30, 8, 4, FAKE, FAKE, None) == MX_ERR_UNSUPPORTED   # T*k past 2^31
+    assert rt(FAKE, 100, 8, 2, None, FAKE, None) == MX_ERR_INVALID_ARG
+    assert rt(None, 0, 8, 2, None, None, None) == MX_OK                     # nothing to do
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

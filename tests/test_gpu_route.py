@@ -208,3 +208,38 @@ def test_mixtral_shape_round_trip(dev):
     assert np.array_equal(q["row"].codes[torch.from_numpy(rows).to(dev)].cpu().numpy(), rc)
     assert np.array_equal(q["row"].scales[torch.from_numpy(rows).to(dev)].cpu().numpy(), rs)
     assert torch.equal(twice.float(), (2.0 * x.float()))   # x + x is exact in bf16
+
+
+@pytest.mark.parametrize("T,E,k,ties", [
+    (0, 8, 2, False), (1, 1, 1, False), (333, 8, 2, False), (1000, 64, 8, True),
+    (257, 1024, 64, True), (500, 100, 7, False), (64, 65, 65 - 1, True), (128, 16, 16, True),
+])
+def test_router_matches_oracle(dev, T, E, k, ties):
+    """Expert ids bit-exact (ties to the lower index); weights within a few
+    fp32 roundings of the fp64 softmax."""
+    rng = np.random.default_rng(T * 7 + E + k)
+    lg = rng.standard_normal((T, E)) * 3
+    if ties:
+        lg = np.round(lg * 2) / 2                      # many equal logits per token
+    lg = lg.astype(np.float32)
+    ids, w = gm.router(torch.from_numpy(lg).to(dev), k)
+    torch.cuda.synchronize()
+    o_ids, o_w = R.router_topk_softmax(lg.astype(np.float64), k)
+    assert np.array_equal(ids.cpu().numpy(), o_ids)
+    assert np.all(np.abs(w.double().cpu().numpy() - o_w) <= o_w * 2.0 ** -18)
+
+
+def test_router_feeds_the_plan(dev):
+    """Router output straight into the plan: every token's slots land in its
+    experts' row ranges, and the sorted weights are the router's."""
+    rng = np.random.default_rng(23)
+    T, E, k = 4096, 8, 2
+    lg = torch.from_numpy(rng.standard_normal((T, E)).astype(np.float32)).to(dev)
+    ids, w = gm.router(lg, k)
+    offs, row_of, tok_of, r_sorted = gm.route_plan(ids, E, w)
+    torch.cuda.synchronize()
+    o_ids, _ = R.router_topk_softmax(lg.double().cpu().numpy(), k)
+    o_offs, o_row, o_tok, M = oracle_plan(o_ids.astype(np.int32), E)
+    assert np.array_equal(offs.cpu().numpy(), o_offs)
+    assert np.array_equal(row_of.cpu().numpy(), o_row)
+    assert np.array_equal(r_sorted.cpu().numpy()[o_row.reshape(-1)], w.cpu().numpy().reshape(-1))
