@@ -20,7 +20,9 @@ timed on a bounded sample as a reported baseline.  A second figure,
 weight copies of an earlier forward (as across the micro-batches of one
 optimizer step); the headline always quantizes the weights.  "routing"
 times the steps around the expert path at the same shape (router, sorted-row plan,
-permute fused with quantization, combine and its backward), not in the step.
+permute fused with quantization, combine and its backward), not in the step;
+"grouped_linear" times GroupedLinear at its own workload (T=8192 top-2, E=8,
+K=1024, N=2816) in MXFP8 and in per-tensor FP8, not in the step either.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -167,6 +169,55 @@ def cpu_baseline(seed, T, M, E, H, F):
             "est_step_s": round(est, 1)}
 
 
+def time_call(f, reps):
+    """Average ms of f() over reps calls on the current stream (one call
+    before, untimed)."""
+    import torch
+    f()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        out = f()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps, out
+
+
+def linear_figures(gm, dev, reps):
+    """GroupedLinear at its MXFP8 workload (T=8192 top-2, E=8, K=1024, N=2816,
+    1% outliers x100): MXFP8 against per-tensor FP8 (not part of the step).
+    Quantizers: algorithmic bytes (bf16 read once, codes and scales written;
+    per-tensor FP8 reads its input twice, amax before cast)."""
+    from workloads import make_linear_case
+    case = make_linear_case("mxfp8_linear", seed=0)
+    x, w, offs = case.X.to(dev), case.W.to(dev), case.offsets.to(dev)
+    M, K = x.shape
+    E, N, _ = w.shape
+    flops = 2.0 * M * N * K
+    gbs = lambda ms, nbytes: round(nbytes / ms / 1e6, 1)
+    ms_mqx, mx_x = time_call(lambda: gm.mxfp8_quantize(x), reps)
+    ms_mqw, mx_w = time_call(lambda: gm.mxfp8_quantize(w), reps)
+    ms_mg, _ = time_call(lambda: gm.grouped_linear_fwd(mx_x["row"], offs, mx_w["row"]), reps)
+    ms_pqx, pt_x = time_call(lambda: gm.fp8_tensor_quantize(x, offs), reps)
+    ms_pqw, pt_w = time_call(lambda: gm.fp8_tensor_quantize(w), reps)
+    ms_pg, _ = time_call(lambda: gm.grouped_linear_fwd_fp8(pt_x, offs, pt_w), reps)
+    mx_bytes = lambda n: n * (2 + 1 + 1 / 32)
+    pt_bytes = lambda n: n * (2 + 2 + 1)
+    return {
+        "shape": {"M": M, "K": K, "N": N, "E": E},
+        "mxfp8": {"quant_x_ms": round(ms_mqx, 4), "quant_x_gbs": gbs(ms_mqx, mx_bytes(M * K)),
+                  "quant_w_ms": round(ms_mqw, 4), "quant_w_gbs": gbs(ms_mqw, mx_bytes(E * N * K)),
+                  "gemm_ms": round(ms_mg, 4), "gemm_tflops": round(flops / ms_mg / 1e9, 1)},
+        "fp8_per_tensor": {"quant_x_ms": round(ms_pqx, 4),
+                           "quant_x_gbs": gbs(ms_pqx, pt_bytes(M * K)),
+                           "quant_w_ms": round(ms_pqw, 4),
+                           "quant_w_gbs": gbs(ms_pqw, pt_bytes(E * N * K)),
+                           "gemm_ms": round(ms_pg, 4),
+                           "gemm_tflops": round(flops / ms_pg / 1e9, 1)},
+    }
+
+
 def routing_figures(gm, case, dev, reps):
     """The steps around the expert path at the same shape (not part of the
     step): the router (top-2 of fp32 logits and their softmax), the
@@ -186,16 +237,7 @@ def routing_figures(gm, case, dev, reps):
     x_tok = case.X[torch.from_numpy(first).to(dev)].contiguous()
     y = case.dY
 
-    def timed(f):
-        f()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            out = f()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps, out
+    timed = lambda f: time_call(f, reps)
 
     logits = torch.randn((T, E), dtype=torch.float32, device=dev,
                          generator=torch.Generator(device=dev).manual_seed(3))
@@ -293,6 +335,7 @@ def main():
     del cbuf
 
     routing = routing_figures(gm, case, dev, reps=max(args.steps, 3))
+    linear = linear_figures(gm, dev, reps=max(args.steps, 3))
 
     ms_step = elapsed / args.steps * 1e3
     tokens_s = T * args.steps / elapsed
@@ -326,6 +369,7 @@ def main():
         "roofline": roofline(agg),
         "kernels": kernels,
         "routing": routing,
+        "grouped_linear": linear,
         "weights_cached": {
             "ms_per_step": round(elapsed_cached / args.steps * 1e3, 4),
             "tokens_per_s": round(T * args.steps / elapsed_cached, 1),

@@ -39,6 +39,8 @@ _SIGS = {
     "mx_padded_rows_bound": (_I64, [_I64, _I32, _I32]),
     "mxfp8_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _I32, _P, _P, _I64, _P, _P]),
     "grouped_linear_fwd": (_I32, [_I32, _P, _P, _P, _I32, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
+    "fp8_tensor_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P]),
+    "grouped_linear_fwd_fp8": (_I32, [_P, _P, _P, _I32, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
     "grouped_mlp_fwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P,
                                _SZ, _P]),
     "grouped_mlp_fwd_ex": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P,
@@ -208,6 +210,65 @@ def grouped_linear_fwd(x, offsets: torch.Tensor, w, row_scale: Optional[torch.Te
     st = lib().grouped_linear_fwd(dtype, _ptr(xc), _ptr(xs), _ptr(offsets), E, M, _ptr(wc),
                                   _ptr(ws), N, K, _ptr(row_scale), _ptr(y), _stream(dev))
     _check("grouped_linear_fwd", st)
+    return y
+
+
+@dataclasses.dataclass
+class Fp8Tensor:
+    """Per-tensor scaled FP8 operand: E4M3 codes (uint8), and per group the
+    amax and scale_inv (fp32)."""
+    codes: torch.Tensor
+    amax: torch.Tensor
+    scale_inv: torch.Tensor
+
+
+def fp8_tensor_quantize(x: torch.Tensor, offsets: Optional[torch.Tensor] = None) -> Fp8Tensor:
+    """Per-tensor FP8 copy of bf16 ``x``: [M, C] with row groups ``offsets``
+    (one scale per group), or [G, R, C] with one scale per matrix."""
+    _need(x, torch.bfloat16, "x")
+    dev = x.device
+    if offsets is not None:
+        if x.dim() != 2:
+            raise ValueError("row groups need a 2-D x")
+        _need(offsets, torch.int64, "offsets", dev)
+        batch, (R, C) = 1, x.shape
+        G = offsets.numel() - 1
+    else:
+        if x.dim() != 3:
+            raise ValueError("without offsets x must be [G, R, C]")
+        batch, R, C = x.shape
+        G = batch
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    amax = torch.empty(G, dtype=torch.float32, device=dev)
+    sinv = torch.empty(G, dtype=torch.float32, device=dev)
+    st = lib().fp8_tensor_quantize(_ptr(x), batch, R, C, _ptr(offsets), G, _ptr(codes),
+                                   _ptr(amax), _ptr(sinv), _stream(dev))
+    _check("fp8_tensor_quantize", st)
+    return Fp8Tensor(codes, amax, sinv)
+
+
+def grouped_linear_fwd_fp8(x: Fp8Tensor, offsets: torch.Tensor, w: Fp8Tensor,
+                           row_scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """GroupedLinear on per-tensor FP8 operands: bf16 [M, N]."""
+    _need(x.codes, torch.uint8, "x.codes")
+    dev = x.codes.device
+    _need(x.scale_inv, torch.float32, "x.scale_inv", dev)
+    _need(w.codes, torch.uint8, "w.codes", dev)
+    _need(w.scale_inv, torch.float32, "w.scale_inv", dev)
+    _need(offsets, torch.int64, "offsets", dev)
+    M, K = x.codes.shape
+    E, N, K2 = w.codes.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: x has {K}, w has {K2}")
+    if offsets.numel() != E + 1 or x.scale_inv.numel() != E or w.scale_inv.numel() != E:
+        raise ValueError("offsets must have E+1 entries and each scale_inv E")
+    if row_scale is not None:
+        _need(row_scale, torch.float32, "row_scale", dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    st = lib().grouped_linear_fwd_fp8(_ptr(x.codes), _ptr(x.scale_inv), _ptr(offsets), E, M,
+                                      _ptr(w.codes), _ptr(w.scale_inv), N, K, _ptr(row_scale),
+                                      _ptr(y), _stream(dev))
+    _check("grouped_linear_fwd_fp8", st)
     return y
 
 
@@ -490,6 +551,7 @@ def combine_bwd(dout: torch.Tensor, row_of: torch.Tensor, M: int,
 
 
 __all__ = ["lib", "last_error", "MxError", "MxTensor", "MlpCtx", "mxfp8_quantize",
-           "grouped_linear_fwd", "grouped_mlp_fwd", "grouped_mlp_bwd", "padded_rows_bound",
+           "grouped_linear_fwd", "fp8_tensor_quantize", "grouped_linear_fwd_fp8", "Fp8Tensor",
+           "grouped_mlp_fwd", "grouped_mlp_bwd", "padded_rows_bound",
            "ws_mx_view", "fwd_ws_bytes", "bwd_ws_bytes", "router", "route_plan", "permute_quantize",
            "combine", "combine_bwd"]

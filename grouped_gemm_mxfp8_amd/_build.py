@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmxmoe.so")
-SOURCES = ["api.cpp", "quantize.hip", "gemm_mxfp8.hip", "gemm_bf16.hip", "route.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm_mxfp8.hip", "gemm_bf16.hip", "route.hip",
+           "fp8_tensor.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

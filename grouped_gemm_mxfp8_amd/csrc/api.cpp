@@ -365,6 +365,74 @@ mx_status grouped_linear_fwd(int32_t dtype, const void* x, const uint8_t* x_scal
     return launched(gemm(p, mx::Epi::kStoreBf16, 2.0 * M * N * K, s), "mx_gemm");
 }
 
+// ---- per-tensor FP8 ------------------------------------------------------------
+mx_status fp8_tensor_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
+                              const int64_t* d_offsets, int32_t G, uint8_t* codes, float* d_amax,
+                              float* d_scale_inv, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (batch < 1 || R < 0 || C < 0 || G < 1)
+        return fail(MX_ERR_INVALID_ARG,
+                    "fp8_tensor_quantize: bad sizes batch=%lld R=%lld C=%lld G=%d",
+                    (long long)batch, (long long)R, (long long)C, G);
+    if (G > mx::kMaxGroups)
+        return fail(MX_ERR_UNSUPPORTED, "fp8_tensor_quantize: G=%d above %d", G, mx::kMaxGroups);
+    if (d_offsets ? batch != 1 : G != batch)
+        return fail(MX_ERR_INVALID_ARG,
+                    "fp8_tensor_quantize: row groups need batch == 1, matrices need G == batch");
+    if (C % 32)
+        return fail(MX_ERR_UNSUPPORTED, "fp8_tensor_quantize: C=%lld is not a multiple of 32",
+                    (long long)C);
+    if (256 * C > kI32Max || (batch * R + 127) / 128 > kI32Max || (C + 63) / 64 > 65535)
+        return fail(MX_ERR_UNSUPPORTED, "fp8_tensor_quantize: tensor too large");
+    if (!d_amax || !d_scale_inv || (batch * R * C > 0 && (!x || !codes)))
+        return fail(MX_ERR_INVALID_ARG, "fp8_tensor_quantize: NULL argument");
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(d_amax, 4) || !aligned(d_scale_inv, 4))
+        return fail(MX_ERR_INVALID_ARG,
+                    "fp8_tensor_quantize: x and codes must be 16-byte aligned, amax and "
+                    "scale_inv 4-byte aligned");
+    const int64_t rows = batch * R;
+    return launched(timed("fp8_tensor_quant", 5.0 * rows * C, MX_WORK_BYTES, s,
+                          [&] {
+                              return mx::launch_fp8_tensor_quant(
+                                  static_cast<const uint16_t*>(x), rows, C, d_offsets, G, R,
+                                  reinterpret_cast<uint32_t*>(d_amax), codes, d_scale_inv, s);
+                          }),
+                    "fp8_tensor_quant");
+}
+
+mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
+                                 const int64_t* d_offsets, int32_t E, int64_t M, const uint8_t* w,
+                                 const float* d_w_scale_inv, int64_t N, int64_t K,
+                                 const float* d_row_scale, void* y, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (!x || !d_x_scale_inv || !d_offsets || !w || !d_w_scale_inv || !y)
+        return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd_fp8: NULL argument");
+    if (E < 1 || E > mx::kMaxGroups || M < 0 || N <= 0 || K <= 0)
+        return fail(MX_ERR_INVALID_ARG,
+                    "grouped_linear_fwd_fp8: bad sizes E=%d M=%lld N=%lld K=%lld", E,
+                    (long long)M, (long long)N, (long long)K);
+    if (!aligned(x, 16) || !aligned(w, 16))
+        return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd_fp8: x and w must be 16-byte aligned");
+    if (K % 128 || N % 32)
+        return fail(MX_ERR_UNSUPPORTED,
+                    "grouped_linear_fwd_fp8: needs K %% 128 == 0 and N %% 32 == 0");
+    if (N * K > kI32Max || 256 * K > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd_fp8: operand too large");
+    if (M == 0) return ok();
+    mx::GemmProblem p{};
+    p.kgroup = false;
+    p.offs = d_offsets;
+    p.G = E;
+    p.M = M; p.N = N; p.K = K;
+    p.A = mx::MxOperand{x, nullptr, K, 0};           // no block scales: one per group
+    p.B = mx::MxOperand{w, nullptr, K, N};
+    p.C = y; p.ldc = N; p.c_gstride = 0;
+    p.rscale = d_row_scale;
+    p.gsa = d_x_scale_inv;
+    p.gsb = d_w_scale_inv;
+    return launched(gemm(p, mx::Epi::kStoreBf16, 2.0 * M * N * K, s), "mx_gemm");
+}
+
 size_t grouped_mlp_ctx_bytes(int64_t M, int64_t H, int64_t F, int32_t E) {
     MlpDims d;
     if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;

@@ -64,9 +64,19 @@ struct ScaleSrc {
     v4i rsrc;
     uint32_t voff, s0, sstep;
 };
+// Four E8M0 codes 127 (scale 1): the scale source of an operand without
+// block scales.  Every lane reads this one dword at every K step.
+__device__ const uint32_t kUnitScales = 0x7f7f7f7fu;
+
+// UNIT: the plain-store kernel, whose operands may come without block
+// scales (scales == nullptr); the fused kernels always have them.
+template <bool UNIT>
 __device__ __forceinline__ ScaleSrc scale_src(const uint8_t* scales, int64_t ld, bool tiled,
                                               int64_t row0, int64_t rvalid, int64_t lane_row,
                                               int64_t klo, int64_t K) {
+    if constexpr (UNIT) {
+        if (!scales) return {make_rsrc(&kUnitScales, 4), 0u, 0u, 0u};
+    }
     if (!tiled) {
         const int64_t lds = ld / 32;
         return {make_rsrc(scales + row0 * lds + klo / 32, (rvalid - 1) * lds + K / 32),
@@ -623,9 +633,9 @@ mx_gemm_kernel(GemmProblem p) {
             aoff[j] = (uint32_t)(r * lda + dma_chunk * 16);
             boff[j] = (uint32_t)(brow(r) * ldb + dma_chunk * 16);
         }
-        const ScaleSrc sa = scale_src(p.A.scales, lda, p.A.tiled, m0, mvalid, wave * 64 + lane,
+        const ScaleSrc sa = scale_src<EPI == Epi::kStoreBf16>(p.A.scales, lda, p.A.tiled, m0, mvalid, wave * 64 + lane,
                                       klo, K);
-        const ScaleSrc sb = scale_src(p.B.scales, ldb, p.B.tiled, brow0, bvalid,
+        const ScaleSrc sb = scale_src<EPI == Epi::kStoreBf16>(p.B.scales, ldb, p.B.tiled, brow0, bvalid,
                                       brow(wave * 64 + lane), klo, K);
         const v4i ras = sa.rsrc, rbs = sb.rsrc;
 
@@ -774,12 +784,13 @@ mx_gemm_kernel(GemmProblem p) {
             // row leaves as 64 contiguous bytes in 16-byte stores.  A block
             // pair (32 columns) is wholly inside or outside N (N % 32 == 0).
             const int codd = q & 1;
+            const float gs = (p.gsa ? p.gsa[g] : 1.0f) * (p.gsb ? p.gsb[g] : 1.0f);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int rl = i * 16 + r16;
                 const bool rok = rl < rows_valid_w;
                 const int64_t row = rwave + (rok ? rl : 0);
-                const float sc = p.rscale ? p.rscale[row] : 1.0f;
+                const float sc = p.rscale ? p.rscale[row] * gs : gs;
 #pragma unroll
                 for (int jp = 0; jp < 4; ++jp) {
                     float va[4], vb[4];

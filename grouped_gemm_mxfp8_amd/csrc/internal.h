@@ -53,7 +53,8 @@ hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
 
 // ---- grouped GEMMs ------------------------------------------------------------
 // Operand of a K-major MXFP8 GEMM: codes [rows][ld], scales row-major
-// [rows][ld/32] or K-step tiled (Kp = ld).
+// [rows][ld/32] or K-step tiled (Kp = ld).  scales == nullptr: every block
+// scale is 1 (code 127), for FP8 operands that carry one scale per group.
 struct MxOperand {
     const uint8_t* codes;
     const uint8_t* scales;
@@ -88,6 +89,8 @@ struct GemmProblem {
     bool qtiled;                // fused outputs: K-step tiled scales
     const int64_t* poff;        // padded token offsets of the column copy
     float* drp; int64_t lddrp;  // kDSwiglu: dr partials [M][lddrp]
+    const float* gsa;           // kStoreBf16: per-group factors of A and of B
+    const float* gsb;           //   (scale_inv of per-tensor FP8), or nullptr
 };
 
 hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s);
@@ -123,6 +126,14 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* row_of, const float*
 hipError_t launch_combine_bwd(const uint16_t* dout, const int32_t* row_of, const float* w,
                               const uint16_t* y, int64_t T, int k, int64_t H, int64_t M,
                               uint16_t* dy, float* dw, hipStream_t s);
+
+// ---- per-tensor FP8 ------------------------------------------------------------
+// Codes [rows][C] of x [rows][C] (C % 32 == 0, 256 * C < 2^31) with one scale
+// per group: row groups offs [G+1], or matrices of R rows when offs is null
+// (rows = G * R).  amax [G] (fp32 bits) and scale_inv [G] are written.
+hipError_t launch_fp8_tensor_quant(const uint16_t* x, int64_t rows, int64_t C,
+                                   const int64_t* offs, int G, int64_t R, uint32_t* amax,
+                                   uint8_t* codes, float* scale_inv, hipStream_t s);
 
 int device_cu_count();
 

@@ -132,6 +132,38 @@ mx_status grouped_linear_fwd(int32_t dtype, const void* x,
                              mx_stream_t stream);
 
 /*
+ * Per-tensor scaled FP8, the plain FP8 format the German page names beside
+ * MXFP8 (paragraph on activation memory; the page gives no recipe).  Every
+ * expert's slice of a grouped operand is one tensor with one fp32 scale:
+ * scale = 448 / amax (IEEE division; amax 0 gives 1, an overflowing quotient
+ * the largest finite fp32), code = E4M3 of the fp32 product x * scale
+ * (nearest even, saturating at +-448), scale_inv = 1 / scale.
+ *
+ * fp8_tensor_quantize -- codes uint8 [batch][R][C] of bf16 x [batch][R][C].
+ *   Groups: with d_offsets (int64 [G+1], batch must be 1) group g is rows
+ *   [off[g], off[g+1]) -- rows outside [off[0], off[G]) are neither counted
+ *   nor written; without, group g is matrix g (G must equal batch).
+ *   d_amax, d_scale_inv  fp32 [G], written (device).  C % 32 == 0,
+ *   256 * C < 2^31 (MX_ERR_UNSUPPORTED otherwise); x and codes 16-byte aligned.
+ *   Three launches on `stream` (amax reset, amax, cast); x is read twice.
+ *
+ * grouped_linear_fwd_fp8 -- GroupedLinear on per-tensor FP8 operands:
+ *   Y[off[e]:off[e+1]] = (X_e codes . W_e codes^T) * x_scale_inv[e]
+ *                        * w_scale_inv[e]  (times r[row] if given)
+ *   x codes [M][K], w codes [E][N][K] (from fp8_tensor_quantize, x with the
+ *   same offsets, w as E matrices), scale_inv fp32 [E] each (device), y bf16
+ *   [M][N].  fp32 accumulation.  K % 128 == 0, N % 32 == 0.
+ */
+mx_status fp8_tensor_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
+                              const int64_t* d_offsets, int32_t G, uint8_t* codes,
+                              float* d_amax, float* d_scale_inv, mx_stream_t stream);
+mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
+                                 const int64_t* d_offsets, int32_t E, int64_t M,
+                                 const uint8_t* w, const float* d_w_scale_inv, int64_t N,
+                                 int64_t K, const float* d_row_scale, void* y,
+                                 mx_stream_t stream);
+
+/*
  * grouped_mlp_fwd -- fused GroupedMLP forward (German page, the paragraph on
  * the GroupedMLP fusion kernel; Portuguese page, third paragraph; French page,
  * third improvement), in the order gate-up projection -> SwiGLU -> routing

@@ -53,14 +53,20 @@ def tensor_scale(amax):
     return s, F32(1.0) / s
 
 
+def encode(x, scale):
+    """E4M3 codes of x * scale, the product rounded to fp32 first (R-pt-code).
+    x: values representable in float32 (bf16 in practice); scale: float32."""
+    prod = np.asarray(x, dtype=np.float32) * F32(scale)     # one fp32 rounding
+    return e4m3_encode(prod.astype(np.float64))
+
+
 def quantize_tensor(x):
     """Codes of one tensor plus its amax and scale_inv (R-pt-scale,
-    R-pt-code).  x: values representable in float32 (bf16 in practice)."""
+    R-pt-code)."""
     x32 = np.asarray(x, dtype=np.float32)
     amax = F32(np.max(np.abs(x32))) if x32.size else F32(0.0)
     s, s_inv = tensor_scale(amax)
-    prod = x32 * s                         # one fp32 rounding per element
-    return e4m3_encode(prod.astype(np.float64)), amax, s_inv
+    return encode(x32, s), amax, s_inv
 
 
 def quantize_groups(x, offsets=None):

@@ -219,6 +219,30 @@ def test_routing_entry_points_reject_bad_arguments(mxlib):
     bwd = mxlib.moe_combine_bwd
     assert bwd(FAKE, 100, 128, 2, FAKE, None, None, 200, FAKE, FAKE, None) == MX_ERR_INVALID_ARG
     assert "needs" in _err(mxlib)
+    fq = mxlib.fp8_tensor_quantize
+    fargs = [FAKE, 1, 100, 64, FAKE, 4, FAKE, FAKE, FAKE, None]
+    a = list(fargs); a[3] = 48                                  # C not a multiple of 32
+    assert fq(*a) == MX_ERR_UNSUPPORTED
+    a = list(fargs); a[1] = 2                                   # row groups with batch 2
+    assert fq(*a) == MX_ERR_INVALID_ARG
+    a = list(fargs); a[4] = None                                # matrices: G must equal batch
+    assert fq(*a) == MX_ERR_INVALID_ARG
+    a = list(fargs); a[5] = 2000
+    assert fq(*a) == MX_ERR_UNSUPPORTED
+    a = list(fargs); a[8] = None                                # no scale_inv buffer
+    assert fq(*a) == MX_ERR_INVALID_ARG
+    a = list(fargs); a[3] = 1 << 24                             # 256 * C past 2^31
+    assert fq(*a) == MX_ERR_UNSUPPORTED
+    lf = mxlib.grouped_linear_fwd_fp8
+    largs = [FAKE, FAKE, FAKE, 8, 100, FAKE, FAKE, 256, 1024, None, FAKE, None]
+    a = list(largs); a[8] = 1000                                # K not a multiple of 128
+    assert lf(*a) == MX_ERR_UNSUPPORTED
+    a = list(largs); a[6] = None                                # no w scale_inv
+    assert lf(*a) == MX_ERR_INVALID_ARG
+    a = list(largs); a[3] = 0
+    assert lf(*a) == MX_ERR_INVALID_ARG
+    a = list(largs); a[4] = 0                                   # no rows: nothing to do
+    assert lf(*a) == MX_OK
     rt = mxlib.moe_router
     assert rt(FAKE, 100, 8, 0, FAKE, FAKE, None) == MX_ERR_INVALID_ARG       # k = 0
     assert rt(FAKE, 100, 8, 9, FAKE, FAKE, None) == MX_ERR_INVALID_ARG       # k > E
