@@ -169,22 +169,26 @@ def cpu_baseline(seed, T, M, E, H, F):
             "est_step_s": round(est, 1)}
 
 
-def time_call(f, reps):
-    """Average ms of f() over reps calls on the current stream (one call
-    before, untimed)."""
+def time_call(gm, lib, f, reps):
+    """GPU ms per call of f(): the library's launch records (events on its
+    stream around each of its launches) over reps calls, one call before,
+    untimed.  Unlike a wall clock around the calls, this leaves out the
+    host's time to issue them, which exceeds the kernels' for the small
+    steps timed here."""
     import torch
     f()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
+    if lib.mx_profile_begin(64 * reps) != 0:
+        raise RuntimeError(gm.last_error())
     for _ in range(reps):
         out = f()
-    b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / reps, out
+    lib.mx_profile_end()
+    agg = kernel_table(gm, lib)
+    return sum(a["ms"] for a in agg.values()) / reps, out
 
 
-def linear_figures(gm, dev, reps):
+def linear_figures(gm, lib, dev, reps):
     """GroupedLinear at its MXFP8 workload (T=8192 top-2, E=8, K=1024, N=2816,
     1% outliers x100): MXFP8 against per-tensor FP8 (not part of the step).
     Quantizers: algorithmic bytes (bf16 read once, codes and scales written;
@@ -196,12 +200,13 @@ def linear_figures(gm, dev, reps):
     E, N, _ = w.shape
     flops = 2.0 * M * N * K
     gbs = lambda ms, nbytes: round(nbytes / ms / 1e6, 1)
-    ms_mqx, mx_x = time_call(lambda: gm.mxfp8_quantize(x), reps)
-    ms_mqw, mx_w = time_call(lambda: gm.mxfp8_quantize(w), reps)
-    ms_mg, _ = time_call(lambda: gm.grouped_linear_fwd(mx_x["row"], offs, mx_w["row"]), reps)
-    ms_pqx, pt_x = time_call(lambda: gm.fp8_tensor_quantize(x, offs), reps)
-    ms_pqw, pt_w = time_call(lambda: gm.fp8_tensor_quantize(w), reps)
-    ms_pg, _ = time_call(lambda: gm.grouped_linear_fwd_fp8(pt_x, offs, pt_w), reps)
+    timed = lambda f: time_call(gm, lib, f, reps)
+    ms_mqx, mx_x = timed(lambda: gm.mxfp8_quantize(x))
+    ms_mqw, mx_w = timed(lambda: gm.mxfp8_quantize(w))
+    ms_mg, _ = timed(lambda: gm.grouped_linear_fwd(mx_x["row"], offs, mx_w["row"]))
+    ms_pqx, pt_x = timed(lambda: gm.fp8_tensor_quantize(x, offs))
+    ms_pqw, pt_w = timed(lambda: gm.fp8_tensor_quantize(w))
+    ms_pg, _ = timed(lambda: gm.grouped_linear_fwd_fp8(pt_x, offs, pt_w))
     mx_bytes = lambda n: n * (2 + 1 + 1 / 32)
     pt_bytes = lambda n: n * (2 + 2 + 1)
     return {
@@ -218,7 +223,7 @@ def linear_figures(gm, dev, reps):
     }
 
 
-def routing_figures(gm, case, dev, reps):
+def routing_figures(gm, lib, case, dev, reps):
     """The steps around the expert path at the same shape (not part of the
     step): the router (top-2 of fp32 logits and their softmax), the
     sorted-row plan of the top-2 routing, the permute of the token
@@ -237,7 +242,7 @@ def routing_figures(gm, case, dev, reps):
     x_tok = case.X[torch.from_numpy(first).to(dev)].contiguous()
     y = case.dY
 
-    timed = lambda f: time_call(f, reps)
+    timed = lambda f: time_call(gm, lib, f, reps)
 
     logits = torch.randn((T, E), dtype=torch.float32, device=dev,
                          generator=torch.Generator(device=dev).manual_seed(3))
@@ -334,8 +339,8 @@ def main():
           file=sys.stderr, flush=True)
     del cbuf
 
-    routing = routing_figures(gm, case, dev, reps=max(args.steps, 3))
-    linear = linear_figures(gm, dev, reps=max(args.steps, 3))
+    routing = routing_figures(gm, lib, case, dev, reps=max(args.steps, 3))
+    linear = linear_figures(gm, lib, dev, reps=max(args.steps, 3))
 
     ms_step = elapsed / args.steps * 1e3
     tokens_s = T * args.steps / elapsed

@@ -8,15 +8,20 @@
 // fp32 product x * scale.  scale_inv = 1 / scale is what the GEMM multiplies
 // its fp32 accumulators by.
 //
-// Three launches over 128-row x 64-column tiles of the flat [rows][C] input
-// (lane t reads 16 bytes, chunk t & 7, of rows t >> 3 + 32 i, so every load
-// instruction moves 32 full 128-byte row segments):
+// Three launches:
 //  * amax_init -- amax[g] = 0;
-//  * amax      -- a tile's max |x|: one atomic max per tile when the tile lies
-//                 in one group, else one per row segment (fp32 bit patterns of
-//                 non-negative values order like unsigned integers);
-//  * cast      -- codes of every row from its group's scale; the first
-//                 workgroup also writes scale_inv of every group.
+//  * amax      -- about two workgroups per CU, each streaming one contiguous
+//                 range of rows; the range is cut at group boundaries and each
+//                 piece (contiguous bytes) is reduced to one atomic max on its
+//                 group (fp32 bit patterns of non-negative values order like
+//                 unsigned integers).  Device-scope atomics on one cache line
+//                 serialize (about 12 ns each here), so their number is kept
+//                 to about the number of workgroups plus the number of groups;
+//  * cast      -- 128-row x 64-column tiles (lane t reads 16 bytes, chunk
+//                 t & 7, of rows t >> 3 + 32 i, so every load instruction
+//                 moves 32 full 128-byte row segments): codes of every row from
+//                 its group's scale; the first workgroup also writes scale_inv
+//                 of every group.
 // The input is read twice (the scale needs the amax of the whole tensor
 // first): 5 bytes per element moved against 4 + 1/16 for the MXFP8 tiles.
 #include <float.h>
@@ -31,6 +36,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2 /* nt */);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -96,45 +105,57 @@ amax_init_kernel(uint32_t* __restrict__ amax, int G) {
     if ((int)threadIdx.x < G) amax[threadIdx.x] = 0u;
 }
 
+// First row of group g (g <= G): offs[g], or g * R for matrices.
+__device__ __forceinline__ int64_t group_start(int g, const int64_t* offs, int64_t R) {
+    return offs ? offs[g] : (int64_t)g * R;
+}
+
 __global__ void __launch_bounds__(256)
 amax_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t C,
-            const int64_t* __restrict__ offs, int G, int64_t R, uint32_t* __restrict__ amax) {
+            const int64_t* __restrict__ offs, int G, int64_t R, int64_t rows_per_block,
+            uint32_t* __restrict__ amax) {
     __shared__ uint32_t red[4];
-    const TileLoad L = load_tile(x, rows, C);
-    const int t = threadIdx.x, lane = t & 63;
-    const int64_t last = min(L.row0 + 127, rows - 1);
-    const int g_first = group_of(L.row0, offs, G, R);
-    const int g_last = group_of(last, offs, G, R);
-    uint32_t m[4];
+    const int t = threadIdx.x;
+    // this workgroup's rows, clipped to the rows the groups cover
+    const int64_t lo = max((int64_t)blockIdx.x * rows_per_block, group_start(0, offs, R));
+    const int64_t hi = min(min((int64_t)(blockIdx.x + 1) * rows_per_block, rows),
+                           group_start(G, offs, R));
+    if (lo >= hi) return;                                   // the whole workgroup
+    const int g_lo = group_of(lo, offs, G, R), g_hi = group_of(hi - 1, offs, G, R);
+    for (int g = g_lo; g <= g_hi; ++g) {
+        const int64_t a = max(lo, group_start(g, offs, R));
+        const int64_t b = min(hi, group_start(g + 1, offs, R));
+        if (a >= b) continue;                               // empty group (uniform)
+        // rows [a, b) are (b - a) * C contiguous values: 16-byte chunks,
+        // four loads in flight per lane
+        const uint4* src = reinterpret_cast<const uint4*>(x + a * C);
+        const int64_t n = (b - a) * C / 8;
+        uint32_t m = 0u;
+        int64_t i = t;
+        for (; i + 3 * 256 < n; i += 4 * 256) {
+            uint4 w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float v[8];
-        unpack8(L.w[i], v);
-        m[i] = 0u;
+            for (int u = 0; u < 4; ++u) w[u] = load_nt(src + i + u * 256);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) m[i] = max(m[i], abs_bits(v[j]));
-    }
-    if (g_first == g_last && g_first >= 0) {
-        uint32_t mm = max(max(m[0], m[1]), max(m[2], m[3]));
+            for (int u = 0; u < 4; ++u) {
+                float v[8];
+                unpack8(w[u], v);
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) mm = max(mm, (uint32_t)__shfl_xor((int)mm, d));
-        if (lane == 0) red[t >> 6] = mm;
-        __syncthreads();
-        if (t == 0) atomicMax(&amax[g_first], max(max(red[0], red[1]), max(red[2], red[3])));
-        return;
-    }
-    // the tile crosses a group boundary (or an edge of the grouped rows): per
-    // row, the 8 lanes of its segment
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t mm = m[i];
-#pragma unroll
-        for (int d = 4; d >= 1; d >>= 1) mm = max(mm, (uint32_t)__shfl_xor((int)mm, d));
-        const int64_t row = L.row0 + (t >> 3) + 32 * i;
-        if ((t & 7) == 0 && row < rows) {
-            const int g = group_of(row, offs, G, R);
-            if (g >= 0) atomicMax(&amax[g], mm);
+                for (int j = 0; j < 8; ++j) m = max(m, abs_bits(v[j]));
+            }
         }
+        for (; i < n; i += 256) {
+            float v[8];
+            unpack8(load_nt(src + i), v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = max(m, abs_bits(v[j]));
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, d));
+        if ((t & 63) == 0) red[t >> 6] = m;
+        __syncthreads();
+        if (t == 0) atomicMax(&amax[g], max(max(red[0], red[1]), max(red[2], red[3])));
+        __syncthreads();                                    // red is reused by the next group
     }
 }
 
@@ -176,9 +197,15 @@ hipError_t launch_fp8_tensor_quant(const uint16_t* x, int64_t rows, int64_t C,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (rows > 0 && C > 0) {
-        const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)((C + 63) / 64));
-        hipLaunchKernelGGL(amax_kernel, grid, dim3(256), 0, s, x, rows, C, offs, G, R, amax);
+        // about two workgroups per CU, each with at least 16 KiB of input
+        int64_t nb = min((int64_t)2 * device_cu_count(), (rows * C + 8191) / 8192);
+        nb = max(nb, (int64_t)1);
+        const int64_t rpb = (rows + nb - 1) / nb;
+        nb = (rows + rpb - 1) / rpb;
+        hipLaunchKernelGGL(amax_kernel, dim3((unsigned)nb), dim3(256), 0, s, x, rows, C, offs, G,
+                           R, rpb, amax);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        const dim3 grid((unsigned)((rows + 127) / 128), (unsigned)((C + 63) / 64));
         hipLaunchKernelGGL(cast_kernel, grid, dim3(256), 0, s, x, rows, C, offs, G, R,
                            (const uint32_t*)amax, codes, scale_inv);
     } else {
