@@ -128,7 +128,7 @@ CtxLayout ctx_layout(const MlpDims& d) {
 }
 
 struct FwdWs {
-    size_t xr, xr_s, w1r, w1r_s, w2r, w2r_s, zr, zr_s, total;
+    size_t xr, xr_s, w1r, w1r_s, w2r, w2r_s, zr, zr_s, split, total;
 };
 FwdWs fwd_ws_layout(const MlpDims& d) {
     Carver c;
@@ -142,6 +142,7 @@ FwdWs fwd_ws_layout(const MlpDims& d) {
     L.xr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
     L.zr = c.take((size_t)d.M * d.F);
     L.zr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.F));
+    L.split = c.take(mx::kSplitWsBytes);      // tail split of the down GEMM
     L.total = c.off;
     return L;
 }
@@ -149,7 +150,7 @@ FwdWs fwd_ws_layout(const MlpDims& d) {
 int64_t dr_parts(int64_t F) { return (F + 255) / 256 * 2; }
 
 struct BwdWs {
-    size_t dyr, dyr_s, dycol, dycol_s, dhr, dhr_s, dhc, dhc_s, drp, total;
+    size_t dyr, dyr_s, dycol, dycol_s, dhr, dhr_s, dhc, dhc_s, drp, split, total;
 };
 BwdWs bwd_ws_layout(const MlpDims& d) {
     Carver c;
@@ -163,6 +164,7 @@ BwdWs bwd_ws_layout(const MlpDims& d) {
     L.dhc = c.take((size_t)2 * d.F * d.Mp);
     L.dhc_s = c.take((size_t)2 * d.F * d.Mp / 32);
     L.drp = c.take((size_t)d.M * dr_parts(d.F) * 4);
+    L.split = c.take(mx::kSplitWsBytes);      // tail split of the gate-up dgrad
     L.total = c.off;
     return L;
 }
@@ -196,7 +198,12 @@ const char* epi_name(mx::Epi e) {
 }
 
 hipError_t gemm(const mx::GemmProblem& p, mx::Epi e, double flops, hipStream_t s) {
-    return timed(epi_name(e), flops, MX_WORK_FLOP, s, [&] { return mx::launch_mx_gemm(p, e, s); });
+    const hipError_t err =
+        timed(epi_name(e), flops, MX_WORK_FLOP, s, [&] { return mx::launch_mx_gemm(p, e, s); });
+    if (err != hipSuccess || e != mx::Epi::kStoreBf16 || !p.split_ws || p.kgroup) return err;
+    // the split tail's partial tiles, added and stored (no-op without a split)
+    return timed("split_fixup", 0.0, MX_WORK_BYTES, s,
+                 [&] { return mx::launch_split_fixup(p, s); });
 }
 
 }  // namespace
@@ -578,6 +585,7 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
     q.A = mx::MxOperand{wb + W.zr, wb + W.zr_s, F, 0, true};
     q.B = mx::MxOperand{wb + W.w2r, wb + W.w2r_s, F, H, true};
     q.C = y; q.ldc = H;
+    q.split_ws = wb + W.split;
     return launched(gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * F, s), "mx_gemm(down)");
 }
 
@@ -656,6 +664,7 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         q.A = mx::MxOperand{wb + W.dhr, wb + W.dhr_s, M2, 0, true};
         q.B = mx::MxOperand{cb + C.w1c, cb + C.w1c_s, M2, H, true};
         q.C = dx; q.ldc = H;
+        q.split_ws = wb + W.split;
         e = gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * M2, s);
         if (e != hipSuccess) return launched(e, "mx_gemm(dgrad-gate-up)");
     }

@@ -454,7 +454,67 @@ __device__ __forceinline__ void pick_unit(const v4f (&acc)[8][8], int ip, float 
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <Epi EPI>
+// Plain epilogue: the tile's accumulators (times the row's routing weight and
+// the group factors when given) to bf16 C.  B is the MFMA's first operand, so
+// acc[i][j] holds the transposed 16 x 16 block: lane (r16, q) has row
+// i*16 + r16 of the wave tile and its 4 consecutive columns j*16 + 4q + v.
+// Lanes q and q^1 (16 lanes apart) hold the same row; one v_permlane16_swap
+// per dword gives the even lane 8 consecutive columns of block 2jp and the odd
+// lane 8 of block 2jp+1, so each row leaves as 64 contiguous bytes in 16-byte
+// stores.  A block pair (32 columns) is wholly inside or outside N
+// (N % 32 == 0).
+__device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[8][8], const GemmProblem& p,
+                                                int g, int64_t m0, int64_t mvalid, int64_t n0,
+                                                int wm, int wn, int lane) {
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t rwave = m0 + wm * 128;
+    const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
+    uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (p.kgroup ? (int64_t)g * p.c_gstride : 0);
+    const int64_t cw = n0 + wn * 128;
+    const int codd = q & 1;
+    const float gs = (p.gsa ? p.gsa[g] : 1.0f) * (p.gsb ? p.gsb[g] : 1.0f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rl = i * 16 + r16;
+        const bool rok = rl < rows_valid_w;
+        const int64_t row = rwave + (rok ? rl : 0);
+        const float sc = p.rscale ? p.rscale[row] * gs : gs;
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+            float va[4], vb[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                va[v] = acc[i][2 * jp][v] * sc;
+                vb[v] = acc[i][2 * jp + 1][v] * sc;
+            }
+            const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
+            const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+            const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+            const int64_t col = cw + (2 * jp + codd) * 16 + 4 * (q & 2);
+            if (rok && cw + 2 * jp * 16 < p.N)
+                store_nt(C + row * p.ldc + col, make_uint4(x[0], y[0], x[1], y[1]));
+        }
+    }
+}
+
+// Tail-split workspace: header, then the partial tiles.  A partial tile keeps
+// the MFMA output layout: block (i, j) of wave w is 1 KiB at float offset
+// ((w * 64 + i * 8 + j) * 64 + lane) * 4, so every store and load of it is
+// one coalesced 1 KiB access.
+struct SplitHdr {
+    int32_t rem;                 // tail tiles that were split (0: none)
+    int32_t S;                   // chunks per tail tile
+    int32_t pad[14];
+    int64_t meta[kSplitItems / 2][4];   // per tail tile: group, m0, mvalid, n0
+};
+static_assert(sizeof(SplitHdr) <= kSplitHdrBytes, "split header fits");
+
+__device__ __forceinline__ float* split_part(uint8_t* ws, int item) {
+    return reinterpret_cast<float*>(ws + kSplitHdrBytes) + (int64_t)item * (BM * BN);
+}
+
+// SPLIT (plain store, row-grouped only): the tail-split schedule below.
+template <Epi EPI, bool SPLIT = false>
 __global__ void __launch_bounds__(NTHREADS, 1)
 mx_gemm_kernel(GemmProblem p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Slot<EPI>::kSmem];
@@ -535,9 +595,39 @@ mx_gemm_kernel(GemmProblem p) {
     const int bid = blockIdx.x;
     const int slot = (grid % 8 == 0) ? (bid % 8) * (grid / 8) + bid / 8 : bid;
 
-    for (int t0 = 0; t0 < total; t0 += grid) {
-        const int t = t0 + slot;
-        if (t >= total) break;
+    // Tail split (plain store, row-grouped): tiles [0, full) run whole; each
+    // of the last round's rem tiles runs as S chunks of its K steps, so that
+    // round keeps rem * S workgroups busy instead of rem.  full is a multiple
+    // of the grid, so the chunks form the last round on their own.
+    int full = total, S = 1;
+    if constexpr (SPLIT) {
+        {
+            const int rem = total % grid;
+            const int nk_all = (int)(p.K / BK);
+            if (rem > 0 && 2 * rem <= grid) {
+                S = min(min(grid / rem, kSplitMax), nk_all);
+                if (S < 2 || rem * S > kSplitItems) S = 1;
+                else full = total - rem;
+            }
+            if (bid == 0 && tid == 0) {
+                SplitHdr* hdr = reinterpret_cast<SplitHdr*>(p.split_ws);
+                hdr->rem = S > 1 ? rem : 0;
+                hdr->S = S;
+            }
+        }
+    }
+    const int items = full + (total - full) * S;
+
+    for (int t0 = 0; t0 < items; t0 += grid) {
+        const int w = t0 + slot;
+        if (w >= items) break;
+        int t = w, chunk = -1;
+        if constexpr (SPLIT) {
+            if (w >= full) {
+                t = full + (w - full) / S;
+                chunk = (w - full) % S;
+            }
+        }
         // Per-lane offsets are derived per tile from an opaque copy of the
         // lane index: hoisted out of the tile loop they would stay live
         // through the epilogue, which needs every register it can get.
@@ -585,6 +675,14 @@ mx_gemm_kernel(GemmProblem p) {
                 mvalid = min((int64_t)BM, p.offs[g + 1] - m0);
                 klo = 0;
                 K = p.K;
+                if constexpr (SPLIT) {
+                    if (chunk >= 0) {       // K steps [c0, c1) of the tile
+                        const int nk_all = (int)(p.K / BK);
+                        const int c0 = chunk * nk_all / S, c1 = (chunk + 1) * nk_all / S;
+                        klo = (int64_t)c0 * BK;
+                        K = (int64_t)(c1 - c0) * BK;
+                    }
+                }
             }
         }
         g = uni(g);
@@ -775,36 +873,24 @@ mx_gemm_kernel(GemmProblem p) {
         const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
 
         if constexpr (EPI == Epi::kStoreBf16) {
-            uint16_t* C = reinterpret_cast<uint16_t*>(p.C) +
-                          (p.kgroup ? (int64_t)g * p.c_gstride : 0);
-            const int64_t cw = n0 + wn * 128;
-            // Lanes q and q^1 (16 lanes apart) hold the same row; one
-            // v_permlane16_swap per dword gives the even lane 8 consecutive
-            // columns of block 2jp and the odd lane 8 of block 2jp+1, so each
-            // row leaves as 64 contiguous bytes in 16-byte stores.  A block
-            // pair (32 columns) is wholly inside or outside N (N % 32 == 0).
-            const int codd = q & 1;
-            const float gs = (p.gsa ? p.gsa[g] : 1.0f) * (p.gsb ? p.gsb[g] : 1.0f);
+            if (!SPLIT || chunk < 0) {
+                store_tile_bf16(acc, p, g, m0, mvalid, n0, wm, wn, lane);
+            } else {
+                // a chunk of a split tail tile: fp32 partial tile to the
+                // workspace; chunk 0 also records the tile's coordinates
+                float* part = split_part(p.split_ws, w - full);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int rl = i * 16 + r16;
-                const bool rok = rl < rows_valid_w;
-                const int64_t row = rwave + (rok ? rl : 0);
-                const float sc = p.rscale ? p.rscale[row] * gs : gs;
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    float va[4], vb[4];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        va[v] = acc[i][2 * jp][v] * sc;
-                        vb[v] = acc[i][2 * jp + 1][v] * sc;
-                    }
-                    const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
-                    const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
-                    const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
-                    const int64_t col = cw + (2 * jp + codd) * 16 + 4 * (q & 2);
-                    if (rok && cw + 2 * jp * 16 < p.N)
-                        store_nt(C + row * p.ldc + col, make_uint4(x[0], y[0], x[1], y[1]));
+                    for (int j = 0; j < 8; ++j)
+                        *reinterpret_cast<v4f*>(part + ((wave * 64 + i * 8 + j) * 64 + lane) * 4) =
+                            acc[i][j];
+                if (chunk == 0 && tid == 0) {
+                    int64_t* meta = reinterpret_cast<SplitHdr*>(p.split_ws)->meta[(w - full) / S];
+                    meta[0] = g;
+                    meta[1] = m0;
+                    meta[2] = mvalid;
+                    meta[3] = n0;
                 }
             }
         } else if constexpr (EPI == Epi::kSwiglu) {
@@ -1008,14 +1094,56 @@ dr_reduce_kernel(const float* __restrict__ drp, int64_t M, int64_t nparts,
     dr[i] = s;
 }
 
+// Sum of the S partial tiles of each split tail tile (chunk order fixed),
+// with the plain epilogue's scaling and bf16 rounding.  One thread per 4
+// consecutive outputs (one v4f of the partial layout: lane (r16, q) of block
+// (i, j) of wave w holds row wm*128 + i*16 + r16, columns wn*128 + j*16 + 4q
+// .. +3), 64 workgroups per tail tile; the grid covers the largest possible
+// tail and workgroups past the recorded count exit.
+__global__ void __launch_bounds__(256)
+split_fixup_kernel(GemmProblem p) {
+    const SplitHdr* hdr = reinterpret_cast<const SplitHdr*>(p.split_ws);
+    const int rem = hdr->rem, S = hdr->S;
+    const int tb = blockIdx.x >> 6;
+    if (tb >= rem) return;
+    const int f4 = (blockIdx.x & 63) * 256 + threadIdx.x;     // v4f index in the tile
+    const int lane = f4 & 63, blk = f4 >> 6;                   // blk = w * 64 + i * 8 + j
+    const int w = blk >> 6, i = (blk >> 3) & 7, j = blk & 7;
+    const int64_t* meta = hdr->meta[tb];
+    const int g = (int)meta[0];
+    const int64_t m0 = meta[1], mvalid = meta[2], n0 = meta[3];
+    const int rl = (w >> 1) * 128 + i * 16 + (lane & 15);
+    const int64_t col = n0 + (w & 1) * 128 + j * 16 + 4 * (lane >> 4);
+    if (rl >= mvalid || col >= p.N) return;
+    const float* part = split_part(p.split_ws, tb * S) + (int64_t)f4 * 4;
+    v4f sum = *reinterpret_cast<const v4f*>(part);
+    for (int c = 1; c < S; ++c) sum += *reinterpret_cast<const v4f*>(part + (int64_t)c * (BM * BN));
+    const int64_t row = m0 + rl;
+    const float gs = (p.gsa ? p.gsa[g] : 1.0f) * (p.gsb ? p.gsb[g] : 1.0f);
+    const float sc = p.rscale ? p.rscale[row] * gs : gs;
+    float v[4] = {sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc};
+    uint16_t* C = reinterpret_cast<uint16_t*>(p.C);
+    *reinterpret_cast<uint2*>(C + row * p.ldc + col) = pack4_bf16(v);
+}
+
 }  // namespace
+
+hipError_t launch_split_fixup(const GemmProblem& p, hipStream_t s) {
+    if (!p.split_ws || p.kgroup) return hipSuccess;
+    hipLaunchKernelGGL(split_fixup_kernel, dim3(64 * (kSplitItems / 2)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s) {
     int grid = device_cu_count();
     grid = grid < 8 ? 8 : grid / 8 * 8;
     switch (epi) {
         case Epi::kStoreBf16:
-            hipLaunchKernelGGL(mx_gemm_kernel<Epi::kStoreBf16>, dim3(grid), dim3(NTHREADS), 0, s, p);
+            if (p.split_ws && !p.kgroup)
+                hipLaunchKernelGGL((mx_gemm_kernel<Epi::kStoreBf16, true>), dim3(grid), dim3(NTHREADS),
+                                   0, s, p);
+            else
+                hipLaunchKernelGGL(mx_gemm_kernel<Epi::kStoreBf16>, dim3(grid), dim3(NTHREADS), 0, s, p);
             break;
         case Epi::kSwiglu:
             hipLaunchKernelGGL(mx_gemm_kernel<Epi::kSwiglu>, dim3(grid), dim3(NTHREADS), 0, s, p);

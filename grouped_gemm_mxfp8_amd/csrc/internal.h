@@ -91,9 +91,25 @@ struct GemmProblem {
     float* drp; int64_t lddrp;  // kDSwiglu: dr partials [M][lddrp]
     const float* gsa;           // kStoreBf16: per-group factors of A and of B
     const float* gsb;           //   (scale_inv of per-tensor FP8), or nullptr
+    uint8_t* split_ws;          // kStoreBf16, row-grouped: tail-split workspace
+                                //   of kSplitWsBytes, or nullptr (no split)
 };
 
+// Tail split of the plain-store row-grouped GEMM.  When the last round of
+// output tiles would leave more than half of the persistent workgroups idle,
+// each of its tiles is cut along K into S <= kSplitMax chunks, one workgroup
+// per chunk; the chunks' fp32 partial tiles go to split_ws and
+// launch_split_fixup (same stream, right after the GEMM) adds them in chunk
+// order and stores the tiles.  Workspace: a header (tail tile count, S and
+// each tail tile's coordinates) and kSplitItems partial tiles of 256 x 256
+// fp32.
+constexpr int kSplitMax = 4;
+constexpr int kSplitItems = 256;
+constexpr size_t kSplitHdrBytes = 8192;
+constexpr size_t kSplitWsBytes = kSplitHdrBytes + (size_t)kSplitItems * 256 * 256 * 4;
+
 hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s);
+hipError_t launch_split_fixup(const GemmProblem& p, hipStream_t s);
 
 // Sum of dr partials: dr[i] = sum_j drp[i][j], j ascending.
 hipError_t launch_dr_reduce(const float* drp, int64_t M, int64_t nparts,
