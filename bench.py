@@ -22,7 +22,9 @@ optimizer step); the headline always quantizes the weights.  "routing"
 times the steps around the expert path at the same shape (router, sorted-row plan,
 permute fused with quantization, combine and its backward), not in the step;
 "grouped_linear" times GroupedLinear at its own workload (T=8192 top-2, E=8,
-K=1024, N=2816) in MXFP8 and in per-tensor FP8, not in the step either.
+K=1024, N=2816) in MXFP8 and in per-tensor FP8, and the tiny BF16 workload
+(T=256 top-2, E=4, K=128, N=256) as one grouped launch against a loop of one
+launch per expert, not in the step either.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -223,6 +225,48 @@ def linear_figures(gm, lib, dev, reps):
     }
 
 
+def grouped_vs_loop_figures(gm, lib, dev, reps=200):
+    """The tiny BF16 GroupedLinear workload (T=256 top-2, E=4, K=128, N=256):
+    one grouped launch driven by the device offsets against one launch per
+    expert (the loop the grouped call replaces; its per-expert row ranges are
+    taken from the host, as such a loop needs them).  Both are bound by launch
+    cost at this size, so the figure is wall-clock time per call with the
+    host's issue included (reps calls back to back, one synchronization at
+    the end), plus the GPU time of the grouped launch from the library's
+    launch records."""
+    import torch
+    from workloads import make_linear_case
+    case = make_linear_case("tiny_bf16_linear", seed=0)
+    x, w, offs = case.X.to(dev), case.W.to(dev), case.offsets.to(dev)
+    E = w.shape[0]
+    off_h = case.offsets.tolist()
+    parts = [(x[off_h[e]:off_h[e + 1]], torch.tensor([0, off_h[e + 1] - off_h[e]],
+                                                    dtype=torch.int64, device=dev), w[e:e + 1])
+             for e in range(E) if off_h[e + 1] > off_h[e]]
+
+    def grouped():
+        return gm.grouped_linear_fwd(x, offs, w)
+
+    def loop():
+        return [gm.grouped_linear_fwd(xe, oe, we) for xe, oe, we in parts]
+
+    def wall_us(f):
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            f()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps * 1e6
+
+    g_us, l_us = wall_us(grouped), wall_us(loop)
+    gpu_ms, _ = time_call(gm, lib, grouped, reps)
+    return {"shape": {"M": int(x.shape[0]), "K": int(x.shape[1]), "N": int(w.shape[1]), "E": E},
+            "grouped_us_per_call": round(g_us, 2), "per_expert_loop_us_per_call": round(l_us, 2),
+            "loop_over_grouped": round(l_us / g_us, 2), "grouped_gpu_us": round(gpu_ms * 1e3, 2)}
+
+
 def routing_figures(gm, lib, case, dev, reps):
     """The steps around the expert path at the same shape (not part of the
     step): the router (top-2 of fp32 logits and their softmax), the
@@ -341,6 +385,7 @@ def main():
 
     routing = routing_figures(gm, lib, case, dev, reps=max(args.steps, 3))
     linear = linear_figures(gm, lib, dev, reps=max(args.steps, 3))
+    linear["bf16_tiny_grouped_vs_loop"] = grouped_vs_loop_figures(gm, lib, dev)
 
     ms_step = elapsed / args.steps * 1e3
     tokens_s = T * args.steps / elapsed
