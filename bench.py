@@ -21,6 +21,8 @@ weight copies of an earlier forward (as across the micro-batches of one
 optimizer step); the headline always quantizes the weights.  "routing"
 times the steps around the expert path at the same shape (router, sorted-row plan,
 permute fused with quantization, combine and its backward), not in the step;
+"fine_grained_64e" times the same fwd+bwd step at the 64-expert long-sequence
+workload (T=32768 top-8, H=2048, F=1408, 8 empty experts), not in the headline.
 "grouped_linear" times GroupedLinear at its own workload (T=8192 top-2, E=8,
 K=1024, N=2816) in MXFP8 and in per-tensor FP8, and the tiny BF16 workload
 (T=256 top-2, E=4, K=128, N=256) as one grouped launch against a loop of one
@@ -267,6 +269,46 @@ def grouped_vs_loop_figures(gm, lib, dev, reps=200):
             "loop_over_grouped": round(l_us / g_us, 2), "grouped_gpu_us": round(gpu_ms * 1e3, 2)}
 
 
+def many_expert_figures(gm, lib, dev, seed, steps):
+    """GroupedMLP fwd+bwd at the fine-grained long-sequence workload (T=32768
+    tokens top-8, M=262144 rows, E=64, H=2048, F=1408; 8 experts get no rows,
+    the largest gets ~12% of them): step time, throughput and the per-kernel
+    split, from the library's launch records (not part of the headline)."""
+    import torch
+    from workloads import make_mlp_case
+    case = make_mlp_case("fine_grained_64e", seed=seed, device=dev)
+    M, H, F, E, T = case.M, case.H, case.F, case.E, case.T
+    fws = torch.empty(gm.fwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+    bws = torch.empty(gm.bwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+
+    def step():
+        y, ctx = gm.grouped_mlp_fwd(case.X, case.offsets, case.W1, case.W2, case.r, ws=fws)
+        return gm.grouped_mlp_bwd(case.dY, case.offsets, case.W1, case.W2, case.r, ctx, ws=bws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    if lib.mx_profile_begin(64 * steps) != 0:
+        raise RuntimeError(gm.last_error())
+    t = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t
+    lib.mx_profile_end()
+    agg = kernel_table(gm, lib)
+    ms = elapsed / steps * 1e3
+    tflops = 18.0 * H * F * M / (ms / 1e3) / 1e12
+    counts = [int(c) for c in case.counts]
+    return {"shape": {"T": T, "k": case.k, "M": M, "E": E, "H": H, "F": F,
+                      "empty_experts": sum(c == 0 for c in counts),
+                      "largest_expert_rows": max(counts)},
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms / 1e3), 1),
+            "tflops": round(tflops, 2), "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+            "kernels_ms_per_step": {k: round(v["ms"] / steps, 4)
+                                    for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["ms"])}}
+
+
 def routing_figures(gm, lib, case, dev, reps):
     """The steps around the expert path at the same shape (not part of the
     step): the router (top-2 of fp32 logits and their softmax), the
@@ -384,6 +426,10 @@ def main():
     del cbuf
 
     routing = routing_figures(gm, lib, case, dev, reps=max(args.steps, 3))
+    expert_rows = [int(c) for c in case.counts]
+    del case, x, w1, w2, r, off, dy, fws, bws
+    torch.cuda.empty_cache()
+    many = many_expert_figures(gm, lib, dev, args.seed, steps=max(args.steps // 2, 3))
     linear = linear_figures(gm, lib, dev, reps=max(args.steps, 3))
     linear["bf16_tiny_grouped_vs_loop"] = grouped_vs_loop_figures(gm, lib, dev)
 
@@ -413,12 +459,13 @@ def main():
         "config": {"workload": "mixtral_fwd_bwd: GroupedMLP fwd+bwd, T=16384 top-2 (M=32768 "
                                "rows), E=8, H=4096, F=14336, Zipf(1.1) loads",
                    "T": T, "M": M, "E": E, "H": H, "F": F,
-                   "expert_rows": [int(c) for c in case.counts]},
+                   "expert_rows": expert_rows},
         "tflops": round(tflops, 2),
         "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
         "roofline": roofline(agg),
         "kernels": kernels,
         "routing": routing,
+        "fine_grained_64e": many,
         "grouped_linear": linear,
         "weights_cached": {
             "ms_per_step": round(elapsed_cached / args.steps * 1e3, 4),
