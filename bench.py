@@ -407,7 +407,8 @@ def main():
     # The same step with the weight quantization cached: the forward reuses
     # the MXFP8 weight copies of the first forward (weights unchanged, as
     # across the micro-batches of one optimizer step).  Not the headline.
-    cbuf = torch.empty(lib.grouped_mlp_ctx_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+    ctx_bytes = lib.grouped_mlp_ctx_bytes(M, H, F, E)
+    cbuf = torch.empty(ctx_bytes, dtype=torch.uint8, device=dev)
     gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, ctx_buf=cbuf)
 
     def step_cached():
@@ -467,6 +468,11 @@ def main():
         "routing": routing,
         "fine_grained_64e": many,
         "grouped_linear": linear,
+        "saved_for_backward": {
+            "ctx_bytes": int(ctx_bytes),
+            "bytes_per_token": round(ctx_bytes / T, 1),
+            "what": "forward context kept for the backward (bf16 pre-activation h, token-axis "
+                    "MXFP8 copies of X and z, columnwise MXFP8 weight copies, padded offsets)"},
         "weights_cached": {
             "ms_per_step": round(elapsed_cached / args.steps * 1e3, 4),
             "tokens_per_s": round(T * args.steps / elapsed_cached, 1),
