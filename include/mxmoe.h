@@ -176,7 +176,11 @@ mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
  *   w2   bf16 [E][H][F];  d_r fp32 [M];  y bf16 [M][H].
  *   ctx  saved-for-backward buffer of grouped_mlp_ctx_bytes() bytes, written
  *        here and read by grouped_mlp_bwd (opaque; 256-byte aligned).
- *   ws   scratch of grouped_mlp_fwd_ws_bytes() bytes (256-byte aligned).
+ *   ws   scratch of grouped_mlp_fwd_ws_bytes() bytes (256-byte aligned): the
+ *        rowwise MXFP8 copies of x, w1, w2 and z, and 64 MiB (plus an 8 KiB
+ *        header) for the fp32 partial tiles of the down GEMM's split tail
+ *        round (the last round of output tiles, cut along K when it would
+ *        leave more than half of the GPU idle).
  * H % 128 == 0, F % 128 == 0, E in [1, 1024].
  */
 mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E,
@@ -226,7 +230,9 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
  *   ctx holds what is needed, including the quantized columnwise copies of
  *   w1 and w2 made by the forward (w1 and w2 must be the tensors given to
  *   the forward that wrote ctx; the backward only checks them for NULL and
- *   alignment).  ws of grouped_mlp_bwd_ws_bytes() bytes.
+ *   alignment).  ws of grouped_mlp_bwd_ws_bytes() bytes: the MXFP8 copies of
+ *   dY and dh, the dr partial sums, and the split-tail scratch of the gate-up
+ *   dgrad (as in the forward).
  */
 mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E,
                           int64_t M, int64_t H, int64_t F, const void* w1,
