@@ -22,7 +22,9 @@ optimizer step); the headline always quantizes the weights.  "routing"
 times the steps around the expert path at the same shape (router, sorted-row plan,
 permute fused with quantization, combine and its backward), not in the step;
 "fine_grained_64e" times the same fwd+bwd step at the 64-expert long-sequence
-workload (T=32768 top-8, H=2048, F=1408, 8 empty experts), not in the headline.
+workload (T=32768 top-8, H=2048, F=1408, 8 empty experts), and
+"ep8_one_rank_share" the share of the slowest rank if the 8 experts were spread
+over 8 GPUs (E=1, the largest expert's 13047 rows), neither in the headline.
 "grouped_linear" times GroupedLinear at its own workload (T=8192 top-2, E=8,
 K=1024, N=2816) in MXFP8 and in per-tensor FP8, and the tiny BF16 workload
 (T=256 top-2, E=4, K=128, N=256) as one grouped launch against a loop of one
@@ -269,6 +271,38 @@ def grouped_vs_loop_figures(gm, lib, dev, reps=200):
             "loop_over_grouped": round(l_us / g_us, 2), "grouped_gpu_us": round(gpu_ms * 1e3, 2)}
 
 
+def one_rank_share_figures(gm, lib, dev, seed, steps):
+    """Expert parallelism over 8 GPUs would give each rank one expert; under the
+    Zipf loads the slowest rank holds the largest expert (13047 rows).  That
+    rank's fwd+bwd at its real shape (E=1, M=13047, H=4096, F=14336), timed on
+    this one GPU (not part of the headline)."""
+    import torch
+    from workloads import make_mlp_case
+    n = 13047
+    case = make_mlp_case(None, seed=seed, T=n, k=1, E=1, H=4096, F=14336, routing="counts",
+                         counts=[n], device=dev)
+    M, H, F, E = case.M, case.H, case.F, case.E
+    fws = torch.empty(gm.fwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+    bws = torch.empty(gm.bwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+
+    def step():
+        y, ctx = gm.grouped_mlp_fwd(case.X, case.offsets, case.W1, case.W2, case.r, ws=fws)
+        return gm.grouped_mlp_bwd(case.dY, case.offsets, case.W1, case.W2, case.r, ctx, ws=bws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t) / steps * 1e3
+    tflops = 18.0 * H * F * M / (ms / 1e3) / 1e12
+    return {"shape": {"M": M, "E": E, "H": H, "F": F}, "ms_per_step": round(ms, 4),
+            "rows_per_s": round(M / (ms / 1e3), 1), "tflops": round(tflops, 2),
+            "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)}
+
+
 def many_expert_figures(gm, lib, dev, seed, steps):
     """GroupedMLP fwd+bwd at the fine-grained long-sequence workload (T=32768
     tokens top-8, M=262144 rows, E=64, H=2048, F=1408; 8 experts get no rows,
@@ -431,6 +465,8 @@ def main():
     del case, x, w1, w2, r, off, dy, fws, bws
     torch.cuda.empty_cache()
     many = many_expert_figures(gm, lib, dev, args.seed, steps=max(args.steps // 2, 3))
+    torch.cuda.empty_cache()
+    share = one_rank_share_figures(gm, lib, dev, args.seed, steps=max(args.steps // 2, 3))
     linear = linear_figures(gm, lib, dev, reps=max(args.steps, 3))
     linear["bf16_tiny_grouped_vs_loop"] = grouped_vs_loop_figures(gm, lib, dev)
 
@@ -467,6 +503,7 @@ def main():
         "kernels": kernels,
         "routing": routing,
         "fine_grained_64e": many,
+        "ep8_one_rank_share": share,
         "grouped_linear": linear,
         "saved_for_backward": {
             "ctx_bytes": int(ctx_bytes),
