@@ -250,6 +250,7 @@ struct Slot {
     static constexpr int kSmem = 4 * kBytes > (int)sizeof(GemmSmem) ? 4 * kBytes
                                                                      : (int)sizeof(GemmSmem);
     static_assert(EPI != Epi::kSwiglu || QStage<64>::kBytes <= kBytes, "staging fits the slot");
+    static_assert(EPI != Epi::kStoreBf16 || 4 * 32768 <= kSmem, "output quadrants fit the stages");
     static_assert(kBytes % 16 == 0 && QStage<256>::kBytes % 16 == 0, "16-byte aligned regions");
 };
 
@@ -494,6 +495,55 @@ __device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[8][8], const Ge
             if (rok && cw + 2 * jp * 16 < p.N)
                 store_nt(C + row * p.ldc + col, make_uint4(x[0], y[0], x[1], y[1]));
         }
+    }
+}
+
+// Plain epilogue through LDS, for the kernel without the tail split (weight
+// gradients, GroupedLinear): each wave writes its 128 x 128 bf16 quadrant into
+// its quarter of the operand stages (rows of 256 B, 16-byte chunk c at
+// c ^ (row & 15), conflict-free), then stores 4 whole rows per instruction, so
+// every store covers whole 128-byte lines.  Measured against the direct
+// stores of half lines: dW2 -3 %, dW1 -4 % (their 2.8 GB of output per step).
+__device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[8][8], const GemmProblem& p,
+                                                    int g, int64_t m0, int64_t mvalid, int64_t n0,
+                                                    int wm, int wn, int lane, uint8_t* quad) {
+    const int r16 = lane & 15, q = lane >> 4;
+    const int64_t rwave = m0 + wm * 128;
+    const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
+    uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (p.kgroup ? (int64_t)g * p.c_gstride : 0);
+    const int64_t cw = n0 + wn * 128;
+    const int codd = q & 1;
+    const float gs = (p.gsa ? p.gsa[g] : 1.0f) * (p.gsb ? p.gsb[g] : 1.0f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rl = i * 16 + r16;
+        const bool rok = rl < rows_valid_w;
+        const int64_t row = rwave + (rok ? rl : 0);
+        const float sc = p.rscale ? p.rscale[row] * gs : gs;
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+            float va[4], vb[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                va[v] = acc[i][2 * jp][v] * sc;
+                vb[v] = acc[i][2 * jp + 1][v] * sc;
+            }
+            const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
+            const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+            const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+            const int chunk = (2 * jp + codd) * 2 + (q >> 1);
+            *reinterpret_cast<uint4*>(quad + rl * 256 + ((chunk ^ r16) << 4)) =
+                make_uint4(x[0], y[0], x[1], y[1]);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int rr = lane >> 4, ch = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const int rl = 4 * t + rr;
+        const uint4 v = *reinterpret_cast<const uint4*>(quad + rl * 256 + ((ch ^ (rl & 15)) << 4));
+        if (rl < rows_valid_w && cw + ch * 8 < p.N)
+            store_nt(C + (rwave + rl) * p.ldc + cw + ch * 8, v);
     }
 }
 
@@ -873,7 +923,16 @@ mx_gemm_kernel(GemmProblem p) {
         const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
 
         if constexpr (EPI == Epi::kStoreBf16) {
-            if (!SPLIT || chunk < 0) {
+            if (!SPLIT) {
+                // the trailing (zero-range) loads write the stages: wait for
+                // them, and for every wave to leave the stages, before staging
+                // the output there; the closing barrier keeps the next tile's
+                // loads off the stages until every wave has read its quarter
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                lds_barrier();
+                store_tile_bf16_lds(acc, p, g, m0, mvalid, n0, wm, wn, lane, smem + wave * 32768);
+                lds_barrier();
+            } else if (chunk < 0) {
                 store_tile_bf16(acc, p, g, m0, mvalid, n0, wm, wn, lane);
             } else {
                 // a chunk of a split tail tile: fp32 partial tile to the
