@@ -456,54 +456,17 @@ __device__ __forceinline__ void pick_unit(const v4f (&acc)[8][8], int ip, float 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Plain epilogue: the tile's accumulators (times the row's routing weight and
-// the group factors when given) to bf16 C.  B is the MFMA's first operand, so
-// acc[i][j] holds the transposed 16 x 16 block: lane (r16, q) has row
-// i*16 + r16 of the wave tile and its 4 consecutive columns j*16 + 4q + v.
-// Lanes q and q^1 (16 lanes apart) hold the same row; one v_permlane16_swap
-// per dword gives the even lane 8 consecutive columns of block 2jp and the odd
-// lane 8 of block 2jp+1, so each row leaves as 64 contiguous bytes in 16-byte
-// stores.  A block pair (32 columns) is wholly inside or outside N
-// (N % 32 == 0).
-__device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[8][8], const GemmProblem& p,
-                                                int g, int64_t m0, int64_t mvalid, int64_t n0,
-                                                int wm, int wn, int lane) {
-    const int r16 = lane & 15, q = lane >> 4;
-    const int64_t rwave = m0 + wm * 128;
-    const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
-    uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (p.kgroup ? (int64_t)g * p.c_gstride : 0);
-    const int64_t cw = n0 + wn * 128;
-    const int codd = q & 1;
-    const float gs = (p.gsa ? p.gsa[g] : 1.0f) * (p.gsb ? p.gsb[g] : 1.0f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int rl = i * 16 + r16;
-        const bool rok = rl < rows_valid_w;
-        const int64_t row = rwave + (rok ? rl : 0);
-        const float sc = p.rscale ? p.rscale[row] * gs : gs;
-#pragma unroll
-        for (int jp = 0; jp < 4; ++jp) {
-            float va[4], vb[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                va[v] = acc[i][2 * jp][v] * sc;
-                vb[v] = acc[i][2 * jp + 1][v] * sc;
-            }
-            const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
-            const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
-            const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
-            const int64_t col = cw + (2 * jp + codd) * 16 + 4 * (q & 2);
-            if (rok && cw + 2 * jp * 16 < p.N)
-                store_nt(C + row * p.ldc + col, make_uint4(x[0], y[0], x[1], y[1]));
-        }
-    }
-}
-
-// Plain epilogue through LDS, for the kernel without the tail split (weight
-// gradients, GroupedLinear): each wave writes its 128 x 128 bf16 quadrant into
-// its quarter of the operand stages (rows of 256 B, 16-byte chunk c at
-// c ^ (row & 15), conflict-free), then stores 4 whole rows per instruction, so
-// every store covers whole 128-byte lines.  Measured against the direct
-// stores of half lines: dW2 -3 %, dW1 -4 % (their 2.8 GB of output per step).
+// the group factors when given) to bf16 C, through LDS.  B is the MFMA's first
+// operand, so acc[i][j] holds the transposed 16 x 16 block: lane (r16, q) has
+// row i*16 + r16 of the wave tile and its 4 consecutive columns j*16 + 4q + v;
+// one v_permlane16_swap per dword gives lane q (of the pair q, q^1 that share
+// a row) 8 consecutive columns.  Each wave writes its 128 x 128 quadrant into
+// a quarter of the operand stages (rows of 256 B, 16-byte chunk c at
+// c ^ (row & 15), no bank conflicts measured), then stores 4 whole rows per
+// instruction, so every store covers whole 128-byte lines: stored directly
+// from the lanes (16 rows x 64 B per instruction), the plain GEMMs wrote a
+// third more bytes to HBM than their output.  A 32-column block pair is
+// wholly inside or outside N (N % 32 == 0).
 __device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[8][8], const GemmProblem& p,
                                                     int g, int64_t m0, int64_t mvalid, int64_t n0,
                                                     int wm, int wn, int lane, uint8_t* quad) {
@@ -923,7 +886,7 @@ mx_gemm_kernel(GemmProblem p) {
         const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
 
         if constexpr (EPI == Epi::kStoreBf16) {
-            if (!SPLIT) {
+            if (!SPLIT || chunk < 0) {
                 // the trailing (zero-range) loads write the stages: wait for
                 // them, and for every wave to leave the stages, before staging
                 // the output there; the closing barrier keeps the next tile's
@@ -932,8 +895,6 @@ mx_gemm_kernel(GemmProblem p) {
                 lds_barrier();
                 store_tile_bf16_lds(acc, p, g, m0, mvalid, n0, wm, wn, lane, smem + wave * 32768);
                 lds_barrier();
-            } else if (chunk < 0) {
-                store_tile_bf16(acc, p, g, m0, mvalid, n0, wm, wn, lane);
             } else {
                 // a chunk of a split tail tile: fp32 partial tile to the
                 // workspace; chunk 0 also records the tile's coordinates
