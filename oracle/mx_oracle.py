@@ -42,8 +42,14 @@ design notes of the repository):
 * R-swiglu  W1 rows [0, F) are the gate, rows [F, 2F) the up projection;
             s = silu(gate) * up, z = r * s, then z is quantized and fed to the
             down projection.
-* R-save    the backward reads the gate-up pre-activation h as saved by the
-            forward, rounded once to bfloat16 (RNE); h is never requantized.
+* R-recomp  the backward uses the gate-up pre-activation h exactly as the
+            forward computed it (float64 here): the fused kernel keeps h on
+            chip and the backward recomputes it from the same quantized
+            operands instead of reading a stored copy (the pages: the fused
+            GroupedMLP does not hold intermediate results in memory).
+* R-save    an alternative mode, ``h_bf16=True``: the forward stores h rounded
+            once to bfloat16 (RNE) and the backward reads that copy, so the
+            SwiGLU backward sees bf16(h); h is never requantized.
 * R-ste     the backward is straight-through: each GEMM quantizes its own two
             operands along its own contraction axis.
 * R-out     Y, dX, dW1, dW2 are the FP64 results; callers compare them with the
@@ -208,8 +214,8 @@ def qdq_tokens(v, offsets, align=128):
 
 
 # --------------------------------------------------------------------------
-# bfloat16 rounding (used where the device stores a bf16 value that a later
-# step reads back: reading R-save).
+# bfloat16 rounding (used where a bf16 value is stored and read back by a
+# later step: the inputs, and h in the R-save mode).
 # --------------------------------------------------------------------------
 
 def round_bf16(v):
@@ -280,12 +286,15 @@ def grouped_mlp_fwd(X, W1, W2, r, offsets, quantize=True):
 
 
 def grouped_mlp_bwd(dY, X, W1, W2, r, offsets, saved, quantize=True,
-                    align=128):
+                    align=128, h_bf16=False):
     """Backward of grouped_mlp_fwd (straight-through quantizers, R-ste).
 
     Returns dict with dX [M, H], dW1 [E, 2F, H], dW2 [E, H, F], dr [M].
     With quantize=False this is the exact gradient of the unquantized
-    forward (loss L = sum(Y * dY)).
+    forward (loss L = sum(Y * dY)).  The SwiGLU backward reads h as the
+    forward computed it (reading R-recomp); with h_bf16=True (quantized mode
+    only) it reads bf16(h) instead, the copy a forward that stores h keeps
+    (reading R-save).
     """
     dY = np.asarray(dY, np.float64)
     X = np.asarray(X, np.float64)
@@ -293,13 +302,16 @@ def grouped_mlp_bwd(dY, X, W1, W2, r, offsets, saved, quantize=True,
     W2 = np.asarray(W2, np.float64)
     r = np.asarray(r, np.float64)
     E, H, F = W2.shape
+    h = saved["h"]                                      # reading R-recomp
     if quantize:
         q_row = qdq_lastdim
         q_tok = lambda t: qdq_tokens(t, offsets, align)
-        h = round_bf16(saved["h"])                      # reading R-save
+        if h_bf16:
+            h = round_bf16(h)                           # reading R-save
     else:
+        if h_bf16:
+            raise ValueError("h_bf16 applies to the quantized backward only")
         q_row = q_tok = lambda t: np.asarray(t, np.float64)
-        h = saved["h"]
     z = saved["z"]
 
     # dgrad of the down projection: dz = dY W2 (K = H), W2 blocks along H.

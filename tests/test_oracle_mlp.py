@@ -230,3 +230,75 @@ def test_single_expert_slices_equal_the_full_computation():
     Ys, dXs, drs, _, _ = expert_reference(X[lo + rows], W1[2], W2[2], r[lo + rows],
                                           dY[lo + rows])
     same(Ys, Y[lo + rows]); same(dXs, g["dX"][lo + rows]); same(drs, g["dr"][lo + rows])
+
+
+def _load_h_rounding_case():
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "mlp_bwd_h_rounding.txt")
+    kv = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            key, *vals = line.split()
+            kv[key] = vals
+    H, F = int(kv["H"][0]), int(kv["F"][0])
+    X = np.zeros((1, H))
+    for t in kv["x"]:
+        i, v = t.split(":")
+        X[0, int(i)] = float(v)
+    W1 = np.zeros((1, 2 * F, H))
+    for t in kv["w1"]:
+        i, j, v = t.split(":")
+        W1[0, int(i), int(j)] = float(v)
+    W2 = np.zeros((1, H, F))
+    for t in kv["w2"]:
+        i, j, v = t.split(":")
+        W2[0, int(i), int(j)] = float(v)
+    dY = np.zeros((1, H))
+    for t in kv["dy"]:
+        i, v = t.split(":")
+        dY[0, int(i)] = float(v)
+    r = np.array([float(kv["r"][0])])
+    exp = {}
+    for mode in ("recompute", "saved_h"):
+        codes = np.zeros(2 * F, dtype=np.uint8)
+        lead = [int(c, 16) for c in kv["codes_" + mode]]
+        codes[:len(lead)] = lead
+        exp[mode] = (codes, np.array([int(s) for s in kv["scales_" + mode]], dtype=np.uint8))
+    return X, W1, W2, dY, r, exp
+
+
+def test_bwd_h_rounding_golden_codes():
+    """Hand-derived dh codes (tests/golden/mlp_bwd_h_rounding.txt): the
+    default backward uses the exact h (its code 1 is 0x39); the saved-h mode
+    reads bf16(h) (code 1 is 0x38).  A rounding of h dropped from one mode or
+    added to the other, or a bf16 rounding of dz or dh, changes a code."""
+    X, W1, W2, dY, r, exp = _load_h_rounding_case()
+    off = np.array([0, 1], dtype=np.int64)
+    # the inputs are MXFP8-exact, so the quantizers leave them unchanged
+    for t in (X, W1, W2.transpose(0, 2, 1), dY):
+        assert np.array_equal(O.qdq_lastdim(t), t)
+    Y, saved = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    assert saved["h"][0, 32] == 288.0 and saved["h"][0, 33] == 1.0634765625
+    for mode, kw in (("recompute", {}), ("saved_h", {"h_bf16": True})):
+        g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved, **kw)
+        codes, scales = O.quantize_lastdim(g["dh"])
+        assert np.array_equal(codes[0], exp[mode][0]), (mode, codes[0][:4])
+        assert np.array_equal(scales[0], exp[mode][1]), (mode, scales[0])
+        assert g["dr"][0] == 0.0                      # s = silu(0) b = 0
+    assert not np.array_equal(exp["recompute"][0], exp["saved_h"][0])
+
+
+def test_bwd_h_bf16_mode_reads_the_rounded_h():
+    """The saved-h mode equals the default backward run on bf16(h), and the
+    two differ once h is not bf16-representable."""
+    rng = np.random.default_rng(29)
+    X, W1, W2, r, off, dY = rand_case(rng, [40, 0, 57], 64, 64)
+    _, saved = O.grouped_mlp_fwd(X, W1, W2, r, off)
+    g_s = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved, h_bf16=True)
+    rounded = dict(saved, h=O.round_bf16(saved["h"]))
+    g_r = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, rounded)
+    for name in ("dX", "dW1", "dW2", "dr", "dh"):
+        assert np.array_equal(g_s[name], g_r[name]), name
+    g = O.grouped_mlp_bwd(dY, X, W1, W2, r, off, saved)
+    assert not np.array_equal(g["dh"], g_s["dh"])
