@@ -441,7 +441,7 @@ def main():
     # The same step with the weight quantization cached: the forward reuses
     # the MXFP8 weight copies of the first forward (weights unchanged, as
     # across the micro-batches of one optimizer step).  Not the headline.
-    ctx_bytes = lib.grouped_mlp_ctx_bytes(M, H, F, E)
+    ctx_bytes = gm.ctx_bytes(M, H, F, E)
     cbuf = torch.empty(ctx_bytes, dtype=torch.uint8, device=dev)
     gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, ctx_buf=cbuf)
 

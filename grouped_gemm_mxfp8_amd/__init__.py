@@ -24,7 +24,10 @@ MX_DTYPE_MXFP8 = 1
 TOKEN_ALIGN = 128
 BLOCK = 32
 MX_CTX_H, MX_CTX_XCOL, MX_CTX_ZCOL, MX_CTX_POFF, MX_CTX_W1COL, MX_CTX_W2COL = 0, 1, 2, 3, 4, 5
-MX_WS_ZROW, MX_WS_DHROW, MX_WS_DHCOL = 0, 1, 2
+MX_CTX_XROW, MX_CTX_W1ROW, MX_CTX_W2ROW = 6, 7, 8
+MX_WS_ZROW, MX_WS_DHROW, MX_WS_DHCOL, MX_WS_DYROW, MX_WS_DYCOL = 0, 1, 2, 3, 4
+MX_FWD_REUSE_WEIGHTS = 1
+MX_MLP_SAVE_H = 2
 
 _lib = None
 
@@ -47,7 +50,9 @@ _SIGS = {
                                   _SZ, ctypes.c_uint32, _P]),
     "grouped_mlp_bwd": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P, _P, _P,
                                _P, _P, _SZ, _P]),
-    "grouped_mlp_ctx_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
+    "grouped_mlp_bwd_ex": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P, _P,
+                                  _P, _P, _P, _SZ, ctypes.c_uint32, _P]),
+    "grouped_mlp_ctx_bytes": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_uint32]),
     "moe_router": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_route_ws_bytes": (_SZ, [_I64, _I32, _I32]),
     "moe_route_plan": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -55,10 +60,10 @@ _SIGS = {
                                     _P, _P]),
     "moe_combine": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P]),
     "moe_combine_bwd": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P, _I64, _P, _P, _P]),
-    "grouped_mlp_fwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
-    "grouped_mlp_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32]),
-    "grouped_mlp_ctx_offset": (_I64, [_I32, _I64, _I64, _I64, _I32]),
-    "grouped_mlp_ws_offset": (_I64, [_I32, _I64, _I64, _I64, _I32]),
+    "grouped_mlp_fwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_uint32]),
+    "grouped_mlp_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I32, ctypes.c_uint32]),
+    "grouped_mlp_ctx_offset": (_I64, [_I32, _I64, _I64, _I64, _I32, ctypes.c_uint32]),
+    "grouped_mlp_ws_offset": (_I64, [_I32, _I64, _I64, _I64, _I32, ctypes.c_uint32]),
 }
 
 
@@ -272,29 +277,38 @@ def grouped_linear_fwd_fp8(x: Fp8Tensor, offsets: torch.Tensor, w: Fp8Tensor,
     return y
 
 
+def _flags(save_h: bool) -> int:
+    return MX_MLP_SAVE_H if save_h else 0
+
+
 @dataclasses.dataclass
 class MlpCtx:
-    """Saved-for-backward state of grouped_mlp_fwd (opaque device buffer)."""
+    """Saved-for-backward state of grouped_mlp_fwd (opaque device buffer).
+    ``save_h``: written in the save-h mode (h stored as bf16) rather than the
+    default recompute mode."""
     buf: torch.Tensor
     M: int
     H: int
     F: int
     E: int
     offsets: Optional[torch.Tensor] = None
+    save_h: bool = False
 
     @property
     def padded_rows(self) -> int:
         return padded_rows_bound(self.M, self.E)
 
     def _off(self, which):
-        off = int(lib().grouped_mlp_ctx_offset(which, self.M, self.H, self.F, self.E))
+        off = int(lib().grouped_mlp_ctx_offset(which, self.M, self.H, self.F, self.E,
+                                               _flags(self.save_h)))
         if off < 0:
             raise MxError("grouped_mlp_ctx_offset", 1, last_error())
         return off
 
     def h(self) -> torch.Tensor:
-        """Saved gate-up pre-activation as bf16 [M, 2F], gathered from the
-        library's 16 x 16 blocked layout (see MX_CTX_H in include/mxmoe.h)."""
+        """Saved gate-up pre-activation as bf16 [M, 2F] (save-h mode only),
+        gathered from the library's 16 x 16 blocked layout (see MX_CTX_H in
+        include/mxmoe.h)."""
         Mp, F = self.padded_rows, self.F
         raw = _region(self.buf, self._off(MX_CTX_H), (Mp // 16, F // 16, 4, 16, 2, 4),
                       torch.bfloat16)[0]
@@ -305,6 +319,19 @@ class MlpCtx:
                 for e in range(self.E)]
         idx = torch.cat(rows).to(hp.device) if rows else torch.zeros(0, dtype=torch.int64)
         return hp.index_select(0, idx)
+
+    def xrow(self) -> MxTensor:
+        """Rowwise MXFP8 copy of X kept for the recompute (default mode):
+        codes [M, H], scales [M, H/32]."""
+        return self._mx(MX_CTX_XROW, (self.M, self.H))
+
+    def w1row(self) -> MxTensor:
+        """Rowwise MXFP8 copy of W1: codes [E*2F, H], scales [E*2F, H/32]."""
+        return self._mx(MX_CTX_W1ROW, (self.E * 2 * self.F, self.H))
+
+    def w2row(self) -> MxTensor:
+        """Rowwise MXFP8 copy of W2: codes [E*H, F], scales [E*H, F/32]."""
+        return self._mx(MX_CTX_W2ROW, (self.E * self.H, self.F))
 
     def xcol(self) -> MxTensor:
         """Token-axis MXFP8 copy of X: codes [H, Mp], scales [H, Mp/32]
@@ -349,30 +376,37 @@ def _mlp_check(x, offsets, w1, w2, r):
     return dev, M, H, F, E
 
 
-def fwd_ws_bytes(M, H, F, E) -> int:
-    return int(lib().grouped_mlp_fwd_ws_bytes(M, H, F, E))
+def ctx_bytes(M, H, F, E, save_h: bool = False) -> int:
+    return int(lib().grouped_mlp_ctx_bytes(M, H, F, E, _flags(save_h)))
 
 
-def bwd_ws_bytes(M, H, F, E) -> int:
-    return int(lib().grouped_mlp_bwd_ws_bytes(M, H, F, E))
+def fwd_ws_bytes(M, H, F, E, save_h: bool = False) -> int:
+    return int(lib().grouped_mlp_fwd_ws_bytes(M, H, F, E, _flags(save_h)))
+
+
+def bwd_ws_bytes(M, H, F, E, save_h: bool = False) -> int:
+    return int(lib().grouped_mlp_bwd_ws_bytes(M, H, F, E, _flags(save_h)))
 
 
 def grouped_mlp_fwd(x, offsets, w1, w2, r, ws: Optional[torch.Tensor] = None,
-                    ctx_buf: Optional[torch.Tensor] = None, reuse_weights: bool = False):
+                    ctx_buf: Optional[torch.Tensor] = None, reuse_weights: bool = False,
+                    save_h: bool = False):
     """Fused GroupedMLP forward.  Returns (y bf16 [M, H], MlpCtx).  ``ws`` and
     ``ctx_buf`` are optional caller-owned uint8 buffers (allocated when
     missing or too small).  ``reuse_weights``: use the MXFP8 weight copies an
-    earlier call with the same weights left in ``ws`` and ``ctx_buf`` (both
-    must then be given) instead of quantizing w1 and w2 again."""
+    earlier call with the same weights (and the same ``save_h``) left in
+    ``ctx_buf`` (which must then be given) instead of quantizing w1 and w2
+    again.  ``save_h``: store h as bf16 for the backward instead of having the
+    backward recompute it."""
     dev, M, H, F, E = _mlp_check(x, offsets, w1, w2, r)
     L = lib()
-    nctx = L.grouped_mlp_ctx_bytes(M, H, F, E)
-    nws = L.grouped_mlp_fwd_ws_bytes(M, H, F, E)
+    fl = _flags(save_h)
+    nctx = L.grouped_mlp_ctx_bytes(M, H, F, E, fl)
+    nws = L.grouped_mlp_fwd_ws_bytes(M, H, F, E, fl)
     if nctx == 0 or nws == 0:
         raise MxError("grouped_mlp_fwd", 2, last_error())
-    if reuse_weights and (ws is None or ctx_buf is None or ws.numel() < nws
-                          or ctx_buf.numel() < nctx):
-        raise ValueError("reuse_weights needs the ws and ctx_buf of the earlier call")
+    if reuse_weights and (ctx_buf is None or ctx_buf.numel() < nctx):
+        raise ValueError("reuse_weights needs the ctx_buf of the earlier call")
     ctx = ctx_buf if ctx_buf is not None and ctx_buf.numel() >= nctx else \
         torch.empty(nctx, dtype=torch.uint8, device=dev)
     if ws is None or ws.numel() < nws:
@@ -380,27 +414,29 @@ def grouped_mlp_fwd(x, offsets, w1, w2, r, ws: Optional[torch.Tensor] = None,
     y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     st = L.grouped_mlp_fwd_ex(_ptr(x), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
                               _ptr(y), _ptr(ctx), ctx.numel(), _ptr(ws), ws.numel(),
-                              1 if reuse_weights else 0, _stream(dev))
+                              fl | (MX_FWD_REUSE_WEIGHTS if reuse_weights else 0), _stream(dev))
     _check("grouped_mlp_fwd", st)
-    return y, MlpCtx(ctx, M, H, F, E, offsets)
+    return y, MlpCtx(ctx, M, H, F, E, offsets, save_h)
 
 
 def grouped_mlp_bwd(dy, offsets, w1, w2, r, ctx: MlpCtx, ws: Optional[torch.Tensor] = None):
-    """Fused GroupedMLP backward.  Returns (dx, dw1, dw2, dr)."""
+    """Fused GroupedMLP backward (in the mode the forward wrote ``ctx`` in).
+    Returns (dx, dw1, dw2, dr)."""
     dev, M, H, F, E = _mlp_check(dy, offsets, w1, w2, r)
     if (ctx.M, ctx.H, ctx.F, ctx.E) != (M, H, F, E):
         raise ValueError("ctx was made for other sizes")
     L = lib()
-    nws = L.grouped_mlp_bwd_ws_bytes(M, H, F, E)
+    fl = _flags(ctx.save_h)
+    nws = L.grouped_mlp_bwd_ws_bytes(M, H, F, E, fl)
     if ws is None or ws.numel() < nws:
         ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     dx = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     dw1 = torch.empty((E, 2 * F, H), dtype=torch.bfloat16, device=dev)
     dw2 = torch.empty((E, H, F), dtype=torch.bfloat16, device=dev)
     dr = torch.empty((M,), dtype=torch.float32, device=dev)
-    st = L.grouped_mlp_bwd(_ptr(dy), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
-                           _ptr(ctx.buf), ctx.buf.numel(), _ptr(dx), _ptr(dw1), _ptr(dw2),
-                           _ptr(dr), _ptr(ws), ws.numel(), _stream(dev))
+    st = L.grouped_mlp_bwd_ex(_ptr(dy), _ptr(offsets), E, M, H, F, _ptr(w1), _ptr(w2), _ptr(r),
+                              _ptr(ctx.buf), ctx.buf.numel(), _ptr(dx), _ptr(dw1), _ptr(dw2),
+                              _ptr(dr), _ptr(ws), ws.numel(), fl, _stream(dev))
     _check("grouped_mlp_bwd", st)
     return dx, dw1, dw2, dr
 
@@ -425,12 +461,13 @@ def _tiled_mx_view(buf: torch.Tensor, off: int, shape) -> MxTensor:
     return MxTensor(codes, scales)
 
 
-def ws_mx_view(ws: torch.Tensor, which: int, M, H, F, E, shape) -> MxTensor:
+def ws_mx_view(ws: torch.Tensor, which: int, M, H, F, E, shape,
+               save_h: bool = False) -> MxTensor:
     """MXFP8 tensor inside a forward/backward workspace: codes of ``shape``
     [R, Kp] at the documented offset, scales at the next 256-byte boundary in
     the K-step tiled layout, returned row-major [R, Kp/32] (see
     include/mxmoe.h)."""
-    off = int(lib().grouped_mlp_ws_offset(which, M, H, F, E))
+    off = int(lib().grouped_mlp_ws_offset(which, M, H, F, E, _flags(save_h)))
     if off < 0:
         raise MxError("grouped_mlp_ws_offset", 1, last_error())
     return _tiled_mx_view(ws, off, shape)
@@ -553,5 +590,5 @@ def combine_bwd(dout: torch.Tensor, row_of: torch.Tensor, M: int,
 __all__ = ["lib", "last_error", "MxError", "MxTensor", "MlpCtx", "mxfp8_quantize",
            "grouped_linear_fwd", "fp8_tensor_quantize", "grouped_linear_fwd_fp8", "Fp8Tensor",
            "grouped_mlp_fwd", "grouped_mlp_bwd", "padded_rows_bound",
-           "ws_mx_view", "fwd_ws_bytes", "bwd_ws_bytes", "router", "route_plan", "permute_quantize",
+           "ws_mx_view", "ctx_bytes", "fwd_ws_bytes", "bwd_ws_bytes", "router", "route_plan", "permute_quantize",
            "combine", "combine_bwd"]

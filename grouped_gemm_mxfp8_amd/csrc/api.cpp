@@ -104,20 +104,38 @@ struct MlpDims {
     int64_t M, H, F, E, Mp;
 };
 
+// Saved-for-backward mode: recompute (default) keeps the X rowwise copy and
+// recomputes h = X W1^T in the backward; save-h (MX_MLP_SAVE_H) stores h as
+// bf16 in the forward and reads it back.
+bool save_h_mode(uint32_t flags) { return (flags & MX_MLP_SAVE_H) != 0; }
+
 struct CtxLayout {
-    size_t h, xcol, xcol_s, zcol, zcol_s, poff, w1c, w1c_s, w2c, w2c_s, total;
+    size_t w1c, w1c_s, w2c, w2c_s, w1r, w1r_s, w2r, w2r_s;   // weight copies
+    size_t h;                                                // save-h only
+    size_t xr, xr_s;                                         // recompute only
+    size_t xcol, xcol_s, zcol, zcol_s, poff, total;
 };
-CtxLayout ctx_layout(const MlpDims& d) {
+CtxLayout ctx_layout(const MlpDims& d, uint32_t flags) {
     Carver c;
-    CtxLayout L;
-    // columnwise weight copies made by the forward's weight pass, for the
-    // data-gradient GEMMs of the backward; first, so that their offsets do
-    // not depend on M (a forward that reuses them may have another M)
+    CtxLayout L{};
+    // the four weight copies made by the forward's weight pass come first,
+    // so that their offsets do not depend on M (a forward that reuses them
+    // may have another M): rowwise for the forward GEMMs and the backward's
+    // recompute, columnwise for the backward's data gradients
     L.w1c = c.take((size_t)d.E * d.H * 2 * d.F);
     L.w1c_s = c.take((size_t)d.E * d.H * 2 * d.F / 32);
     L.w2c = c.take((size_t)d.E * d.F * d.H);
     L.w2c_s = c.take((size_t)d.E * d.F * d.H / 32);
-    L.h = c.take((size_t)d.Mp * d.F * 4);     // blocked [Mp/16][F/16] x 1 KiB
+    L.w1r = c.take((size_t)d.E * 2 * d.F * d.H);
+    L.w1r_s = c.take((size_t)d.E * 2 * d.F * d.H / 32);
+    L.w2r = c.take((size_t)d.E * d.H * d.F);
+    L.w2r_s = c.take((size_t)d.E * d.H * d.F / 32);
+    if (save_h_mode(flags)) {
+        L.h = c.take((size_t)d.Mp * d.F * 4);     // blocked [Mp/16][F/16] x 1 KiB
+    } else {
+        L.xr = c.take((size_t)d.M * d.H);
+        L.xr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
+    }
     L.xcol = c.take((size_t)d.H * d.Mp);
     L.xcol_s = c.take((size_t)d.H * d.Mp / 32);
     L.zcol = c.take((size_t)d.F * d.Mp);
@@ -128,18 +146,15 @@ CtxLayout ctx_layout(const MlpDims& d) {
 }
 
 struct FwdWs {
-    size_t xr, xr_s, w1r, w1r_s, w2r, w2r_s, zr, zr_s, split, total;
+    size_t xr, xr_s, zr, zr_s, split, total;
 };
-FwdWs fwd_ws_layout(const MlpDims& d) {
+FwdWs fwd_ws_layout(const MlpDims& d, uint32_t flags) {
     Carver c;
-    FwdWs L;
-    // rowwise weight copies first (offsets independent of M, see ctx_layout)
-    L.w1r = c.take((size_t)d.E * 2 * d.F * d.H);
-    L.w1r_s = c.take((size_t)d.E * 2 * d.F * d.H / 32);
-    L.w2r = c.take((size_t)d.E * d.H * d.F);
-    L.w2r_s = c.take((size_t)d.E * d.H * d.F / 32);
-    L.xr = c.take((size_t)d.M * d.H);
-    L.xr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
+    FwdWs L{};
+    if (save_h_mode(flags)) {     // the recompute mode keeps this copy in ctx
+        L.xr = c.take((size_t)d.M * d.H);
+        L.xr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.H));
+    }
     L.zr = c.take((size_t)d.M * d.F);
     L.zr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, d.F));
     L.split = c.take(mx::kSplitWsBytes);      // tail split of the down GEMM
@@ -147,12 +162,17 @@ FwdWs fwd_ws_layout(const MlpDims& d) {
     return L;
 }
 
-int64_t dr_parts(int64_t F) { return (F + 255) / 256 * 2; }
+// dr partial sums per row: one per 128 columns of F handled by one wave
+// (save-h: waves of 128 columns in 256-column tiles; recompute: waves of 64
+// columns in 128-column tiles)
+int64_t dr_parts(int64_t F, uint32_t flags) {
+    return save_h_mode(flags) ? (F + 255) / 256 * 2 : F / 128 * 2;
+}
 
 struct BwdWs {
     size_t dyr, dyr_s, dycol, dycol_s, dhr, dhr_s, dhc, dhc_s, drp, split, total;
 };
-BwdWs bwd_ws_layout(const MlpDims& d) {
+BwdWs bwd_ws_layout(const MlpDims& d, uint32_t flags) {
     Carver c;
     BwdWs L;
     L.dyr = c.take((size_t)d.M * d.H);
@@ -163,7 +183,7 @@ BwdWs bwd_ws_layout(const MlpDims& d) {
     L.dhr_s = c.take((size_t)mx::tiled_scale_bytes(d.M, 2 * d.F));
     L.dhc = c.take((size_t)2 * d.F * d.Mp);
     L.dhc_s = c.take((size_t)2 * d.F * d.Mp / 32);
-    L.drp = c.take((size_t)d.M * dr_parts(d.F) * 4);
+    L.drp = c.take((size_t)d.M * dr_parts(d.F, flags) * 4);
     L.split = c.take(mx::kSplitWsBytes);      // tail split of the gate-up dgrad
     L.total = c.off;
     return L;
@@ -193,6 +213,7 @@ const char* epi_name(mx::Epi e) {
         case mx::Epi::kStoreBf16: return "mx_gemm<store_bf16>";
         case mx::Epi::kSwiglu: return "mx_gemm<swiglu_quant>";
         case mx::Epi::kDSwiglu: return "mx_gemm<dswiglu_quant>";
+        case mx::Epi::kDSwigluR: return "mx_gemm<dswiglu_recompute>";
     }
     return "mx_gemm";
 }
@@ -440,46 +461,68 @@ mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
     return launched(gemm(p, mx::Epi::kStoreBf16, 2.0 * M * N * K, s), "mx_gemm");
 }
 
-size_t grouped_mlp_ctx_bytes(int64_t M, int64_t H, int64_t F, int32_t E) {
+constexpr uint32_t kFwdFlags = MX_FWD_REUSE_WEIGHTS | MX_MLP_SAVE_H;
+
+size_t grouped_mlp_ctx_bytes(int64_t M, int64_t H, int64_t F, int32_t E, uint32_t flags) {
     MlpDims d;
-    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
-    return ctx_layout(d).total;
+    if ((flags & ~(uint32_t)MX_MLP_SAVE_H) || check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
+    return ctx_layout(d, flags).total;
 }
-size_t grouped_mlp_fwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E) {
+size_t grouped_mlp_fwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E, uint32_t flags) {
     MlpDims d;
-    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
-    return fwd_ws_layout(d).total;
+    if ((flags & ~(uint32_t)MX_MLP_SAVE_H) || check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
+    return fwd_ws_layout(d, flags).total;
 }
-size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E) {
+size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E, uint32_t flags) {
     MlpDims d;
-    if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
-    return bwd_ws_layout(d).total;
+    if ((flags & ~(uint32_t)MX_MLP_SAVE_H) || check_mlp_dims(M, H, F, E, &d) != MX_OK) return 0;
+    return bwd_ws_layout(d, flags).total;
 }
 
-int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F, int32_t E) {
+int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F, int32_t E,
+                               uint32_t flags) {
     MlpDims d;
+    if (flags & ~(uint32_t)MX_MLP_SAVE_H) {
+        fail(MX_ERR_INVALID_ARG, "grouped_mlp_ctx_offset: unknown flags 0x%x", flags);
+        return -1;
+    }
     if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return -1;
-    const CtxLayout L = ctx_layout(d);
+    const bool sh = save_h_mode(flags);
+    const CtxLayout L = ctx_layout(d, flags);
     switch (which) {
-        case MX_CTX_H: return (int64_t)L.h;
+        case MX_CTX_H: if (sh) return (int64_t)L.h; break;
+        case MX_CTX_XROW: if (!sh) return (int64_t)L.xr; break;
         case MX_CTX_XCOL: return (int64_t)L.xcol;
         case MX_CTX_ZCOL: return (int64_t)L.zcol;
         case MX_CTX_POFF: return (int64_t)L.poff;
         case MX_CTX_W1COL: return (int64_t)L.w1c;
         case MX_CTX_W2COL: return (int64_t)L.w2c;
-        default: return -1;
+        case MX_CTX_W1ROW: return (int64_t)L.w1r;
+        case MX_CTX_W2ROW: return (int64_t)L.w2r;
+        default: break;
     }
+    fail(MX_ERR_INVALID_ARG, "grouped_mlp_ctx_offset: region %d not in a ctx of this mode", which);
+    return -1;
 }
 
-int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F, int32_t E) {
+int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F, int32_t E,
+                              uint32_t flags) {
     MlpDims d;
+    if (flags & ~(uint32_t)MX_MLP_SAVE_H) {
+        fail(MX_ERR_INVALID_ARG, "grouped_mlp_ws_offset: unknown flags 0x%x", flags);
+        return -1;
+    }
     if (check_mlp_dims(M, H, F, E, &d) != MX_OK) return -1;
     switch (which) {
-        case MX_WS_ZROW: return (int64_t)fwd_ws_layout(d).zr;
-        case MX_WS_DHROW: return (int64_t)bwd_ws_layout(d).dhr;
-        case MX_WS_DHCOL: return (int64_t)bwd_ws_layout(d).dhc;
-        default: return -1;
+        case MX_WS_ZROW: return (int64_t)fwd_ws_layout(d, flags).zr;
+        case MX_WS_DHROW: return (int64_t)bwd_ws_layout(d, flags).dhr;
+        case MX_WS_DHCOL: return (int64_t)bwd_ws_layout(d, flags).dhc;
+        case MX_WS_DYROW: return (int64_t)bwd_ws_layout(d, flags).dyr;
+        case MX_WS_DYCOL: return (int64_t)bwd_ws_layout(d, flags).dycol;
+        default: break;
     }
+    fail(MX_ERR_INVALID_ARG, "grouped_mlp_ws_offset: unknown region %d", which);
+    return -1;
 }
 
 mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E, int64_t M,
@@ -496,15 +539,16 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
                              size_t ws_bytes, uint32_t flags, mx_stream_t stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool reuse = (flags & MX_FWD_REUSE_WEIGHTS) != 0;
-    if (flags & ~(uint32_t)MX_FWD_REUSE_WEIGHTS)
+    const bool sh = save_h_mode(flags);
+    if (flags & ~kFwdFlags)
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_fwd: unknown flags 0x%x", flags);
     if (!x || !d_offsets || (!reuse && (!w1 || !w2)) || !d_r || !y || !ctx || !ws)
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_fwd: NULL argument");
     MlpDims d;
     mx_status st = check_mlp_dims(M, H, F, E, &d);
     if (st != MX_OK) return st;
-    const CtxLayout C = ctx_layout(d);
-    const FwdWs W = fwd_ws_layout(d);
+    const CtxLayout C = ctx_layout(d, flags);
+    const FwdWs W = fwd_ws_layout(d, flags);
     if (ctx_bytes < C.total)
         return fail(MX_ERR_WORKSPACE, "grouped_mlp_fwd: ctx needs %zu bytes, got %zu", C.total,
                     ctx_bytes);
@@ -515,10 +559,13 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
         !aligned(ws, kAlign))
         return fail(MX_ERR_INVALID_ARG,
                     "grouped_mlp_fwd: tensors must be 16-byte and ctx/ws 256-byte aligned");
-    // with reuse the weight copies in ws and ctx are the previous call's
+    // with reuse the weight copies in ctx are the previous call's
     uint8_t* cb = static_cast<uint8_t*>(ctx);
     uint8_t* wb = static_cast<uint8_t*>(ws);
     int64_t* poff = reinterpret_cast<int64_t*>(cb + C.poff);
+    // rowwise X: in ctx for the recompute backward, else forward scratch
+    uint8_t* xr = sh ? wb + W.xr : cb + C.xr;
+    uint8_t* xr_s = sh ? wb + W.xr_s : cb + C.xr_s;
     const int64_t M2 = 2 * F;
     hipError_t e;
 
@@ -529,46 +576,47 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
     if (M > 0) {
         e = timed("quant_tiles", quant_bytes(M, H, true, true), MX_WORK_BYTES, s, [&] {
             return mx::launch_quant_tiles(static_cast<const uint16_t*>(x), 1, M, H, d_offsets,
-                                          poff, E, d.Mp, wb + W.xr, wb + W.xr_s, cb + C.xcol,
+                                          poff, E, d.Mp, xr, xr_s, cb + C.xcol,
                                           cb + C.xcol_s, d.Mp, true, s);
         });
         if (e != hipSuccess) return launched(e, "quant_tiles(x)");
     }
     // (2) weights, one pass each: rowwise copies for the forward GEMMs (W1
     // blocks along H, W2 along F) and the columnwise copies the backward's
-    // data gradients use (W1 blocks along 2F, W2 along H), saved in ctx.
+    // data gradients use (W1 blocks along 2F, W2 along H), all kept in ctx.
     // Skipped when the caller reuses the copies of an earlier call.
     if (!reuse) {
         e = timed("quant_tiles", quant_bytes((int64_t)E * M2, H, true, true), MX_WORK_BYTES, s,
                   [&] {
                       return mx::launch_quant_tiles(static_cast<const uint16_t*>(w1), E, M2, H,
-                                                    nullptr, nullptr, 1, 0, wb + W.w1r,
-                                                    wb + W.w1r_s, cb + C.w1c, cb + C.w1c_s, M2,
+                                                    nullptr, nullptr, 1, 0, cb + C.w1r,
+                                                    cb + C.w1r_s, cb + C.w1c, cb + C.w1c_s, M2,
                                                     true, s);
                   });
         if (e != hipSuccess) return launched(e, "quant_tiles(w1)");
         e = timed("quant_tiles", quant_bytes((int64_t)E * H, F, true, true), MX_WORK_BYTES, s,
                   [&] {
                       return mx::launch_quant_tiles(static_cast<const uint16_t*>(w2), E, H, F,
-                                                    nullptr, nullptr, 1, 0, wb + W.w2r,
-                                                    wb + W.w2r_s, cb + C.w2c, cb + C.w2c_s, H,
+                                                    nullptr, nullptr, 1, 0, cb + C.w2r,
+                                                    cb + C.w2r_s, cb + C.w2c, cb + C.w2c_s, H,
                                                     true, s);
                   });
         if (e != hipSuccess) return launched(e, "quant_tiles(w2)");
     }
     if (M == 0) return ok();
 
-    // (3) gate-up GEMM with the SwiGLU / routing-scale / requantize epilogue
+    // (3) gate-up GEMM with the SwiGLU / routing-scale / requantize epilogue;
+    // h leaves the chip only in the save-h mode
     mx::GemmProblem p{};
     p.kgroup = false;
     p.offs = d_offsets;
     p.G = E;
     p.M = M; p.N = M2; p.K = H;
-    p.A = mx::MxOperand{wb + W.xr, wb + W.xr_s, H, 0, true};
-    p.B = mx::MxOperand{wb + W.w1r, wb + W.w1r_s, H, M2, true};
+    p.A = mx::MxOperand{xr, xr_s, H, 0, true};
+    p.B = mx::MxOperand{cb + C.w1r, cb + C.w1r_s, H, M2, true};
     p.rscale = d_r;
     p.F = F;
-    p.h = reinterpret_cast<uint16_t*>(cb + C.h);
+    p.h = sh ? reinterpret_cast<uint16_t*>(cb + C.h) : nullptr;
     p.qr = wb + W.zr; p.qrs = wb + W.zr_s; p.ldqr = F;
     p.qc = cb + C.zcol; p.qcs = cb + C.zcol_s; p.ldqc = d.Mp;
     p.qtiled = true;
@@ -583,7 +631,7 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
     q.G = E;
     q.M = M; q.N = H; q.K = F;
     q.A = mx::MxOperand{wb + W.zr, wb + W.zr_s, F, 0, true};
-    q.B = mx::MxOperand{wb + W.w2r, wb + W.w2r_s, F, H, true};
+    q.B = mx::MxOperand{cb + C.w2r, cb + C.w2r_s, F, H, true};
     q.C = y; q.ldc = H;
     q.split_ws = wb + W.split;
     return launched(gemm(q, mx::Epi::kStoreBf16, 2.0 * M * H * F, s), "mx_gemm(down)");
@@ -594,14 +642,26 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
                           const float* d_r, const void* ctx, size_t ctx_bytes, void* dx,
                           void* dw1, void* dw2, float* d_dr, void* ws, size_t ws_bytes,
                           mx_stream_t stream) {
+    return grouped_mlp_bwd_ex(dy, d_offsets, E, M, H, F, w1, w2, d_r, ctx, ctx_bytes, dx, dw1,
+                              dw2, d_dr, ws, ws_bytes, 0u, stream);
+}
+
+mx_status grouped_mlp_bwd_ex(const void* dy, const int64_t* d_offsets, int32_t E, int64_t M,
+                             int64_t H, int64_t F, const void* w1, const void* w2,
+                             const float* d_r, const void* ctx, size_t ctx_bytes, void* dx,
+                             void* dw1, void* dw2, float* d_dr, void* ws, size_t ws_bytes,
+                             uint32_t flags, mx_stream_t stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (flags & ~(uint32_t)MX_MLP_SAVE_H)
+        return fail(MX_ERR_INVALID_ARG, "grouped_mlp_bwd: unknown flags 0x%x", flags);
+    const bool sh = save_h_mode(flags);
     if (!dy || !d_offsets || !w1 || !w2 || !d_r || !ctx || !dx || !dw1 || !dw2 || !d_dr || !ws)
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_bwd: NULL argument");
     MlpDims d;
     mx_status st = check_mlp_dims(M, H, F, E, &d);
     if (st != MX_OK) return st;
-    const CtxLayout C = ctx_layout(d);
-    const BwdWs W = bwd_ws_layout(d);
+    const CtxLayout C = ctx_layout(d, flags);
+    const BwdWs W = bwd_ws_layout(d, flags);
     if (ctx_bytes < C.total)
         return fail(MX_ERR_WORKSPACE, "grouped_mlp_bwd: ctx needs %zu bytes, got %zu", C.total,
                     ctx_bytes);
@@ -616,7 +676,7 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
     uint8_t* wb = static_cast<uint8_t*>(ws);
     const int64_t* poff = reinterpret_cast<const int64_t*>(cb + C.poff);
     const int64_t M2 = 2 * F;
-    const int64_t nparts = dr_parts(F);
+    const int64_t nparts = dr_parts(F, flags);
     hipError_t e;
 
     // (1) dY: rowwise for the data gradient, token-axis for dW2
@@ -628,26 +688,39 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E, i
         });
         if (e != hipSuccess) return launched(e, "quant_tiles(dy)");
     }
-    // (2) the weights' columnwise copies were made by the forward (ctx)
+    // (2) the weights' copies were made by the forward (ctx)
 
     if (M > 0) {
-        // (3) dz = dY W2 with the SwiGLU-backward / dr / requantize epilogue
+        // (3) dz = dY W2 with the SwiGLU-backward / dr / requantize epilogue;
+        // the recompute mode also recomputes h = X W1^T in the same tile
         mx::GemmProblem p{};
         p.kgroup = false;
         p.offs = d_offsets;
         p.G = E;
-        p.M = M; p.N = F; p.K = H;
-        p.A = mx::MxOperand{wb + W.dyr, wb + W.dyr_s, H, 0, true};
-        p.B = mx::MxOperand{cb + C.w2c, cb + C.w2c_s, H, F, true};
+        p.M = M; p.K = H;
         p.rscale = d_r;
         p.F = F;
-        p.h = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(cb + C.h));
         p.qr = wb + W.dhr; p.qrs = wb + W.dhr_s; p.ldqr = M2;
         p.qc = wb + W.dhc; p.qcs = wb + W.dhc_s; p.ldqc = d.Mp;
         p.qtiled = true;
         p.poff = poff;
         p.drp = reinterpret_cast<float*>(wb + W.drp); p.lddrp = nparts;
-        e = gemm(p, mx::Epi::kDSwiglu, 2.0 * M * F * H, s);
+        const mx::MxOperand dyr{wb + W.dyr, wb + W.dyr_s, H, 0, true};
+        const mx::MxOperand w2c{cb + C.w2c, cb + C.w2c_s, H, F, true};
+        if (sh) {
+            p.N = F;
+            p.A = dyr;
+            p.B = w2c;
+            p.h = const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(cb + C.h));
+            e = gemm(p, mx::Epi::kDSwiglu, 2.0 * M * F * H, s);
+        } else {
+            p.N = M2;
+            p.A = mx::MxOperand{cb + C.xr, cb + C.xr_s, H, 0, true};
+            p.B = mx::MxOperand{cb + C.w1r, cb + C.w1r_s, H, M2, true};
+            p.A2 = dyr;
+            p.B2 = w2c;
+            e = gemm(p, mx::Epi::kDSwigluR, 2.0 * M * F * H, s);
+        }
         if (e != hipSuccess) return launched(e, "mx_gemm(dgrad-down)");
         e = timed("dr_reduce", 4.0 * M * (nparts + 1), MX_WORK_BYTES, s, [&] {
             return mx::launch_dr_reduce(reinterpret_cast<const float*>(wb + W.drp), M, nparts,

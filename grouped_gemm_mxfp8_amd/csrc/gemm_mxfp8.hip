@@ -250,6 +250,7 @@ struct Slot {
     static constexpr int kSmem = 4 * kBytes > (int)sizeof(GemmSmem) ? 4 * kBytes
                                                                      : (int)sizeof(GemmSmem);
     static_assert(EPI != Epi::kSwiglu || QStage<64>::kBytes <= kBytes, "staging fits the slot");
+    static_assert(EPI != Epi::kDSwigluR || QStage<128>::kBytes <= kBytes, "staging fits the slot");
     static_assert(EPI != Epi::kStoreBf16 || 4 * 32768 <= kSmem, "output quadrants fit the stages");
     static_assert(kBytes % 16 == 0 && QStage<256>::kBytes % 16 == 0, "16-byte aligned regions");
 };
@@ -359,7 +360,7 @@ __device__ __forceinline__ void flush_rows(const uint8_t* st, const QDest& d, in
         }
     }
     // scales: C/32 bytes per row; a split row is two runs of C/64 bytes
-    constexpr int kRun = C >= 128 ? 4 : C / 32;
+    constexpr int kRun = C >= 256 ? 4 : 2;
     constexpr int kRunsPerRow = (C / 32) / kRun;
     static_assert(32 * kRunsPerRow <= 64, "one pass covers the slice's scale runs");
     const int srow = lane / kRunsPerRow, sblk = (lane % kRunsPerRow) * kRun;
@@ -434,8 +435,8 @@ __device__ __forceinline__ void flush_col_scales(const uint8_t* st, const QDest&
 // accumulator registers indexed by constants, and the empty asm in each
 // branch stops the compiler from turning the branches into selects (which
 // would read every candidate out of the accumulators at once).
-template <int J0>
-__device__ __forceinline__ void pick_unit(const v4f (&acc)[8][8], int ip, float (&u)[2][2][4]) {
+template <int J0, int NJ>
+__device__ __forceinline__ void pick_unit(const v4f (&acc)[8][NJ], int ip, float (&u)[2][2][4]) {
     static_for<4>([&](auto c) {
         constexpr int k = decltype(c)::value;
         if (ip == k) {
@@ -526,6 +527,202 @@ __device__ __forceinline__ float* split_part(uint8_t* ws, int item) {
     return reinterpret_cast<float*>(ws + kSplitHdrBytes) + (int64_t)item * (BM * BN);
 }
 
+// Sources of one GEMM of a tile: buffer descriptors of the A and B codes
+// (ranges end with the last valid row's K range, so rows past the valid
+// ones read as zeros whether or not the scalar K offset takes part in the
+// range check), each lane's offsets for the direct loads, and the scale
+// sources.
+struct TileSrc {
+    v4i ra, rb;
+    ScaleSrc sa, sb;
+    uint32_t aoff[8], boff[8];
+};
+
+// A: rows m0 .. m0 + mvalid - 1 of A.  B: tile row b is row brow0 + brow(b)
+// of B (bvalid rows from brow0 are valid).  The B tile has NJ * 32 rows.
+// Direct global->LDS loads move 64 lanes x 16 B = 8 tile rows into 1 KiB of
+// LDS per instruction, lane l landing at byte 16*l: lane l fetches row
+// (l >> 3) of the 8 and the logical chunk that the swizzle places at
+// physical chunk (l & 7).
+template <bool UNIT, int NJ, class BRow>
+__device__ __forceinline__ TileSrc tile_src(const MxOperand& A, const MxOperand& B, int64_t m0,
+                                            int64_t mvalid, int64_t brow0, int64_t bvalid,
+                                            int64_t klo, int64_t K, BRow brow, int wave, int lane) {
+    TileSrc o;
+    const int64_t lda = A.ld, ldb = B.ld;
+    o.ra = make_rsrc(A.codes + m0 * lda + klo, (mvalid - 1) * lda + K);
+    o.rb = make_rsrc(B.codes + brow0 * ldb + klo, (bvalid - 1) * ldb + K);
+    const int dma_row = lane >> 3;
+    const int dma_chunk = (lane & 7) ^ (dma_row & 7);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        o.aoff[j] = (uint32_t)(((wave * 8 + j) * 8 + dma_row) * lda + dma_chunk * 16);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+        o.boff[j] = (uint32_t)(brow((wave * NJ + j) * 8 + dma_row) * ldb + dma_chunk * 16);
+    o.sa = scale_src<UNIT>(A.scales, lda, A.tiled, m0, mvalid, wave * 64 + lane, klo, K);
+    o.sb = scale_src<UNIT>(B.scales, ldb, B.tiled, brow0, bvalid, brow(wave * 64 + lane), klo, K);
+    return o;
+}
+
+// Placement of one K step's loads (u < 8: A rows, u < 8 + NJ: B rows,
+// 8 + NJ: A scales, 9 + NJ: B scales) over the MFMA slots of the two passes
+// of a step: a_at(s) / b_at(s) give the load issued after pass-A / pass-B
+// slot s, or -1.  kNA loads go into pass A.
+template <int NJ> struct Sched;
+template <> struct Sched<8> {       // 256 x 256 tile: 18 loads, 64 MFMAs per wave
+    static constexpr int kLoads = 18, kNA = 12;
+    // 12 after slots 1, 4, 6 of every 8; 6 after slots 5, 9, ..., 25
+    static constexpr int a_at(int s) {
+        return s % 8 == 1 ? 3 * (s / 8) : s % 8 == 4 ? 3 * (s / 8) + 1
+                                        : s % 8 == 6 ? 3 * (s / 8) + 2 : -1;
+    }
+    static constexpr int b_at(int s) {
+        return (s >= 5 && s <= 25 && s % 4 == 1) ? 12 + (s - 5) / 4 : -1;
+    }
+};
+template <> struct Sched<4> {       // 256 x 128 tile: 14 loads, 32 MFMAs per wave
+    static constexpr int kLoads = 14, kNA = 9;
+    static constexpr int a_at(int s) {
+        return s == 0 ? 0 : s == 1 ? 1 : s == 3 ? 2 : s == 5 ? 3 : s == 7 ? 4 : s == 8 ? 5
+             : s == 10 ? 6 : s == 12 ? 7 : s == 14 ? 8 : -1;
+    }
+    static constexpr int b_at(int s) {
+        return s == 5 ? 9 : s == 7 ? 10 : s == 9 ? 11 : s == 10 ? 12 : s == 11 ? 13 : -1;
+    }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else static_assert(N < 0, "add the wait count");
+}
+
+// acc[8][NJ] += A-tile . B-tile^T over nk K steps of 128.  Wave (wm, wn)
+// owns rows wm*128 .. +128 of the 256-row tile and B rows wn*NJ*16 .. +NJ*16;
+// B is the MFMA's first operand, so acc[i][j] holds the transposed 16 x 16
+// block (lane (r16, q): row i*16 + r16, columns j*16 + 4q .. +3).
+//
+// Software pipeline over two LDS stages (stage k & 1 holds step k):
+//  * S1 (start of step k): every wave has step k's fragments in registers,
+//    so stage k is free; the loads of step k+2 go into it, kNA of them
+//    spread over pass A and the rest over pass B.
+//  * pass A: MFMA rows 0..3 over the NJ columns.
+//  * S2: vmcnt(kNA) -- this wave's loads of step k+1 have landed (only the
+//    pass-A loads of step k+2 may still be in flight) -- then a barrier,
+//    after which stage k+1 is complete for every wave.  The next step's A
+//    rows 0..3 are read into the registers pass A freed.
+//  * pass B: MFMA rows 4..7; after column j the next step's B fragment j is
+//    read, and in the last column each A row i is read as soon as its last
+//    MFMA has issued.
+// So the LDS reads overlap the MFMAs and use no extra registers, and each
+// load has about one and a half steps to land.  Every MFMA sits in its own
+// slot so that its execution hides the instructions issued after it.
+// Barriers fence LDS only (a workgroup fence would also wait for loads in
+// flight).  Output stores of an earlier tile may still be in flight: loads
+// complete in order among themselves, so the vmcnt waits stay sufficient
+// with older stores outstanding (they only make them stricter).  Steps at
+// or past nk use zero-range descriptors: they write zeros into a stage
+// nobody reads, so every step issues the same instructions and the vmcnt
+// counts hold without branches; the caller waits for those trailing loads
+// before it reuses the stages.
+template <int NJ>
+__device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const TileSrc& o,
+                                          int nk, int wave, int wm, int wn, int lane) {
+    using SC = Sched<NJ>;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int swz = r16 & 7;
+    auto dma_u = [&](auto uc, int st, int ks) {
+        constexpr int u = decltype(uc)::value;
+        const bool live = ks < nk;
+        const uint32_t k0 = (uint32_t)ks * BK;
+        if constexpr (u < 8) {
+            const v4i r = live ? o.ra : v4i{o.ra.x, o.ra.y, 0, o.ra.w};
+            dma_b128(r, uni(lds_addr(&sm.a[st][(wave * 8 + u) * 1024])), o.aoff[u], k0);
+        } else if constexpr (u < 8 + NJ) {
+            const v4i r = live ? o.rb : v4i{o.rb.x, o.rb.y, 0, o.rb.w};
+            dma_b128(r, uni(lds_addr(&sm.b[st][(wave * NJ + (u - 8)) * 1024])), o.boff[u - 8], k0);
+        } else if constexpr (u == 8 + NJ) {
+            const v4i rs = o.sa.rsrc;
+            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
+            dma_b32(r, uni(lds_addr(&sm.as[st][wave * 64])), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
+        } else {
+            const v4i rs = o.sb.rsrc;
+            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
+            dma_b32(r, uni(lds_addr(&sm.bs[st][wave * 64])), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
+        }
+    };
+
+    // Fragments of stage st into registers.  The scaled 16x16x128 MFMA reads
+    // a lane's 32 operand bytes as two 16-byte runs of K, [16q, 16q+16) and
+    // [64+16q, 64+16q+16), and the scale byte of lane (r, q) as that of K
+    // block q of row r (pinned on the device by per-block scale probes).
+    v8i af[8], bfr[NJ];
+    int asc[8], bsc[NJ];
+    auto read_a = [&](auto ic, int st) {
+        constexpr int i = decltype(ic)::value;
+        const int row = wm * 128 + i * 16 + r16;
+        const uint8_t* base = &sm.a[st][row * BK];
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        asc[i] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
+    };
+    auto read_b = [&](auto jc, int st) {
+        constexpr int j = decltype(jc)::value;
+        const int row = wn * (NJ * 16) + j * 16 + r16;
+        const uint8_t* base = &sm.b[st][row * BK];
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
+    };
+    auto mfma = [&](auto ic, auto jc) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
+    };
+
+    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 0, 0); });
+    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 1, 1); });
+    wait_vmcnt<SC::kLoads>();                           // step 0 (this wave)
+    lds_barrier();                                      // step 0 (every wave)
+    static_for<8>([&](auto ic) { read_a(ic, 0); });
+    static_for<NJ>([&](auto jc) { read_b(jc, 0); });
+    for (int ks = 0; ks < nk; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        lds_barrier();                                  // S1: stage cur is free
+        // pass A: slot s is column j = s / 4, row i = s % 4
+        static_for<4 * NJ>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{});
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int u = SC::a_at(s);
+            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_vmcnt<SC::kNA>();
+        lds_barrier();                                  // S2: stage nxt complete
+        // pass B: slot s is column j = s / 4, row i = 4 + s % 4
+        static_for<4 * NJ>([&](auto sc) {
+            constexpr int s = decltype(sc)::value, j = s / 4, i = 4 + s % 4;
+            mfma(std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (s < 4) read_a(std::integral_constant<int, s>{}, nxt);
+            if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, i>{}, nxt);
+            if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
+            constexpr int u = SC::b_at(s);
+            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+}
+
 // SPLIT (plain store, row-grouped only): the tail-split schedule below.
 template <Epi EPI, bool SPLIT = false>
 __global__ void __launch_bounds__(NTHREADS, 1)
@@ -542,9 +739,11 @@ mx_gemm_kernel(GemmProblem p) {
     const int G = p.G;
 
     // output columns per tile: the gate-up tile pairs 128 gate with 128 up
-    // rows of W1 and produces 128 columns of z
-    constexpr int TN_OUT = (EPI == Epi::kSwiglu) ? BN / 2 : BN;
-    const int64_t n_out = (EPI == Epi::kSwiglu) ? p.F : p.N;
+    // rows of W1 and produces 128 columns of z;
+    // columns of F per tile: the recompute backward pairs 128 gate, 128 up
+    // and 128 dz columns
+    constexpr int TN_OUT = (EPI == Epi::kSwiglu || EPI == Epi::kDSwigluR) ? BN / 2 : BN;
+    const int64_t n_out = (EPI == Epi::kSwiglu || EPI == Epi::kDSwigluR) ? p.F : p.N;
     const int ntn = (int)((n_out + TN_OUT - 1) / TN_OUT);
     const int mtn_k = (int)((p.M + BM - 1) / BM);     // k-grouped: M tiles
 
@@ -706,174 +905,55 @@ mx_gemm_kernel(GemmProblem p) {
         K = uni64(K);
         const int nk = (int)(K / BK);
 
-        // ---- operand descriptors for this tile ----
-        // Range of each descriptor: the last valid row's K range ends the
-        // buffer, so rows past the valid ones read as zeros whether or not the
-        // scalar (K) offset takes part in the range check.
-        const int64_t lda = p.A.ld, ldb = p.B.ld;
-        const v4i ra =
-            make_rsrc(p.A.codes + m0 * lda + klo, (mvalid - 1) * lda + K);
-        // B rows are addressed from brow0: the tile's first row, or for the
-        // gate-up tile the expert's first W1 row (gate and up halves are F
-        // rows apart)
-        const int64_t bg = p.kgroup ? 0 : (int64_t)g * p.B.gstride;
-        const int64_t brow0 = bg + ((EPI == Epi::kSwiglu) ? 0 : n0);
-        const int64_t bvalid = (EPI == Epi::kSwiglu) ? p.N : p.N - n0;
-        const v4i rb =
-            make_rsrc(p.B.codes + brow0 * ldb + klo, (bvalid - 1) * ldb + K);
-
-        // B row (relative to brow0) staged at tile row b
-        auto brow = [&](int b) -> int64_t {
-            if constexpr (EPI == Epi::kSwiglu) {
-                const int wnb = b >> 7, half = (b >> 6) & 1, c = b & 63;
-                return half * p.F + n0 + wnb * 64 + c;
-            } else {
-                return b;
-            }
+        // ---- main loop(s) ----
+        // The fused gate-up tile pairs 128 gate with 128 up rows of W1 (gate
+        // and up halves are F rows apart): B row b of the tile is W1 row
+        // half * F + n0 + (b >> 7) * 64 + (b & 63), half = (b >> 6) & 1, so
+        // wave wn's 128 B rows are the gate then the up rows of its 64 output
+        // columns.  Plain tiles read B rows n0 + b.
+        auto brow_gu = [&](int b) -> int64_t {
+            return ((b >> 6) & 1) * p.F + n0 + (b >> 7) * 64 + (b & 63);
         };
-        // Direct global->LDS loads: one instruction moves 64 lanes x 16 B =
-        // 8 tile rows into 1 KiB of LDS, lane l landing at byte 16*l.  Lane l
-        // therefore fetches row (l >> 3) of the 8 and the logical chunk that
-        // the swizzle places at physical chunk (l & 7).
-        const int dma_row = lane >> 3;
-        const int dma_chunk = (lane & 7) ^ (dma_row & 7);
-        uint32_t aoff[8], boff[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = (wave * 8 + j) * 8 + dma_row;
-            aoff[j] = (uint32_t)(r * lda + dma_chunk * 16);
-            boff[j] = (uint32_t)(brow(r) * ldb + dma_chunk * 16);
-        }
-        const ScaleSrc sa = scale_src<EPI == Epi::kStoreBf16>(p.A.scales, lda, p.A.tiled, m0, mvalid, wave * 64 + lane,
-                                      klo, K);
-        const ScaleSrc sb = scale_src<EPI == Epi::kStoreBf16>(p.B.scales, ldb, p.B.tiled, brow0, bvalid,
-                                      brow(wave * 64 + lane), klo, K);
-        const v4i ras = sa.rsrc, rbs = sb.rsrc;
-
+        auto brow_plain = [](int b) -> int64_t { return b; };
+        const int64_t bg = p.kgroup ? 0 : (int64_t)g * p.B.gstride;
+        constexpr bool kGU = EPI == Epi::kSwiglu || EPI == Epi::kDSwigluR;
         v4f acc[8][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-        // One K step's loads: 8 + 8 + 2 instructions per wave into stage st
-        // (u < 8: A rows, u < 16: B rows, 16: A scales, 17: B scales).  Steps
-        // at or past nk use zero-range descriptors: they write zeros into a
-        // stage nobody reads, so every step issues the same instructions and
-        // the vmcnt counts below hold without branches.
-        auto dma_u = [&](auto uc, int st, int ks) {
-            constexpr int u = decltype(uc)::value;
-            const bool live = ks < nk;
-            const uint32_t k0 = (uint32_t)ks * BK;
-            if constexpr (u < 8) {
-                const v4i r = live ? ra : v4i{ra.x, ra.y, 0, ra.w};
-                dma_b128(r, uni(lds_addr(&sm.a[st][(wave * 8 + u) * 1024])), aoff[u], k0);
-            } else if constexpr (u < 16) {
-                const v4i r = live ? rb : v4i{rb.x, rb.y, 0, rb.w};
-                dma_b128(r, uni(lds_addr(&sm.b[st][(wave * 8 + (u - 8)) * 1024])), boff[u - 8], k0);
-            } else if constexpr (u == 16) {
-                const v4i r = live ? ras : v4i{ras.x, ras.y, 0, ras.w};
-                dma_b32(r, uni(lds_addr(&sm.as[st][wave * 64])), sa.voff, sa.s0 + ks * sa.sstep);
-            } else {
-                const v4i r = live ? rbs : v4i{rbs.x, rbs.y, 0, rbs.w};
-                dma_b32(r, uni(lds_addr(&sm.bs[st][wave * 64])), sb.voff, sb.s0 + ks * sb.sstep);
-            }
-        };
-
-        // Fragments of stage st into registers.  The scaled 16x16x128 MFMA
-        // reads a lane's 32 operand bytes as two 16-byte runs of K, [16q,
-        // 16q+16) and [64+16q, 64+16q+16), and the scale byte of lane (r, q)
-        // as that of K block q of row r (pinned on the device by per-block
-        // scale probes).
-        v8i af[8], bfr[8];
-        int asc[8], bsc[8];
-        auto read_a = [&](auto ic, int st) {
-            constexpr int i = decltype(ic)::value;
-            const int row = wm * 128 + i * 16 + r16;
-            const uint8_t* base = &sm.a[st][row * BK];
-            const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-            const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
-            af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            asc[i] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
-        };
-        auto read_b = [&](auto jc, int st) {
-            constexpr int j = decltype(jc)::value;
-            const int row = wn * 128 + j * 16 + r16;
-            const uint8_t* base = &sm.b[st][row * BK];
-            const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-            const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
-            bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
-        };
-        auto mfma = [&](auto ic, auto jc) {
-            constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
-        };
-
-        // Software pipeline over two LDS stages (stage k & 1 holds step k):
-        //  * S1 (start of step k): every wave has step k's fragments in
-        //    registers, so stage k is free; the 18 loads of step k+2 go into
-        //    it, 12 spread over pass A and 6 over pass B.
-        //  * pass A: MFMA rows 0..3 over the 8 columns.
-        //  * S2: vmcnt(12) -- this wave's loads of step k+1 have landed (only
-        //    the 12 pass-A loads of step k+2 may still be in flight) -- then a
-        //    barrier, after which stage k+1 is complete for every wave.  The
-        //    next step's A rows 0..3 are read into the registers pass A freed.
-        //  * pass B: MFMA rows 4..7; after column j the next step's B
-        //    fragment j is read, and in the last column each A row i is read
-        //    as soon as its last MFMA has issued.
-        // So the LDS reads overlap the MFMAs and use no extra registers, and
-        // each load has about one and a half steps to land.  Barriers fence
-        // LDS only (a workgroup fence would also wait for loads in flight).
-        // The previous tile's output stores may still be in flight: loads
-        // complete in order among themselves, so the vmcnt waits below stay
-        // sufficient with older stores outstanding (they only make them
-        // stricter), and the stores drain under this tile's first steps.
-        static_for<18>([&](auto uc) { dma_u(uc, 0, 0); });
-        static_for<18>([&](auto uc) { dma_u(uc, 1, 1); });
-        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // step 0 (this wave)
-        lds_barrier();                                      // step 0 (every wave)
-        static_for<8>([&](auto ic) { read_a(ic, 0); });
-        static_for<8>([&](auto jc) { read_b(jc, 0); });
-        for (int ks = 0; ks < nk; ++ks) {
-            const int cur = ks & 1, nxt = cur ^ 1;
-            lds_barrier();                                  // S1: stage cur is free
-            // Pass A: one MFMA per slot (column j = s / 4, row i = s % 4), the
-            // 12 pass-A loads after slots 1, 4, 6 of every 8, so each
-            // MFMA's execution hides the instructions issued after it.
-            static_for<32>([&](auto sc) {
-                constexpr int s = decltype(sc)::value, r = s % 8, g = s / 8;
-                mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{});
-                __builtin_amdgcn_sched_barrier(0);
-                constexpr int u = r == 1 ? 3 * g : r == 4 ? 3 * g + 1 : r == 6 ? 3 * g + 2 : -1;
-                if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-            lds_barrier();                                  // S2: stage nxt complete
-            // Pass B: slots s (column j = s / 4, row i = 4 + s % 4); the next
-            // step's A rows 0..3 after slots 0..3, B column j after slot
-            // 4j+3, A row i (4..7) right after its last MFMA (slots 28..31),
-            // the 6 pass-B loads after slots 5, 9, 13, 17, 21, 25.
-            static_for<32>([&](auto sc) {
-                constexpr int s = decltype(sc)::value, j = s / 4, i = 4 + s % 4;
-                mfma(std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (s < 4) read_a(std::integral_constant<int, s>{}, nxt);
-                if constexpr (s >= 28) read_a(std::integral_constant<int, i>{}, nxt);
-                if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
-                if constexpr (s >= 5 && s <= 25 && s % 4 == 1)
-                    dma_u(std::integral_constant<int, 12 + (s - 5) / 4>{}, cur, ks + 2);
-                __builtin_amdgcn_sched_barrier(0);
-            });
+        if constexpr (kGU) {
+            const TileSrc o = tile_src<false, 8>(p.A, p.B, m0, mvalid, bg, 2 * p.F, klo, K,
+                                                 brow_gu, wave, lane);
+            tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane);
+        } else {
+            const TileSrc o = tile_src<EPI == Epi::kStoreBf16, 8>(p.A, p.B, m0, mvalid, bg + n0,
+                                                                  p.N - n0, klo, K, brow_plain,
+                                                                  wave, lane);
+            tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane);
         }
         // The fused epilogues stage their outputs in LDS, which overlaps every
         // wave's operand stages: wait until the trailing (zero-range) loads of
-        // all waves have landed.  The plain epilogue does not touch LDS.
+        // all waves have landed.  The plain epilogue waits in its own branch.
         if constexpr (EPI != Epi::kStoreBf16) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+        }
+        // Recompute backward: the second GEMM of the tile, dz = dY . W2 for
+        // the same rows and the tile's 128 columns of F (A2: dY rowwise, B2:
+        // W2 columnwise, K = H), while acc keeps the recomputed [a | b].
+        v4f dacc[8][4];
+        if constexpr (EPI == Epi::kDSwigluR) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            int lane2 = lane_id;
+            asm volatile("" : "+v"(lane2));
+            const TileSrc o = tile_src<false, 4>(p.A2, p.B2, m0, mvalid,
+                                                 (int64_t)g * p.B2.gstride + n0, p.F - n0, 0, K,
+                                                 brow_plain, wave, lane2);
+            tile_gemm<4>(dacc, sm, o, nk, wave, wm, wn, lane2);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         }
@@ -960,7 +1040,7 @@ mx_gemm_kernel(GemmProblem p) {
                                 gu[ii][jj][v] = rv ? gu[ii][jj][v] : 0.f;
                                 uu[ii][jj][v] = rv ? uu[ii][jj][v] : 0.f;
                             }
-                            if (rows_pad_w > 0) {
+                            if (p.h && rows_pad_w > 0) {
                                 const uint2 g2 = pack4_bf16(gu[ii][jj]), u2 = pack4_bf16(uu[ii][jj]);
                                 store_nt(h_block(p.h, prow + i * 16, cw + j * 16, F, lane),
                                          make_uint4(g2.x, g2.y, u2.x, u2.y));
@@ -980,7 +1060,7 @@ mx_gemm_kernel(GemmProblem p) {
                 lds_wait();
             }
             if (rows_pad_w > 0) flush_col_scales<64>(st, d, prow, lane);
-        } else {   // kDSwiglu
+        } else if constexpr (EPI == Epi::kDSwiglu) {
             const int64_t F = p.F;
             const int64_t glo = p.offs[g];
             const int64_t prow = p.poff[g] + (rwave - glo);
@@ -1098,6 +1178,77 @@ mx_gemm_kernel(GemmProblem p) {
                 lds_wait();
             }
             if (cw < F && rows_pad_w > 0) flush_col_scales<256>(st, d, prow, lane);
+        } else {   // kDSwigluR
+            // acc holds the recomputed [a | b] (acc[i][j], j < 4: gate; j + 4:
+            // up, same columns) and dacc the dz of the wave's 64 columns of F
+            // (cw .. cw + 63, all below F since F % 128 == 0).  dh = [da | db]
+            // leaves as rowwise codes (da at columns cw.., db at F + cw..) and
+            // token-axis codes; dr partial part = the wave's column block.
+            const int64_t F = p.F;
+            const int64_t glo = p.offs[g];
+            const int64_t prow = p.poff[g] + (rwave - glo);
+            const int64_t npad = p.poff[g + 1] - p.poff[g];
+            const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
+            const int64_t cw = n0 + wn * 64;
+            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true, p.qtiled};
+            uint8_t* st = smem + wave * Slot<EPI>::kBytes;
+            const int part = (int)(n0 / 128) * 2 + wn;
+#pragma nounroll
+            for (int ip = 0; ip < 4; ++ip) {
+                // lane-derived values re-derived per slice (see the forward)
+                int lane = lane_id;
+                asm volatile("" : "+v"(lane));
+                const int r16 = lane & 15, q = lane >> 4;
+                float rr[2], drs[2];
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const int rl = (2 * ip + ii) * 16 + r16;
+                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                    drs[ii] = 0.f;
+                }
+                static_for<2>([&](auto jpc) {
+                    constexpr int jp = decltype(jpc)::value;
+                    float ga[2][2][4], ua[2][2][4], dzu[2][2][4], da[2][2][4], db[2][2][4];
+                    pick_unit<2 * jp>(acc, ip, ga);
+                    pick_unit<2 * jp + 4>(acc, ip, ua);
+                    pick_unit<2 * jp>(dacc, ip, dzu);
+                    // Rows past the expert's valid rows are selected to 0 (a,
+                    // b and dz): rows past M read never-written scale bytes,
+                    // so their accumulators may be anything, NaN included,
+                    // and the padded rows take part in the token-axis blocks.
+#pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
+#pragma unroll
+                        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const float av = rv ? ga[ii][jj][v] : 0.f;
+                                const float bv = rv ? ua[ii][jj][v] : 0.f;
+                                const float dz = rv ? dzu[ii][jj][v] : 0.f;
+                                float sg;
+                                const float sl_ = silu_sig(av, sg);
+                                drs[ii] += dz * (sl_ * bv);
+                                const float ds = rr[ii] * dz;
+                                da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
+                                db[ii][jj][v] = ds * sl_;
+                            }
+                    }
+                    quant_unit<128>(da, 2 * jp * 16, ip, st, lane);
+                    quant_unit<128>(db, 64 + 2 * jp * 16, ip, st, lane);
+                });
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii) {
+                    const float sum = sum4q(drs[ii]);
+                    const int rl = (2 * ip + ii) * 16 + r16;
+                    if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                }
+                lds_wait();
+                flush_rows<128, false>(st, d, rwave, ip, rows_valid_w, lane);
+                if ((ip & 1) && rows_pad_w > 0) flush_cols<128, false>(st, d, prow + (ip >> 1) * 64, lane);
+                lds_wait();
+            }
+            if (rows_pad_w > 0) flush_col_scales<128>(st, d, prow, lane);
         }
         // the next tile's loads overwrite other waves' staging areas
         if constexpr (EPI != Epi::kStoreBf16) lds_barrier();
@@ -1170,6 +1321,9 @@ hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s) {
             break;
         case Epi::kDSwiglu:
             hipLaunchKernelGGL(mx_gemm_kernel<Epi::kDSwiglu>, dim3(grid), dim3(NTHREADS), 0, s, p);
+            break;
+        case Epi::kDSwigluR:
+            hipLaunchKernelGGL(mx_gemm_kernel<Epi::kDSwigluR>, dim3(grid), dim3(NTHREADS), 0, s, p);
             break;
     }
     return hipGetLastError();

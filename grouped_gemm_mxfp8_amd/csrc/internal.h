@@ -66,7 +66,9 @@ struct MxOperand {
 enum class Epi : int {
     kStoreBf16 = 0,   // C = acc (* row scale) -> bf16
     kSwiglu = 1,      // gate-up: h -> bf16, z = r silu(a) b -> MXFP8 row+col
-    kDSwiglu = 2,     // dz -> dr partials, dh = [da|db] -> MXFP8 row+col
+    kDSwiglu = 2,     // dz -> dr partials, dh = [da|db] -> MXFP8 row+col (h read)
+    kDSwigluR = 3,    // [a|b] = X W1^T recomputed, dz = dY W2 (A2, B2) in the
+                      //   same tile -> dr partials, dh -> MXFP8 row+col
 };
 
 struct GemmProblem {
@@ -83,16 +85,19 @@ struct GemmProblem {
     const float* rscale;        // kStoreBf16 and fused: per-row routing weight
     // fused epilogues
     int64_t F;
-    uint16_t* h;                // kSwiglu writes, kDSwiglu reads: bf16 [M][2F]
+    uint16_t* h;                // kSwiglu writes (if set), kDSwiglu reads: bf16 [M][2F]
     uint8_t* qr; uint8_t* qrs; int64_t ldqr;   // rowwise MXFP8 output
     uint8_t* qc; uint8_t* qcs; int64_t ldqc;   // columnwise MXFP8 output
     bool qtiled;                // fused outputs: K-step tiled scales
     const int64_t* poff;        // padded token offsets of the column copy
-    float* drp; int64_t lddrp;  // kDSwiglu: dr partials [M][lddrp]
+    float* drp; int64_t lddrp;  // kDSwiglu(R): dr partials [M][lddrp]
     const float* gsa;           // kStoreBf16: per-group factors of A and of B
     const float* gsb;           //   (scale_inv of per-tensor FP8), or nullptr
     uint8_t* split_ws;          // kStoreBf16, row-grouped: tail-split workspace
                                 //   of kSplitWsBytes, or nullptr (no split)
+    // kDSwigluR: operands of the tile's second GEMM, dz = A2 . B2^T (A2
+    // row-grouped like A, B2 of group g at rows g * B2.gstride; K = K)
+    MxOperand A2, B2;
 };
 
 // Tail split of the plain-store row-grouped GEMM.  When the last round of

@@ -20,9 +20,13 @@
  *     rounded to nearest even and saturate at +-448.
  *   - GroupedMLP: gate-up projection, SwiGLU scaled by the routing weight and
  *     the quantization fused into one forward and one backward pass whose
- *     intermediates are not materialised as separate tensors (German page, the
- *     paragraph on the third bottleneck; Portuguese page, third paragraph;
- *     French page, third improvement).
+ *     intermediates are not held in memory (German page, the paragraph on the
+ *     GroupedMLP fusion kernel; Portuguese page, third paragraph; French page,
+ *     third improvement): the gate-up pre-activation h and the SwiGLU output
+ *     stay on chip, only their requantized MXFP8 codes leave it, and the
+ *     backward recomputes h from the saved X codes.  An optional mode
+ *     (MX_MLP_SAVE_H) stores h as bf16 instead, trading 4 bytes per row and
+ *     column of F for the recompute.
  *
  * Conventions shared by every entry point
  *   - All pointers named d_* and every tensor pointer are DEVICE pointers on
@@ -174,13 +178,17 @@ mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
  *
  *   x    bf16 [M][H];  w1 bf16 [E][2F][H] (rows [0,F) gate, [F,2F) up);
  *   w2   bf16 [E][H][F];  d_r fp32 [M];  y bf16 [M][H].
- *   ctx  saved-for-backward buffer of grouped_mlp_ctx_bytes() bytes, written
- *        here and read by grouped_mlp_bwd (opaque; 256-byte aligned).
- *   ws   scratch of grouped_mlp_fwd_ws_bytes() bytes (256-byte aligned): the
- *        rowwise MXFP8 copies of x, w1, w2 and z, and 64 MiB (plus an 8 KiB
- *        header) for the fp32 partial tiles of the down GEMM's split tail
- *        round (the last round of output tiles, cut along K when it would
- *        leave more than half of the GPU idle).
+ *   ctx  saved-for-backward buffer of grouped_mlp_ctx_bytes(.., 0) bytes,
+ *        written here and read by grouped_mlp_bwd (opaque; 256-byte
+ *        aligned): the MXFP8 copies of w1 and w2 (rowwise and columnwise),
+ *        the rowwise and token-axis copies of x, the token-axis copy of z and
+ *        the padded token offsets.  h is not stored (the backward recomputes
+ *        it).
+ *   ws   scratch of grouped_mlp_fwd_ws_bytes(.., 0) bytes (256-byte aligned):
+ *        the rowwise MXFP8 copy of z, and 64 MiB (plus an 8 KiB header) for
+ *        the fp32 partial tiles of the down GEMM's split tail round (the last
+ *        round of output tiles, cut along K when it would leave more than
+ *        half of the GPU idle).
  * H % 128 == 0, F % 128 == 0, E in [1, 1024].
  */
 mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E,
@@ -194,18 +202,28 @@ mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E,
  * grouped_mlp_fwd).
  *
  * MX_FWD_REUSE_WEIGHTS: skip quantizing the weights and use the MXFP8 copies
- * that an earlier forward with the same w1, w2, E, H and F left in this ctx
- * (columnwise copies) and this ws (rowwise copies): the caching of weight
- * quantization across micro-batches that the 16-bit master weights allow
- * while they do not change (German page, the paragraph on quantization
- * between 16-bit master weights and the 8-bit path).  The weight regions sit
- * at the start of ctx and ws, so M may differ from that earlier call.  w1
- * and w2 are not read and may be NULL.  The caller guarantees that the
- * weights have not changed and that nothing else has written those regions
- * (grouped_mlp_bwd only reads them); with any other contents the results are
- * undefined, not an error.  Unknown flag bits: MX_ERR_INVALID_ARG.
+ * that an earlier forward with the same w1, w2, E, H, F and MX_MLP_SAVE_H
+ * setting left in this ctx: the caching of weight quantization across
+ * micro-batches that the 16-bit master weights allow while they do not
+ * change (German page, the paragraph on quantization between 16-bit master
+ * weights and the 8-bit path).  The weight regions sit at the start of ctx,
+ * so M may differ from that earlier call.  w1 and w2 are not read and may be
+ * NULL.  The caller guarantees that the weights have not changed and that
+ * nothing else has written those regions (grouped_mlp_bwd only reads them);
+ * with any other contents the results are undefined, not an error.
+ *
+ * MX_MLP_SAVE_H: the save-h mode.  The forward stores the gate-up
+ * pre-activation h as bf16 (RNE of the fp32 accumulator) in ctx and the
+ * backward reads it instead of recomputing it: the backward then runs one
+ * GEMM fewer over K = H per expert row block (2*M*2F*H fewer flops) for
+ * M*2F*2 more bytes of ctx.  The backward's SwiGLU gradient then sees
+ * bf16(h).  ctx and ws sizes, views and the backward must be given the same
+ * flag (grouped_mlp_bwd_ex).
+ *
+ * Unknown flag bits: MX_ERR_INVALID_ARG.
  */
 #define MX_FWD_REUSE_WEIGHTS 1u
+#define MX_MLP_SAVE_H 2u
 mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
                              int64_t M, int64_t H, int64_t F, const void* w1,
                              const void* w2, const float* d_r, void* y,
@@ -219,7 +237,9 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
  * along its own contraction axis: rowwise copies feed the data gradients,
  * columnwise (token-axis) copies the weight gradients.
  *   dz  = Q(dY_e) . Q(W2_e)          (blocks along H)
- *   dr  = sum_f dz * s,  s = silu(a) * b, (a, b) = h saved by the forward
+ *   h   = Q(X_e) . Q(W1_e)^T = [a | b], recomputed in the same kernel tile
+ *         as dz from the forward's saved codes (save-h mode: read from ctx)
+ *   dr  = sum_f dz * s,  s = silu(a) * b
  *   dh  = [r dz b silu'(a) | r dz silu(a)]
  *   dX  = Q(dh) . Q(W1_e)            (blocks along 2F)
  *   dW2_e = Q_tok(dY_e)^T . Q_tok(z_e),  dW1_e = Q_tok(dh_e)^T . Q_tok(X_e)
@@ -227,12 +247,17 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
  *
  *   dy bf16 [M][H]; outputs dx bf16 [M][H], dw1 bf16 [E][2F][H],
  *   dw2 bf16 [E][H][F], d_dr fp32 [M].  Same sizes, x-free: the forward's
- *   ctx holds what is needed, including the quantized columnwise copies of
- *   w1 and w2 made by the forward (w1 and w2 must be the tensors given to
- *   the forward that wrote ctx; the backward only checks them for NULL and
- *   alignment).  ws of grouped_mlp_bwd_ws_bytes() bytes: the MXFP8 copies of
- *   dY and dh, the dr partial sums, and the split-tail scratch of the gate-up
+ *   ctx holds what is needed, including the quantized copies of w1 and w2
+ *   made by the forward (w1 and w2 must be the tensors given to the forward
+ *   that wrote ctx; the backward only checks them for NULL and alignment).
+ *   ws of grouped_mlp_bwd_ws_bytes(.., flags) bytes: the MXFP8 copies of dY
+ *   and dh, the dr partial sums, and the split-tail scratch of the gate-up
  *   dgrad (as in the forward).
+ *
+ * grouped_mlp_bwd_ex -- grouped_mlp_bwd with flags: MX_MLP_SAVE_H for a ctx
+ *   written by a forward with that flag (0: same as grouped_mlp_bwd).  A
+ *   ctx read in the other mode than it was written gives undefined results.
+ *   Unknown flag bits: MX_ERR_INVALID_ARG.
  */
 mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E,
                           int64_t M, int64_t H, int64_t F, const void* w1,
@@ -240,47 +265,60 @@ mx_status grouped_mlp_bwd(const void* dy, const int64_t* d_offsets, int32_t E,
                           size_t ctx_bytes, void* dx, void* dw1, void* dw2,
                           float* d_dr, void* ws, size_t ws_bytes,
                           mx_stream_t stream);
+mx_status grouped_mlp_bwd_ex(const void* dy, const int64_t* d_offsets, int32_t E,
+                             int64_t M, int64_t H, int64_t F, const void* w1,
+                             const void* w2, const float* d_r, const void* ctx,
+                             size_t ctx_bytes, void* dx, void* dw1, void* dw2,
+                             float* d_dr, void* ws, size_t ws_bytes,
+                             uint32_t flags, mx_stream_t stream);
 
-/* Byte sizes of the buffers above (0 on bad arguments). */
-size_t grouped_mlp_ctx_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
-size_t grouped_mlp_fwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
-size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E);
+/* Byte sizes of the buffers above for the mode in flags (0 or
+ * MX_MLP_SAVE_H); 0 on bad arguments. */
+size_t grouped_mlp_ctx_bytes(int64_t M, int64_t H, int64_t F, int32_t E, uint32_t flags);
+size_t grouped_mlp_fwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E, uint32_t flags);
+size_t grouped_mlp_bwd_ws_bytes(int64_t M, int64_t H, int64_t F, int32_t E, uint32_t flags);
 
 /*
- * Views into a forward ctx, for inspection and tests (offsets in bytes from
- * the ctx base; all regions 256-byte aligned):
- *   MX_CTX_H        gate-up pre-activation h (bf16, RNE of fp32) in 16 x 16
+ * Views into a forward ctx of the mode in flags, for inspection and tests
+ * (offsets in bytes from the ctx base; all regions 256-byte aligned):
+ *   MX_CTX_H        (save-h mode only) gate-up pre-activation h (bf16, RNE of fp32) in 16 x 16
  *                   blocks: block (pr/16, c/16), pr = padded row (expert e's
  *                   row off[e]+t sits at padded row poff[e]+t), c in [0, F),
  *                   is 1 KiB at byte ((pr/16)*(F/16) + c/16)*1024; within it
  *                   lane l = 16*q + r holds 16 bytes: gate h[pr+r][c+4q+v] for
  *                   v = 0..3, then up h[pr+r][F+c+4q+v].  Mp*F*4 bytes.
+ *   MX_CTX_XROW     (recompute mode only) X rowwise codes [M][H] then scales
  *   MX_CTX_XCOL     X columnwise codes [H][Mp] then scales
  *   MX_CTX_ZCOL     z columnwise codes [F][Mp] then scales
  *   MX_CTX_POFF     int64 [E+1] padded token offsets
  *   MX_CTX_W1COL    W1 columnwise codes [E*H][2F] (blocks along 2F) + scales
  *   MX_CTX_W2COL    W2 columnwise codes [E*F][H] (blocks along H) + scales
+ *   MX_CTX_W1ROW    W1 rowwise codes [E*2F][H] (blocks along H) + scales
+ *   MX_CTX_W2ROW    W2 rowwise codes [E*H][F] (blocks along F) + scales
  * with Mp = mx_padded_rows_bound(M, E, 128).  In every codes-then-scales
  * pair here and below, the scales start at the first 256-byte boundary after
  * the last code byte, and (unlike the public entry points' row-major scales)
  * are K-step tiled: for codes [R][Kp], the scale of row r and block kb (codes
  * kb*32 .. kb*32+31) is byte ((r/32)*(Kp/128) + kb/4)*128 + (r%32)*4 + kb%4,
- * with R rounded up to a multiple of 32.  Returns -1 on bad arguments.
+ * with R rounded up to a multiple of 32.  Returns -1 on bad arguments and for
+ * a region the mode does not have.
  */
 enum { MX_CTX_H = 0, MX_CTX_XCOL = 1, MX_CTX_ZCOL = 2, MX_CTX_POFF = 3, MX_CTX_W1COL = 4,
-       MX_CTX_W2COL = 5 };
+       MX_CTX_W2COL = 5, MX_CTX_XROW = 6, MX_CTX_W1ROW = 7, MX_CTX_W2ROW = 8 };
 int64_t grouped_mlp_ctx_offset(int32_t which, int64_t M, int64_t H, int64_t F,
-                               int32_t E);
+                               int32_t E, uint32_t flags);
 
 /*
- * Views into the forward/backward workspaces, for tests: the rowwise z
- * (codes [M][F] + K-step tiled scales) the forward fed its down projection,
- * and the rowwise and columnwise dh of the backward (codes [M][2F] + scales;
- * columnwise codes [2F][Mp] + scales).  Returns -1 on bad arguments.
+ * Views into the forward/backward workspaces of the mode in flags, for tests:
+ * the rowwise z (codes [M][F] + K-step tiled scales) the forward fed its down
+ * projection; the backward's rowwise dY (codes [M][H] + scales) and
+ * token-axis dY (codes [H][Mp] + scales), and its rowwise and columnwise dh
+ * (codes [M][2F] + scales; columnwise codes [2F][Mp] + scales).  Returns -1
+ * on bad arguments.
  */
-enum { MX_WS_ZROW = 0, MX_WS_DHROW = 1, MX_WS_DHCOL = 2 };
+enum { MX_WS_ZROW = 0, MX_WS_DHROW = 1, MX_WS_DHCOL = 2, MX_WS_DYROW = 3, MX_WS_DYCOL = 4 };
 int64_t grouped_mlp_ws_offset(int32_t which, int64_t M, int64_t H, int64_t F,
-                              int32_t E);
+                              int32_t E, uint32_t flags);
 
 /*
  * Routing around the expert path: the sorted-row plan of a top-k routing,

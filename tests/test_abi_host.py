@@ -61,24 +61,46 @@ def test_padded_bound_dominates_every_split(mxlib):
         assert padded <= mxlib.mx_padded_rows_bound(M, G, 128)
 
 
+SAVE_H = 2
+
+
 def test_mlp_sizes(mxlib):
     M, H, F, E = 32768, 4096, 14336, 8
-    ctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
     Mp = mxlib.mx_padded_rows_bound(M, E, 128)
-    # h (bf16, 16x16 blocks over padded rows: Mp*F*4 bytes) + X and z token-axis
-    # copies + scales + padded offsets + the weights' columnwise copies + scales
-    need = Mp * F * 4 + (H + F) * Mp * (1 + 1 / 32) + E * (2 * F * H + F * H) * (1 + 1 / 32)
-    assert need <= ctx <= need + 64 * 256
-    assert mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E) > 0
-    assert mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E) > 0
-    for which in range(6):
-        off = mxlib.grouped_mlp_ctx_offset(which, M, H, F, E)
-        assert 0 <= off < ctx and off % 256 == 0
-    assert mxlib.grouped_mlp_ctx_offset(9, M, H, F, E) == -1
-    # unsupported sizes give 0 / -1
-    assert mxlib.grouped_mlp_ctx_bytes(M, 4000, F, E) == 0
-    assert mxlib.grouped_mlp_ctx_bytes(M, H, F, 0) == 0
-    assert mxlib.grouped_mlp_ctx_offset(0, M, H, 100, E) == -1
+    weights = E * (2 * F * H + F * H) * 2 * (1 + 1 / 32)       # rowwise + columnwise copies
+    tok = (H + F) * Mp * (1 + 1 / 32)                          # X and z token-axis copies
+    # recompute mode: X rowwise copy (the backward recomputes h from it)
+    ctx_r = mxlib.grouped_mlp_ctx_bytes(M, H, F, E, 0)
+    need_r = weights + tok + M * H * (1 + 1 / 32)
+    assert need_r <= ctx_r <= need_r + 64 * 256
+    # save-h mode: h (bf16, 16x16 blocks over padded rows: Mp*F*4 bytes)
+    ctx_s = mxlib.grouped_mlp_ctx_bytes(M, H, F, E, SAVE_H)
+    need_s = weights + tok + Mp * F * 4
+    assert need_s <= ctx_s <= need_s + 64 * 256
+    for fl in (0, SAVE_H):
+        assert mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E, fl) > 0
+        assert mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E, fl) > 0
+    # regions of each mode
+    both = (1, 2, 3, 4, 5, 7, 8)
+    for fl, own, other in ((0, 6, 0), (SAVE_H, 0, 6)):
+        ctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E, fl)
+        for which in both + (own,):
+            off = mxlib.grouped_mlp_ctx_offset(which, M, H, F, E, fl)
+            assert 0 <= off < ctx and off % 256 == 0
+        assert mxlib.grouped_mlp_ctx_offset(other, M, H, F, E, fl) == -1
+        assert "mode" in _err(mxlib)
+        assert mxlib.grouped_mlp_ctx_offset(9, M, H, F, E, fl) == -1
+        for which in range(5):
+            assert mxlib.grouped_mlp_ws_offset(which, M, H, F, E, fl) >= 0
+        assert mxlib.grouped_mlp_ws_offset(5, M, H, F, E, fl) == -1
+    # unsupported sizes and unknown flags give 0 / -1
+    assert mxlib.grouped_mlp_ctx_bytes(M, 4000, F, E, 0) == 0
+    assert mxlib.grouped_mlp_ctx_bytes(M, H, F, 0, 0) == 0
+    assert mxlib.grouped_mlp_ctx_bytes(M, H, F, E, 1) == 0
+    assert mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E, 4) == 0
+    assert mxlib.grouped_mlp_ctx_offset(1, M, H, 100, E, 0) == -1
+    assert mxlib.grouped_mlp_ctx_offset(1, M, H, F, E, 8) == -1
+    assert "flags" in _err(mxlib)
 
 
 def _err(mxlib):
@@ -137,9 +159,9 @@ def test_grouped_linear_rejects_bad_arguments(mxlib):
 def test_grouped_mlp_rejects_bad_arguments(mxlib):
     fwd, bwd = mxlib.grouped_mlp_fwd, mxlib.grouped_mlp_bwd
     M, H, F, E = 1024, 256, 256, 4
-    nctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
-    nws = mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E)
-    nbws = mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E)
+    nctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E, 0)
+    nws = mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E, 0)
+    nbws = mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E, 0)
     args = lambda **kw: [kw.get("x", FAKE), FAKE, kw.get("E", E), M, kw.get("H", H), F, FAKE,
                          FAKE, FAKE, FAKE, FAKE, kw.get("nctx", nctx), FAKE, kw.get("nws", nws),
                          None]
@@ -155,6 +177,17 @@ def test_grouped_mlp_rejects_bad_arguments(mxlib):
     assert bwd(*b) == MX_ERR_WORKSPACE
     b[0] = None
     assert bwd(*b) == MX_ERR_INVALID_ARG
+    # the save-h backward needs the (larger) ctx of the save-h mode
+    bex = mxlib.grouped_mlp_bwd_ex
+    nctx_s = mxlib.grouped_mlp_ctx_bytes(M, H, F, E, SAVE_H)
+    nbws_s = mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E, SAVE_H)
+    assert nctx_s > nctx
+    b = [FAKE, FAKE, E, M, H, F, FAKE, FAKE, FAKE, FAKE, nctx, FAKE, FAKE, FAKE, FAKE, FAKE,
+         nbws_s, SAVE_H, None]
+    assert bex(*b) == MX_ERR_WORKSPACE
+    b[17] = 4
+    assert bex(*b) == MX_ERR_INVALID_ARG
+    assert "flags" in _err(mxlib)
 
 
 def test_grouped_mlp_fwd_ex_checks_flags_and_weights(mxlib):
@@ -162,22 +195,27 @@ def test_grouped_mlp_fwd_ex_checks_flags_and_weights(mxlib):
     required unless reused, workspace sizes (no GPU call is reached)."""
     fwd = mxlib.grouped_mlp_fwd_ex
     M, H, F, E = 1024, 256, 256, 4
-    nctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E)
-    nws = mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E)
+    nctx = mxlib.grouped_mlp_ctx_bytes(M, H, F, E, 0)
+    nws = mxlib.grouped_mlp_fwd_ws_bytes(M, H, F, E, SAVE_H)     # the larger of the two
     args = lambda flags, w=FAKE, n=nctx: [FAKE, FAKE, E, M, H, F, w, w, FAKE, FAKE, FAKE, n,
                                           FAKE, nws, flags, None]
-    assert fwd(*args(2)) == MX_ERR_INVALID_ARG
+    assert fwd(*args(4)) == MX_ERR_INVALID_ARG
     assert "flags" in _err(mxlib)
     assert fwd(*args(0, w=None)) == MX_ERR_INVALID_ARG
     assert fwd(*args(1, w=None, n=nctx - 1)) == MX_ERR_WORKSPACE
+    # the save-h forward needs the save-h ctx
+    assert fwd(*args(SAVE_H)) == MX_ERR_WORKSPACE
+    assert fwd(*args(SAVE_H | 1, w=None)) == MX_ERR_WORKSPACE
 
 
 def test_weight_regions_do_not_move_with_m(mxlib):
     """Reused weight copies sit at offsets that do not depend on M."""
     H, F, E = 256, 512, 4
-    for which in (4, 5):     # the ctx regions of the weights' columnwise copies
-        offs = {mxlib.grouped_mlp_ctx_offset(which, M, H, F, E) for M in (0, 100, 4096, 9999)}
-        assert len(offs) == 1 and offs.pop() >= 0
+    for fl in (0, SAVE_H):
+        for which in (4, 5, 7, 8):     # the ctx regions of the weight copies
+            offs = {mxlib.grouped_mlp_ctx_offset(which, M, H, F, E, fl)
+                    for M in (0, 100, 4096, 9999)}
+            assert len(offs) == 1 and offs.pop() >= 0
 
 
 def test_routing_entry_points_reject_bad_arguments(mxlib):

@@ -66,7 +66,7 @@ def _run_full(dev, case, samples):
         # buffers start as 0xFF bytes: nothing unwritten may reach a result
         fws = torch.full((gm.fwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
         bws = torch.full((gm.bwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
-        cbuf = torch.full((gm.lib().grouped_mlp_ctx_bytes(M, H, F, E),), 255,
+        cbuf = torch.full((gm.ctx_bytes(M, H, F, E),), 255,
                           dtype=torch.uint8, device=dev)
         y, ctx = gm.grouped_mlp_fwd(case.X, case.offsets, case.W1, case.W2, case.r, ws=fws,
                                     ctx_buf=cbuf)

@@ -75,69 +75,105 @@ def tok_rows(colmx, off_np, poff, n_rows):
     return out
 
 
-def run_case(dev, case):
+def run_case(dev, case, save_h=False, reuse_from=None):
+    """Forward and backward of ``case`` on the GPU, checked stage by stage
+    and end to end against the oracle.  save_h: the save-h mode (h stored as
+    bf16; the oracle's h_bf16 mode), else the recompute mode.  reuse_from:
+    another case with the same weights whose forward runs first into the same
+    ctx; this case's forward then reuses the weight copies it left there."""
     M, H, F, E = case.M, case.H, case.F, case.E
     off_np = case.offsets.numpy()
     poff = O.padded_offsets(off_np)
     x, w1, w2 = case.X.to(dev), case.W1.to(dev), case.W2.to(dev)
     r, off, dy = case.r.to(dev), case.offsets.to(dev), case.dY.to(dev)
+    Mb = max(M, reuse_from.M) if reuse_from is not None else M
     # Workspaces and ctx start as 0xFF bytes (E8M0 NaN scales, E4M3 NaN
     # codes): anything the library reads without having written it shows.
-    fws = torch.full((gm.fwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
-    bws = torch.full((gm.bwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
-    cbuf = torch.full((gm.lib().grouped_mlp_ctx_bytes(M, H, F, E),), 255, dtype=torch.uint8,
-                      device=dev)
-    y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, ctx_buf=cbuf)
+    fws = torch.full((gm.fwd_ws_bytes(Mb, H, F, E, save_h),), 255, dtype=torch.uint8, device=dev)
+    bws = torch.full((gm.bwd_ws_bytes(M, H, F, E, save_h),), 255, dtype=torch.uint8, device=dev)
+    cbuf = torch.full((gm.ctx_bytes(Mb, H, F, E, save_h),), 255, dtype=torch.uint8, device=dev)
+    if reuse_from is not None:
+        a = reuse_from
+        gm.grouped_mlp_fwd(a.X.to(dev), a.offsets.to(dev), w1, w2, a.r.to(dev), ws=fws,
+                           ctx_buf=cbuf, save_h=save_h)
+    y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, ctx_buf=cbuf, save_h=save_h,
+                                reuse_weights=reuse_from is not None)
     dx, dw1, dw2, dr = gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx, ws=bws)
     torch.cuda.synchronize()
-    print(f"case M={M} H={H} F={F} E={E} counts={list(case.counts)}", flush=True)
+    print(f"case M={M} H={H} F={F} E={E} counts={list(case.counts)} "
+          f"mode={'save-h' if save_h else 'recompute'}"
+          f"{' reusing weights' if reuse_from is not None else ''}", flush=True)
 
     X64, W164, W264, dY64 = to64(case.X), to64(case.W1), to64(case.W2), to64(case.dY)
     r64 = case.r.numpy().astype(np.float64)
     rep = Report()
     assert np.array_equal(ctx.padded_offsets().cpu().numpy(), poff)
 
+    # ---- quantized copies of the bf16 inputs: bit-exact ----
+    n = int(poff[-1])
+    xc_o, xs_o, _ = O.quantize_tokens(X64, off_np)
+    assert np.array_equal(ctx.xcol().codes.cpu().numpy()[:, :n], xc_o)
+    assert np.array_equal(ctx.xcol().scales.cpu().numpy()[:, : n // 32], xs_o)
+    if not save_h:
+        # the rowwise X copy the backward recomputes h from
+        c_ref, s_ref = O.quantize_lastdim(X64)
+        assert np.array_equal(ctx.xrow().codes.cpu().numpy(), c_ref)
+        assert np.array_equal(ctx.xrow().scales.cpu().numpy(), s_ref)
+    # the weights' copies the forward saved: rowwise (blocks along H for W1,
+    # along F for W2) and columnwise (blocks along 2F for W1, along H for W2)
+    for got, w64 in ((ctx.w1row(), W164), (ctx.w2row(), W264),
+                     (ctx.w1col(), W164.transpose(0, 2, 1)),
+                     (ctx.w2col(), W264.transpose(0, 2, 1))):
+        c_ref, s_ref = O.quantize_lastdim(w64)
+        assert np.array_equal(got.codes.cpu().numpy(), c_ref.reshape(-1, c_ref.shape[-1]))
+        assert np.array_equal(got.scales.cpu().numpy(), s_ref.reshape(-1, s_ref.shape[-1]))
+    # the backward's dY copies: rowwise (dgrad) and token-axis (dW2)
+    dyrow = gm.ws_mx_view(bws, gm.MX_WS_DYROW, M, H, F, E, (M, H), save_h)
+    c_ref, s_ref = O.quantize_lastdim(dY64)
+    assert np.array_equal(dyrow.codes.cpu().numpy(), c_ref)
+    assert np.array_equal(dyrow.scales.cpu().numpy(), s_ref)
+    dycol = gm.ws_mx_view(bws, gm.MX_WS_DYCOL, M, H, F, E, (H, ctx.padded_rows), save_h)
+    c_ref, s_ref, _ = O.quantize_tokens(dY64, off_np)
+    assert np.array_equal(dycol.codes.cpu().numpy()[:, :n], c_ref)
+    assert np.array_equal(dycol.scales.cpu().numpy()[:, : n // 32], s_ref)
+
     # ---- forward, stage by stage ----
     qX, qW1, qW2 = O.qdq_lastdim(X64), O.qdq_lastdim(W164), O.qdq_lastdim(W264)
     h_ref = O.grouped_linear(qX, qW1, off_np)
-    h_gpu = to64(ctx.h())
-    rep.check("h", h_gpu, h_ref)
-    zrow = gm.ws_mx_view(fws, gm.MX_WS_ZROW, M, H, F, E, (M, F))
+    if save_h:
+        h_gpu = to64(ctx.h())
+        rep.check("h", h_gpu, h_ref)
+    zrow = gm.ws_mx_view(fws, gm.MX_WS_ZROW, M, H, F, E, (M, F), save_h)
     rep.check("Y|z_gpu", to64(y), O.grouped_linear(deq(zrow), qW2, off_np))
     a, b = h_ref[:, :F], h_ref[:, F:]
     z_ref = r64[:, None] * a * O.sigmoid(a) * b
     rep.rate("z flips", np.mean(zrow.codes.cpu().numpy() != O.quantize_lastdim(z_ref)[0]),
              FLIP_MAX)
-    n = int(poff[-1])
-    xc_o, xs_o, _ = O.quantize_tokens(X64, off_np)
-    assert np.array_equal(ctx.xcol().codes.cpu().numpy()[:, :n], xc_o)
-    assert np.array_equal(ctx.xcol().scales.cpu().numpy()[:, : n // 32], xs_o)
     rep.rate("zcol flips", np.mean(ctx.zcol().codes.cpu().numpy()[:, :n]
                                    != O.quantize_tokens(z_ref, off_np)[0]), FLIP_MAX)
-    # the weights' columnwise copies the forward saved for the backward:
-    # blocks along 2F (W1) and along H (W2), bit-exact
-    for got, w64 in ((ctx.w1col(), W164), (ctx.w2col(), W264)):
-        c_ref, s_ref = O.quantize_lastdim(w64.transpose(0, 2, 1))
-        assert np.array_equal(got.codes.cpu().numpy(), c_ref.reshape(-1, c_ref.shape[-1]))
-        assert np.array_equal(got.scales.cpu().numpy(), s_ref.reshape(-1, s_ref.shape[-1]))
 
-    # ---- backward, stage by stage (on the GPU's own saved h and codes) ----
+    # ---- backward, stage by stage (on the GPU's own codes; the SwiGLU
+    # backward on the h the GPU reads: bf16 saved h, or the exact h it
+    # recomputes from the same codes) ----
     dz_ref = O.grouped_linear(O.qdq_lastdim(dY64), O.qdq_lastdim(W264.transpose(0, 2, 1)),
                               off_np)
-    ag, bg = h_gpu[:, :F], h_gpu[:, F:]
+    h_bwd = h_gpu if save_h else h_ref
+    ag, bg = h_bwd[:, :F], h_bwd[:, F:]
     sg = O.sigmoid(ag)
-    s_gpu = ag * sg * bg
-    rep.check("dr", dr.cpu().numpy().astype(np.float64), (dz_ref * s_gpu).sum(axis=1))
+    s_bwd = ag * sg * bg
+    rep.check("dr", dr.cpu().numpy().astype(np.float64), (dz_ref * s_bwd).sum(axis=1))
     ds = r64[:, None] * dz_ref
     dh_ref = np.concatenate([ds * bg * sg * (1.0 + ag * (1.0 - sg)), ds * ag * sg], axis=1)
-    dhrow = gm.ws_mx_view(bws, gm.MX_WS_DHROW, M, H, F, E, (M, 2 * F))
+    dhrow = gm.ws_mx_view(bws, gm.MX_WS_DHROW, M, H, F, E, (M, 2 * F), save_h)
     rep.rate("dh flips", np.mean(dhrow.codes.cpu().numpy() != O.quantize_lastdim(dh_ref)[0]),
              FLIP_MAX)
     rep.check("dX|dh_gpu", to64(dx),
               O.grouped_linear(deq(dhrow), O.qdq_lastdim(W164.transpose(0, 2, 1)), off_np))
-    dycol_rows = O.qdq_tokens(dY64, off_np)                  # bit-exact on the GPU side
+    dycol_rows = O.qdq_tokens(dY64, off_np)
     zt = tok_rows(ctx.zcol(), off_np, poff, M)
-    dhcol = gm.ws_mx_view(bws, gm.MX_WS_DHCOL, M, H, F, E, (2 * F, ctx.padded_rows))
+    dhcol = gm.ws_mx_view(bws, gm.MX_WS_DHCOL, M, H, F, E, (2 * F, ctx.padded_rows), save_h)
+    rep.rate("dhcol flips", np.mean(dhcol.codes.cpu().numpy()[:, :n]
+                                    != O.quantize_tokens(dh_ref, off_np)[0]), FLIP_MAX)
     dht = tok_rows(dhcol, off_np, poff, M)
     xt = O.qdq_tokens(X64, off_np)
     dW2_ref = np.zeros((E, H, F))
@@ -154,7 +190,7 @@ def run_case(dev, case):
 
     # ---- end to end: the oracle sees only the bf16 inputs ----
     Yo, saved = O.grouped_mlp_fwd(X64, W164, W264, r64, off_np)
-    go = O.grouped_mlp_bwd(dY64, X64, W164, W264, r64, off_np, saved)
+    go = O.grouped_mlp_bwd(dY64, X64, W164, W264, r64, off_np, saved, h_bf16=save_h)
     rep.check("Y e2e", to64(y), Yo, row=E2E_ROW_MAX)
     rep.check("dX e2e", to64(dx), go["dX"], row=E2E_ROW_MAX)
     # Weight gradients contract over one expert's tokens, which are
@@ -163,7 +199,7 @@ def run_case(dev, case):
     # codes move, shifting single elements of dW by up to ~1/sqrt(tokens) of
     # their row's RMS.  End to end they are held to the Frobenius bar per
     # expert (experts with >= 64 tokens); every element is covered by the
-    # stage-wise check above.
+    # stage-wise check above.  The max-row figure is printed for the record.
     rep.check("dW1 e2e", to64(dw1), go["dW1"], row=np.inf)
     rep.check("dW2 e2e", to64(dw2), go["dW2"], row=np.inf)
     for e in range(E):
@@ -188,21 +224,26 @@ def small_case(counts, H, F, seed=0):
                          routing="counts", counts=counts)
 
 
+MODES = [pytest.param(False, id="recompute"), pytest.param(True, id="save_h")]
+
+
+@pytest.mark.parametrize("save_h", MODES)
 @pytest.mark.parametrize("counts,H,F", [
-    ([300, 0, 257, 143], 256, 384),          # F/256 not integral: masked dz tiles
+    ([300, 0, 257, 143], 256, 384),          # F/256 not integral: masked dz tiles (save-h)
     ([1, 33, 0, 250, 95, 0, 129, 6], 512, 256),
     ([600, 600], 384, 128),
 ])
-def test_mlp_small(dev, counts, H, F):
-    run_case(dev, small_case(counts, H, F, seed=H + F))
+def test_mlp_small(dev, counts, H, F, save_h):
+    run_case(dev, small_case(counts, H, F, seed=H + F), save_h=save_h)
 
 
-def test_mlp_zipf_scaled_down(dev):
+@pytest.mark.parametrize("save_h", MODES)
+def test_mlp_zipf_scaled_down(dev, save_h):
     """Zipf(1.1) loads over 8 experts as in the Mixtral-shape workload, with
     T=2048 tokens, H=1024, F=1024."""
     case = make_mlp_case(None, seed=0, T=2048, k=2, E=8, H=1024, F=1024, routing="zipf",
                          zipf_s=1.1)
-    run_case(dev, case)
+    run_case(dev, case, save_h=save_h)
 
 
 def test_mlp_zero_routing_weight_rows(dev):
@@ -214,56 +255,62 @@ def test_mlp_zero_routing_weight_rows(dev):
     assert not dx[7].any()
 
 
-def test_mlp_deterministic(dev):
+@pytest.mark.parametrize("save_h", MODES)
+def test_mlp_deterministic(dev, save_h):
     case = small_case([250, 200, 62], 256, 256, seed=4)
-    a = run_case(dev, case)
-    b = run_case(dev, case)
+    a = run_case(dev, case, save_h=save_h)
+    b = run_case(dev, case, save_h=save_h)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
 
 
-def test_mlp_zero_dy_gives_zero_gradients(dev):
+@pytest.mark.parametrize("save_h", MODES)
+def test_mlp_zero_dy_gives_zero_gradients(dev, save_h):
     case = small_case([130, 70, 60], 256, 128, seed=5)
     case.dY.zero_()
-    dev_ = dev
-    x, w1, w2 = case.X.to(dev_), case.W1.to(dev_), case.W2.to(dev_)
-    r, off, dy = case.r.to(dev_), case.offsets.to(dev_), case.dY.to(dev_)
-    y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r)
+    x, w1, w2 = case.X.to(dev), case.W1.to(dev), case.W2.to(dev)
+    r, off, dy = case.r.to(dev), case.offsets.to(dev), case.dY.to(dev)
+    y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, save_h=save_h)
     dx, dw1, dw2, dr = gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx)
     torch.cuda.synchronize()
     for t in (dx, dw1, dw2, dr):
         assert not t.any()
 
 
-def test_mlp_reuse_weights_matches_fresh_quantization(dev):
-    """A forward that reuses the weight copies an earlier forward left in its
-    ws and ctx (another batch with another M, same weights) gives the same
-    bits as a forward that quantizes the weights itself, and so does the
-    backward that follows it."""
+def test_recompute_and_save_h_agree_within_the_bar(dev):
+    """The two modes differ only in the h the SwiGLU backward reads (exact
+    fp32 accumulator vs its bf16 rounding): outputs agree within the
+    end-to-end bar, the forward is identical."""
+    case = small_case([300, 0, 257, 143], 256, 384, seed=9)
+    x, w1, w2 = case.X.to(dev), case.W1.to(dev), case.W2.to(dev)
+    r, off, dy = case.r.to(dev), case.offsets.to(dev), case.dY.to(dev)
+    out = {}
+    for sh in (False, True):
+        y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, save_h=sh)
+        out[sh] = (y,) + tuple(gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx))
+    torch.cuda.synchronize()
+    assert torch.equal(out[False][0], out[True][0])
+    for name, u, v in zip(("dX", "dW1", "dW2", "dr"), out[False][1:], out[True][1:]):
+        rel, _ = O.parity_metrics(to64(u), to64(v))
+        print(f"  {name} recompute vs save-h rel_fro={rel:.3e}", flush=True)
+        assert rel <= 3e-2, name
+
+
+@pytest.mark.parametrize("save_h", MODES)
+def test_mlp_reuse_weights_against_oracle(dev, save_h):
+    """A forward that reuses the weight copies an earlier forward (another
+    batch with another M, same weights) left in its ctx: every stage-wise and
+    end-to-end check against the oracle, and the same bits as a forward that
+    quantizes the weights itself, backward included."""
     H, F = 256, 384
     a = small_case([300, 0, 257, 143], H, F, seed=11)
     b = small_case([110, 40, 0, 78], H, F, seed=12)
-    E = a.E
-    w1, w2 = a.W1.to(dev), a.W2.to(dev)
-    Mx = max(a.M, b.M)
-    fws = torch.full((gm.fwd_ws_bytes(Mx, H, F, E),), 255, dtype=torch.uint8, device=dev)
-    cbuf = torch.full((gm.lib().grouped_mlp_ctx_bytes(Mx, H, F, E),), 255, dtype=torch.uint8,
-                      device=dev)
-    gm.grouped_mlp_fwd(a.X.to(dev), a.offsets.to(dev), w1, w2, a.r.to(dev), ws=fws,
-                       ctx_buf=cbuf)
+    b.W1, b.W2 = a.W1, a.W2
+    g_re = run_case(dev, b, save_h=save_h, reuse_from=a)
     xb, offb, rb, dyb = b.X.to(dev), b.offsets.to(dev), b.r.to(dev), b.dY.to(dev)
-    y_re, ctx_re = gm.grouped_mlp_fwd(xb, offb, w1, w2, rb, ws=fws, ctx_buf=cbuf,
-                                      reuse_weights=True)
-    g_re = gm.grouped_mlp_bwd(dyb, offb, w1, w2, rb, ctx_re)
-    y_fr, ctx_fr = gm.grouped_mlp_fwd(xb, offb, w1, w2, rb)
-    g_fr = gm.grouped_mlp_bwd(dyb, offb, w1, w2, rb, ctx_fr)
+    w1, w2 = b.W1.to(dev), b.W2.to(dev)
+    y_fr, ctx_fr = gm.grouped_mlp_fwd(xb, offb, w1, w2, rb, save_h=save_h)
+    g_fr = (y_fr,) + tuple(gm.grouped_mlp_bwd(dyb, offb, w1, w2, rb, ctx_fr))
     torch.cuda.synchronize()
-    n = int(O.padded_offsets(b.offsets.numpy())[-1])
-    assert torch.equal(y_re, y_fr)
-    assert torch.equal(ctx_re.h(), ctx_fr.h())
-    for get in (lambda c: c.xcol(), lambda c: c.zcol()):
-        u, v = get(ctx_re), get(ctx_fr)
-        assert torch.equal(u.codes[:, :n], v.codes[:, :n])
-        assert torch.equal(u.scales[:, : n // 32], v.scales[:, : n // 32])
     for u, v in zip(g_re, g_fr):
         assert torch.equal(u, v)
