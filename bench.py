@@ -7,16 +7,24 @@ Workload (the Mixtral-8x7B expert shape): T=16384 tokens routed top-2
 [13047, 6087, 3897, 2839, 2221, 1818, 1534, 1325], dY ~ N(0, 1).  Seeded
 synthetic inputs drawn on the GPU; everything stays resident in HBM.
 
-One step = grouped_mlp_fwd + grouped_mlp_bwd: quantization of X, W1, W2 and
-dY (rowwise and columnwise), the fused gate-up/SwiGLU/routing-scale/requant
-GEMM, the down GEMM, the fused dgrad/SwiGLU-backward/dr/requant GEMM, the
-gate-up dgrad GEMM and both weight-gradient GEMMs.
+One step = grouped_mlp_fwd + grouped_mlp_bwd in the default recompute mode:
+quantization of X, W1, W2 and dY (rowwise and columnwise), the fused
+gate-up/SwiGLU/routing-scale/requant GEMM (h stays on chip), the down GEMM,
+the fused backward GEMM (h recomputed from the saved X codes, dz, SwiGLU
+backward, dr, requant), the gate-up dgrad GEMM and both weight-gradient GEMMs.
 
-Prints one JSON line: tokens/s (value), TFLOP/s counted as 18*H*F per routed
-row, the dominant kernel's roofline (launch durations from HIP events the
-library records on its stream around each launch), and the FP64 CPU oracle
-timed on a bounded sample as a reported baseline.  A second figure,
-"weights_cached", times the same step with the forward reusing the MXFP8
+Prints one JSON line: tokens/s (value) over exactly K steps bracketed by
+device synchronizations, per-step GPU times (median, min, p90) from events on
+the stream the library runs on, TFLOP/s counted as 18*H*F per routed row
+(algorithmic; the recompute's 4*H*F per row is reported as the executed
+figure beside it), the dominant kernel's roofline (launch durations from HIP
+events the library records on its stream around each of its launches, in a
+second pass of the same K steps so that the headline carries no event
+overhead), and the FP64 CPU oracle timed on a bounded sample as a reported
+baseline.  "save_h" times the same step in the mode that stores h as bf16
+instead of recomputing it, with the activation bytes each mode keeps for the
+backward; "forward_only" times the forward alone (with and without the weight
+quantization); "weights_cached" the step with the forward reusing the MXFP8
 weight copies of an earlier forward (as across the micro-batches of one
 optimizer step); the headline always quantizes the weights.  "routing"
 times the steps around the expert path at the same shape (router, sorted-row plan,
@@ -84,6 +92,54 @@ def kernel_table(gm, lib):
     return agg
 
 
+def step_stats(ms_list):
+    """Median, min and p90 (nearest rank) of per-step GPU times in ms."""
+    v = sorted(ms_list)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    p90 = v[min(n - 1, max(0, -(-9 * n // 10) - 1))]
+    return {"median": round(med, 4), "min": round(v[0], 4), "p90": round(p90, 4)}
+
+
+def time_steps(step, steps, warmup, label):
+    """Wall time of exactly `steps` calls of step(), bracketed by device
+    synchronizations (after `warmup` untimed calls), and each call's GPU time
+    from a pair of events on the current stream, the stream the library's
+    kernels run on."""
+    import torch
+    for i in range(warmup):
+        step()
+        torch.cuda.synchronize()
+        print(f"[bench] {label}: warmup {i + 1}/{warmup}", file=sys.stderr, flush=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(f"[bench] {label}: {steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    return elapsed, step_stats([a.elapsed_time(b) for a, b in evs])
+
+
+def profiled_pass(gm, lib, step, steps):
+    """Per-kernel launch records of `steps` calls of step() (library launch
+    timing on), after one untimed call."""
+    import torch
+    step()
+    torch.cuda.synchronize()
+    if lib.mx_profile_begin(64 * max(steps, 1)) != 0:
+        raise RuntimeError(gm.last_error())
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    lib.mx_profile_end()
+    return kernel_table(gm, lib)
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "mixtral_fwd_bwd_hbm_traffic.json")
 
 
@@ -144,9 +200,20 @@ def cpu_baseline(seed, T, M, E, H, F):
     import numpy as np
     import torch
     from oracle import mx_oracle as O
+    # every host CPU this process may run on, all given to the BLAS the
+    # oracle's matmuls call
+    ncpu = len(os.sched_getaffinity(0))
+    blas = "unknown"
+    limiter = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=ncpu, user_api="blas")
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(i.get("num_threads", 1) for i in info)
+        else:
+            threads = 1
     except Exception:
         threads = 1
     Fs, n = 1024, 512
@@ -165,28 +232,34 @@ def cpu_baseline(seed, T, M, E, H, F):
 
     t1 = run(n)
     t2 = run(2 * n)
+    if limiter is not None:
+        limiter.unregister()
     per_row = max((t2 - t1) / n, 1e-12)
     per_expert = max(t1 - n * per_row, 0.0)
     est = (F / Fs) * (E * per_expert + M * per_row)
-    return {"value": round(T / est, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(T / est, 3), "unit": "tokens/s", "cores": threads,
+            "host_cpus": ncpu, "blas": blas, "kind": "oracle",
             "sample": (f"FP64 NumPy oracle fwd+bwd on 1 expert, H={H}, F slice {Fs}/{F}, "
                        f"{n} and {2 * n} rows ({t1:.1f} s + {t2:.1f} s); step time "
                        f"extrapolated linearly to E={E}, M={M} rows, F={F}: {est:.0f} s"),
             "est_step_s": round(est, 1)}
 
 
-def time_call(gm, lib, f, reps):
+def time_call(gm, lib, f, reps, flush=None):
     """GPU ms per call of f(): the library's launch records (events on its
     stream around each of its launches) over reps calls, one call before,
     untimed.  Unlike a wall clock around the calls, this leaves out the
     host's time to issue them, which exceeds the kernels' for the small
-    steps timed here."""
+    steps timed here.  flush: called before each timed call (not timed),
+    to evict the caches."""
     import torch
     f()
     torch.cuda.synchronize()
     if lib.mx_profile_begin(64 * reps) != 0:
         raise RuntimeError(gm.last_error())
     for _ in range(reps):
+        if flush is not None:
+            flush()
         out = f()
     torch.cuda.synchronize()
     lib.mx_profile_end()
@@ -210,6 +283,14 @@ def linear_figures(gm, lib, dev, reps):
     ms_mqx, mx_x = timed(lambda: gm.mxfp8_quantize(x))
     ms_mqw, mx_w = timed(lambda: gm.mxfp8_quantize(w))
     ms_mg, _ = timed(lambda: gm.grouped_linear_fwd(mx_x["row"], offs, mx_w["row"]))
+    # the same calls with the caches flushed before each one: the whole
+    # working set fits the 256 MB Infinity Cache, so warm calls read it from
+    # there; a 512 MB write in between evicts it
+    flush = make_flush(dev)
+    flushed = lambda f: time_call(gm, lib, f, reps, flush=flush)[0]
+    fl_mqx = flushed(lambda: gm.mxfp8_quantize(x))
+    fl_mg = flushed(lambda: gm.grouped_linear_fwd(mx_x["row"], offs, mx_w["row"]))
+    T = case.T
     ms_pqx, pt_x = timed(lambda: gm.fp8_tensor_quantize(x, offs))
     ms_pqw, pt_w = timed(lambda: gm.fp8_tensor_quantize(w))
     ms_pg, _ = timed(lambda: gm.grouped_linear_fwd_fp8(pt_x, offs, pt_w))
@@ -219,7 +300,15 @@ def linear_figures(gm, lib, dev, reps):
         "shape": {"M": M, "K": K, "N": N, "E": E},
         "mxfp8": {"quant_x_ms": round(ms_mqx, 4), "quant_x_gbs": gbs(ms_mqx, mx_bytes(M * K)),
                   "quant_w_ms": round(ms_mqw, 4), "quant_w_gbs": gbs(ms_mqw, mx_bytes(E * N * K)),
-                  "gemm_ms": round(ms_mg, 4), "gemm_tflops": round(flops / ms_mg / 1e9, 1)},
+                  "gemm_ms": round(ms_mg, 4), "gemm_tflops": round(flops / ms_mg / 1e9, 1),
+                  "gemm_frac_fp8_peak": round(flops / ms_mg / 1e9 / FP8_PEAK_TFLOPS, 4),
+                  "quant_x_plus_gemm_tokens_per_s": round(T / ((ms_mqx + ms_mg) / 1e3), 1),
+                  "flushed": {"quant_x_ms": round(fl_mqx, 4),
+                              "quant_x_gbs": gbs(fl_mqx, mx_bytes(M * K)),
+                              "gemm_ms": round(fl_mg, 4),
+                              "gemm_tflops": round(flops / fl_mg / 1e9, 1),
+                              "quant_x_plus_gemm_tokens_per_s":
+                                  round(T / ((fl_mqx + fl_mg) / 1e3), 1)}},
         "fp8_per_tensor": {"quant_x_ms": round(ms_pqx, 4),
                            "quant_x_gbs": gbs(ms_pqx, pt_bytes(M * K)),
                            "quant_w_ms": round(ms_pqw, 4),
@@ -227,6 +316,19 @@ def linear_figures(gm, lib, dev, reps):
                            "gemm_ms": round(ms_pg, 4),
                            "gemm_tflops": round(flops / ms_pg / 1e9, 1)},
     }
+
+
+def make_flush(dev, mib=512):
+    """A device write of `mib` MiB, twice the Infinity Cache, that evicts
+    earlier data from the caches."""
+    import torch
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    state = {"v": 0}
+
+    def flush():
+        state["v"] = (state["v"] + 1) & 0xFF
+        buf.fill_(state["v"])
+    return flush
 
 
 def grouped_vs_loop_figures(gm, lib, dev, reps=200):
@@ -266,9 +368,11 @@ def grouped_vs_loop_figures(gm, lib, dev, reps=200):
 
     g_us, l_us = wall_us(grouped), wall_us(loop)
     gpu_ms, _ = time_call(gm, lib, grouped, reps)
+    gpu_fl_ms, _ = time_call(gm, lib, grouped, min(reps, 50), flush=make_flush(dev))
     return {"shape": {"M": int(x.shape[0]), "K": int(x.shape[1]), "N": int(w.shape[1]), "E": E},
             "grouped_us_per_call": round(g_us, 2), "per_expert_loop_us_per_call": round(l_us, 2),
-            "loop_over_grouped": round(l_us / g_us, 2), "grouped_gpu_us": round(gpu_ms * 1e3, 2)}
+            "loop_over_grouped": round(l_us / g_us, 2), "grouped_gpu_us": round(gpu_ms * 1e3, 2),
+            "grouped_gpu_us_flushed": round(gpu_fl_ms * 1e3, 2)}
 
 
 def one_rank_share_figures(gm, lib, dev, seed, steps):
@@ -404,28 +508,26 @@ def main():
     case = make_mlp_case("mixtral_fwd_bwd", seed=args.seed, device=dev)
     M, H, F, E, T = case.M, case.H, case.F, case.E, case.T
     x, w1, w2, r, off, dy = case.X, case.W1, case.W2, case.r, case.offsets, case.dY
-    fws = torch.empty(gm.fwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
-    bws = torch.empty(gm.bwd_ws_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+    # workspaces large enough for both modes
+    fws = torch.empty(max(gm.fwd_ws_bytes(M, H, F, E, sh) for sh in (False, True)),
+                      dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(gm.bwd_ws_bytes(M, H, F, E, sh) for sh in (False, True)),
+                      dtype=torch.uint8, device=dev)
+    flops_step = 18.0 * H * F * M                 # algorithmic
+    flops_recompute = 4.0 * H * F * M             # h = X W1^T again in the backward
 
-    def step():
-        y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws)
-        return gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx, ws=bws)
+    def make_step(save_h):
+        def step():
+            y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, save_h=save_h)
+            return gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx, ws=bws)
+        return step
 
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        print(f"[bench] warmup {i + 1}/{args.warmup}", file=sys.stderr, flush=True)
-
-    if lib.mx_profile_begin(64 * max(args.steps, 1)) != 0:
-        raise RuntimeError(gm.last_error())
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    lib.mx_profile_end()
-    print(f"[bench] {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+    # ---- headline: recompute mode, library launch timing off ----
+    step = make_step(False)
+    elapsed, stats = time_steps(step, args.steps, args.warmup, "fwd+bwd")
+    # the same steps with the library's launch records on, for the per-kernel
+    # table and the roofline
+    agg = profiled_pass(gm, lib, step, args.steps)
 
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
@@ -435,29 +537,51 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] calibration copy of {args.copy_calib_mib} MiB done", file=sys.stderr,
               flush=True)
+        del src, dst
 
-    agg = kernel_table(gm, lib)
+    def kernels_of(agg, steps):
+        return {k: {"launches_per_step": v["launches"] / steps,
+                    "ms_per_step": round(v["ms"] / steps, 4),
+                    ("tflops" if v["unit"] == 0 else "gbs"):
+                        round(v["work"] / (v["ms"] / 1e3) / (1e12 if v["unit"] == 0 else 1e9), 2)}
+                for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["ms"])}
 
-    # The same step with the weight quantization cached: the forward reuses
-    # the MXFP8 weight copies of the first forward (weights unchanged, as
-    # across the micro-batches of one optimizer step).  Not the headline.
-    ctx_bytes = gm.ctx_bytes(M, H, F, E)
-    cbuf = torch.empty(ctx_bytes, dtype=torch.uint8, device=dev)
+    # ---- the save-h mode beside it ----
+    nside = max(args.steps // 2, 3)
+    el_s, stats_s = time_steps(make_step(True), nside, 1, "fwd+bwd save-h")
+    agg_s = profiled_pass(gm, lib, make_step(True), 2)
+
+    def saved_bytes(save_h):
+        """Bytes the forward keeps for the backward that scale with the batch
+        (everything in ctx past the weight copies)."""
+        first = gm.MX_CTX_H if save_h else gm.MX_CTX_XROW
+        off0 = int(lib.grouped_mlp_ctx_offset(first, M, H, F, E, gm.MX_MLP_SAVE_H if save_h else 0))
+        return gm.ctx_bytes(M, H, F, E, save_h) - off0
+
+    # ---- forward only, with and without the weight quantization ----
+    fwd_flops = 6.0 * H * F * M
+    cbuf = torch.empty(gm.ctx_bytes(M, H, F, E), dtype=torch.uint8, device=dev)
+    el_f, stats_f = time_steps(lambda: gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws,
+                                                          ctx_buf=cbuf),
+                               args.steps, 1, "fwd")
+    el_fc, stats_fc = time_steps(lambda: gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws,
+                                                            ctx_buf=cbuf, reuse_weights=True),
+                                 args.steps, 1, "fwd, weights cached")
+
+    def fwd_fig(el, st, n):
+        ms = el / n * 1e3
+        tf = fwd_flops / (ms / 1e3) / 1e12
+        return {"ms_per_step": round(ms, 4), "gpu_ms": st, "tokens_per_s": round(T / (ms / 1e3), 1),
+                "tflops": round(tf, 2), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+
+    # ---- fwd+bwd with the weight quantization cached ----
     gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, ctx_buf=cbuf)
 
     def step_cached():
         y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, ws=fws, ctx_buf=cbuf, reuse_weights=True)
         return gm.grouped_mlp_bwd(dy, off, w1, w2, r, ctx, ws=bws)
 
-    step_cached()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for _ in range(args.steps):
-        step_cached()
-    torch.cuda.synchronize()
-    elapsed_cached = time.perf_counter() - t1
-    print(f"[bench] {args.steps} steps with cached weight quantization in {elapsed_cached:.3f} s",
-          file=sys.stderr, flush=True)
+    el_c, stats_c = time_steps(step_cached, args.steps, 1, "fwd+bwd, weights cached")
     del cbuf
 
     routing = routing_figures(gm, lib, case, dev, reps=max(args.steps, 3))
@@ -472,13 +596,9 @@ def main():
 
     ms_step = elapsed / args.steps * 1e3
     tokens_s = T * args.steps / elapsed
-    flops_step = 18.0 * H * F * M
     tflops = flops_step * args.steps / elapsed / 1e12
-    kernels = {k: {"launches_per_step": v["launches"] / args.steps,
-                   "ms_per_step": round(v["ms"] / args.steps, 4),
-                   ("tflops" if v["unit"] == 0 else "gbs"):
-                       round(v["work"] / (v["ms"] / 1e3) / (1e12 if v["unit"] == 0 else 1e9), 2)}
-               for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["ms"])}
+    ms_s = el_s / nside * 1e3
+    tf_s = flops_step / (ms_s / 1e3) / 1e12
 
     out = {
         "metric": "GroupedMLP fwd+bwd tokens/s & TFLOP/s (MXFP8), Mixtral-8x7B expert shape",
@@ -494,27 +614,51 @@ def main():
         "dtype": "mxfp8_e4m3 (fp32 accumulate)",
         "data": "synthetic",
         "config": {"workload": "mixtral_fwd_bwd: GroupedMLP fwd+bwd, T=16384 top-2 (M=32768 "
-                               "rows), E=8, H=4096, F=14336, Zipf(1.1) loads",
+                               "rows), E=8, H=4096, F=14336, Zipf(1.1) loads; backward "
+                               "recomputes h (nothing intermediate kept in HBM)",
                    "T": T, "M": M, "E": E, "H": H, "F": F,
                    "expert_rows": expert_rows},
+        "gpu_ms_per_step": stats,
         "tflops": round(tflops, 2),
         "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+        "tflops_executed": round((flops_step + flops_recompute) * args.steps / elapsed / 1e12, 2),
+        "frac_fp8_peak_executed": round((flops_step + flops_recompute) * args.steps / elapsed
+                                        / 1e12 / FP8_PEAK_TFLOPS, 4),
         "roofline": roofline(agg),
-        "kernels": kernels,
+        "kernels": kernels_of(agg, args.steps),
+        "saved_for_backward": {
+            "recompute": {"bytes": saved_bytes(False),
+                          "bytes_per_token": round(saved_bytes(False) / T, 1),
+                          "what": "rowwise and token-axis MXFP8 copies of X, token-axis copy "
+                                  "of z, padded offsets"},
+            "save_h": {"bytes": saved_bytes(True),
+                       "bytes_per_token": round(saved_bytes(True) / T, 1),
+                       "what": "bf16 pre-activation h, token-axis MXFP8 copies of X and z, "
+                               "padded offsets"},
+            "weights": {"bytes": int(lib.grouped_mlp_ctx_offset(gm.MX_CTX_XROW, M, H, F, E, 0)),
+                        "what": "MXFP8 copies of W1 and W2 (rowwise and columnwise), made once "
+                                "per step, independent of the batch"}},
+        "save_h": {
+            "ms_per_step": round(ms_s, 4), "gpu_ms_per_step": stats_s,
+            "tokens_per_s": round(T / (ms_s / 1e3), 1), "tflops": round(tf_s, 2),
+            "frac_fp8_peak": round(tf_s / FP8_PEAK_TFLOPS, 4),
+            "kernels": kernels_of(agg_s, 2),
+            "what": "same step, forward stores h as bf16 and the backward reads it instead of "
+                    "recomputing it"},
+        "forward_only": {
+            "with_weight_quantization": fwd_fig(el_f, stats_f, args.steps),
+            "weights_cached": fwd_fig(el_fc, stats_fc, args.steps),
+            "what": "grouped_mlp_fwd alone (6*H*F flops per row): quantize X (and W1, W2), fused "
+                    "gate-up + SwiGLU + routing scale + requantize, down GEMM"},
+        "weights_cached": {
+            "ms_per_step": round(el_c / args.steps * 1e3, 4), "gpu_ms_per_step": stats_c,
+            "tokens_per_s": round(T * args.steps / el_c, 1),
+            "what": "same step, forward reusing the MXFP8 weight copies of an earlier forward "
+                    "(weights unchanged across micro-batches)"},
         "routing": routing,
         "fine_grained_64e": many,
         "ep8_one_rank_share": share,
         "grouped_linear": linear,
-        "saved_for_backward": {
-            "ctx_bytes": int(ctx_bytes),
-            "bytes_per_token": round(ctx_bytes / T, 1),
-            "what": "forward context kept for the backward (bf16 pre-activation h, token-axis "
-                    "MXFP8 copies of X and z, columnwise MXFP8 weight copies, padded offsets)"},
-        "weights_cached": {
-            "ms_per_step": round(elapsed_cached / args.steps * 1e3, 4),
-            "tokens_per_s": round(T * args.steps / elapsed_cached, 1),
-            "what": "same step, forward reusing the MXFP8 weight copies of an earlier forward "
-                    "(weights unchanged across micro-batches)"},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -243,6 +243,9 @@ struct QStage {
 // fused epilogues as four per-wave slots.  The backward's slot adds a ring of
 // four h units (4 x 4 KiB) after its staging area.
 constexpr int kHRing = 4 * 4 * 1024;
+// The recompute backward's slot adds the stash of the wave's last 32-row
+// slice of [a | b] (16 x 1 KiB: 64 floats per lane).
+constexpr int kStash = 16 * 1024;
 template <Epi EPI>
 struct Slot {
     static constexpr int kBytes = EPI == Epi::kDSwiglu ? QStage<256>::kBytes + kHRing
@@ -250,7 +253,8 @@ struct Slot {
     static constexpr int kSmem = 4 * kBytes > (int)sizeof(GemmSmem) ? 4 * kBytes
                                                                      : (int)sizeof(GemmSmem);
     static_assert(EPI != Epi::kSwiglu || QStage<64>::kBytes <= kBytes, "staging fits the slot");
-    static_assert(EPI != Epi::kDSwigluR || QStage<128>::kBytes <= kBytes, "staging fits the slot");
+    static_assert(EPI != Epi::kDSwigluR || QStage<128>::kBytes + kStash <= kBytes,
+                  "staging and stash fit the slot");
     static_assert(EPI != Epi::kStoreBf16 || 4 * 32768 <= kSmem, "output quadrants fit the stages");
     static_assert(kBytes % 16 == 0 && QStage<256>::kBytes % 16 == 0, "16-byte aligned regions");
 };
@@ -452,6 +456,41 @@ __device__ __forceinline__ void pick_unit(const v4f (&acc)[8][NJ], int ip, float
                     }
         }
     });
+}
+
+// pick_unit for the recompute backward's [a | b], whose last slice (rows
+// 6, 7) was moved to the wave's LDS stash: block (ii, j) of it is 1 KiB at
+// ((ii * 8 + j) * 64 + lane) * 16, one v4f per lane.
+template <int J0>
+__device__ __forceinline__ void pick_unit_stashed(const v4f (&acc)[8][8], int ip,
+                                                  float (&u)[2][2][4], const uint8_t* stash,
+                                                  int lane) {
+    static_for<3>([&](auto c) {
+        constexpr int k = decltype(c)::value;
+        if (ip == k) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = acc[2 * k + ii][J0 + jj][v];
+                        asm volatile("" : "+v"(x));
+                        u[ii][jj][v] = x;
+                    }
+        }
+    });
+    if (ip == 3) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const v4f x = *reinterpret_cast<const v4f*>(
+                    stash + ((ii * 8 + J0 + jj) * 64 + lane) * 16);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) u[ii][jj][v] = x[v];
+            }
+    }
 }
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -723,6 +762,141 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
     }
 }
 
+// tile_gemm with only four A fragments in registers (rows 0..3 of the wave's
+// eight, then rows 4..7 in the same registers), for a tile GEMM that runs
+// while other accumulators stay live.  Changes to the schedule of tile_gemm:
+//  * pass A reads rows 4..7 of the current step from stage cur as soon as
+//    the matching row 0..3 has issued its last MFMA, so the part of stage
+//    cur that holds rows 4..7 (rows 64..127 and 192..255 of the tile) and
+//    the A scales are still in use after S1;
+//  * hence the loads of step k+2 into those regions (4 A loads per wave and
+//    the A scales) are issued in pass B, after the S2 barrier, by which every
+//    wave has read them; the 4 other A loads (rows 0..63 and 128..191), the
+//    B loads and the B scales go into pass A as before.
+// Load u of wave w: u < 4 A rows of region R0, u < 8 A rows of region R1,
+// u < 8 + NJ B rows, 8 + NJ B scales, 9 + NJ A scales.  Region R0 is tile rows
+// 0..63 and 128..191, R1 the other half; each is 16 loads of 8 rows, load
+// t = 4w + (u & 3) of a region covering its rows 8t .. 8t + 7 (t < 8) or
+// 128 + 8(t - 8) .. (t >= 8), offset by 64 for R1.
+template <int NJ> struct LeanSched;
+template <> struct LeanSched<4> {   // 256 x 128 tile: 14 loads, 32 MFMAs per wave
+    static constexpr int kLoads = 14, kNA = 9;
+    // pass A: R0 A loads 0..3, B loads 8..11, B scales 12
+    static constexpr int a_at(int s) {
+        return s == 0 ? 0 : s == 2 ? 8 : s == 3 ? 1 : s == 5 ? 9 : s == 6 ? 2 : s == 8 ? 10
+             : s == 9 ? 3 : s == 11 ? 11 : s == 13 ? 12 : -1;
+    }
+    // pass B: R1 A loads 4..7, A scales 13
+    static constexpr int b_at(int s) {
+        return s == 1 ? 4 : s == 4 ? 5 : s == 6 ? 6 : s == 8 ? 7 : s == 10 ? 13 : -1;
+    }
+};
+
+__device__ __forceinline__ constexpr int lean_arow(int w, int u) {
+    return ((u >= 4) ? 64 : 0) + ((4 * w + (u & 3)) < 8 ? 8 * (4 * w + (u & 3))
+                                                       : 128 + 8 * (4 * w + (u & 3) - 8));
+}
+
+template <int NJ>
+__device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, const TileSrc& o,
+                                               int nk, int wave, int wm, int wn, int lane,
+                                               int64_t lda) {
+    using SC = LeanSched<NJ>;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int swz = r16 & 7;
+    const int dma_row = lane >> 3;
+    const int dma_chunk = (lane & 7) ^ (dma_row & 7);
+    // A offsets of this wave's 8 loads (the region layout above); o.aoff is
+    // not used
+    uint32_t aoffl[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        aoffl[u] = (uint32_t)((lean_arow(wave, u) + dma_row) * lda + dma_chunk * 16);
+    auto dma_u = [&](auto uc, int st, int ks) {
+        constexpr int u = decltype(uc)::value;
+        const bool live = ks < nk;
+        const uint32_t k0 = (uint32_t)ks * BK;
+        if constexpr (u < 8) {
+            const v4i r = live ? o.ra : v4i{o.ra.x, o.ra.y, 0, o.ra.w};
+            dma_b128(r, uni(lds_addr(&sm.a[st][lean_arow(wave, u) * BK])), aoffl[u], k0);
+        } else if constexpr (u < 8 + NJ) {
+            const v4i r = live ? o.rb : v4i{o.rb.x, o.rb.y, 0, o.rb.w};
+            dma_b128(r, uni(lds_addr(&sm.b[st][(wave * NJ + (u - 8)) * 1024])), o.boff[u - 8], k0);
+        } else if constexpr (u == 8 + NJ) {
+            const v4i rs = o.sb.rsrc;
+            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
+            dma_b32(r, uni(lds_addr(&sm.bs[st][wave * 64])), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
+        } else {
+            const v4i rs = o.sa.rsrc;
+            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
+            dma_b32(r, uni(lds_addr(&sm.as[st][wave * 64])), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
+        }
+    };
+    v8i af[4], bfr[NJ];
+    int asc[4], bsc[NJ];
+    // row i (0..7) of the wave into register slot i & 3
+    auto read_a = [&](auto ic, int st) {
+        constexpr int i = decltype(ic)::value;
+        const int row = wm * 128 + i * 16 + r16;
+        const uint8_t* base = &sm.a[st][row * BK];
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        af[i & 3] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        asc[i & 3] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
+    };
+    auto read_b = [&](auto jc, int st) {
+        constexpr int j = decltype(jc)::value;
+        const int row = wn * (NJ * 16) + j * 16 + r16;
+        const uint8_t* base = &sm.b[st][row * BK];
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
+    };
+    auto mfma = [&](auto ic, auto jc) {     // ic: wave row 0..7 (register slot ic & 3)
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bfr[j], af[i & 3], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i & 3]);
+    };
+
+    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 0, 0); });
+    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 1, 1); });
+    wait_vmcnt<SC::kLoads>();                           // step 0 (this wave)
+    lds_barrier();                                      // step 0 (every wave)
+    static_for<4>([&](auto ic) { read_a(ic, 0); });
+    static_for<NJ>([&](auto jc) { read_b(jc, 0); });
+    for (int ks = 0; ks < nk; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        lds_barrier();                                  // S1: B, R0 and B scales of cur are free
+        // pass A: rows 0..3; in the last column row i + 4 replaces row i
+        static_for<4 * NJ>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, 4 + s % 4>{}, cur);
+            constexpr int u = SC::a_at(s);
+            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_vmcnt<SC::kNA>();
+        lds_barrier();                                  // S2: stage nxt complete; R1 of cur read
+        // pass B: rows 4..7; the next step's B column j after its last MFMA
+        // here, row i (0..3) after row i + 4's last MFMA
+        static_for<4 * NJ>([&](auto sc) {
+            constexpr int s = decltype(sc)::value, j = s / 4, i = 4 + s % 4;
+            mfma(std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
+            if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, s % 4>{}, nxt);
+            constexpr int u = SC::b_at(s);
+            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+}
+
 // SPLIT (plain store, row-grouped only): the tail-split schedule below.
 template <Epi EPI, bool SPLIT = false>
 __global__ void __launch_bounds__(NTHREADS, 1)
@@ -953,7 +1127,7 @@ mx_gemm_kernel(GemmProblem p) {
             const TileSrc o = tile_src<false, 4>(p.A2, p.B2, m0, mvalid,
                                                  (int64_t)g * p.B2.gstride + n0, p.F - n0, 0, K,
                                                  brow_plain, wave, lane2);
-            tile_gemm<4>(dacc, sm, o, nk, wave, wm, wn, lane2);
+            tile_gemm_lean<4>(dacc, sm, o, nk, wave, wm, wn, lane2, p.A2.ld);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_barrier();
         }
@@ -1193,6 +1367,16 @@ mx_gemm_kernel(GemmProblem p) {
             const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true, p.qtiled};
             uint8_t* st = smem + wave * Slot<EPI>::kBytes;
             const int part = (int)(n0 / 128) * 2 + wn;
+            // the last slice's [a | b] to the stash: 384 accumulators plus the
+            // epilogue's working set would not fit the registers
+            uint8_t* const stash = st + QStage<128>::kBytes;
+            static_for<2>([&](auto iic) {
+                constexpr int ii = decltype(iic)::value;
+                static_for<8>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    *reinterpret_cast<v4f*>(stash + ((ii * 8 + j) * 64 + lane) * 16) = acc[6 + ii][j];
+                });
+            });
 #pragma nounroll
             for (int ip = 0; ip < 4; ++ip) {
                 // lane-derived values re-derived per slice (see the forward)
@@ -1209,8 +1393,8 @@ mx_gemm_kernel(GemmProblem p) {
                 static_for<2>([&](auto jpc) {
                     constexpr int jp = decltype(jpc)::value;
                     float ga[2][2][4], ua[2][2][4], dzu[2][2][4], da[2][2][4], db[2][2][4];
-                    pick_unit<2 * jp>(acc, ip, ga);
-                    pick_unit<2 * jp + 4>(acc, ip, ua);
+                    pick_unit_stashed<2 * jp>(acc, ip, ga, stash, lane);
+                    pick_unit_stashed<2 * jp + 4>(acc, ip, ua, stash, lane);
                     pick_unit<2 * jp>(dacc, ip, dzu);
                     // Rows past the expert's valid rows are selected to 0 (a,
                     // b and dz): rows past M read never-written scale bytes,
