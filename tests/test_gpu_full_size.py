@@ -3,18 +3,31 @@ top-2, E=8, H=4096, F=14336, Zipf(1.1) loads, forward + backward) and of the
 64-expert long-sequence workload (T=32768 top-8, E=64, H=2048, F=1408, 8
 empty experts), run exactly as bench.py runs the headline workload: inputs
 drawn on the GPU by the seeded generator, one grouped_mlp_fwd and one
-grouped_mlp_bwd on the library's default launch configuration.
+grouped_mlp_bwd (recompute mode) on the library's default launch
+configuration.
 
-The FP64 oracle cannot run these sizes whole, so it is run on samples it can
-compute exactly (see tests/_oracle_workers.py): whole experts (every output
-of the expert, including dW1[e] and dW2[e]) and row subsets of the largest
-expert (Y, dX and dr of those rows), in worker processes while the GPU runs.
-Bars as in test_gpu_mlp.py end to end: relative Frobenius error <= 1e-2 for
-every compared tensor, max |err| / rms(reference row) <= 0.1 for Y, dX and
-dr (a requantized intermediate code can flip next to a rounding boundary),
-weight gradients held to the Frobenius bar per expert.  Properties over the
-whole output: every value finite, empty experts' weight gradients exactly
-zero."""
+The FP64 oracle cannot run these sizes whole, so it runs on samples it can
+compute exactly:
+
+* stage-wise, at the spec's bar (relative Frobenius error <= 1e-2, max
+  |err| / rms(reference row) <= 5e-2): each GEMM against the oracle's GEMM
+  (FP64, dequantized operands) on the GPU's own MXFP8 codes, read back from
+  ctx and the workspaces -- Y and dX on the sampled rows, the requantized z
+  and dh codes (flip rate < 2e-3 against the oracle's SwiGLU forward and
+  backward of the recomputed h), dr, and whole rows of dW1 and dW2: every
+  row for small experts, 256-row slices (gate, up and tail rows) for the
+  largest expert, whose weight gradients contract over its 13047 (31457)
+  tokens, the longest K of the weight-gradient GEMMs.
+* end to end (the oracle sees only the bf16 inputs, in worker processes
+  while the GPU runs, see tests/_oracle_workers.py): whole experts and row
+  subsets of the largest expert, with the end-to-end bars of
+  test_gpu_mlp.py (max-row 0.1 for Y, dX and dr; weight gradients held to
+  the Frobenius bar).
+
+The Mixtral workload's split tail (the last round of output tiles of the
+down GEMM and the gate-up dgrad, cut along K) falls in the last expert, which
+is also the smallest and is compared whole.  Properties over the whole
+output: every value finite, empty experts' weight gradients exactly zero."""
 import multiprocessing as mp
 from concurrent.futures import ProcessPoolExecutor
 
@@ -29,24 +42,45 @@ from workloads import make_mlp_case
 
 pytestmark = pytest.mark.gpu
 
-REL_F, E2E_ROW_MAX = 1e-2, 0.1
+REL_F, ROW_MAX, E2E_ROW_MAX = 1e-2, 5e-2, 0.1
+FLIP_MAX = 2e-3
+# exact value of every E4M3 code (the oracle's decode), for a fast gather
+LUT = O.e4m3_decode(np.arange(256))
+
+
+def deq(codes, scales):
+    """The oracle's dequantization (code value times 2^(scale - 127) per
+    block of 32 along the last axis) as a table lookup, float64."""
+    codes = np.asarray(codes)
+    v = LUT[codes].reshape(codes.shape[:-1] + (codes.shape[-1] // 32, 32))
+    return (v * O.e8m0_decode(np.asarray(scales))[..., None]).reshape(codes.shape)
+
+
+def rows_of(mx, lo, hi):
+    """Codes and scales of rows [lo, hi) of a K-major MXFP8 view, on the CPU."""
+    return mx.codes[lo:hi].cpu().numpy(), mx.scales[lo:hi].cpu().numpy()
 
 
 def _np32(t):
     return t.float().cpu().numpy()
 
 
-def _check(name, got, ref, row=E2E_ROW_MAX):
-    rel, worst = O.parity_metrics(np.asarray(got, dtype=np.float64), ref)
-    print(f"  {name:24s} rel_fro={rel:.3e} max_row={worst:.3e}", flush=True)
-    assert rel <= REL_F and worst <= row, (name, rel, worst)
+def _check(name, got, ref, row=ROW_MAX, rel=REL_F):
+    r, worst = O.parity_metrics(np.asarray(got, dtype=np.float64), ref)
+    print(f"    {name:26s} rel_fro={r:.3e} max_row={worst:.3e}", flush=True)
+    assert r <= rel and worst <= row, (name, r, worst)
+
+
+def _rate(name, value):
+    print(f"    {name:26s} {value:.3e} (bound {FLIP_MAX:.0e})", flush=True)
+    assert value < FLIP_MAX, (name, value)
 
 
 def _jobs(case, samples):
-    """Oracle inputs of each sample: (label, expert, row indices or None)."""
+    """End-to-end oracle inputs of each sample (label, expert, rows)."""
     off = case.offsets.cpu().numpy()
     out = []
-    for label, e, rows in samples:
+    for label, e, rows, _ in samples:
         lo, hi = int(off[e]), int(off[e + 1])
         idx = np.arange(lo, hi) if rows is None else lo + np.asarray(rows)
         ti = torch.from_numpy(idx).to(case.X.device)
@@ -54,6 +88,66 @@ def _jobs(case, samples):
                     (_np32(case.X.index_select(0, ti)), _np32(case.W1[e]), _np32(case.W2[e]),
                      case.r.index_select(0, ti).cpu().numpy(), _np32(case.dY.index_select(0, ti)))))
     return out
+
+
+def _stagewise(case, e, idx, wrows, views, outs):
+    """Stage-wise checks of expert e on its sampled rows idx (global) and
+    weight-gradient rows wrows (None: all rows)."""
+    M, H, F = case.M, case.H, case.F
+    y, dx, dw1, dw2, dr = outs
+    v = views
+    off = case.offsets.cpu().numpy()
+    poff = v["poff"]
+    lo, n = int(off[e]), int(off[e + 1] - off[e])
+    p0 = int(poff[e])
+    ti = torch.from_numpy(idx).to(y.device)
+    sel = lambda mx: (mx.codes.index_select(0, ti).cpu().numpy(),
+                      mx.scales.index_select(0, ti).cpu().numpy())
+    r = case.r.index_select(0, ti).cpu().numpy().astype(np.float64)
+
+    # forward: h = X W1^T on the GPU's codes (the recompute reads the same
+    # codes), z requantized, Y = z W2^T
+    h = deq(*sel(v["xrow"])) @ deq(*rows_of(v["w1row"], e * 2 * F, (e + 1) * 2 * F)).T
+    a, b = h[:, :F], h[:, F:]
+    sg = O.sigmoid(a)
+    s = a * sg * b
+    zc, zs = sel(v["zrow"])
+    _rate("z flips", np.mean(zc != O.quantize_lastdim(r[:, None] * s)[0]))
+    _check("Y | z codes", _np32(y.index_select(0, ti)),
+           deq(zc, zs) @ deq(*rows_of(v["w2row"], e * H, (e + 1) * H)).T)
+    # backward: dz = dY W2 on the GPU's codes, SwiGLU backward of the exact h
+    dz = deq(*sel(v["dyrow"])) @ deq(*rows_of(v["w2col"], e * F, (e + 1) * F)).T
+    _check("dr", dr.index_select(0, ti).cpu().numpy().astype(np.float64), (dz * s).sum(axis=1))
+    ds = r[:, None] * dz
+    dh = np.concatenate([ds * b * sg * (1.0 + a * (1.0 - sg)), ds * a * sg], axis=1)
+    dhc, dhs = sel(v["dhrow"])
+    _rate("dh flips", np.mean(dhc != O.quantize_lastdim(dh)[0]))
+    _check("dX | dh codes", _np32(dx.index_select(0, ti)),
+           deq(dhc, dhs) @ deq(*rows_of(v["w1col"], e * H, (e + 1) * H)).T)
+
+    # weight gradients over the expert's whole token range, on the token-axis
+    # codes (columns p0 .. p0 + n of the padded axis)
+    if n == 0:
+        return
+    # p0 is a multiple of 128, so the expert's blocks start at column p0;
+    # decode whole blocks of the padded range, then keep the n real tokens
+    npad = (n + 31) // 32 * 32
+
+    def tokvals(mx, rows):
+        c = mx.codes[rows][:, p0:p0 + npad].cpu().numpy()
+        s = mx.scales[rows][:, p0 // 32:(p0 + npad) // 32].cpu().numpy()
+        return deq(c, s)[:, :n]
+
+    all_h, all_f, all_2f = slice(0, H), slice(0, F), slice(0, 2 * F)
+    r2 = all_h if wrows is None else wrows["dW2"]
+    r1 = all_2f if wrows is None else wrows["dW1"]
+    dyt = tokvals(v["dycol"], r2)                 # [rows of dW2, n]
+    zt = tokvals(v["zcol"], all_f)                # [F, n]
+    _check(f"dW2[{e}] rows | codes", _np32(dw2[e][r2]), dyt @ zt.T)
+    del dyt, zt
+    dht = tokvals(v["dhcol"], r1)                 # [rows of dW1, n]
+    xt = tokvals(v["xcol"], all_h)                # [H, n]
+    _check(f"dW1[{e}] rows | codes", _np32(dw1[e][r1]), dht @ xt.T)
 
 
 def _run_full(dev, case, samples):
@@ -66,8 +160,7 @@ def _run_full(dev, case, samples):
         # buffers start as 0xFF bytes: nothing unwritten may reach a result
         fws = torch.full((gm.fwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
         bws = torch.full((gm.bwd_ws_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
-        cbuf = torch.full((gm.ctx_bytes(M, H, F, E),), 255,
-                          dtype=torch.uint8, device=dev)
+        cbuf = torch.full((gm.ctx_bytes(M, H, F, E),), 255, dtype=torch.uint8, device=dev)
         y, ctx = gm.grouped_mlp_fwd(case.X, case.offsets, case.W1, case.W2, case.r, ws=fws,
                                     ctx_buf=cbuf)
         dx, dw1, dw2, dr = gm.grouped_mlp_bwd(case.dY, case.offsets, case.W1, case.W2, case.r,
@@ -79,26 +172,54 @@ def _run_full(dev, case, samples):
             if int(case.counts[e]) == 0:
                 assert not dw1[e].any() and not dw2[e].any(), f"empty expert {e}"
         print("  library outputs finite; empty experts' dW exactly zero", flush=True)
-        for (label, e, whole, idx, _), fut in zip(jobs, futs):
+        Mp = ctx.padded_rows
+        views = {"xrow": ctx.xrow(), "w1row": ctx.w1row(), "w2row": ctx.w2row(),
+                 "w1col": ctx.w1col(), "w2col": ctx.w2col(), "xcol": ctx.xcol(),
+                 "zcol": ctx.zcol(), "poff": ctx.padded_offsets().cpu().numpy(),
+                 "zrow": gm.ws_mx_view(fws, gm.MX_WS_ZROW, M, H, F, E, (M, F)),
+                 "dyrow": gm.ws_mx_view(bws, gm.MX_WS_DYROW, M, H, F, E, (M, H)),
+                 "dycol": gm.ws_mx_view(bws, gm.MX_WS_DYCOL, M, H, F, E, (H, Mp)),
+                 "dhrow": gm.ws_mx_view(bws, gm.MX_WS_DHROW, M, H, F, E, (M, 2 * F)),
+                 "dhcol": gm.ws_mx_view(bws, gm.MX_WS_DHCOL, M, H, F, E, (2 * F, Mp))}
+        outs = (y, dx, dw1, dw2, dr)
+        for (label, e, whole, idx, _), (_, _, _, wrows), fut in zip(jobs, samples, futs):
+            print(f" {label}: expert {e}, {len(idx)} rows", flush=True)
+            print("  stage-wise (GPU codes)", flush=True)
+            _stagewise(case, e, idx, wrows, views, outs)
+            print("  end to end (bf16 inputs)", flush=True)
             Yr, dXr, drr, dW1r, dW2r = fut.result()
             ti = torch.from_numpy(idx).to(dev)
-            print(f" {label}: expert {e}, {len(idx)} rows", flush=True)
-            _check("Y", _np32(y.index_select(0, ti)), Yr)
-            _check("dX", _np32(dx.index_select(0, ti)), dXr)
-            _check("dr", dr.index_select(0, ti).cpu().numpy(), drr)
+            _check("Y e2e", _np32(y.index_select(0, ti)), Yr, row=E2E_ROW_MAX)
+            _check("dX e2e", _np32(dx.index_select(0, ti)), dXr, row=E2E_ROW_MAX)
+            _check("dr e2e", dr.index_select(0, ti).cpu().numpy(), drr, row=E2E_ROW_MAX)
             if whole:
-                _check("dW1[e]", _np32(dw1[e]), dW1r, row=np.inf)
-                _check("dW2[e]", _np32(dw2[e]), dW2r, row=np.inf)
+                _check("dW1[e] e2e", _np32(dw1[e]), dW1r, row=np.inf)
+                _check("dW2[e] e2e", _np32(dw2[e]), dW2r, row=np.inf)
+
+
+def _big_rows(n):
+    return list(range(16)) + list(range(n // 2, n // 2 + 16)) + list(range(n - 32, n))
+
+
+def _wslices(H, F):
+    """256 rows of each weight gradient of the largest expert: the first and
+    last 64 gate rows, the first and last 64 up rows of dW1 [2F, H]; the
+    first, a middle and the last rows of dW2 [H, F]."""
+    dw1 = np.r_[0:64, F - 64:F, F:F + 64, 2 * F - 64:2 * F]
+    dw2 = np.r_[0:96, H // 2:H // 2 + 64, H - 96:H]
+    return {"dW1": dw1, "dW2": dw2}
 
 
 def test_mixtral_fwd_bwd_full_size(dev):
     case = make_mlp_case("mixtral_fwd_bwd", seed=0, device=dev)
     counts = [int(c) for c in case.counts]
     small, big = int(np.argmin(counts)), int(np.argmax(counts))
-    n = counts[big]
-    rows = list(range(16)) + list(range(n // 2, n // 2 + 16)) + list(range(n - 32, n))
-    _run_full(dev, case, [("smallest expert, whole", small, None),
-                          ("largest expert, 64 rows", big, rows)])
+    # the split tail of the down GEMM and the gate-up dgrad is in the last
+    # expert, the smallest one here, compared whole
+    assert small == case.E - 1
+    _run_full(dev, case, [("smallest expert, whole", small, None, None),
+                          ("largest expert, 64 rows; dW row slices", big, _big_rows(counts[big]),
+                           _wslices(case.H, case.F))])
 
 
 def test_fine_grained_64e_full_size(dev):
@@ -109,8 +230,7 @@ def test_fine_grained_64e_full_size(dev):
     small = min(nz, key=lambda e: counts[e])
     big = max(nz, key=lambda e: counts[e])
     mid = sorted(nz, key=lambda e: counts[e])[len(nz) // 2]
-    n = counts[big]
-    rows = list(range(16)) + list(range(n // 2, n // 2 + 16)) + list(range(n - 32, n))
-    _run_full(dev, case, [("smallest expert, whole", small, None),
-                          ("median expert, whole", mid, None),
-                          ("largest expert, 64 rows", big, rows)])
+    _run_full(dev, case, [("smallest expert, whole", small, None, None),
+                          ("median expert, whole", mid, None, None),
+                          ("largest expert, 64 rows; dW row slices", big,
+                           _big_rows(counts[big]), _wslices(case.H, case.F))])

@@ -207,3 +207,14 @@ def test_round_bf16_matches_torch():
     ref = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
     ours = O.round_bf16(v32.astype(np.float64))
     assert np.array_equal(ours, ref)
+
+
+def test_table_dequantization_of_the_full_size_tests():
+    """The full-size GPU tests dequantize with a 256-entry table of the
+    oracle's decode; it equals the oracle's dequantization."""
+    from tests.test_gpu_full_size import deq
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, (7, 96)).astype(np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0                  # no NaN codes
+    scales = rng.integers(0, 255, (7, 3)).astype(np.uint8)
+    assert np.array_equal(deq(codes, scales), O.dequantize_lastdim(codes, scales))
