@@ -56,6 +56,7 @@ _SIGS = {
     "moe_router": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "moe_route_ws_bytes": (_SZ, [_I64, _I32, _I32]),
     "moe_route_plan": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_plan_noalloc": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_permute_quantize": (_I32, [_P, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _P, _P, _I64,
                                     _P, _P]),
     "moe_combine": (_I32, [_P, _I64, _I64, _P, _I64, _I32, _P, _P, _P]),
@@ -518,6 +519,30 @@ def route_plan(ids: torch.Tensor, E: int, w: Optional[torch.Tensor] = None):
     return offsets, row_of, tok_of, r_sorted
 
 
+def route_plan_noalloc(ids: torch.Tensor, E: int, w: Optional[torch.Tensor] = None):
+    """``route_plan`` through the entry point that allocates nothing on the
+    device: the library's own scratch replaces the workspace (calls that
+    overlap on one GPU race; see include/mxmoe.h).  The outputs are still
+    allocated here, by torch."""
+    _need(ids, torch.int32, "ids")
+    dev = ids.device
+    if ids.dim() != 2:
+        raise ValueError("ids must be [T, k]")
+    T, k = ids.shape
+    if w is not None:
+        _need(w, torch.float32, "w", dev)
+        if tuple(w.shape) != (T, k):
+            raise ValueError("w must match ids")
+    offsets = torch.empty(E + 1, dtype=torch.int64, device=dev)
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tok_of = torch.empty(T * k, dtype=torch.int32, device=dev)
+    r_sorted = torch.empty(T * k, dtype=torch.float32, device=dev) if w is not None else None
+    st = lib().moe_route_plan_noalloc(_ptr(ids), T, k, E, _ptr(w), _ptr(offsets), _ptr(row_of),
+                                      _ptr(tok_of), _ptr(r_sorted), _stream(dev))
+    _check("moe_route_plan_noalloc", st)
+    return offsets, row_of, tok_of, r_sorted
+
+
 def permute_quantize(x: torch.Tensor, tok_of: torch.Tensor, offsets: torch.Tensor, M: int,
                      rowwise: bool = True, colwise: bool = True):
     """MXFP8 copies of the sorted rows x[tok_of[row]] (x bf16 [T, H]), made
@@ -590,5 +615,6 @@ def combine_bwd(dout: torch.Tensor, row_of: torch.Tensor, M: int,
 __all__ = ["lib", "last_error", "MxError", "MxTensor", "MlpCtx", "mxfp8_quantize",
            "grouped_linear_fwd", "fp8_tensor_quantize", "grouped_linear_fwd_fp8", "Fp8Tensor",
            "grouped_mlp_fwd", "grouped_mlp_bwd", "padded_rows_bound",
-           "ws_mx_view", "ctx_bytes", "fwd_ws_bytes", "bwd_ws_bytes", "router", "route_plan", "permute_quantize",
+           "ws_mx_view", "ctx_bytes", "fwd_ws_bytes", "bwd_ws_bytes", "router", "route_plan",
+           "route_plan_noalloc", "permute_quantize",
            "combine", "combine_bwd"]

@@ -227,6 +227,36 @@ hipError_t gemm(const mx::GemmProblem& p, mx::Epi e, double flops, hipStream_t s
                  [&] { return mx::launch_split_fixup(p, s); });
 }
 
+// Host validation shared by the two plan entry points.
+mx_status check_route_plan(const char* fn, const int32_t* d_ids, int64_t T, int32_t k, int32_t E,
+                           const float* d_w, int64_t* d_offsets, int32_t* d_row_of,
+                           int32_t* d_tok_of, float* d_r_sorted) {
+    if (T < 0 || k < 1 || k > 64 || E < 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: bad sizes T=%lld k=%d E=%d", fn, (long long)T, k, E);
+    if (E > mx::kMaxGroups)
+        return fail(MX_ERR_UNSUPPORTED, "%s: E=%d exceeds %d", fn, E, mx::kMaxGroups);
+    if (T * k > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "%s: T*k=%lld rows exceed int32", fn,
+                    (long long)(T * k));
+    if (!d_offsets || (T > 0 && (!d_ids || !d_row_of || !d_tok_of)))
+        return fail(MX_ERR_INVALID_ARG, "%s: NULL argument", fn);
+    if ((d_w == nullptr) != (d_r_sorted == nullptr))
+        return fail(MX_ERR_INVALID_ARG, "%s: d_w and d_r_sorted go together", fn);
+    return MX_OK;
+}
+
+mx_status launch_plan(const int32_t* d_ids, int64_t T, int32_t k, int32_t E, const float* d_w,
+                      int64_t* d_offsets, int32_t* d_row_of, int32_t* d_tok_of,
+                      float* d_r_sorted, int32_t* hist, hipStream_t s) {
+    return launched(timed("route_plan", 16.0 * T * k, MX_WORK_BYTES, s,
+                          [&] {
+                              return mx::launch_route_plan(d_ids, T, k, E, d_w, d_offsets,
+                                                           d_row_of, d_tok_of, d_r_sorted, hist,
+                                                           s);
+                          }),
+                    "route_plan");
+}
+
 }  // namespace
 
 // ---- misc -------------------------------------------------------------------
@@ -792,30 +822,39 @@ mx_status moe_route_plan(const int32_t* d_ids, int64_t T, int32_t k, int32_t E, 
                          int64_t* d_offsets, int32_t* d_row_of, int32_t* d_tok_of,
                          float* d_r_sorted, void* ws, size_t ws_bytes, mx_stream_t stream) {
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (T < 0 || k < 1 || k > 64 || E < 1)
-        return fail(MX_ERR_INVALID_ARG, "moe_route_plan: bad sizes T=%lld k=%d E=%d",
-                    (long long)T, k, E);
-    if (E > mx::kMaxGroups)
-        return fail(MX_ERR_UNSUPPORTED, "moe_route_plan: E=%d exceeds %d", E, mx::kMaxGroups);
-    if (T * k > kI32Max)
-        return fail(MX_ERR_UNSUPPORTED, "moe_route_plan: T*k=%lld rows exceed int32",
-                    (long long)(T * k));
-    if (!d_offsets || !ws || (T > 0 && (!d_ids || !d_row_of || !d_tok_of)))
-        return fail(MX_ERR_INVALID_ARG, "moe_route_plan: NULL argument");
-    if ((d_w == nullptr) != (d_r_sorted == nullptr))
-        return fail(MX_ERR_INVALID_ARG, "moe_route_plan: d_w and d_r_sorted go together");
+    mx_status st = check_route_plan("moe_route_plan", d_ids, T, k, E, d_w, d_offsets, d_row_of,
+                                    d_tok_of, d_r_sorted);
+    if (st != MX_OK) return st;
+    if (!ws) return fail(MX_ERR_INVALID_ARG, "moe_route_plan: NULL argument");
     if (ws_bytes < moe_route_ws_bytes(T, k, E))
         return fail(MX_ERR_WORKSPACE, "moe_route_plan: ws needs %zu bytes, got %zu",
                     moe_route_ws_bytes(T, k, E), ws_bytes);
     if (!aligned(ws, 4))
         return fail(MX_ERR_INVALID_ARG, "moe_route_plan: ws must be 4-byte aligned");
-    return launched(timed("route_plan", 16.0 * T * k, MX_WORK_BYTES, s,
-                          [&] {
-                              return mx::launch_route_plan(d_ids, T, k, E, d_w, d_offsets,
-                                                           d_row_of, d_tok_of, d_r_sorted,
-                                                           static_cast<int32_t*>(ws), s);
-                          }),
-                    "route_plan");
+    return launch_plan(d_ids, T, k, E, d_w, d_offsets, d_row_of, d_tok_of, d_r_sorted,
+                       static_cast<int32_t*>(ws), s);
+}
+
+mx_status moe_route_plan_noalloc(const int32_t* d_ids, int64_t T, int32_t k, int32_t E,
+                                 const float* d_w, int64_t* d_offsets, int32_t* d_row_of,
+                                 int32_t* d_tok_of, float* d_r_sorted, mx_stream_t stream) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    mx_status st = check_route_plan("moe_route_plan_noalloc", d_ids, T, k, E, d_w, d_offsets,
+                                    d_row_of, d_tok_of, d_r_sorted);
+    if (st != MX_OK) return st;
+    const int64_t need = mx::route_chunks(T * k) * E;
+    if (need > mx::kPlanScratchInts)
+        return fail(MX_ERR_UNSUPPORTED,
+                    "moe_route_plan_noalloc: ceil(T*k/256)*E = %lld counters exceed the "
+                    "library's scratch of %lld (use moe_route_plan with a workspace)",
+                    (long long)need, (long long)mx::kPlanScratchInts);
+    int32_t* scratch = nullptr;
+    const hipError_t e = mx::route_plan_scratch(&scratch);
+    if (e != hipSuccess)
+        return fail(MX_ERR_LAUNCH, "moe_route_plan_noalloc: scratch lookup failed: %s",
+                    hipGetErrorString(e));
+    return launch_plan(d_ids, T, k, E, d_w, d_offsets, d_row_of, d_tok_of, d_r_sorted, scratch,
+                       s);
 }
 
 mx_status moe_permute_quantize(const void* x, int64_t T, int64_t H, const int32_t* d_tok_of,

@@ -132,6 +132,11 @@ hipError_t launch_bf16_grouped(const uint16_t* x, const int64_t* offs, int G,
 // r_sorted [M] = w of each row when w is given.  hist: route_chunks(T*k) * E
 // int32 of scratch.
 int64_t route_chunks(int64_t n);
+// The library-owned plan scratch of the no-allocation entry point:
+// kPlanScratchInts int32 per GPU (4 MiB); *out = its device address on the
+// current device (looked up once per device).
+constexpr int64_t kPlanScratchInts = (int64_t)1 << 20;
+hipError_t route_plan_scratch(int32_t** out);
 // Top-k of logits [T][E] (E <= kMaxGroups, 1 <= k <= min(E, 64)) and the
 // softmax of the k selected: ids [T][k] in selection order, w [T][k].
 hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,

@@ -22,10 +22,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "mx_device.h"
 
 namespace mx {
+
+// Library-owned scratch of the plan for callers that cannot allocate
+// (moe_route_plan_noalloc): the per-chunk expert counts, kPlanScratchInts
+// int32.  Each GPU holds its own copy for the life of the process; in host
+// code this name is only a stand-in for the device symbol, so kernels are
+// given the address route_plan_scratch() looks up.
+static __device__ __align__(256) int32_t scratch[kPlanScratchInts];
+
 namespace {
 
 constexpr int kChunk = 256;   // routing slots per workgroup in the plan
@@ -249,6 +259,26 @@ combine_dw_kernel(const uint16_t* __restrict__ dout, const uint16_t* __restrict_
 }  // namespace
 
 int64_t route_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
+
+hipError_t route_plan_scratch(int32_t** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int32_t* ptrs[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        // once per device, with that device current: this GPU's copy
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptrs[dev] = static_cast<int32_t*>(p);
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_router(const float* logits, int64_t T, int E, int k, int32_t* ids, float* w,
                          hipStream_t s) {

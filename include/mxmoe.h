@@ -378,6 +378,25 @@ mx_status moe_route_plan(const int32_t* d_ids, int64_t T, int32_t k, int32_t E,
                          const float* d_w, int64_t* d_offsets, int32_t* d_row_of,
                          int32_t* d_tok_of, float* d_r_sorted, void* ws,
                          size_t ws_bytes, mx_stream_t stream);
+/*
+ * moe_route_plan_noalloc -- moe_route_plan without a workspace, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, outputs
+ * and checks as moe_route_plan, minus ws / ws_bytes.  The per-chunk counts
+ * go to a scratch array the library owns: 2^20 int32 (4 MiB) per GPU, held
+ * from the first call on that GPU until the process ends; nothing is
+ * allocated or freed by the call.  Limit: ceil(T*k/256) * E <= 2^20 (for
+ * example T*k <= 33,554,432 at E = 8, or T*k <= 262,144 at E = 1024);
+ * larger plans return MX_ERR_UNSUPPORTED (use moe_route_plan).  Every call
+ * on one GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ * different streams, or from threads whose calls are not ordered) race and
+ * give undefined results; calls on one stream are ordered and safe.  The
+ * scratch needs no clearing (every counter a call reads it writes first).
+ */
+mx_status moe_route_plan_noalloc(const int32_t* d_ids, int64_t T, int32_t k, int32_t E,
+                                 const float* d_w, int64_t* d_offsets,
+                                 int32_t* d_row_of, int32_t* d_tok_of,
+                                 float* d_r_sorted, mx_stream_t stream);
 mx_status moe_permute_quantize(const void* x, int64_t T, int64_t H,
                                const int32_t* d_tok_of, int64_t M,
                                const int64_t* d_offsets, int32_t E,
