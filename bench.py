@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline step only (and its launch-record pass): no side "
+                         "figures, for short profiler runs")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many "
                          "MiB (read + write), the reference dispatch that scales "
@@ -545,6 +548,17 @@ def main():
                     ("tflops" if v["unit"] == 0 else "gbs"):
                         round(v["work"] / (v["ms"] / 1e3) / (1e12 if v["unit"] == 0 else 1e9), 2)}
                 for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["ms"])}
+
+    if args.headline_only:
+        out = {"metric": "GroupedMLP fwd+bwd tokens/s & TFLOP/s (MXFP8), Mixtral-8x7B expert shape",
+               "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup,
+               "ms_per_step": round(elapsed / args.steps * 1e3, 4), "gpu_ms_per_step": stats,
+               "tflops": round(flops_step * args.steps / elapsed / 1e12, 2),
+               "roofline": roofline(agg), "kernels": kernels_of(agg, args.steps),
+               "note": "headline only (--headline-only)"}
+        print(json.dumps(out), flush=True)
+        return 0
 
     # ---- the save-h mode beside it ----
     nside = max(args.steps // 2, 3)
