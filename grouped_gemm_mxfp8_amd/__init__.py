@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmxmoe.so")
+# MXMOE_LIB names another build of the same library (e.g. a host-sanitizer
+# build); by default the in-tree one
+LIB_PATH = os.environ.get("MXMOE_LIB") or os.path.join(HERE, "libmxmoe.so")
 
 MX_DTYPE_BF16 = 0
 MX_DTYPE_MXFP8 = 1
@@ -40,6 +42,7 @@ _SIGS = {
     "mx_last_error": (ctypes.c_char_p, []),
     "mx_version": (ctypes.c_char_p, []),
     "mx_padded_rows_bound": (_I64, [_I64, _I32, _I32]),
+    "mx_validate_offsets": (_I32, [_P, _I32, _I64]),
     "mxfp8_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _I32, _P, _P, _I64, _P, _P]),
     "grouped_linear_fwd": (_I32, [_I32, _P, _P, _P, _I32, _I64, _P, _P, _I64, _I64, _P, _P, _P]),
     "fp8_tensor_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _I32, _P, _P, _P, _P]),

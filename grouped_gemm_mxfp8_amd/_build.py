@@ -61,6 +61,40 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host AddressSanitizer on the C-ABI layer (api.cpp holds only host code);
+# each sanitizer flag applies to the host compilation only.
+HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_asan(dest: str) -> str:
+    """libmxmoe.so with api.cpp built under host AddressSanitizer, into
+    ``dest``; the kernel objects are the ones build() made (compiled first if
+    missing or older than their source).  Load it with the sanitizer runtime
+    preloaded (LD_PRELOAD of libasan) and MXMOE_LIB pointing at it."""
+    os.makedirs(OBJ, exist_ok=True)
+    os.makedirs(dest, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        if src == "api.cpp":
+            continue
+        obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+        if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(os.path.join(CSRC, src)):
+            obj = _compile(src)
+        objs.append(obj)
+    api_obj = os.path.join(dest, "api_asan.o")
+    cmd = [hipcc(), *FLAGS, "-g", *HOST_ASAN, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    lib = os.path.join(dest, "libmxmoe.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *HOST_ASAN, api_obj, *objs,
+           "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -7,6 +7,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -94,6 +95,51 @@ struct Carver {
 };
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---- MX_CHECK: validation of device-side offsets --------------------------
+// The offsets arrays live on the device, so the host validation above cannot
+// see them; a bad array (decreasing, or not ending at the row count) is
+// undefined behaviour for the kernels.  With MX_CHECK=1 in the environment,
+// every entry point that takes device offsets copies them to the host on its
+// stream, waits for the copy, and checks them before it launches anything.
+// Off (the default) the library never synchronises.
+bool check_enabled() {
+    const char* v = std::getenv("MX_CHECK");
+    return v && v[0] == '1' && v[1] == '\0';
+}
+
+// offsets [G+1] in host memory: non-decreasing; from_zero: offsets[0] == 0;
+// end >= 0: offsets[G] == end; else 0 <= offsets[0] and offsets[G] <= -end - 1
+mx_status check_offsets_host(const char* fn, const int64_t* h, int32_t G, int64_t end,
+                             bool from_zero) {
+    if (from_zero ? h[0] != 0 : h[0] < 0)
+        return fail(MX_ERR_INVALID_ARG, "%s: offsets[0] = %lld, expected %s", fn, (long long)h[0],
+                    from_zero ? "0" : ">= 0");
+    for (int32_t g = 0; g < G; ++g)
+        if (h[g + 1] < h[g])
+            return fail(MX_ERR_INVALID_ARG, "%s: offsets decrease at group %d (%lld > %lld)", fn, g,
+                        (long long)h[g], (long long)h[g + 1]);
+    if (end >= 0 && h[G] != end)
+        return fail(MX_ERR_INVALID_ARG, "%s: offsets[%d] = %lld, expected the row count %lld", fn,
+                    G, (long long)h[G], (long long)end);
+    if (end < 0 && h[G] > -end - 1)
+        return fail(MX_ERR_INVALID_ARG, "%s: offsets[%d] = %lld past the %lld rows", fn, G,
+                    (long long)h[G], (long long)(-end - 1));
+    return MX_OK;
+}
+
+mx_status check_device_offsets(const char* fn, const int64_t* d_offsets, int32_t G, int64_t end,
+                               bool from_zero, hipStream_t s) {
+    if (!check_enabled()) return MX_OK;
+    std::vector<int64_t> h((size_t)G + 1);
+    hipError_t e = hipMemcpyAsync(h.data(), d_offsets, h.size() * sizeof(int64_t),
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return fail(MX_ERR_LAUNCH, "%s: MX_CHECK could not read the offsets: %s", fn,
+                    hipGetErrorString(e));
+    return check_offsets_host(fn, h.data(), G, end, from_zero);
+}
 
 int64_t padded_bound(int64_t M, int64_t G, int64_t align) {
     return (M + G * (align - 1)) / align * align;
@@ -338,6 +384,10 @@ mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
         if (bound / 128 > 65535 || batch > 65535)
             return fail(MX_ERR_UNSUPPORTED, "mxfp8_quantize: too many rows for one launch");
     }
+    if (d_offsets) {
+        const mx_status cs = check_device_offsets("mxfp8_quantize", d_offsets, G, R, true, s);
+        if (cs != MX_OK) return cs;
+    }
     if (batch * R == 0 || C == 0) {
         if (want_col && d_offsets)
             return launched(timed("padded_offsets", 16.0 * (G + 1), MX_WORK_BYTES, s,
@@ -385,6 +435,10 @@ mx_status grouped_linear_fwd(int32_t dtype, const void* x, const uint8_t* x_scal
                     E, (long long)M, (long long)N, (long long)K);
     if (!aligned(x, 16) || !aligned(w, 16))
         return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: x and w must be 16-byte aligned");
+    if (dtype == MX_DTYPE_BF16 || dtype == MX_DTYPE_MXFP8) {
+        const mx_status cs = check_device_offsets("grouped_linear_fwd", d_offsets, E, M, true, s);
+        if (cs != MX_OK) return cs;
+    }
     if (dtype == MX_DTYPE_BF16) {
         if (x_scales || w_scales)
             return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: bf16 takes no scales");
@@ -449,6 +503,11 @@ mx_status fp8_tensor_quantize(const void* x, int64_t batch, int64_t R, int64_t C
                     "fp8_tensor_quantize: x and codes must be 16-byte aligned, amax and "
                     "scale_inv 4-byte aligned");
     const int64_t rows = batch * R;
+    if (d_offsets) {
+        const mx_status cs = check_device_offsets("fp8_tensor_quantize", d_offsets, G, -rows - 1,
+                                                  false, s);
+        if (cs != MX_OK) return cs;
+    }
     return launched(timed("fp8_tensor_quant", 5.0 * rows * C, MX_WORK_BYTES, s,
                           [&] {
                               return mx::launch_fp8_tensor_quant(
@@ -476,6 +535,10 @@ mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
                     "grouped_linear_fwd_fp8: needs K %% 128 == 0 and N %% 32 == 0");
     if (N * K > kI32Max || 256 * K > kI32Max)
         return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd_fp8: operand too large");
+    {
+        const mx_status cs = check_device_offsets("grouped_linear_fwd_fp8", d_offsets, E, M, true, s);
+        if (cs != MX_OK) return cs;
+    }
     if (M == 0) return ok();
     mx::GemmProblem p{};
     p.kgroup = false;
@@ -572,7 +635,8 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
     const bool sh = save_h_mode(flags);
     if (flags & ~kFwdFlags)
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_fwd: unknown flags 0x%x", flags);
-    if (!x || !d_offsets || (!reuse && (!w1 || !w2)) || !d_r || !y || !ctx || !ws)
+    // the [M, *] tensors may be NULL when M == 0
+    if (!d_offsets || (!reuse && (!w1 || !w2)) || !ctx || !ws || (M > 0 && (!x || !d_r || !y)))
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_fwd: NULL argument");
     MlpDims d;
     mx_status st = check_mlp_dims(M, H, F, E, &d);
@@ -589,6 +653,10 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
         !aligned(ws, kAlign))
         return fail(MX_ERR_INVALID_ARG,
                     "grouped_mlp_fwd: tensors must be 16-byte and ctx/ws 256-byte aligned");
+    {
+        const mx_status cs = check_device_offsets("grouped_mlp_fwd", d_offsets, E, M, true, s);
+        if (cs != MX_OK) return cs;
+    }
     // with reuse the weight copies in ctx are the previous call's
     uint8_t* cb = static_cast<uint8_t*>(ctx);
     uint8_t* wb = static_cast<uint8_t*>(ws);
@@ -685,7 +753,9 @@ mx_status grouped_mlp_bwd_ex(const void* dy, const int64_t* d_offsets, int32_t E
     if (flags & ~(uint32_t)MX_MLP_SAVE_H)
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_bwd: unknown flags 0x%x", flags);
     const bool sh = save_h_mode(flags);
-    if (!dy || !d_offsets || !w1 || !w2 || !d_r || !ctx || !dx || !dw1 || !dw2 || !d_dr || !ws)
+    // the [M, *] tensors may be NULL when M == 0
+    if (!d_offsets || !w1 || !w2 || !ctx || !dw1 || !dw2 || !ws ||
+        (M > 0 && (!dy || !d_r || !dx || !d_dr)))
         return fail(MX_ERR_INVALID_ARG, "grouped_mlp_bwd: NULL argument");
     MlpDims d;
     mx_status st = check_mlp_dims(M, H, F, E, &d);
@@ -702,6 +772,10 @@ mx_status grouped_mlp_bwd_ex(const void* dy, const int64_t* d_offsets, int32_t E
         !aligned(ws, kAlign))
         return fail(MX_ERR_INVALID_ARG,
                     "grouped_mlp_bwd: tensors must be 16-byte and ctx/ws 256-byte aligned");
+    {
+        const mx_status cs = check_device_offsets("grouped_mlp_bwd", d_offsets, E, M, true, s);
+        if (cs != MX_OK) return cs;
+    }
     const uint8_t* cb = static_cast<const uint8_t*>(ctx);
     uint8_t* wb = static_cast<uint8_t*>(ws);
     const int64_t* poff = reinterpret_cast<const int64_t*>(cb + C.poff);
@@ -893,6 +967,10 @@ mx_status moe_permute_quantize(const void* x, int64_t T, int64_t H, const int32_
                     (long long)col_ld, (long long)bound);
     if (bound / 128 > 65535)
         return fail(MX_ERR_UNSUPPORTED, "moe_permute_quantize: too many rows for one launch");
+    {
+        const mx_status cs = check_device_offsets("moe_permute_quantize", d_offsets, E, M, true, s);
+        if (cs != MX_OK) return cs;
+    }
     hipError_t e = timed("padded_offsets", 16.0 * (E + 1), MX_WORK_BYTES, s, [&] {
         return mx::launch_padded_offsets(d_offsets, E, d_padded_offsets, s);
     });
@@ -951,6 +1029,14 @@ mx_status moe_combine_bwd(const void* dout, int64_t T, int64_t H, int32_t k,
                                   static_cast<uint16_t*>(dy), d_dw, s);
                           }),
                     "combine_bwd");
+}
+
+mx_status mx_validate_offsets(const int64_t* h_offsets, int32_t G, int64_t M) {
+    if (!h_offsets || G < 1 || M < 0)
+        return fail(MX_ERR_INVALID_ARG, "mx_validate_offsets: NULL offsets or bad sizes G=%d M=%lld",
+                    G, (long long)M);
+    const mx_status st = check_offsets_host("mx_validate_offsets", h_offsets, G, M, true);
+    return st == MX_OK ? ok() : st;
 }
 
 mx_status mx_profile_begin(int32_t capacity) {

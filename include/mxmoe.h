@@ -47,7 +47,12 @@
  *   - Errors: host-side validation returns a status and never touches the
  *     device; mx_last_error() gives the thread's last message.  Kernel launch
  *     failures return MX_ERR_LAUNCH.  Device-side contract violations (bad
- *     offsets) are undefined behaviour.
+ *     offsets) are undefined behaviour, unless MX_CHECK=1 is set in the
+ *     environment: then every entry point that takes device offsets copies
+ *     them to the host on its stream, waits for the copy (the one case where
+ *     the library synchronises) and returns MX_ERR_INVALID_ARG, launching
+ *     nothing, if they do not start at 0, decrease, or do not end at the row
+ *     count (fp8_tensor_quantize: start >= 0, end <= rows).
  *   - Every call is re-entrant; calls on one stream are ordered.
  */
 #ifndef MXMOE_H
@@ -78,6 +83,12 @@ const char* mx_last_error(void);
 
 /* Library version string. */
 const char* mx_version(void);
+
+/* Host-side check of a per-group offsets array in HOST memory: offsets[0] ==
+ * 0, non-decreasing, offsets[G] == M.  MX_OK, or MX_ERR_INVALID_ARG with the
+ * first violation in mx_last_error().  This is what MX_CHECK=1 runs on a copy
+ * of the device offsets an entry point is given. */
+mx_status mx_validate_offsets(const int64_t* h_offsets, int32_t G, int64_t M);
 
 /* Upper bound of the padded length of G row groups holding M rows in total,
  * each padded to a multiple of `align`: the leading dimension the caller
@@ -177,7 +188,8 @@ mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
  *   Y_e = Q(z) . Q(W2_e)^T          [rows of e, H]    (blocks along F)
  *
  *   x    bf16 [M][H];  w1 bf16 [E][2F][H] (rows [0,F) gate, [F,2F) up);
- *   w2   bf16 [E][H][F];  d_r fp32 [M];  y bf16 [M][H].
+ *   w2   bf16 [E][H][F];  d_r fp32 [M];  y bf16 [M][H].  With M == 0, x, d_r
+ *        and y may be NULL (the weights are still quantized into ctx).
  *   ctx  saved-for-backward buffer of grouped_mlp_ctx_bytes(.., 0) bytes,
  *        written here and read by grouped_mlp_bwd (opaque; 256-byte
  *        aligned): the MXFP8 copies of w1 and w2 (rowwise and columnwise),
@@ -246,7 +258,8 @@ mx_status grouped_mlp_fwd_ex(const void* x, const int64_t* d_offsets, int32_t E,
  * Experts with no rows get dW1_e = dW2_e = 0.
  *
  *   dy bf16 [M][H]; outputs dx bf16 [M][H], dw1 bf16 [E][2F][H],
- *   dw2 bf16 [E][H][F], d_dr fp32 [M].  Same sizes, x-free: the forward's
+ *   dw2 bf16 [E][H][F], d_dr fp32 [M] (dy, d_r, dx and d_dr may be NULL when
+ *   M == 0; dw1 and dw2 are then all zeros).  Same sizes, x-free: the forward's
  *   ctx holds what is needed, including the quantized copies of w1 and w2
  *   made by the forward (w1 and w2 must be the tensors given to the forward
  *   that wrote ctx; the backward only checks them for NULL and alignment).

@@ -297,3 +297,36 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(gm, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         gm.lib()
+
+
+def test_validate_offsets_on_host_crafted_arrays(mxlib):
+    """The offsets check that MX_CHECK=1 runs on a copy of the device offsets:
+    start at 0, never decrease, end at the row count."""
+    import numpy as np
+
+    def v(arr, M):
+        a = np.ascontiguousarray(np.asarray(arr, dtype=np.int64))
+        return mxlib.mx_validate_offsets(a.ctypes.data_as(ctypes.c_void_p), len(a) - 1, M)
+
+    assert v([0, 3, 3, 10], 10) == MX_OK
+    assert v([0, 0], 0) == MX_OK                        # one empty group
+    assert v([0, 0, 0, 0], 0) == MX_OK
+    assert v([1, 3, 10], 10) == MX_ERR_INVALID_ARG      # does not start at 0
+    assert "offsets[0]" in _err(mxlib)
+    assert v([0, 5, 4, 10], 10) == MX_ERR_INVALID_ARG   # decreases
+    assert "decrease at group 1" in _err(mxlib)
+    assert v([0, 3, 9], 10) == MX_ERR_INVALID_ARG       # does not end at M
+    assert "expected the row count 10" in _err(mxlib)
+    assert v([0, 3, 11], 10) == MX_ERR_INVALID_ARG
+    assert v([0, -1, 10], 10) == MX_ERR_INVALID_ARG
+    assert mxlib.mx_validate_offsets(None, 3, 10) == MX_ERR_INVALID_ARG
+    rng = np.random.default_rng(1)
+    for _ in range(100):
+        counts = rng.integers(0, 50, int(rng.integers(1, 40)))
+        off = np.concatenate([[0], np.cumsum(counts)])
+        assert v(off, int(off[-1])) == MX_OK
+        if len(counts) > 1 and counts.sum() > 0:
+            i = int(rng.integers(1, len(off) - 1))
+            bad = off.copy()
+            bad[i] = off[-1] + 1                         # past the end: decreases after it
+            assert v(bad, int(off[-1])) == MX_ERR_INVALID_ARG

@@ -71,9 +71,14 @@ def _check(name, got, ref, row=ROW_MAX, rel=REL_F):
     assert r <= rel and worst <= row, (name, r, worst)
 
 
-def _rate(name, value):
-    print(f"    {name:26s} {value:.3e} (bound {FLIP_MAX:.0e})", flush=True)
-    assert value < FLIP_MAX, (name, value)
+def _rate(name, mismatch):
+    """Flipped requantized codes (boolean array): at most FLIP_MAX of them
+    plus Poisson slack, as in test_gpu_mlp.py."""
+    n = mismatch.size
+    flips = int(np.count_nonzero(mismatch))
+    limit = FLIP_MAX * n + 4.0 * np.sqrt(FLIP_MAX * n) + 3.0
+    print(f"    {name:26s} {flips / n:.3e} ({flips} of {n}; at most {limit:.0f})", flush=True)
+    assert flips <= limit, (name, flips, n)
 
 
 def _jobs(case, samples):
@@ -112,7 +117,7 @@ def _stagewise(case, e, idx, wrows, views, outs):
     sg = O.sigmoid(a)
     s = a * sg * b
     zc, zs = sel(v["zrow"])
-    _rate("z flips", np.mean(zc != O.quantize_lastdim(r[:, None] * s)[0]))
+    _rate("z flips", zc != O.quantize_lastdim(r[:, None] * s)[0])
     _check("Y | z codes", _np32(y.index_select(0, ti)),
            deq(zc, zs) @ deq(*rows_of(v["w2row"], e * H, (e + 1) * H)).T)
     # backward: dz = dY W2 on the GPU's codes, SwiGLU backward of the exact h
@@ -121,7 +126,7 @@ def _stagewise(case, e, idx, wrows, views, outs):
     ds = r[:, None] * dz
     dh = np.concatenate([ds * b * sg * (1.0 + a * (1.0 - sg)), ds * a * sg], axis=1)
     dhc, dhs = sel(v["dhrow"])
-    _rate("dh flips", np.mean(dhc != O.quantize_lastdim(dh)[0]))
+    _rate("dh flips", dhc != O.quantize_lastdim(dh)[0])
     _check("dX | dh codes", _np32(dx.index_select(0, ti)),
            deq(dhc, dhs) @ deq(*rows_of(v["w1col"], e * H, (e + 1) * H)).T)
 
@@ -234,3 +239,25 @@ def test_fine_grained_64e_full_size(dev):
                           ("median expert, whole", mid, None, None),
                           ("largest expert, 64 rows; dW row slices", big,
                            _big_rows(counts[big]), _wslices(case.H, case.F))])
+
+
+def test_mixtral_full_size_deterministic(dev):
+    """Two runs of the Mixtral fwd+bwd at full size, the second with other
+    buffers (fresh ctx and workspaces holding other bytes), give the same bits
+    in every output: no atomics, fixed reduction orders."""
+    case = make_mlp_case("mixtral_fwd_bwd", seed=0, device=dev)
+    M, H, F, E = case.M, case.H, case.F, case.E
+    outs = []
+    for fill in (255, 0):
+        fws = torch.full((gm.fwd_ws_bytes(M, H, F, E),), fill, dtype=torch.uint8, device=dev)
+        bws = torch.full((gm.bwd_ws_bytes(M, H, F, E),), fill, dtype=torch.uint8, device=dev)
+        cbuf = torch.full((gm.ctx_bytes(M, H, F, E),), fill, dtype=torch.uint8, device=dev)
+        y, ctx = gm.grouped_mlp_fwd(case.X, case.offsets, case.W1, case.W2, case.r, ws=fws,
+                                    ctx_buf=cbuf)
+        g = gm.grouped_mlp_bwd(case.dY, case.offsets, case.W1, case.W2, case.r, ctx, ws=bws)
+        torch.cuda.synchronize()
+        outs.append((y,) + tuple(g))
+        del fws, bws, cbuf, ctx
+    for name, u, v in zip(("Y", "dX", "dW1", "dW2", "dr"), *outs):
+        assert torch.equal(u, v), name
+    print("  Mixtral fwd+bwd bitwise identical across two runs", flush=True)

@@ -15,7 +15,10 @@ a little less exactly than fp32: the GPU's dz differs from the exact one by
 ~1e-5 relative, see the dr check).  The flip rate is bounded (< 2e-3), and
 end to end (oracle fed only the bf16 inputs) the relative Frobenius bar of
 1e-2 still holds, with a wider max-row bound of 0.1 because one flipped code
-moves a whole output row by a few 1e-2 of its RMS."""
+moves a whole output row by a few 1e-2 of its RMS.  The flip bound is a bound
+on the probability of a flip: the count of flipped codes may exceed 2e-3 of
+the codes by Poisson counting noise (four standard deviations plus three
+codes), which matters for small experts only."""
 import numpy as np
 import pytest
 import torch
@@ -54,12 +57,19 @@ class Report:
         if not ok:
             self.fails.append((name, r, w))
 
-    def rate(self, name, value, bound):
-        ok = value < bound
-        print(f"  {name:10s} {value:.3e} (bound {bound:.0e}) {'ok' if ok else 'FAIL'}",
-              flush=True)
+    def rate(self, name, mismatch, bound):
+        """Requantized codes that differ from the oracle's (a boolean array):
+        their probability is bounded by ``bound``; the count is held to that
+        rate plus Poisson slack (four standard deviations and three codes),
+        so that small samples are not failed by counting noise."""
+        n = mismatch.size
+        flips = int(np.count_nonzero(mismatch))
+        limit = bound * n + 4.0 * np.sqrt(bound * n) + 3.0
+        ok = flips <= limit
+        print(f"  {name:10s} {flips / max(n, 1):.3e} ({flips} of {n}; at most {limit:.0f}) "
+              f"{'ok' if ok else 'FAIL'}", flush=True)
         if not ok:
-            self.fails.append((name, value))
+            self.fails.append((name, flips, n))
 
     def done(self):
         assert not self.fails, self.fails
@@ -147,10 +157,9 @@ def run_case(dev, case, save_h=False, reuse_from=None):
     rep.check("Y|z_gpu", to64(y), O.grouped_linear(deq(zrow), qW2, off_np))
     a, b = h_ref[:, :F], h_ref[:, F:]
     z_ref = r64[:, None] * a * O.sigmoid(a) * b
-    rep.rate("z flips", np.mean(zrow.codes.cpu().numpy() != O.quantize_lastdim(z_ref)[0]),
-             FLIP_MAX)
-    rep.rate("zcol flips", np.mean(ctx.zcol().codes.cpu().numpy()[:, :n]
-                                   != O.quantize_tokens(z_ref, off_np)[0]), FLIP_MAX)
+    rep.rate("z flips", zrow.codes.cpu().numpy() != O.quantize_lastdim(z_ref)[0], FLIP_MAX)
+    rep.rate("zcol flips", ctx.zcol().codes.cpu().numpy()[:, :n]
+             != O.quantize_tokens(z_ref, off_np)[0], FLIP_MAX)
 
     # ---- backward, stage by stage (on the GPU's own codes; the SwiGLU
     # backward on the h the GPU reads: bf16 saved h, or the exact h it
@@ -165,15 +174,14 @@ def run_case(dev, case, save_h=False, reuse_from=None):
     ds = r64[:, None] * dz_ref
     dh_ref = np.concatenate([ds * bg * sg * (1.0 + ag * (1.0 - sg)), ds * ag * sg], axis=1)
     dhrow = gm.ws_mx_view(bws, gm.MX_WS_DHROW, M, H, F, E, (M, 2 * F), save_h)
-    rep.rate("dh flips", np.mean(dhrow.codes.cpu().numpy() != O.quantize_lastdim(dh_ref)[0]),
-             FLIP_MAX)
+    rep.rate("dh flips", dhrow.codes.cpu().numpy() != O.quantize_lastdim(dh_ref)[0], FLIP_MAX)
     rep.check("dX|dh_gpu", to64(dx),
               O.grouped_linear(deq(dhrow), O.qdq_lastdim(W164.transpose(0, 2, 1)), off_np))
     dycol_rows = O.qdq_tokens(dY64, off_np)
     zt = tok_rows(ctx.zcol(), off_np, poff, M)
     dhcol = gm.ws_mx_view(bws, gm.MX_WS_DHCOL, M, H, F, E, (2 * F, ctx.padded_rows), save_h)
-    rep.rate("dhcol flips", np.mean(dhcol.codes.cpu().numpy()[:, :n]
-                                    != O.quantize_tokens(dh_ref, off_np)[0]), FLIP_MAX)
+    rep.rate("dhcol flips", dhcol.codes.cpu().numpy()[:, :n]
+             != O.quantize_tokens(dh_ref, off_np)[0], FLIP_MAX)
     dht = tok_rows(dhcol, off_np, poff, M)
     xt = O.qdq_tokens(X64, off_np)
     dW2_ref = np.zeros((E, H, F))
@@ -314,3 +322,24 @@ def test_mlp_reuse_weights_against_oracle(dev, save_h):
     torch.cuda.synchronize()
     for u, v in zip(g_re, g_fr):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("save_h", MODES)
+def test_mlp_empty_batch(dev, save_h):
+    """No routed rows at all (M = 0, every expert empty): the forward only
+    quantizes the weights, the backward's weight gradients are exact zeros
+    (outputs start poisoned)."""
+    H, F, E = 256, 128, 3
+    g = torch.Generator().manual_seed(7)
+    w1 = (torch.randn((E, 2 * F, H), generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    w2 = (torch.randn((E, H, F), generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=dev)
+    r = torch.empty((0,), dtype=torch.float32, device=dev)
+    off = torch.zeros(E + 1, dtype=torch.int64, device=dev)
+    y, ctx = gm.grouped_mlp_fwd(x, off, w1, w2, r, save_h=save_h)
+    dx, dw1, dw2, dr = gm.grouped_mlp_bwd(x, off, w1, w2, r, ctx)
+    torch.cuda.synchronize()
+    assert y.shape == (0, H) and dx.shape == (0, H) and dr.shape == (0,)
+    assert not dw1.any() and not dw2.any()
+    c_ref, s_ref = O.quantize_lastdim(to64(w1))
+    assert np.array_equal(ctx.w1row().codes.cpu().numpy(), c_ref.reshape(-1, H))
