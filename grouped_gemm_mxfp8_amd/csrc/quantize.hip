@@ -256,6 +256,142 @@ quant_tiles_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
             sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
 }
 
+// 128 rows x 128 columns per workgroup of 256 lanes, for C % 128 == 0 (every
+// operand of the MLP path): twice the bytes of quant_tiles_kernel's tile.
+// Lane t reads the 16-byte chunk (t & 15) of rows 2 (t >> 4) + h of each of
+// four 32-row slabs, so each load instruction moves 16 whole 256-byte row
+// segments and every lane has eight loads in flight; its 8-byte rowwise code
+// stores cover whole 128-byte lines (16 lanes per row).  A row's four 32-blocks
+// sit in lanes c16 = 0, 4, 8, 12 of its 16-lane row: one dword of scale codes
+// per row.  The columnwise copy goes through the same kind of LDS transpose,
+// [column][row pair] with a row stride of 65 dwords.
+__global__ void __launch_bounds__(256)
+quant_tiles128_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                      const int64_t* __restrict__ offs,
+                      const int64_t* __restrict__ poff, int G,
+                      uint8_t* __restrict__ rc, uint8_t* __restrict__ rs,
+                      uint8_t* __restrict__ cc, uint8_t* __restrict__ cs,
+                      int64_t ld, bool tiled, const int32_t* __restrict__ gather,
+                      int64_t src_rows) {
+    constexpr int kStride = 65;
+    __shared__ uint32_t tile[128 * kStride];
+    const int64_t b = blockIdx.z;
+    const int64_t p0 = (int64_t)blockIdx.y * 128;
+    int64_t src0, valid;
+    if (offs) {
+        if (p0 >= poff[G]) return;
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (poff[mid] <= p0) lo = mid; else hi = mid - 1;
+        }
+        src0 = offs[lo] + (p0 - poff[lo]);
+        valid = offs[lo + 1] - src0;
+    } else {
+        src0 = p0;
+        valid = R - p0;
+    }
+    valid = valid < 0 ? 0 : (valid > 128 ? 128 : valid);
+
+    const int t = threadIdx.x;
+    const int c16 = t & 15, rg = t >> 4;
+    const int64_t col0 = (int64_t)blockIdx.x * 128;
+    const int64_t ccol = col0 + c16 * 8;              // this lane's 8 columns (all < C)
+    const __amdgpu_buffer_rsrc_t xr = gather
+        ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0,
+                                            (int)(src_rows * C * 2), 0x00020000)
+        : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (b * R + src0) * C),
+                                            (short)0, (int)(valid * C * 2), 0x00020000);
+    uint4 wl[4][2];
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = it * 32 + 2 * rg + h;
+            uint32_t off;
+            if (gather) {
+                const int32_t sr = r < valid ? gather[src0 + r] : -1;
+                off = sr >= 0 && sr < src_rows ? ((uint32_t)sr * (uint32_t)C + (uint32_t)ccol) * 2u
+                                               : 0x7ffffff0u;
+            } else {
+                off = ((uint32_t)r * (uint32_t)C + (uint32_t)ccol) * 2u;
+            }
+            wl[it][h] = load_stream(xr, off);
+        }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int r0 = it * 32 + 2 * rg;
+        float v[2][8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) unpack8(wl[it][h], v[h]);
+        if (rc) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) m = max(m, abs_bits(v[h][j]));
+                m = max(m, MXQ_DPP(m, 0xB1));         // quad_perm [1,0,3,2]
+                m = max(m, MXQ_DPP(m, 0x4E));         // quad_perm [2,3,0,1]
+                const uint32_t sc = scale_code_from_amax_bits(m);
+                // the row's other three blocks: lanes c16 + 4, + 8, + 12
+                const uint32_t s1 = MXQ_DPP(sc, 0x104), s2 = MXQ_DPP(sc, 0x108),
+                               s3 = MXQ_DPP(sc, 0x10C);   // row_shl:4, 8, 12
+                const int64_t row = b * R + src0 + r0 + h;
+                if (r0 + h < valid) {
+                    store_nt(rc + row * C + ccol, encode8(v[h], inv_scale_from_code(sc)));
+                    if (c16 == 0) {
+                        const uint32_t w4 = sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
+                        if (tiled) {
+                            *reinterpret_cast<uint32_t*>(rs + tiled_scale_offset(row, col0 / 32, C)) = w4;
+                        } else {
+                            uint8_t* d = rs + row * (C / 32) + col0 / 32;
+                            d[0] = (uint8_t)sc; d[1] = (uint8_t)s1;
+                            d[2] = (uint8_t)s2; d[3] = (uint8_t)s3;
+                        }
+                    }
+                }
+            }
+        }
+        if (cc) {
+            const uint4 w0 = wl[it][0], w1 = wl[it][1];
+            const uint32_t a4[4] = {w0.x, w0.y, w0.z, w0.w};
+            const uint32_t b4[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tile[(c16 * 8 + 2 * i) * kStride + it * 16 + rg] = __builtin_amdgcn_perm(b4[i], a4[i], 0x05040100u);
+                tile[(c16 * 8 + 2 * i + 1) * kStride + it * 16 + rg] = __builtin_amdgcn_perm(b4[i], a4[i], 0x07060302u);
+            }
+        }
+    }
+    if (!cc) return;
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int col = pass * 64 + (t >> 2), blk = t & 3;
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t d = tile[col * kStride + blk * 16 + i];
+            v[2 * i] = __uint_as_float(d << 16);
+            v[2 * i + 1] = __uint_as_float(d & 0xffff0000u);
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) m = max(m, abs_bits(v[i]));
+        const uint32_t sc = scale_code_from_amax_bits(m);
+        const float inv = inv_scale_from_code(sc);
+        const uint32_t s1 = MXQ_DPP(sc, 0x55), s2 = MXQ_DPP(sc, 0xAA), s3 = MXQ_DPP(sc, 0xFF);
+        const int64_t crow = b * C + col0 + col;
+        uint4* dst = reinterpret_cast<uint4*>(cc + crow * ld + p0 + blk * 32);
+        store_nt(dst, encode16(v, inv));
+        store_nt(dst + 1, encode16(v + 16, inv));
+        if (blk == 0)
+            *reinterpret_cast<uint32_t*>(cs + (tiled ? tiled_scale_offset(crow, p0 / 32, ld)
+                                                     : crow * (ld / 32) + p0 / 32)) =
+                sc | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_padded_offsets(const int64_t* offs, int G, int64_t* poff,
@@ -284,6 +420,12 @@ hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
                               const int32_t* gather, int64_t src_rows) {
     const int64_t ytiles = offs ? row_bound / 128 : (R + 127) / 128;
     if (ytiles == 0 || C == 0 || batch == 0) return hipSuccess;
+    if (C % 128 == 0) {
+        dim3 grid((unsigned)(C / 128), (unsigned)ytiles, (unsigned)batch);
+        hipLaunchKernelGGL(quant_tiles128_kernel, grid, dim3(256), 0, s, x, R, C, offs,
+                           poff, G, rc, rs, cc, cs, ld, tiled, gather, src_rows);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)((C + 63) / 64), (unsigned)ytiles, (unsigned)batch);
     hipLaunchKernelGGL(quant_tiles_kernel, grid, dim3(256), 0, s, x, R, C, offs,
                        poff, G, rc, rs, cc, cs, ld, tiled, gather, src_rows);
