@@ -245,11 +245,17 @@ mx_status check_mlp_dims(int64_t M, int64_t H, int64_t F, int32_t E, MlpDims* ou
         return fail(MX_ERR_UNSUPPORTED, "H=%lld and F=%lld must be multiples of 128",
                     (long long)H, (long long)F);
     const int64_t Mp = padded_bound(M, E, mx::kTokenAlign);
-    const int64_t big = (H > 2 * F ? H : 2 * F);
-    if (2 * F * H > kI32Max || big * Mp > kI32Max || 2 * F * 256 > kI32Max)
-        return fail(MX_ERR_UNSUPPORTED, "operand too large for 32-bit buffer offsets");
+    // Buffer descriptors are rebased per tile, so only one expert's weight
+    // matrix (2F x H) and one tile's rows need 32-bit offsets; the largest
+    // per-tile range, 256 rows of a token-axis copy (256 * Mp bytes in the
+    // weight-gradient GEMMs), stays below 2^31 with the padded-row bound below
+    // (also the quantizer's grid limit of 65535 row tiles).
+    if (2 * F * H > kI32Max || 2 * F * 256 > kI32Max)
+        return fail(MX_ERR_UNSUPPORTED, "an expert's weights (2F x H = %lld) exceed 2^31 - 1 bytes",
+                    (long long)(2 * F * H));
     if (Mp / 128 > 65535)
-        return fail(MX_ERR_UNSUPPORTED, "M=%lld too large", (long long)M);
+        return fail(MX_ERR_UNSUPPORTED, "M=%lld too large: %lld padded rows exceed 65535 x 128",
+                    (long long)M, (long long)Mp);
     *out = MlpDims{M, H, F, E, Mp};
     return MX_OK;
 }

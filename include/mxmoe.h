@@ -201,7 +201,9 @@ mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
  *        the fp32 partial tiles of the down GEMM's split tail round (the last
  *        round of output tiles, cut along K when it would leave more than
  *        half of the GPU idle).
- * H % 128 == 0, F % 128 == 0, E in [1, 1024].
+ * H % 128 == 0, F % 128 == 0, E in [1, 1024], 2F * H < 2^31 (one expert's
+ * weights), and mx_padded_rows_bound(M, E, 128) <= 65535 * 128 = 8,388,480
+ * rows (MX_ERR_UNSUPPORTED otherwise).
  */
 mx_status grouped_mlp_fwd(const void* x, const int64_t* d_offsets, int32_t E,
                           int64_t M, int64_t H, int64_t F, const void* w1,

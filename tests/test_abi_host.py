@@ -330,3 +330,21 @@ def test_validate_offsets_on_host_crafted_arrays(mxlib):
             bad = off.copy()
             bad[i] = off[-1] + 1                         # past the end: decreases after it
             assert v(bad, int(off[-1])) == MX_ERR_INVALID_ARG
+
+
+def test_mlp_accepts_calls_past_two_gib_token_axis_copies(mxlib):
+    """Descriptors are rebased per tile: M with 2F * Mp above 2^31 bytes (a
+    token-axis copy of dh past 2 GiB) is accepted at the Mixtral shape; the
+    limits are one expert's weights below 2^31 bytes and 65535 * 128 padded
+    rows."""
+    H, F = 4096, 14336
+    for M, E in ((80000, 1), (1_000_000, 8), (8_388_480, 1)):
+        Mp = mxlib.mx_padded_rows_bound(M, E, 128)
+        assert 2 * F * Mp > 2 ** 31
+        for fl in (0, SAVE_H):
+            assert mxlib.grouped_mlp_ctx_bytes(M, H, F, E, fl) > 2 * F * Mp // 2
+            assert mxlib.grouped_mlp_bwd_ws_bytes(M, H, F, E, fl) > 2 * F * Mp
+    assert mxlib.grouped_mlp_ctx_bytes(8_388_481, H, F, 1, 0) == 0    # past the row bound
+    assert "padded rows" in _err(mxlib)
+    assert mxlib.grouped_mlp_ctx_bytes(1024, 32768, 32768, 1, 0) == 0  # 2F x H past 2^31
+    assert "weights" in _err(mxlib)

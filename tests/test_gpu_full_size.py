@@ -144,15 +144,18 @@ def _stagewise(case, e, idx, wrows, views, outs):
         return deq(c, s)[:, :n]
 
     all_h, all_f, all_2f = slice(0, H), slice(0, F), slice(0, 2 * F)
-    r2 = all_h if wrows is None else wrows["dW2"]
-    r1 = all_2f if wrows is None else wrows["dW1"]
+    w = wrows or {}
+    r2, r1 = w.get("dW2", all_h), w.get("dW1", all_2f)
+    # optional column slices, for token counts whose full FP64 operands would
+    # not fit the host's memory
+    c2, c1 = w.get("dW2_cols", all_f), w.get("dW1_cols", all_h)
     dyt = tokvals(v["dycol"], r2)                 # [rows of dW2, n]
-    zt = tokvals(v["zcol"], all_f)                # [F, n]
-    _check(f"dW2[{e}] rows | codes", _np32(dw2[e][r2]), dyt @ zt.T)
+    zt = tokvals(v["zcol"], c2)                   # [columns of dW2, n]
+    _check(f"dW2[{e}] rows | codes", _np32(dw2[e][r2][:, c2]), dyt @ zt.T)
     del dyt, zt
     dht = tokvals(v["dhcol"], r1)                 # [rows of dW1, n]
-    xt = tokvals(v["xcol"], all_h)                # [H, n]
-    _check(f"dW1[{e}] rows | codes", _np32(dw1[e][r1]), dht @ xt.T)
+    xt = tokvals(v["xcol"], c1)                   # [columns of dW1, n]
+    _check(f"dW1[{e}] rows | codes", _np32(dw1[e][r1][:, c1]), dht @ xt.T)
 
 
 def _run_full(dev, case, samples):
@@ -261,3 +264,19 @@ def test_mixtral_full_size_deterministic(dev):
     for name, u, v in zip(("Y", "dX", "dW1", "dW2", "dr"), *outs):
         assert torch.equal(u, v), name
     print("  Mixtral fwd+bwd bitwise identical across two runs", flush=True)
+
+
+def test_past_two_gib_token_axis_copies(dev):
+    """One expert with 80,000 routed rows at H=4096, F=14336: the token-axis
+    dh copy (2F x Mp bytes = 2.29e9) and dW1's contraction are past 2^31 bytes,
+    which calls used to be refused for.  Stage-wise and end to end on 64 rows,
+    and 256-row slices of dW1 and dW2 over 2048 of their columns, contracted
+    over all 80,000 tokens."""
+    n = 80000
+    case = make_mlp_case(None, seed=5, T=n, k=1, E=1, H=4096, F=14336, routing="counts",
+                         counts=[n], device=dev)
+    assert 2 * case.F * gm.padded_rows_bound(n, 1) > 2 ** 31
+    w = _wslices(case.H, case.F)
+    w["dW2_cols"] = np.r_[0:1024, case.F - 1024:case.F]
+    w["dW1_cols"] = np.r_[0:1024, case.H - 1024:case.H]
+    _run_full(dev, case, [("80,000-row expert, 64 rows; dW row slices", 0, _big_rows(n), w)])
