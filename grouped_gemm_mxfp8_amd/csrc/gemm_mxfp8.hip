@@ -25,7 +25,11 @@
 // without branches.  The grid is persistent (one workgroup per CU); tiles are
 // walked in bands of 8 M-tiles so that the 32 tiles one XCD runs at a time
 // share 8 A panels and 4 B panels in that XCD's L2, and weight-gradient
-// groups run longest-K first.
+// groups run longest-K first.  Plain-store tiles run as a chain per
+// workgroup: a tile's last two K steps load the next tile's first two, and
+// its output leaves straight from the registers (whole 128-byte lines per
+// store) while those land, so neither the first loads nor the output stores
+// of a tile stand between two tiles' MFMAs.
 #include <utility>
 
 #include "internal.h"
@@ -90,6 +94,22 @@ __device__ __forceinline__ ScaleSrc scale_src(const uint8_t* scales, int64_t ld,
 // LDS byte address of a __shared__ location.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS byte address of byte off of stage st of one GemmSmem member, from the
+// region's LDS base taken once per tile: casting a generic pointer to LDS
+// per load costs a 64-bit add and a null test each, which in the main loops
+// adds some 70 scalar instructions per step.
+enum SmemPart { kPartA, kPartB, kPartAs, kPartBs };
+template <SmemPart PART>
+__device__ __forceinline__ uint32_t stage_lds(uint32_t smb, int st, int off) {
+    constexpr uint32_t kOff = PART == kPartA ? offsetof(GemmSmem, a)
+                            : PART == kPartB ? offsetof(GemmSmem, b)
+                            : PART == kPartAs ? offsetof(GemmSmem, as) : offsetof(GemmSmem, bs);
+    constexpr uint32_t kStage = PART == kPartA ? sizeof(GemmSmem::a[0])
+                              : PART == kPartB ? sizeof(GemmSmem::b[0])
+                              : PART == kPartAs ? sizeof(GemmSmem::as[0]) : sizeof(GemmSmem::bs[0]);
+    return smb + kOff + (uint32_t)st * kStage + (uint32_t)off;
 }
 
 // Global -> LDS load of 16 (or 4) bytes per lane: lane l's bytes land at LDS
@@ -495,58 +515,74 @@ __device__ __forceinline__ void pick_unit_stashed(const v4f (&acc)[8][8], int ip
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Plain epilogue: the tile's accumulators (times the row's routing weight and
-// the group factors when given) to bf16 C, through LDS.  B is the MFMA's first
-// operand, so acc[i][j] holds the transposed 16 x 16 block: lane (r16, q) has
-// row i*16 + r16 of the wave tile and its 4 consecutive columns j*16 + 4q + v;
-// one v_permlane16_swap per dword gives lane q (of the pair q, q^1 that share
-// a row) 8 consecutive columns.  Each wave writes its 128 x 128 quadrant into
-// a quarter of the operand stages (rows of 256 B, 16-byte chunk c at
-// c ^ (row & 15), no bank conflicts measured), then stores 4 whole rows per
-// instruction, so every store covers whole 128-byte lines: stored directly
-// from the lanes (16 rows x 64 B per instruction), the plain GEMMs wrote a
-// third more bytes to HBM than their output.  A 32-column block pair is
-// wholly inside or outside N (N % 32 == 0).
-__device__ __forceinline__ void store_tile_bf16_lds(const v4f (&acc)[8][8], const GemmProblem& p,
-                                                    int g, int64_t m0, int64_t mvalid, int64_t n0,
-                                                    int wm, int wn, int lane, uint8_t* quad) {
+// The plain epilogue straight from the registers, for tiles whose LDS holds
+// the next tile's operands.  After the same v_permlane16_swap pairing, lane
+// (r16, q) holds 8 consecutive columns of row i*16 + r16 for each jp: with
+// jp = 2c and 2c + 1, the four lanes of a row hold the eight 16-byte chunks
+// of 128-byte line c of the wave's row.  One DPP rotation by 8 within each
+// 16-lane row then hands lane r16 < 8 the jp = 2c chunk of row r16 + 8, and
+// lane r16 >= 8 the jp = 2c + 1 chunk of row r16 - 8, so that each store
+// instruction writes whole lines: rows (r16 & 7) of the block, then rows 8
+// + (r16 & 7), with lanes r16 < 8 on the jp = 2c half of the line and lanes
+// r16 >= 8 on the other.  (Stored as the pairs left the swap, each
+// instruction would write half lines, and the output would cost more.)
+__device__ __forceinline__ void store_tile_bf16_regs(const v4f (&acc)[8][8], const GemmProblem& p,
+                                                     int g, int64_t m0, int64_t mvalid, int64_t n0,
+                                                     int wm, int wn, int lane) {
     const int r16 = lane & 15, q = lane >> 4;
+    const bool lo8 = r16 < 8;
     const int64_t rwave = m0 + wm * 128;
     const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
     uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (p.kgroup ? (int64_t)g * p.c_gstride : 0);
     const int64_t cw = n0 + wn * 128;
-    const int codd = q & 1;
     const float gs = (p.gsa ? p.gsa[g] : 1.0f) * (p.gsb ? p.gsb[g] : 1.0f);
+    auto ror8 = [](uint32_t v) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+    };
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int rl = i * 16 + r16;
         const bool rok = rl < rows_valid_w;
-        const int64_t row = rwave + (rok ? rl : 0);
-        const float sc = p.rscale ? p.rscale[row] * gs : gs;
+        const float sc = p.rscale ? p.rscale[rwave + (rok ? rl : 0)] * gs : gs;
+        const int rl1 = i * 16 + (r16 & 7), rl2 = rl1 + 8;
 #pragma unroll
-        for (int jp = 0; jp < 4; ++jp) {
-            float va[4], vb[4];
+        for (int c = 0; c < 2; ++c) {
+            uint32_t d[2][4];                       // jp = 2c + h, after the swap
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int jp = 2 * c + h;
+                float va[4], vb[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    va[v] = acc[i][2 * jp][v] * sc;
+                    vb[v] = acc[i][2 * jp + 1][v] * sc;
+                }
+                const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
+                const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+                d[h][0] = x[0];
+                d[h][1] = y[0];
+                d[h][2] = x[1];
+                d[h][3] = y[1];
+            }
+            uint32_t rv[4], s1[4], s2[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                va[v] = acc[i][2 * jp][v] * sc;
-                vb[v] = acc[i][2 * jp + 1][v] * sc;
+                rv[v] = ror8(lo8 ? d[1][v] : d[0][v]);
+                s1[v] = lo8 ? d[0][v] : rv[v];
+                s2[v] = lo8 ? rv[v] : d[1][v];
             }
-            const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
-            const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
-            const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
-            const int chunk = (2 * jp + codd) * 2 + (q >> 1);
-            *reinterpret_cast<uint4*>(quad + rl * 256 + ((chunk ^ r16) << 4)) =
-                make_uint4(x[0], y[0], x[1], y[1]);
+            const int jp = 2 * c + (lo8 ? 0 : 1);
+            const int chunk = (2 * jp + (q & 1)) * 2 + (q >> 1);
+            if (cw + chunk * 8 < p.N) {
+                if (rl1 < rows_valid_w)
+                    store_nt(C + (rwave + rl1) * p.ldc + cw + chunk * 8,
+                             make_uint4(s1[0], s1[1], s1[2], s1[3]));
+                if (rl2 < rows_valid_w)
+                    store_nt(C + (rwave + rl2) * p.ldc + cw + chunk * 8,
+                             make_uint4(s2[0], s2[1], s2[2], s2[3]));
+            }
         }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    const int rr = lane >> 4, ch = lane & 15;
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-        const int rl = 4 * t + rr;
-        const uint4 v = *reinterpret_cast<const uint4*>(quad + rl * 256 + ((ch ^ (rl & 15)) << 4));
-        if (rl < rows_valid_w && cw + ch * 8 < p.N)
-            store_nt(C + (rwave + rl) * p.ldc + cw + ch * 8, v);
     }
 }
 
@@ -674,24 +710,25 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
     using SC = Sched<NJ>;
     const int r16 = lane & 15, q = lane >> 4;
     const int swz = r16 & 7;
+    const uint32_t smb = uni((int)lds_addr(&sm));
     auto dma_u = [&](auto uc, int st, int ks) {
         constexpr int u = decltype(uc)::value;
         const bool live = ks < nk;
         const uint32_t k0 = (uint32_t)ks * BK;
         if constexpr (u < 8) {
             const v4i r = live ? o.ra : v4i{o.ra.x, o.ra.y, 0, o.ra.w};
-            dma_b128(r, uni(lds_addr(&sm.a[st][(wave * 8 + u) * 1024])), o.aoff[u], k0);
+            dma_b128(r, stage_lds<kPartA>(smb, st, (wave * 8 + u) * 1024), o.aoff[u], k0);
         } else if constexpr (u < 8 + NJ) {
             const v4i r = live ? o.rb : v4i{o.rb.x, o.rb.y, 0, o.rb.w};
-            dma_b128(r, uni(lds_addr(&sm.b[st][(wave * NJ + (u - 8)) * 1024])), o.boff[u - 8], k0);
+            dma_b128(r, stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024), o.boff[u - 8], k0);
         } else if constexpr (u == 8 + NJ) {
             const v4i rs = o.sa.rsrc;
             const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, uni(lds_addr(&sm.as[st][wave * 64])), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
+            dma_b32(r, stage_lds<kPartAs>(smb, st, wave * 64 * 4), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
         } else {
             const v4i rs = o.sb.rsrc;
             const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, uni(lds_addr(&sm.bs[st][wave * 64])), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
+            dma_b32(r, stage_lds<kPartBs>(smb, st, wave * 64 * 4), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
         }
     };
 
@@ -762,6 +799,150 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
     }
 }
 
+// The per-tile part of a plain tile's sources: its lane offsets of the code
+// loads depend only on the wave, the lane and the leading dimensions, which
+// every tile of a launch shares, so the next tile needs only its buffer
+// descriptors, its scale offsets and its K-step count.
+struct TileNext {
+    v4i ra, rb, sar, sbr;
+    uint32_t sav, sbv, sa0, sb0;
+    int nk;                      // K steps (0: no next tile)
+};
+
+// (the scalar fields pass through readfirstlane: values that came from LDS
+// reads are not known to be wave-uniform, and buffer descriptors and scalar
+// offsets must sit in scalar registers)
+__device__ __forceinline__ v4i uni4(const v4i& v) { return v4i{uni(v.x), uni(v.y), uni(v.z), uni(v.w)}; }
+__device__ __forceinline__ TileNext tile_next(const TileSrc& o, int nk) {
+    return TileNext{uni4(o.ra), uni4(o.rb), uni4(o.sa.rsrc), uni4(o.sb.rsrc), o.sa.voff, o.sb.voff,
+                    (uint32_t)uni((int)o.sa.s0), (uint32_t)uni((int)o.sb.s0), uni(nk)};
+}
+
+// tile_gemm<8> for a chain of plain tiles, one after another on one
+// workgroup: the loads that tile_gemm spends on zero-range steps past the
+// end (steps nk and nk + 1) fetch the next tile's steps 0 and 1 instead, so
+// that tile's first operands arrive while this one finishes and while its
+// epilogue runs (which must then leave LDS alone).  Stage parity runs on
+// across tiles: step ks of this tile lives in stage (base + ks) & 1.
+//  * pre: steps 0 and 1 of this tile were issued by the previous tile, and
+//    step 0 is complete for every wave (the previous tile's last S2 wait and
+//    barrier); otherwise this tile issues them itself, after waiting for any
+//    loads still in flight into the stages.
+//  * Steps 0 .. nk - 3 load steps 2 .. nk - 1 of this tile, all of them
+//    within its K range, so that loop carries no zero-range selects.  The
+//    last two steps load from next_src(): steps 0 and 1 of the next tile, or
+//    zero-range loads where it has no such step (nk = 0 when there is no
+//    next tile).  It is called after the first loop, so that the next
+//    tile's sources take the registers of this tile's.
+// The waits of the main loop stay sufficient with the previous tile's
+// output stores in flight between the loads: loads complete in order among
+// themselves, and every vmcnt wait here leaves only loads younger than the
+// ones it waits for, so a pending older load would keep the count above the
+// wait's bound (stores complete whenever they do; nothing waits for them).
+template <class NextSrc>
+__device__ __forceinline__ void tile_gemm_chain(v4f (&acc)[8][8], GemmSmem& sm, const TileSrc& o,
+                                                NextSrc next_src, int nk, int base, bool pre,
+                                                int wave, int wm, int wn, int lane) {
+    using SC = Sched<8>;
+    constexpr int NJ = 8;
+    const int r16 = lane & 15, q = lane >> 4;
+    const int swz = r16 & 7;
+    const int b0 = uni(base);    // stage addresses stay scalar
+    const uint32_t smb = uni((int)lds_addr(&sm));
+    // loads of step ks of source s into stage st; LIVE: within its K range
+    auto dma_u = [&](auto uc, auto livec, const TileNext& src, int st, int ks) {
+        constexpr int u = decltype(uc)::value;
+        constexpr bool kLive = decltype(livec)::value;
+        const bool live = kLive || ks < src.nk;
+        const uint32_t k0 = (uint32_t)ks * BK;
+        auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
+        if constexpr (u < 8) {
+            dma_b128(rng(src.ra), stage_lds<kPartA>(smb, st, (wave * 8 + u) * 1024), o.aoff[u], k0);
+        } else if constexpr (u < 8 + NJ) {
+            dma_b128(rng(src.rb), stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024),
+                     o.boff[u - 8], k0);
+        } else if constexpr (u == 8 + NJ) {
+            dma_b32(rng(src.sar), stage_lds<kPartAs>(smb, st, wave * 64 * 4), src.sav,
+                    src.sa0 + ks * o.sa.sstep);
+        } else {
+            dma_b32(rng(src.sbr), stage_lds<kPartBs>(smb, st, wave * 64 * 4), src.sbv,
+                    src.sb0 + ks * o.sb.sstep);
+        }
+    };
+
+    v8i af[8], bfr[NJ];
+    int asc[8], bsc[NJ];
+    auto read_a = [&](auto ic, int st) {
+        constexpr int i = decltype(ic)::value;
+        const int row = wm * 128 + i * 16 + r16;
+        const uint8_t* b = &sm.a[st][row * BK];
+        const uint4 lo = *reinterpret_cast<const uint4*>(b + ((q ^ swz) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(b + (((q + 4) ^ swz) << 4));
+        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        asc[i] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
+    };
+    auto read_b = [&](auto jc, int st) {
+        constexpr int j = decltype(jc)::value;
+        const int row = wn * (NJ * 16) + j * 16 + r16;
+        const uint8_t* b = &sm.b[st][row * BK];
+        const uint4 lo = *reinterpret_cast<const uint4*>(b + ((q ^ swz) << 4));
+        const uint4 hi = *reinterpret_cast<const uint4*>(b + (((q + 4) ^ swz) << 4));
+        bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
+    };
+    auto mfma = [&](auto ic, auto jc) {
+        constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
+    };
+    // one K step: the MFMAs of step ks, the loads of step kl of src
+    auto step = [&](int ks, auto livec, const TileNext& src, int kl) {
+        const int cur = (b0 + ks) & 1, nxt = cur ^ 1;
+        lds_barrier();                                  // S1: stage cur is free
+        static_for<4 * NJ>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{});
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int u = SC::a_at(s);
+            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, livec, src, cur, kl);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_vmcnt<SC::kNA>();
+        lds_barrier();                                  // S2: stage nxt complete
+        static_for<4 * NJ>([&](auto sc) {
+            constexpr int s = decltype(sc)::value, j = s / 4, i = 4 + s % 4;
+            mfma(std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (s < 4) read_a(std::integral_constant<int, s>{}, nxt);
+            if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, i>{}, nxt);
+            if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
+            constexpr int u = SC::b_at(s);
+            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, livec, src, cur, kl);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    const TileNext own = tile_next(o, nk);
+    if (!pre) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();                                  // no load in flight, stages free
+        static_for<SC::kLoads>([&](auto uc) { dma_u(uc, std::false_type{}, own, b0, 0); });
+        static_for<SC::kLoads>([&](auto uc) { dma_u(uc, std::false_type{}, own, b0 ^ 1, 1); });
+        wait_vmcnt<SC::kLoads>();
+        lds_barrier();
+    }
+    static_for<8>([&](auto ic) { read_a(ic, b0); });
+    static_for<NJ>([&](auto jc) { read_b(jc, b0); });
+    int ks = 0;
+    for (; ks + 2 < nk; ++ks) step(ks, std::true_type{}, own, ks + 2);
+    if (ks < nk) {
+        const TileNext nx = next_src();
+        for (; ks < nk; ++ks) step(ks, std::false_type{}, nx, ks + 2 - nk);
+    }
+}
+
 // tile_gemm with only four A fragments in registers (rows 0..3 of the wave's
 // eight, then rows 4..7 in the same registers), for a tile GEMM that runs
 // while other accumulators stay live.  Changes to the schedule of tile_gemm:
@@ -812,24 +993,25 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
 #pragma unroll
     for (int u = 0; u < 8; ++u)
         aoffl[u] = (uint32_t)((lean_arow(wave, u) + dma_row) * lda + dma_chunk * 16);
+    const uint32_t smb = uni((int)lds_addr(&sm));
     auto dma_u = [&](auto uc, int st, int ks) {
         constexpr int u = decltype(uc)::value;
         const bool live = ks < nk;
         const uint32_t k0 = (uint32_t)ks * BK;
         if constexpr (u < 8) {
             const v4i r = live ? o.ra : v4i{o.ra.x, o.ra.y, 0, o.ra.w};
-            dma_b128(r, uni(lds_addr(&sm.a[st][lean_arow(wave, u) * BK])), aoffl[u], k0);
+            dma_b128(r, stage_lds<kPartA>(smb, st, lean_arow(wave, u) * BK), aoffl[u], k0);
         } else if constexpr (u < 8 + NJ) {
             const v4i r = live ? o.rb : v4i{o.rb.x, o.rb.y, 0, o.rb.w};
-            dma_b128(r, uni(lds_addr(&sm.b[st][(wave * NJ + (u - 8)) * 1024])), o.boff[u - 8], k0);
+            dma_b128(r, stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024), o.boff[u - 8], k0);
         } else if constexpr (u == 8 + NJ) {
             const v4i rs = o.sb.rsrc;
             const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, uni(lds_addr(&sm.bs[st][wave * 64])), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
+            dma_b32(r, stage_lds<kPartBs>(smb, st, wave * 64 * 4), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
         } else {
             const v4i rs = o.sa.rsrc;
             const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, uni(lds_addr(&sm.as[st][wave * 64])), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
+            dma_b32(r, stage_lds<kPartAs>(smb, st, wave * 64 * 4), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
         }
     };
     v8i af[4], bfr[NJ];
@@ -897,6 +1079,12 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
     }
 }
 
+// Position of one tile (or split-tail chunk) of a launch.
+struct TileLoc {
+    int g, chunk;
+    int64_t m0, mvalid, n0, klo, K;
+};
+
 // SPLIT (plain store, row-grouped only): the tail-split schedule below.
 template <Epi EPI, bool SPLIT = false>
 __global__ void __launch_bounds__(NTHREADS, 1)
@@ -905,6 +1093,10 @@ mx_gemm_kernel(GemmProblem p) {
     GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem);
     __shared__ int s_prefix[kMaxGroups + 1];
     __shared__ int s_perm[kMaxGroups];
+    // the plain kernel keeps the offsets in LDS: a global load while its
+    // operand loads and output stores are in flight would wait for all of them
+    constexpr bool kOffsLds = EPI == Epi::kStoreBf16;
+    __shared__ int64_t s_offs[kOffsLds ? kMaxGroups + 1 : 1];
 
     const int tid = threadIdx.x;
     const int lane_id = tid & 63;
@@ -957,6 +1149,13 @@ mx_gemm_kernel(GemmProblem p) {
         }
         if (lane_id == 63) s_prefix[G] = incl;
     }
+    if constexpr (kOffsLds) {
+        for (int g = tid; g <= G; g += NTHREADS) s_offs[g] = p.offs[g];
+    }
+    auto offs_of = [&](int g) -> int64_t {
+        if constexpr (kOffsLds) return s_offs[g];
+        else return p.offs[g];
+    };
     if (p.kgroup) {
         // longest contraction first (ties: lower group first)
         for (int g = tid; g < G; g += NTHREADS) {
@@ -973,7 +1172,7 @@ mx_gemm_kernel(GemmProblem p) {
         }
     }
     __syncthreads();
-    const int total = s_prefix[G];
+    const int total = uni(s_prefix[G]);
 
     // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
     // contiguous run of tiles per round.
@@ -1004,9 +1203,9 @@ mx_gemm_kernel(GemmProblem p) {
     }
     const int items = full + (total - full) * S;
 
-    for (int t0 = 0; t0 < items; t0 += grid) {
-        const int w = t0 + slot;
-        if (w >= items) break;
+    // Tile w of the launch: its group, first row, valid rows, first output
+    // column and K range; chunk >= 0 for a chunk of a split tail tile.
+    auto locate = [&](int w) -> TileLoc {
         int t = w, chunk = -1;
         if constexpr (SPLIT) {
             if (w >= full) {
@@ -1014,15 +1213,6 @@ mx_gemm_kernel(GemmProblem p) {
                 chunk = (w - full) % S;
             }
         }
-        // Per-lane offsets are derived per tile from an opaque copy of the
-        // lane index: hoisted out of the tile loop they would stay live
-        // through the epilogue, which needs every register it can get.
-        int lane = lane_id;
-        asm volatile("" : "+v"(lane));
-        const int r16 = lane & 15, q = lane >> 4;
-        const int swz = r16 & 7;
-
-        // ---- locate the tile ----
         int g;
         int64_t m0, mvalid, n0, klo, K;
         int local, mtiles;
@@ -1042,400 +1232,443 @@ mx_gemm_kernel(GemmProblem p) {
             local = t - s_prefix[g];
             mtiles = (s_prefix[g + 1] - s_prefix[g]) / ntn;
         }
-        {
-            const int bandsz = BAND * ntn;
-            const int band = local / bandsz;
-            const int rem = local - band * bandsz;
-            const int bm = min(BAND, mtiles - band * BAND);
-            const int mt = band * BAND + rem % bm;
-            const int nt = rem / bm;
-            n0 = (int64_t)nt * TN_OUT;
-            if (p.kgroup) {
-                m0 = (int64_t)mt * BM;
-                mvalid = min((int64_t)BM, p.M - m0);
-                klo = p.offs[g];
-                K = p.offs[g + 1] - klo;
-            } else {
-                const int64_t lo_row = p.offs[g];
-                m0 = lo_row + (int64_t)mt * BM;
-                mvalid = min((int64_t)BM, p.offs[g + 1] - m0);
-                klo = 0;
-                K = p.K;
-                if constexpr (SPLIT) {
-                    if (chunk >= 0) {       // K steps [c0, c1) of the tile
-                        const int nk_all = (int)(p.K / BK);
-                        const int c0 = chunk * nk_all / S, c1 = (chunk + 1) * nk_all / S;
-                        klo = (int64_t)c0 * BK;
-                        K = (int64_t)(c1 - c0) * BK;
-                    }
+        const int bandsz = BAND * ntn;
+        const int band = local / bandsz;
+        const int rem = local - band * bandsz;
+        const int bm = min(BAND, mtiles - band * BAND);
+        const int mt = band * BAND + rem % bm;
+        const int nt = rem / bm;
+        n0 = (int64_t)nt * TN_OUT;
+        if (p.kgroup) {
+            m0 = (int64_t)mt * BM;
+            mvalid = min((int64_t)BM, p.M - m0);
+            klo = offs_of(g);
+            K = offs_of(g + 1) - klo;
+        } else {
+            const int64_t lo_row = offs_of(g);
+            m0 = lo_row + (int64_t)mt * BM;
+            mvalid = min((int64_t)BM, offs_of(g + 1) - m0);
+            klo = 0;
+            K = p.K;
+            if constexpr (SPLIT) {
+                if (chunk >= 0) {           // K steps [c0, c1) of the tile
+                    const int nk_all = (int)(p.K / BK);
+                    const int c0 = chunk * nk_all / S, c1 = (chunk + 1) * nk_all / S;
+                    klo = (int64_t)c0 * BK;
+                    K = (int64_t)(c1 - c0) * BK;
                 }
             }
         }
-        g = uni(g);
-        m0 = uni64(m0);
-        mvalid = uni64(mvalid);
-        n0 = uni64(n0);
-        klo = uni64(klo);
-        K = uni64(K);
-        const int nk = (int)(K / BK);
+        return TileLoc{uni(g), uni(chunk), uni64(m0), uni64(mvalid), uni64(n0), uni64(klo),
+                       uni64(K)};
+    };
+    auto brow_plain = [](int b) -> int64_t { return b; };
 
-        // ---- main loop(s) ----
-        // The fused gate-up tile pairs 128 gate with 128 up rows of W1 (gate
-        // and up halves are F rows apart): B row b of the tile is W1 row
-        // half * F + n0 + (b >> 7) * 64 + (b & 63), half = (b >> 6) & 1, so
-        // wave wn's 128 B rows are the gate then the up rows of its 64 output
-        // columns.  Plain tiles read B rows n0 + b.
-        auto brow_gu = [&](int b) -> int64_t {
-            return ((b >> 6) & 1) * p.F + n0 + (b >> 7) * 64 + (b & 63);
-        };
-        auto brow_plain = [](int b) -> int64_t { return b; };
-        const int64_t bg = p.kgroup ? 0 : (int64_t)g * p.B.gstride;
-        constexpr bool kGU = EPI == Epi::kSwiglu || EPI == Epi::kDSwigluR;
-        v4f acc[8][8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-        if constexpr (kGU) {
-            const TileSrc o = tile_src<false, 8>(p.A, p.B, m0, mvalid, bg, 2 * p.F, klo, K,
-                                                 brow_gu, wave, lane);
-            tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane);
-        } else {
-            const TileSrc o = tile_src<EPI == Epi::kStoreBf16, 8>(p.A, p.B, m0, mvalid, bg + n0,
-                                                                  p.N - n0, klo, K, brow_plain,
-                                                                  wave, lane);
-            tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane);
-        }
-        // The fused epilogues stage their outputs in LDS, which overlaps every
-        // wave's operand stages: wait until the trailing (zero-range) loads of
-        // all waves have landed.  The plain epilogue waits in its own branch.
-        if constexpr (EPI != Epi::kStoreBf16) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
-        }
-        // Recompute backward: the second GEMM of the tile, dz = dY . W2 for
-        // the same rows and the tile's 128 columns of F (A2: dY rowwise, B2:
-        // W2 columnwise, K = H), while acc keeps the recomputed [a | b].
-        v4f dacc[8][4];
-        if constexpr (EPI == Epi::kDSwigluR) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-            int lane2 = lane_id;
-            asm volatile("" : "+v"(lane2));
-            const TileSrc o = tile_src<false, 4>(p.A2, p.B2, m0, mvalid,
-                                                 (int64_t)g * p.B2.gstride + n0, p.F - n0, 0, K,
-                                                 brow_plain, wave, lane2);
-            tile_gemm_lean<4>(dacc, sm, o, nk, wave, wm, wn, lane2, p.A2.ld);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
-        }
-
-        // ---- epilogue ----
-        // B is the MFMA's first operand, so acc[i][j] holds the transposed
-        // 16 x 16 block: lane (r16, q) has row i*16 + r16 of the wave tile and
-        // its 4 consecutive columns j*16 + 4q + v.
-        const int64_t rwave = m0 + wm * 128;          // first row of this wave
-        const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
-
-        if constexpr (EPI == Epi::kStoreBf16) {
-            if (!SPLIT || chunk < 0) {
-                // the trailing (zero-range) loads write the stages: wait for
-                // them, and for every wave to leave the stages, before staging
-                // the output there; the closing barrier keeps the next tile's
-                // loads off the stages until every wave has read its quarter
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                lds_barrier();
-                store_tile_bf16_lds(acc, p, g, m0, mvalid, n0, wm, wn, lane, smem + wave * 32768);
-                lds_barrier();
-            } else {
-                // a chunk of a split tail tile: fp32 partial tile to the
-                // workspace; chunk 0 also records the tile's coordinates
-                float* part = split_part(p.split_ws, w - full);
+    if constexpr (EPI == Epi::kStoreBf16) {
+        // Plain tiles run as one chain per workgroup (tile_gemm_chain): the
+        // last two K steps of a tile fetch the next tile's first two, and the
+        // epilogue stores from the registers while they land.
+        int w = slot;
+        if (w < items) {
+            TileLoc L = locate(w);
+            bool pre = false;
+            int base = 0;
+            for (;;) {
+                const int wnext = w + grid;
+                const bool has_next = wnext < items;
+                // per-lane offsets from an opaque copy of the lane index, so
+                // that they are not kept live through the epilogue
+                int lane = lane_id;
+                asm volatile("" : "+v"(lane));
+                const int nk = (int)(L.K / BK);
+                auto src_of = [&](const TileLoc& T) {
+                    const int64_t bg = p.kgroup ? 0 : (int64_t)T.g * p.B.gstride;
+                    return tile_src<true, 8>(p.A, p.B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0,
+                                             T.klo, T.K, brow_plain, wave, lane);
+                };
+                const TileSrc o = src_of(L);
+                auto next_src = [&]() -> TileNext {
+                    if (!has_next) return tile_next(o, 0);
+                    const TileLoc Ln = locate(wnext);
+                    return tile_next(src_of(Ln), (int)(Ln.K / BK));
+                };
+                v4f acc[8][8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        *reinterpret_cast<v4f*>(part + ((wave * 64 + i * 8 + j) * 64 + lane) * 4) =
-                            acc[i][j];
-                if (chunk == 0 && tid == 0) {
-                    int64_t* meta = reinterpret_cast<SplitHdr*>(p.split_ws)->meta[(w - full) / S];
-                    meta[0] = g;
-                    meta[1] = m0;
-                    meta[2] = mvalid;
-                    meta[3] = n0;
+                    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                tile_gemm_chain(acc, sm, o, next_src, nk, base, pre, wave, wm, wn, lane);
+                if (!SPLIT || L.chunk < 0) {
+                    store_tile_bf16_regs(acc, p, L.g, L.m0, L.mvalid, L.n0, wm, wn, lane);
+                } else {
+                    // a chunk of a split tail tile: fp32 partial tile to the
+                    // workspace; chunk 0 also records the tile's coordinates
+                    float* part = split_part(p.split_ws, w - full);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            *reinterpret_cast<v4f*>(part + ((wave * 64 + i * 8 + j) * 64 + lane) * 4) =
+                                acc[i][j];
+                    if (L.chunk == 0 && tid == 0) {
+                        int64_t* meta = reinterpret_cast<SplitHdr*>(p.split_ws)->meta[(w - full) / S];
+                        meta[0] = L.g;
+                        meta[1] = L.m0;
+                        meta[2] = L.mvalid;
+                        meta[3] = L.n0;
+                    }
                 }
+                if (!has_next) break;
+                pre = nk >= 2;               // tile_gemm_chain switched to the next tile
+                base = pre ? (base + nk) & 1 : 0;
+                w = wnext;
+                L = locate(w);
             }
-        } else if constexpr (EPI == Epi::kSwiglu) {
-            // acc[i][j], j < 4: gate; acc[i][j+4]: up, same output columns
-            const int64_t F = p.F;
-            const int64_t glo = p.offs[g];
-            const int64_t prow = p.poff[g] + (rwave - glo);       // padded position
-            const int64_t npad = p.poff[g + 1] - p.poff[g];
-            const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
-            const int64_t cw = n0 + wn * 64;                       // wave's first z column
-            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, false, p.qtiled};
-            uint8_t* st = smem + wave * Slot<EPI>::kBytes;
-#pragma nounroll
-            for (int ip = 0; ip < 4; ++ip) {
-                // Lane-derived values are re-derived from an opaque copy of the
-                // lane index in every slice: hoisted out of the tile loop they
-                // would stay live through the main loop and crowd out the
-                // accumulators.
-                int lane = lane_id;
-                asm volatile("" : "+v"(lane));
-                const int r16 = lane & 15, q = lane >> 4;
-                float rr[2];
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int rl = (2 * ip + ii) * 16 + r16;
-                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
-                }
-                static_for<2>([&](auto jpc) {
-                    constexpr int jp = decltype(jpc)::value;
-                    float gu[2][2][4], uu[2][2][4], z[2][2][4];
-                    pick_unit<2 * jp>(acc, ip, gu);
-                    pick_unit<2 * jp + 4>(acc, ip, uu);
-                    // Rows past the expert's valid rows are selected to 0 (h
-                    // and z): the padded rows take part in the token-axis
-                    // blocks, and rows past M read never-written scale bytes
-                    // (the tiled layout pads rows to 32), so their
-                    // accumulators may be anything, NaN included.
-#pragma unroll
-                    for (int ii = 0; ii < 2; ++ii) {
-                        const int i = 2 * ip + ii;
-                        const bool rv = i * 16 + r16 < rows_valid_w;
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) {
-                            const int j = 2 * jp + jj;
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                gu[ii][jj][v] = rv ? gu[ii][jj][v] : 0.f;
-                                uu[ii][jj][v] = rv ? uu[ii][jj][v] : 0.f;
-                            }
-                            if (p.h && rows_pad_w > 0) {
-                                const uint2 g2 = pack4_bf16(gu[ii][jj]), u2 = pack4_bf16(uu[ii][jj]);
-                                store_nt(h_block(p.h, prow + i * 16, cw + j * 16, F, lane),
-                                         make_uint4(g2.x, g2.y, u2.x, u2.y));
-                            }
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                float sg;
-                                z[ii][jj][v] = rr[ii] * (silu_sig(gu[ii][jj][v], sg) * uu[ii][jj][v]);
-                            }
-                        }
-                    }
-                    quant_unit<64>(z, 2 * jp * 16, ip, st, lane);
-                });
-                lds_wait();
-                flush_rows<64, true>(st, d, rwave, ip, rows_valid_w, lane);
-                if ((ip & 1) && rows_pad_w > 0) flush_cols<64, true>(st, d, prow + (ip >> 1) * 64, lane);
-                lds_wait();
-            }
-            if (rows_pad_w > 0) flush_col_scales<64>(st, d, prow, lane);
-        } else if constexpr (EPI == Epi::kDSwiglu) {
-            const int64_t F = p.F;
-            const int64_t glo = p.offs[g];
-            const int64_t prow = p.poff[g] + (rwave - glo);
-            const int64_t npad = p.poff[g + 1] - p.poff[g];
-            const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
-            const int64_t cw = n0 + wn * 128;
-            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true, p.qtiled};
-            uint8_t* st = smem + wave * Slot<EPI>::kBytes;
-            const int part = (int)(n0 / BN) * 2 + wn;
-            // h = [a | b] of unit (ip, jp) (32 rows x 32 columns) is four 1 KiB
-            // blocks, each moved by one global->LDS load into the unit's buffer
-            // of the ring.  While slice ip is processed, unit jp's buffer is
-            // refilled with unit (ip + 1, jp), so each load has a whole slice
-            // to land.  Blocks past F or past the padded rows use a zero-range
-            // descriptor (zeros, masked); the last slice loads nothing.
-            uint8_t* const ring = st + QStage<256>::kBytes;
-            auto dma_unit = [&](int ipn, auto jpc, int lane) {
-                constexpr int jp = decltype(jpc)::value;
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                    for (int jj = 0; jj < 2; ++jj) {
-                        const int64_t col = cw + (2 * jp + jj) * 16;
-                        const bool in = rows_pad_w > 0 && col < F && ipn < 4;
-                        const uint8_t* blk = reinterpret_cast<const uint8_t*>(p.h) +
-                            (((prow >> 4) + 2 * ipn + ii) * (F >> 4) + (col >> 4)) * 1024;
-                        const v4i rs = make_rsrc(in ? blk : reinterpret_cast<const uint8_t*>(p.h),
-                                                 in ? 1024 : 0);
-                        dma_b128(rs, uni(lds_addr(ring + ((jp * 2 + ii) * 2 + jj) * 1024)),
-                                 (uint32_t)lane * 16, 0);
-                    }
-            };
-            static_for<4>([&](auto jpc) { dma_unit(0, jpc, lane); });
-#pragma nounroll
-            for (int ip = 0; ip < 4; ++ip) {
-                // Lane-derived values are re-derived from an opaque copy of the
-                // lane index in every slice: hoisted out of the tile loop they
-                // would stay live through the main loop and crowd out the
-                // accumulators.
-                int lane = lane_id;
-                asm volatile("" : "+v"(lane));
-                const int r16 = lane & 15, q = lane >> 4;
-                float rr[2], drs[2];
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int rl = (2 * ip + ii) * 16 + r16;
-                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
-                    drs[ii] = 0.f;
-                }
-                static_for<4>([&](auto jpc) {
-                    constexpr int jp = decltype(jpc)::value;
-                    float dzu[2][2][4], da[2][2][4], db[2][2][4];
-                    uint4 hb[2][2];
-                    // this unit's ring loads: 12 younger ring loads follow them,
-                    // except in the last slice, which issues none
-                    if (ip < 3) {
-                        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-                    } else {
-                        if constexpr (jp == 0) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-                        if constexpr (jp == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                        if constexpr (jp == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-                        if constexpr (jp == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    }
-#pragma unroll
-                    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj)
-                            hb[ii][jj] = *reinterpret_cast<const uint4*>(
-                                ring + ((jp * 2 + ii) * 2 + jj) * 1024 + lane * 16);
-                    lds_wait();                 // the buffer is free for the next slice's unit
-                    if (ip < 3) dma_unit(ip + 1, jpc, lane);
-                    pick_unit<2 * jp>(acc, ip, dzu);
-                    // Rows past the expert's valid rows get dz = 0 by a select
-                    // (rows past M read never-written scale bytes, so their
-                    // accumulators may be anything, NaN included); their h is
-                    // 0 (the forward stores 0 there), so da = db = 0 in the
-                    // token-axis blocks they share with valid rows.  A wave's
-                    // columns are all below F or all past it (dz = 0 from
-                    // zero-filled B rows, h loads of zero range).
-#pragma unroll
-                    for (int ii = 0; ii < 2; ++ii) {
-                        const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj) {
-                            float a[4], b[4];
-                            const uint4 hv = hb[ii][jj];
-                            unpack4_bf16(make_uint2(hv.x, hv.y), a);
-                            unpack4_bf16(make_uint2(hv.z, hv.w), b);
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const float av = a[v], bv = b[v];
-                                const float dz = rv ? dzu[ii][jj][v] : 0.f;
-                                float sg;
-                                const float sl_ = silu_sig(av, sg);
-                                drs[ii] += dz * (sl_ * bv);
-                                const float ds = rr[ii] * dz;
-                                da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
-                                db[ii][jj][v] = ds * sl_;
-                            }
-                        }
-                    }
-                    quant_unit<256>(da, 2 * jp * 16, ip, st, lane);
-                    quant_unit<256>(db, 128 + 2 * jp * 16, ip, st, lane);
-                });
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const float sum = sum4q(drs[ii]);
-                    const int rl = (2 * ip + ii) * 16 + r16;
-                    if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
-                }
-                // the wave's 128 columns are all below F or all at or past it
-                lds_wait();
-                if (cw < F) flush_rows<256, false>(st, d, rwave, ip, rows_valid_w, lane);
-                if (cw < F && rows_pad_w > 0) flush_cols<256, false>(st, d, prow + ip * 32, lane);
-                lds_wait();
-            }
-            if (cw < F && rows_pad_w > 0) flush_col_scales<256>(st, d, prow, lane);
-        } else {   // kDSwigluR
-            // acc holds the recomputed [a | b] (acc[i][j], j < 4: gate; j + 4:
-            // up, same columns) and dacc the dz of the wave's 64 columns of F
-            // (cw .. cw + 63, all below F since F % 128 == 0).  dh = [da | db]
-            // leaves as rowwise codes (da at columns cw.., db at F + cw..) and
-            // token-axis codes; dr partial part = the wave's column block.
-            const int64_t F = p.F;
-            const int64_t glo = p.offs[g];
-            const int64_t prow = p.poff[g] + (rwave - glo);
-            const int64_t npad = p.poff[g + 1] - p.poff[g];
-            const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
-            const int64_t cw = n0 + wn * 64;
-            const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true, p.qtiled};
-            uint8_t* st = smem + wave * Slot<EPI>::kBytes;
-            const int part = (int)(n0 / 128) * 2 + wn;
-            // the last slice's [a | b] to the stash: 384 accumulators plus the
-            // epilogue's working set would not fit the registers
-            uint8_t* const stash = st + QStage<128>::kBytes;
-            static_for<2>([&](auto iic) {
-                constexpr int ii = decltype(iic)::value;
-                static_for<8>([&](auto jc) {
-                    constexpr int j = decltype(jc)::value;
-                    *reinterpret_cast<v4f*>(stash + ((ii * 8 + j) * 64 + lane) * 16) = acc[6 + ii][j];
-                });
-            });
-#pragma nounroll
-            for (int ip = 0; ip < 4; ++ip) {
-                // lane-derived values re-derived per slice (see the forward)
-                int lane = lane_id;
-                asm volatile("" : "+v"(lane));
-                const int r16 = lane & 15, q = lane >> 4;
-                float rr[2], drs[2];
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int rl = (2 * ip + ii) * 16 + r16;
-                    rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
-                    drs[ii] = 0.f;
-                }
-                static_for<2>([&](auto jpc) {
-                    constexpr int jp = decltype(jpc)::value;
-                    float ga[2][2][4], ua[2][2][4], dzu[2][2][4], da[2][2][4], db[2][2][4];
-                    pick_unit_stashed<2 * jp>(acc, ip, ga, stash, lane);
-                    pick_unit_stashed<2 * jp + 4>(acc, ip, ua, stash, lane);
-                    pick_unit<2 * jp>(dacc, ip, dzu);
-                    // Rows past the expert's valid rows are selected to 0 (a,
-                    // b and dz): rows past M read never-written scale bytes,
-                    // so their accumulators may be anything, NaN included,
-                    // and the padded rows take part in the token-axis blocks.
-#pragma unroll
-                    for (int ii = 0; ii < 2; ++ii) {
-                        const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
-#pragma unroll
-                        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const float av = rv ? ga[ii][jj][v] : 0.f;
-                                const float bv = rv ? ua[ii][jj][v] : 0.f;
-                                const float dz = rv ? dzu[ii][jj][v] : 0.f;
-                                float sg;
-                                const float sl_ = silu_sig(av, sg);
-                                drs[ii] += dz * (sl_ * bv);
-                                const float ds = rr[ii] * dz;
-                                da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
-                                db[ii][jj][v] = ds * sl_;
-                            }
-                    }
-                    quant_unit<128>(da, 2 * jp * 16, ip, st, lane);
-                    quant_unit<128>(db, 64 + 2 * jp * 16, ip, st, lane);
-                });
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const float sum = sum4q(drs[ii]);
-                    const int rl = (2 * ip + ii) * 16 + r16;
-                    if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
-                }
-                lds_wait();
-                flush_rows<128, false>(st, d, rwave, ip, rows_valid_w, lane);
-                if ((ip & 1) && rows_pad_w > 0) flush_cols<128, false>(st, d, prow + (ip >> 1) * 64, lane);
-                lds_wait();
-            }
-            if (rows_pad_w > 0) flush_col_scales<128>(st, d, prow, lane);
         }
-        // the next tile's loads overwrite other waves' staging areas
-        if constexpr (EPI != Epi::kStoreBf16) lds_barrier();
+        // no load may still be landing in LDS when the workgroup ends
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+        for (int t0 = 0; t0 < items; t0 += grid) {
+            const int w = t0 + slot;
+            if (w >= items) break;
+            // Per-lane offsets are derived per tile from an opaque copy of the
+            // lane index: hoisted out of the tile loop they would stay live
+            // through the epilogue, which needs every register it can get.
+            int lane = lane_id;
+            asm volatile("" : "+v"(lane));
+            const int r16 = lane & 15, q = lane >> 4;
+            const int swz = r16 & 7;
+            const TileLoc L = locate(w);
+            const int g = L.g;
+            const int64_t m0 = L.m0, mvalid = L.mvalid, n0 = L.n0, klo = L.klo, K = L.K;
+            const int nk = (int)(K / BK);
+
+            // ---- main loop(s) ----
+            // The fused gate-up tile pairs 128 gate with 128 up rows of W1 (gate
+            // and up halves are F rows apart): B row b of the tile is W1 row
+            // half * F + n0 + (b >> 7) * 64 + (b & 63), half = (b >> 6) & 1, so
+            // wave wn's 128 B rows are the gate then the up rows of its 64 output
+            // columns.  Plain tiles read B rows n0 + b.
+            auto brow_gu = [&](int b) -> int64_t {
+                return ((b >> 6) & 1) * p.F + n0 + (b >> 7) * 64 + (b & 63);
+            };
+            const int64_t bg = p.kgroup ? 0 : (int64_t)g * p.B.gstride;
+            constexpr bool kGU = EPI == Epi::kSwiglu || EPI == Epi::kDSwigluR;
+            v4f acc[8][8];
+    #pragma unroll
+            for (int i = 0; i < 8; ++i)
+    #pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+            if constexpr (kGU) {
+                const TileSrc o = tile_src<false, 8>(p.A, p.B, m0, mvalid, bg, 2 * p.F, klo, K,
+                                                     brow_gu, wave, lane);
+                tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane);
+            } else {
+                const TileSrc o = tile_src<false, 8>(p.A, p.B, m0, mvalid, bg + n0, p.N - n0, klo,
+                                                     K, brow_plain, wave, lane);
+                tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane);
+            }
+            // The fused epilogues stage their outputs in LDS, which overlaps every
+            // wave's operand stages: wait until the trailing (zero-range) loads of
+            // all waves have landed.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            // Recompute backward: the second GEMM of the tile, dz = dY . W2 for
+            // the same rows and the tile's 128 columns of F (A2: dY rowwise, B2:
+            // W2 columnwise, K = H), while acc keeps the recomputed [a | b].
+            v4f dacc[8][4];
+            if constexpr (EPI == Epi::kDSwigluR) {
+    #pragma unroll
+                for (int i = 0; i < 8; ++i)
+    #pragma unroll
+                    for (int j = 0; j < 4; ++j) dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                int lane2 = lane_id;
+                asm volatile("" : "+v"(lane2));
+                const TileSrc o = tile_src<false, 4>(p.A2, p.B2, m0, mvalid,
+                                                     (int64_t)g * p.B2.gstride + n0, p.F - n0, 0, K,
+                                                     brow_plain, wave, lane2);
+                tile_gemm_lean<4>(dacc, sm, o, nk, wave, wm, wn, lane2, p.A2.ld);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                lds_barrier();
+            }
+
+            // ---- epilogue ----
+            // B is the MFMA's first operand, so acc[i][j] holds the transposed
+            // 16 x 16 block: lane (r16, q) has row i*16 + r16 of the wave tile and
+            // its 4 consecutive columns j*16 + 4q + v.
+            const int64_t rwave = m0 + wm * 128;          // first row of this wave
+            const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
+
+            if constexpr (EPI == Epi::kSwiglu) {
+                // acc[i][j], j < 4: gate; acc[i][j+4]: up, same output columns
+                const int64_t F = p.F;
+                const int64_t glo = p.offs[g];
+                const int64_t prow = p.poff[g] + (rwave - glo);       // padded position
+                const int64_t npad = p.poff[g + 1] - p.poff[g];
+                const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
+                const int64_t cw = n0 + wn * 64;                       // wave's first z column
+                const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, false, p.qtiled};
+                uint8_t* st = smem + wave * Slot<EPI>::kBytes;
+    #pragma nounroll
+                for (int ip = 0; ip < 4; ++ip) {
+                    // Lane-derived values are re-derived from an opaque copy of the
+                    // lane index in every slice: hoisted out of the tile loop they
+                    // would stay live through the main loop and crowd out the
+                    // accumulators.
+                    int lane = lane_id;
+                    asm volatile("" : "+v"(lane));
+                    const int r16 = lane & 15, q = lane >> 4;
+                    float rr[2];
+    #pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int rl = (2 * ip + ii) * 16 + r16;
+                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                    }
+                    static_for<2>([&](auto jpc) {
+                        constexpr int jp = decltype(jpc)::value;
+                        float gu[2][2][4], uu[2][2][4], z[2][2][4];
+                        pick_unit<2 * jp>(acc, ip, gu);
+                        pick_unit<2 * jp + 4>(acc, ip, uu);
+                        // Rows past the expert's valid rows are selected to 0 (h
+                        // and z): the padded rows take part in the token-axis
+                        // blocks, and rows past M read never-written scale bytes
+                        // (the tiled layout pads rows to 32), so their
+                        // accumulators may be anything, NaN included.
+    #pragma unroll
+                        for (int ii = 0; ii < 2; ++ii) {
+                            const int i = 2 * ip + ii;
+                            const bool rv = i * 16 + r16 < rows_valid_w;
+    #pragma unroll
+                            for (int jj = 0; jj < 2; ++jj) {
+                                const int j = 2 * jp + jj;
+    #pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    gu[ii][jj][v] = rv ? gu[ii][jj][v] : 0.f;
+                                    uu[ii][jj][v] = rv ? uu[ii][jj][v] : 0.f;
+                                }
+                                if (p.h && rows_pad_w > 0) {
+                                    const uint2 g2 = pack4_bf16(gu[ii][jj]), u2 = pack4_bf16(uu[ii][jj]);
+                                    store_nt(h_block(p.h, prow + i * 16, cw + j * 16, F, lane),
+                                             make_uint4(g2.x, g2.y, u2.x, u2.y));
+                                }
+    #pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    float sg;
+                                    z[ii][jj][v] = rr[ii] * (silu_sig(gu[ii][jj][v], sg) * uu[ii][jj][v]);
+                                }
+                            }
+                        }
+                        quant_unit<64>(z, 2 * jp * 16, ip, st, lane);
+                    });
+                    lds_wait();
+                    flush_rows<64, true>(st, d, rwave, ip, rows_valid_w, lane);
+                    if ((ip & 1) && rows_pad_w > 0) flush_cols<64, true>(st, d, prow + (ip >> 1) * 64, lane);
+                    lds_wait();
+                }
+                if (rows_pad_w > 0) flush_col_scales<64>(st, d, prow, lane);
+            } else if constexpr (EPI == Epi::kDSwiglu) {
+                const int64_t F = p.F;
+                const int64_t glo = p.offs[g];
+                const int64_t prow = p.poff[g] + (rwave - glo);
+                const int64_t npad = p.poff[g + 1] - p.poff[g];
+                const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
+                const int64_t cw = n0 + wn * 128;
+                const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true, p.qtiled};
+                uint8_t* st = smem + wave * Slot<EPI>::kBytes;
+                const int part = (int)(n0 / BN) * 2 + wn;
+                // h = [a | b] of unit (ip, jp) (32 rows x 32 columns) is four 1 KiB
+                // blocks, each moved by one global->LDS load into the unit's buffer
+                // of the ring.  While slice ip is processed, unit jp's buffer is
+                // refilled with unit (ip + 1, jp), so each load has a whole slice
+                // to land.  Blocks past F or past the padded rows use a zero-range
+                // descriptor (zeros, masked); the last slice loads nothing.
+                uint8_t* const ring = st + QStage<256>::kBytes;
+                auto dma_unit = [&](int ipn, auto jpc, int lane) {
+                    constexpr int jp = decltype(jpc)::value;
+    #pragma unroll
+                    for (int ii = 0; ii < 2; ++ii)
+    #pragma unroll
+                        for (int jj = 0; jj < 2; ++jj) {
+                            const int64_t col = cw + (2 * jp + jj) * 16;
+                            const bool in = rows_pad_w > 0 && col < F && ipn < 4;
+                            const uint8_t* blk = reinterpret_cast<const uint8_t*>(p.h) +
+                                (((prow >> 4) + 2 * ipn + ii) * (F >> 4) + (col >> 4)) * 1024;
+                            const v4i rs = make_rsrc(in ? blk : reinterpret_cast<const uint8_t*>(p.h),
+                                                     in ? 1024 : 0);
+                            dma_b128(rs, uni(lds_addr(ring + ((jp * 2 + ii) * 2 + jj) * 1024)),
+                                     (uint32_t)lane * 16, 0);
+                        }
+                };
+                static_for<4>([&](auto jpc) { dma_unit(0, jpc, lane); });
+    #pragma nounroll
+                for (int ip = 0; ip < 4; ++ip) {
+                    // Lane-derived values are re-derived from an opaque copy of the
+                    // lane index in every slice: hoisted out of the tile loop they
+                    // would stay live through the main loop and crowd out the
+                    // accumulators.
+                    int lane = lane_id;
+                    asm volatile("" : "+v"(lane));
+                    const int r16 = lane & 15, q = lane >> 4;
+                    float rr[2], drs[2];
+    #pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int rl = (2 * ip + ii) * 16 + r16;
+                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                        drs[ii] = 0.f;
+                    }
+                    static_for<4>([&](auto jpc) {
+                        constexpr int jp = decltype(jpc)::value;
+                        float dzu[2][2][4], da[2][2][4], db[2][2][4];
+                        uint4 hb[2][2];
+                        // this unit's ring loads: 12 younger ring loads follow them,
+                        // except in the last slice, which issues none
+                        if (ip < 3) {
+                            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+                        } else {
+                            if constexpr (jp == 0) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+                            if constexpr (jp == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                            if constexpr (jp == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                            if constexpr (jp == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        }
+    #pragma unroll
+                        for (int ii = 0; ii < 2; ++ii)
+    #pragma unroll
+                            for (int jj = 0; jj < 2; ++jj)
+                                hb[ii][jj] = *reinterpret_cast<const uint4*>(
+                                    ring + ((jp * 2 + ii) * 2 + jj) * 1024 + lane * 16);
+                        lds_wait();                 // the buffer is free for the next slice's unit
+                        if (ip < 3) dma_unit(ip + 1, jpc, lane);
+                        pick_unit<2 * jp>(acc, ip, dzu);
+                        // Rows past the expert's valid rows get dz = 0 by a select
+                        // (rows past M read never-written scale bytes, so their
+                        // accumulators may be anything, NaN included); their h is
+                        // 0 (the forward stores 0 there), so da = db = 0 in the
+                        // token-axis blocks they share with valid rows.  A wave's
+                        // columns are all below F or all past it (dz = 0 from
+                        // zero-filled B rows, h loads of zero range).
+    #pragma unroll
+                        for (int ii = 0; ii < 2; ++ii) {
+                            const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
+    #pragma unroll
+                            for (int jj = 0; jj < 2; ++jj) {
+                                float a[4], b[4];
+                                const uint4 hv = hb[ii][jj];
+                                unpack4_bf16(make_uint2(hv.x, hv.y), a);
+                                unpack4_bf16(make_uint2(hv.z, hv.w), b);
+    #pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    const float av = a[v], bv = b[v];
+                                    const float dz = rv ? dzu[ii][jj][v] : 0.f;
+                                    float sg;
+                                    const float sl_ = silu_sig(av, sg);
+                                    drs[ii] += dz * (sl_ * bv);
+                                    const float ds = rr[ii] * dz;
+                                    da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
+                                    db[ii][jj][v] = ds * sl_;
+                                }
+                            }
+                        }
+                        quant_unit<256>(da, 2 * jp * 16, ip, st, lane);
+                        quant_unit<256>(db, 128 + 2 * jp * 16, ip, st, lane);
+                    });
+    #pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const float sum = sum4q(drs[ii]);
+                        const int rl = (2 * ip + ii) * 16 + r16;
+                        if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                    }
+                    // the wave's 128 columns are all below F or all at or past it
+                    lds_wait();
+                    if (cw < F) flush_rows<256, false>(st, d, rwave, ip, rows_valid_w, lane);
+                    if (cw < F && rows_pad_w > 0) flush_cols<256, false>(st, d, prow + ip * 32, lane);
+                    lds_wait();
+                }
+                if (cw < F && rows_pad_w > 0) flush_col_scales<256>(st, d, prow, lane);
+            } else {   // kDSwigluR
+                // acc holds the recomputed [a | b] (acc[i][j], j < 4: gate; j + 4:
+                // up, same columns) and dacc the dz of the wave's 64 columns of F
+                // (cw .. cw + 63, all below F since F % 128 == 0).  dh = [da | db]
+                // leaves as rowwise codes (da at columns cw.., db at F + cw..) and
+                // token-axis codes; dr partial part = the wave's column block.
+                const int64_t F = p.F;
+                const int64_t glo = p.offs[g];
+                const int64_t prow = p.poff[g] + (rwave - glo);
+                const int64_t npad = p.poff[g + 1] - p.poff[g];
+                const int rows_pad_w = (int)min((int64_t)128, max((int64_t)0, npad - (rwave - glo)));
+                const int64_t cw = n0 + wn * 64;
+                const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, true, p.qtiled};
+                uint8_t* st = smem + wave * Slot<EPI>::kBytes;
+                const int part = (int)(n0 / 128) * 2 + wn;
+                // the last slice's [a | b] to the stash: 384 accumulators plus the
+                // epilogue's working set would not fit the registers
+                uint8_t* const stash = st + QStage<128>::kBytes;
+                static_for<2>([&](auto iic) {
+                    constexpr int ii = decltype(iic)::value;
+                    static_for<8>([&](auto jc) {
+                        constexpr int j = decltype(jc)::value;
+                        *reinterpret_cast<v4f*>(stash + ((ii * 8 + j) * 64 + lane) * 16) = acc[6 + ii][j];
+                    });
+                });
+    #pragma nounroll
+                for (int ip = 0; ip < 4; ++ip) {
+                    // lane-derived values re-derived per slice (see the forward)
+                    int lane = lane_id;
+                    asm volatile("" : "+v"(lane));
+                    const int r16 = lane & 15, q = lane >> 4;
+                    float rr[2], drs[2];
+    #pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const int rl = (2 * ip + ii) * 16 + r16;
+                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                        drs[ii] = 0.f;
+                    }
+                    static_for<2>([&](auto jpc) {
+                        constexpr int jp = decltype(jpc)::value;
+                        float ga[2][2][4], ua[2][2][4], dzu[2][2][4], da[2][2][4], db[2][2][4];
+                        pick_unit_stashed<2 * jp>(acc, ip, ga, stash, lane);
+                        pick_unit_stashed<2 * jp + 4>(acc, ip, ua, stash, lane);
+                        pick_unit<2 * jp>(dacc, ip, dzu);
+                        // Rows past the expert's valid rows are selected to 0 (a,
+                        // b and dz): rows past M read never-written scale bytes,
+                        // so their accumulators may be anything, NaN included,
+                        // and the padded rows take part in the token-axis blocks.
+    #pragma unroll
+                        for (int ii = 0; ii < 2; ++ii) {
+                            const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
+    #pragma unroll
+                            for (int jj = 0; jj < 2; ++jj)
+    #pragma unroll
+                                for (int v = 0; v < 4; ++v) {
+                                    const float av = rv ? ga[ii][jj][v] : 0.f;
+                                    const float bv = rv ? ua[ii][jj][v] : 0.f;
+                                    const float dz = rv ? dzu[ii][jj][v] : 0.f;
+                                    float sg;
+                                    const float sl_ = silu_sig(av, sg);
+                                    drs[ii] += dz * (sl_ * bv);
+                                    const float ds = rr[ii] * dz;
+                                    da[ii][jj][v] = ds * bv * sg * (1.0f + av * (1.0f - sg));
+                                    db[ii][jj][v] = ds * sl_;
+                                }
+                        }
+                        quant_unit<128>(da, 2 * jp * 16, ip, st, lane);
+                        quant_unit<128>(db, 64 + 2 * jp * 16, ip, st, lane);
+                    });
+    #pragma unroll
+                    for (int ii = 0; ii < 2; ++ii) {
+                        const float sum = sum4q(drs[ii]);
+                        const int rl = (2 * ip + ii) * 16 + r16;
+                        if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                    }
+                    lds_wait();
+                    flush_rows<128, false>(st, d, rwave, ip, rows_valid_w, lane);
+                    if ((ip & 1) && rows_pad_w > 0) flush_cols<128, false>(st, d, prow + (ip >> 1) * 64, lane);
+                    lds_wait();
+                }
+                if (rows_pad_w > 0) flush_col_scales<128>(st, d, prow, lane);
+            }
+            // the next tile's loads overwrite other waves' staging areas
+            lds_barrier();
+        }
     }
 }
 
