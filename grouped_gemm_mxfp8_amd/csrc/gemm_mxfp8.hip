@@ -1092,11 +1092,18 @@ mx_gemm_kernel(GemmProblem p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[Slot<EPI>::kSmem];
     GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem);
     __shared__ int s_prefix[kMaxGroups + 1];
-    __shared__ int s_perm[kMaxGroups];
+    // weight-gradient (k-grouped) launches are plain-store only
+    constexpr bool kKgOk = EPI == Epi::kStoreBf16;
+    const bool kgroup = kKgOk && p.kgroup;
+    __shared__ int s_perm[kKgOk ? kMaxGroups : 1];
     // the plain kernel keeps the offsets in LDS: a global load while its
     // operand loads and output stores are in flight would wait for all of them
     constexpr bool kOffsLds = EPI == Epi::kStoreBf16;
     __shared__ int64_t s_offs[kOffsLds ? kMaxGroups + 1 : 1];
+    // the fused epilogues read the tile's routing weights from LDS: a global
+    // load in the epilogue would wait (vmcnt) for the output stores in flight
+    constexpr bool kRsLds = EPI != Epi::kStoreBf16;
+    __shared__ float s_rs[kRsLds ? BM : 1];
 
     const int tid = threadIdx.x;
     const int lane_id = tid & 63;
@@ -1122,7 +1129,7 @@ mx_gemm_kernel(GemmProblem p) {
             const int g = lane_id * 16 + u;
             int c = 0;
             if (g < G) {
-                if (p.kgroup) {
+                if (kgroup) {
                     c = mtn_k * ntn;
                 } else {
                     const int64_t n = p.offs[g + 1] - p.offs[g];
@@ -1156,7 +1163,7 @@ mx_gemm_kernel(GemmProblem p) {
         if constexpr (kOffsLds) return s_offs[g];
         else return p.offs[g];
     };
-    if (p.kgroup) {
+    if (kgroup) {
         // longest contraction first (ties: lower group first)
         for (int g = tid; g < G; g += NTHREADS) {
             int rank = g;
@@ -1216,7 +1223,7 @@ mx_gemm_kernel(GemmProblem p) {
         int g;
         int64_t m0, mvalid, n0, klo, K;
         int local, mtiles;
-        if (p.kgroup) {
+        if (kgroup) {
             const int per = mtn_k * ntn;
             const int gi = t / per;
             g = s_perm[gi];
@@ -1239,7 +1246,7 @@ mx_gemm_kernel(GemmProblem p) {
         const int mt = band * BAND + rem % bm;
         const int nt = rem / bm;
         n0 = (int64_t)nt * TN_OUT;
-        if (p.kgroup) {
+        if (kgroup) {
             m0 = (int64_t)mt * BM;
             mvalid = min((int64_t)BM, p.M - m0);
             klo = offs_of(g);
@@ -1282,7 +1289,7 @@ mx_gemm_kernel(GemmProblem p) {
                 asm volatile("" : "+v"(lane));
                 const int nk = (int)(L.K / BK);
                 auto src_of = [&](const TileLoc& T) {
-                    const int64_t bg = p.kgroup ? 0 : (int64_t)T.g * p.B.gstride;
+                    const int64_t bg = kgroup ? 0 : (int64_t)T.g * p.B.gstride;
                     return tile_src<true, 8>(p.A, p.B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0,
                                              T.klo, T.K, brow_plain, wave, lane);
                 };
@@ -1352,12 +1359,21 @@ mx_gemm_kernel(GemmProblem p) {
             auto brow_gu = [&](int b) -> int64_t {
                 return ((b >> 6) & 1) * p.F + n0 + (b >> 7) * 64 + (b & 63);
             };
-            const int64_t bg = p.kgroup ? 0 : (int64_t)g * p.B.gstride;
+            const int64_t bg = kgroup ? 0 : (int64_t)g * p.B.gstride;
             constexpr bool kGU = EPI == Epi::kSwiglu || EPI == Epi::kDSwigluR;
+            // the routing weights of rows m0 .. m0 + 255 (zero past mvalid) into
+            // s_rs, ahead of the first operand loads, so the main loop's first
+            // wait covers them; the previous tile's epilogue has left s_rs
+            // (its closing barrier)
+            if constexpr (kRsLds) {
+                const v4i rr = make_rsrc(p.rscale + m0, mvalid * 4);
+                dma_b32(rr, uni((int)lds_addr(&s_rs[wave * 64])), (uint32_t)(wave * 64 + lane) * 4u,
+                        0u);
+            }
             v4f acc[8][8];
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 8; ++i)
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
             if constexpr (kGU) {
                 const TileSrc o = tile_src<false, 8>(p.A, p.B, m0, mvalid, bg, 2 * p.F, klo, K,
@@ -1378,9 +1394,9 @@ mx_gemm_kernel(GemmProblem p) {
             // W2 columnwise, K = H), while acc keeps the recomputed [a | b].
             v4f dacc[8][4];
             if constexpr (EPI == Epi::kDSwigluR) {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 8; ++i)
-    #pragma unroll
+#pragma unroll
                     for (int j = 0; j < 4; ++j) dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
                 int lane2 = lane_id;
                 asm volatile("" : "+v"(lane2));
@@ -1409,7 +1425,7 @@ mx_gemm_kernel(GemmProblem p) {
                 const int64_t cw = n0 + wn * 64;                       // wave's first z column
                 const QDest d{p.qr, p.qrs, p.ldqr, p.qc, p.qcs, p.ldqc, cw, F, false, p.qtiled};
                 uint8_t* st = smem + wave * Slot<EPI>::kBytes;
-    #pragma nounroll
+#pragma nounroll
                 for (int ip = 0; ip < 4; ++ip) {
                     // Lane-derived values are re-derived from an opaque copy of the
                     // lane index in every slice: hoisted out of the tile loop they
@@ -1419,10 +1435,10 @@ mx_gemm_kernel(GemmProblem p) {
                     asm volatile("" : "+v"(lane));
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2];
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const int rl = (2 * ip + ii) * 16 + r16;
-                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                        rr[ii] = rl < rows_valid_w ? s_rs[wm * 128 + rl] : 0.0f;
                     }
                     static_for<2>([&](auto jpc) {
                         constexpr int jp = decltype(jpc)::value;
@@ -1434,14 +1450,14 @@ mx_gemm_kernel(GemmProblem p) {
                         // blocks, and rows past M read never-written scale bytes
                         // (the tiled layout pads rows to 32), so their
                         // accumulators may be anything, NaN included.
-    #pragma unroll
+#pragma unroll
                         for (int ii = 0; ii < 2; ++ii) {
                             const int i = 2 * ip + ii;
                             const bool rv = i * 16 + r16 < rows_valid_w;
-    #pragma unroll
+#pragma unroll
                             for (int jj = 0; jj < 2; ++jj) {
                                 const int j = 2 * jp + jj;
-    #pragma unroll
+#pragma unroll
                                 for (int v = 0; v < 4; ++v) {
                                     gu[ii][jj][v] = rv ? gu[ii][jj][v] : 0.f;
                                     uu[ii][jj][v] = rv ? uu[ii][jj][v] : 0.f;
@@ -1451,7 +1467,7 @@ mx_gemm_kernel(GemmProblem p) {
                                     store_nt(h_block(p.h, prow + i * 16, cw + j * 16, F, lane),
                                              make_uint4(g2.x, g2.y, u2.x, u2.y));
                                 }
-    #pragma unroll
+#pragma unroll
                                 for (int v = 0; v < 4; ++v) {
                                     float sg;
                                     z[ii][jj][v] = rr[ii] * (silu_sig(gu[ii][jj][v], sg) * uu[ii][jj][v]);
@@ -1485,9 +1501,9 @@ mx_gemm_kernel(GemmProblem p) {
                 uint8_t* const ring = st + QStage<256>::kBytes;
                 auto dma_unit = [&](int ipn, auto jpc, int lane) {
                     constexpr int jp = decltype(jpc)::value;
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < 2; ++ii)
-    #pragma unroll
+#pragma unroll
                         for (int jj = 0; jj < 2; ++jj) {
                             const int64_t col = cw + (2 * jp + jj) * 16;
                             const bool in = rows_pad_w > 0 && col < F && ipn < 4;
@@ -1500,7 +1516,7 @@ mx_gemm_kernel(GemmProblem p) {
                         }
                 };
                 static_for<4>([&](auto jpc) { dma_unit(0, jpc, lane); });
-    #pragma nounroll
+#pragma nounroll
                 for (int ip = 0; ip < 4; ++ip) {
                     // Lane-derived values are re-derived from an opaque copy of the
                     // lane index in every slice: hoisted out of the tile loop they
@@ -1510,10 +1526,10 @@ mx_gemm_kernel(GemmProblem p) {
                     asm volatile("" : "+v"(lane));
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2], drs[2];
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const int rl = (2 * ip + ii) * 16 + r16;
-                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                        rr[ii] = rl < rows_valid_w ? s_rs[wm * 128 + rl] : 0.0f;
                         drs[ii] = 0.f;
                     }
                     static_for<4>([&](auto jpc) {
@@ -1530,9 +1546,9 @@ mx_gemm_kernel(GemmProblem p) {
                             if constexpr (jp == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
                             if constexpr (jp == 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                         }
-    #pragma unroll
+#pragma unroll
                         for (int ii = 0; ii < 2; ++ii)
-    #pragma unroll
+#pragma unroll
                             for (int jj = 0; jj < 2; ++jj)
                                 hb[ii][jj] = *reinterpret_cast<const uint4*>(
                                     ring + ((jp * 2 + ii) * 2 + jj) * 1024 + lane * 16);
@@ -1546,16 +1562,16 @@ mx_gemm_kernel(GemmProblem p) {
                         // token-axis blocks they share with valid rows.  A wave's
                         // columns are all below F or all past it (dz = 0 from
                         // zero-filled B rows, h loads of zero range).
-    #pragma unroll
+#pragma unroll
                         for (int ii = 0; ii < 2; ++ii) {
                             const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
-    #pragma unroll
+#pragma unroll
                             for (int jj = 0; jj < 2; ++jj) {
                                 float a[4], b[4];
                                 const uint4 hv = hb[ii][jj];
                                 unpack4_bf16(make_uint2(hv.x, hv.y), a);
                                 unpack4_bf16(make_uint2(hv.z, hv.w), b);
-    #pragma unroll
+#pragma unroll
                                 for (int v = 0; v < 4; ++v) {
                                     const float av = a[v], bv = b[v];
                                     const float dz = rv ? dzu[ii][jj][v] : 0.f;
@@ -1571,7 +1587,7 @@ mx_gemm_kernel(GemmProblem p) {
                         quant_unit<256>(da, 2 * jp * 16, ip, st, lane);
                         quant_unit<256>(db, 128 + 2 * jp * 16, ip, st, lane);
                     });
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const float sum = sum4q(drs[ii]);
                         const int rl = (2 * ip + ii) * 16 + r16;
@@ -1609,17 +1625,17 @@ mx_gemm_kernel(GemmProblem p) {
                         *reinterpret_cast<v4f*>(stash + ((ii * 8 + j) * 64 + lane) * 16) = acc[6 + ii][j];
                     });
                 });
-    #pragma nounroll
+#pragma nounroll
                 for (int ip = 0; ip < 4; ++ip) {
                     // lane-derived values re-derived per slice (see the forward)
                     int lane = lane_id;
                     asm volatile("" : "+v"(lane));
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2], drs[2];
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const int rl = (2 * ip + ii) * 16 + r16;
-                        rr[ii] = rl < rows_valid_w ? p.rscale[rwave + rl] : 0.0f;
+                        rr[ii] = rl < rows_valid_w ? s_rs[wm * 128 + rl] : 0.0f;
                         drs[ii] = 0.f;
                     }
                     static_for<2>([&](auto jpc) {
@@ -1632,12 +1648,12 @@ mx_gemm_kernel(GemmProblem p) {
                         // b and dz): rows past M read never-written scale bytes,
                         // so their accumulators may be anything, NaN included,
                         // and the padded rows take part in the token-axis blocks.
-    #pragma unroll
+#pragma unroll
                         for (int ii = 0; ii < 2; ++ii) {
                             const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
-    #pragma unroll
+#pragma unroll
                             for (int jj = 0; jj < 2; ++jj)
-    #pragma unroll
+#pragma unroll
                                 for (int v = 0; v < 4; ++v) {
                                     const float av = rv ? ga[ii][jj][v] : 0.f;
                                     const float bv = rv ? ua[ii][jj][v] : 0.f;
@@ -1653,7 +1669,7 @@ mx_gemm_kernel(GemmProblem p) {
                         quant_unit<128>(da, 2 * jp * 16, ip, st, lane);
                         quant_unit<128>(db, 64 + 2 * jp * 16, ip, st, lane);
                     });
-    #pragma unroll
+#pragma unroll
                     for (int ii = 0; ii < 2; ++ii) {
                         const float sum = sum4q(drs[ii]);
                         const int rl = (2 * ip + ii) * 16 + r16;
