@@ -703,33 +703,51 @@ __device__ __forceinline__ void wait_vmcnt() {
 // or past nk use zero-range descriptors: they write zeros into a stage
 // nobody reads, so every step issues the same instructions and the vmcnt
 // counts hold without branches; the caller waits for those trailing loads
-// before it reuses the stages.
-template <int NJ>
+// before it reuses the stages.  A Tail other than ZeroTail replaces those
+// trailing loads: tail(slot, stage, kn) issues load slot u (same count per
+// pass) of step kn = 0, 1 of whatever runs next on the stages.  The steps
+// whose loads fall inside the K range run a loop body without the
+// zero-range selects.
+struct ZeroTail {};
+struct ZeroTailMaker {
+    __device__ ZeroTail operator()() const { return {}; }
+};
+
+template <int NJ, class MakeTail = ZeroTailMaker>
 __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const TileSrc& o,
-                                          int nk, int wave, int wm, int wn, int lane) {
+                                          int nk, int wave, int wm, int wn, int lane,
+                                          MakeTail make_tail = {}) {
     using SC = Sched<NJ>;
     const int r16 = lane & 15, q = lane >> 4;
     const int swz = r16 & 7;
     const uint32_t smb = uni((int)lds_addr(&sm));
-    auto dma_u = [&](auto uc, int st, int ks) {
+    // load slot u of step ks into stage st; LIVE: the step is known to be
+    // inside the K range, else it is checked
+    auto dma_u = [&](auto uc, auto livec, int st, int ks) {
         constexpr int u = decltype(uc)::value;
-        const bool live = ks < nk;
+        const bool live = decltype(livec)::value || ks < nk;
         const uint32_t k0 = (uint32_t)ks * BK;
+        auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
         if constexpr (u < 8) {
-            const v4i r = live ? o.ra : v4i{o.ra.x, o.ra.y, 0, o.ra.w};
-            dma_b128(r, stage_lds<kPartA>(smb, st, (wave * 8 + u) * 1024), o.aoff[u], k0);
+            dma_b128(rng(o.ra), stage_lds<kPartA>(smb, st, (wave * 8 + u) * 1024), o.aoff[u], k0);
         } else if constexpr (u < 8 + NJ) {
-            const v4i r = live ? o.rb : v4i{o.rb.x, o.rb.y, 0, o.rb.w};
-            dma_b128(r, stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024), o.boff[u - 8], k0);
+            dma_b128(rng(o.rb), stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024),
+                     o.boff[u - 8], k0);
         } else if constexpr (u == 8 + NJ) {
-            const v4i rs = o.sa.rsrc;
-            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, stage_lds<kPartAs>(smb, st, wave * 64 * 4), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
+            dma_b32(rng(o.sa.rsrc), stage_lds<kPartAs>(smb, st, wave * 64 * 4), o.sa.voff,
+                    o.sa.s0 + ks * o.sa.sstep);
         } else {
-            const v4i rs = o.sb.rsrc;
-            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, stage_lds<kPartBs>(smb, st, wave * 64 * 4), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
+            dma_b32(rng(o.sb.rsrc), stage_lds<kPartBs>(smb, st, wave * 64 * 4), o.sb.voff,
+                    o.sb.s0 + ks * o.sb.sstep);
         }
+    };
+    // the loads of a step: within the K range, or past its end (the tail)
+    using Tail = decltype(make_tail());
+    auto load = [&](auto uc, auto tailc, const Tail* tail, int st, int ks) {
+        if constexpr (!decltype(tailc)::value || std::is_same<Tail, ZeroTail>::value)
+            dma_u(uc, std::integral_constant<bool, !decltype(tailc)::value>{}, st, ks);
+        else
+            (*tail)(uc, st, ks - nk);
     };
 
     // Fragments of stage st into registers.  The scaled 16x16x128 MFMA reads
@@ -763,14 +781,7 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
     };
-
-    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 0, 0); });
-    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 1, 1); });
-    wait_vmcnt<SC::kLoads>();                           // step 0 (this wave)
-    lds_barrier();                                      // step 0 (every wave)
-    static_for<8>([&](auto ic) { read_a(ic, 0); });
-    static_for<NJ>([&](auto jc) { read_b(jc, 0); });
-    for (int ks = 0; ks < nk; ++ks) {
+    auto step = [&](int ks, auto tailc, const Tail* tail) {
         const int cur = ks & 1, nxt = cur ^ 1;
         lds_barrier();                                  // S1: stage cur is free
         // pass A: slot s is column j = s / 4, row i = s % 4
@@ -779,7 +790,7 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
             mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{});
             __builtin_amdgcn_sched_barrier(0);
             constexpr int u = SC::a_at(s);
-            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            if constexpr (u >= 0) load(std::integral_constant<int, u>{}, tailc, tail, cur, ks + 2);
             __builtin_amdgcn_sched_barrier(0);
         });
         wait_vmcnt<SC::kNA>();
@@ -793,9 +804,22 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
             if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, i>{}, nxt);
             if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
             constexpr int u = SC::b_at(s);
-            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            if constexpr (u >= 0) load(std::integral_constant<int, u>{}, tailc, tail, cur, ks + 2);
             __builtin_amdgcn_sched_barrier(0);
         });
+    };
+
+    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, std::false_type{}, 0, 0); });
+    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, std::false_type{}, 1, 1); });
+    wait_vmcnt<SC::kLoads>();                           // step 0 (this wave)
+    lds_barrier();                                      // step 0 (every wave)
+    static_for<8>([&](auto ic) { read_a(ic, 0); });
+    static_for<NJ>([&](auto jc) { read_b(jc, 0); });
+    int ks = 0;
+    for (; ks + 2 < nk; ++ks) step(ks, std::false_type{}, nullptr);
+    if (ks < nk) {
+        const Tail tail = make_tail();
+        for (; ks < nk; ++ks) step(ks, std::true_type{}, &tail);
     }
 }
 
@@ -978,42 +1002,57 @@ __device__ __forceinline__ constexpr int lean_arow(int w, int u) {
                                                        : 128 + 8 * (4 * w + (u & 3) - 8));
 }
 
+// The loads of one K step of tile_gemm_lean<NJ>: load u of step ks into
+// stage st (the region layout above; steps at or past nk are zero-range).
+// Also the tail of the GEMM that runs before it on the same stages.
+template <int NJ>
+struct LeanLoads {
+    TileSrc o;                   // o.aoff is not used: A rows follow the regions
+    uint32_t aoffl[8];
+    uint32_t smb;
+    int wave, nk;
+    __device__ LeanLoads(const TileSrc& o_, int64_t lda, uint32_t smb_, int wave_, int lane,
+                         int nk_)
+        : o(o_), smb(smb_), wave(wave_), nk(nk_) {
+        const int dma_row = lane >> 3;
+        const int dma_chunk = (lane & 7) ^ (dma_row & 7);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            aoffl[u] = (uint32_t)((lean_arow(wave, u) + dma_row) * lda + dma_chunk * 16);
+    }
+    template <int u>
+    __device__ __forceinline__ void load(int st, int ks) const {
+        const bool live = ks < nk;
+        const uint32_t k0 = (uint32_t)ks * BK;
+        auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
+        if constexpr (u < 8) {
+            dma_b128(rng(o.ra), stage_lds<kPartA>(smb, st, lean_arow(wave, u) * BK), aoffl[u], k0);
+        } else if constexpr (u < 8 + NJ) {
+            dma_b128(rng(o.rb), stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024),
+                     o.boff[u - 8], k0);
+        } else if constexpr (u == 8 + NJ) {
+            dma_b32(rng(o.sb.rsrc), stage_lds<kPartBs>(smb, st, wave * 64 * 4), o.sb.voff,
+                    o.sb.s0 + ks * o.sb.sstep);
+        } else {
+            dma_b32(rng(o.sa.rsrc), stage_lds<kPartAs>(smb, st, wave * 64 * 4), o.sa.voff,
+                    o.sa.s0 + ks * o.sa.sstep);
+        }
+    }
+};
+
+// pre: steps 0 and 1 were issued by the GEMM before it (its tail) into
+// stages base and base ^ 1, and step 0 is complete for every wave; step ks
+// lives in stage (base + ks) & 1.
 template <int NJ>
 __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, const TileSrc& o,
                                                int nk, int wave, int wm, int wn, int lane,
-                                               int64_t lda) {
+                                               int64_t lda, int base = 0, bool pre = false) {
     using SC = LeanSched<NJ>;
     const int r16 = lane & 15, q = lane >> 4;
     const int swz = r16 & 7;
-    const int dma_row = lane >> 3;
-    const int dma_chunk = (lane & 7) ^ (dma_row & 7);
-    // A offsets of this wave's 8 loads (the region layout above); o.aoff is
-    // not used
-    uint32_t aoffl[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-        aoffl[u] = (uint32_t)((lean_arow(wave, u) + dma_row) * lda + dma_chunk * 16);
-    const uint32_t smb = uni((int)lds_addr(&sm));
-    auto dma_u = [&](auto uc, int st, int ks) {
-        constexpr int u = decltype(uc)::value;
-        const bool live = ks < nk;
-        const uint32_t k0 = (uint32_t)ks * BK;
-        if constexpr (u < 8) {
-            const v4i r = live ? o.ra : v4i{o.ra.x, o.ra.y, 0, o.ra.w};
-            dma_b128(r, stage_lds<kPartA>(smb, st, lean_arow(wave, u) * BK), aoffl[u], k0);
-        } else if constexpr (u < 8 + NJ) {
-            const v4i r = live ? o.rb : v4i{o.rb.x, o.rb.y, 0, o.rb.w};
-            dma_b128(r, stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024), o.boff[u - 8], k0);
-        } else if constexpr (u == 8 + NJ) {
-            const v4i rs = o.sb.rsrc;
-            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, stage_lds<kPartBs>(smb, st, wave * 64 * 4), o.sb.voff, o.sb.s0 + ks * o.sb.sstep);
-        } else {
-            const v4i rs = o.sa.rsrc;
-            const v4i r = live ? rs : v4i{rs.x, rs.y, 0, rs.w};
-            dma_b32(r, stage_lds<kPartAs>(smb, st, wave * 64 * 4), o.sa.voff, o.sa.s0 + ks * o.sa.sstep);
-        }
-    };
+    const int b0 = uni(base);
+    const LeanLoads<NJ> L(o, lda, uni((int)lds_addr(&sm)), wave, lane, nk);
+    auto dma_u = [&](auto uc, int st, int ks) { L.template load<decltype(uc)::value>(st, ks); };
     v8i af[4], bfr[NJ];
     int asc[4], bsc[NJ];
     // row i (0..7) of the wave into register slot i & 3
@@ -1043,14 +1082,16 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
             bfr[j], af[i & 3], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i & 3]);
     };
 
-    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 0, 0); });
-    static_for<SC::kLoads>([&](auto uc) { dma_u(uc, 1, 1); });
-    wait_vmcnt<SC::kLoads>();                           // step 0 (this wave)
-    lds_barrier();                                      // step 0 (every wave)
-    static_for<4>([&](auto ic) { read_a(ic, 0); });
-    static_for<NJ>([&](auto jc) { read_b(jc, 0); });
+    if (!pre) {
+        static_for<SC::kLoads>([&](auto uc) { dma_u(uc, b0, 0); });
+        static_for<SC::kLoads>([&](auto uc) { dma_u(uc, b0 ^ 1, 1); });
+        wait_vmcnt<SC::kLoads>();                       // step 0 (this wave)
+        lds_barrier();                                  // step 0 (every wave)
+    }
+    static_for<4>([&](auto ic) { read_a(ic, b0); });
+    static_for<NJ>([&](auto jc) { read_b(jc, b0); });
     for (int ks = 0; ks < nk; ++ks) {
-        const int cur = ks & 1, nxt = cur ^ 1;
+        const int cur = (b0 + ks) & 1, nxt = cur ^ 1;
         lds_barrier();                                  // S1: B, R0 and B scales of cur are free
         // pass A: rows 0..3; in the last column row i + 4 replaces row i
         static_for<4 * NJ>([&](auto sc) {
@@ -1375,7 +1416,38 @@ mx_gemm_kernel(GemmProblem p) {
             for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-            if constexpr (kGU) {
+            // the recompute backward's dz GEMM (A2: dY rowwise, B2: W2
+            // columnwise, K = H) for the tile's rows and 128 columns of F
+            auto dz_src = [&](int ln) {
+                return tile_src<false, 4>(p.A2, p.B2, m0, mvalid, (int64_t)g * p.B2.gstride + n0,
+                                          p.F - n0, 0, K, brow_plain, wave, ln);
+            };
+            if constexpr (EPI == Epi::kDSwigluR) {
+                // [a | b]'s last two K steps fetch the dz GEMM's first two (its
+                // loads 0..13 in the slots of loads 0..13, the 4 slots left as
+                // zero-range loads into the half of the B stage the dz GEMM
+                // does not use), so that GEMM starts without a prologue
+                const TileSrc o = tile_src<false, 8>(p.A, p.B, m0, mvalid, bg, 2 * p.F, klo, K,
+                                                     brow_gu, wave, lane);
+                const uint32_t smb = uni((int)lds_addr(&sm));
+                auto make_tail = [&]() {
+                    int lane3 = lane_id;
+                    asm volatile("" : "+v"(lane3));
+                    const LeanLoads<4> L(dz_src(lane3), p.A2.ld, smb, wave, lane3, nk);
+                    return [L, smb, wave](auto uc, int st, int kn) {
+                        constexpr int u = decltype(uc)::value;
+                        if constexpr (u < LeanSched<4>::kLoads) {
+                            L.template load<u>(st, kn);
+                        } else {
+                            const v4i z{L.o.rb.x, L.o.rb.y, 0, L.o.rb.w};
+                            dma_b128(z, stage_lds<kPartB>(smb, st, (16 + wave * 4 + (u - 14)) * 1024),
+                                     0u, 0u);
+                        }
+                    };
+                };
+                static_assert(Sched<8>::kLoads == LeanSched<4>::kLoads + 4, "tail slots");
+                tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane, make_tail);
+            } else if constexpr (kGU) {
                 const TileSrc o = tile_src<false, 8>(p.A, p.B, m0, mvalid, bg, 2 * p.F, klo, K,
                                                      brow_gu, wave, lane);
                 tile_gemm<8>(acc, sm, o, nk, wave, wm, wn, lane);
@@ -1386,12 +1458,16 @@ mx_gemm_kernel(GemmProblem p) {
             }
             // The fused epilogues stage their outputs in LDS, which overlaps every
             // wave's operand stages: wait until the trailing (zero-range) loads of
-            // all waves have landed.
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();
+            // all waves have landed (before the dz GEMM only if [a | b] did not
+            // chain into it).
+            const bool chained = EPI == Epi::kDSwigluR && nk >= 2;
+            if (!chained) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                lds_barrier();
+            }
             // Recompute backward: the second GEMM of the tile, dz = dY . W2 for
-            // the same rows and the tile's 128 columns of F (A2: dY rowwise, B2:
-            // W2 columnwise, K = H), while acc keeps the recomputed [a | b].
+            // the same rows and the tile's 128 columns of F, while acc keeps the
+            // recomputed [a | b].
             v4f dacc[8][4];
             if constexpr (EPI == Epi::kDSwigluR) {
 #pragma unroll
@@ -1400,10 +1476,8 @@ mx_gemm_kernel(GemmProblem p) {
                     for (int j = 0; j < 4; ++j) dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
                 int lane2 = lane_id;
                 asm volatile("" : "+v"(lane2));
-                const TileSrc o = tile_src<false, 4>(p.A2, p.B2, m0, mvalid,
-                                                     (int64_t)g * p.B2.gstride + n0, p.F - n0, 0, K,
-                                                     brow_plain, wave, lane2);
-                tile_gemm_lean<4>(dacc, sm, o, nk, wave, wm, wn, lane2, p.A2.ld);
+                tile_gemm_lean<4>(dacc, sm, dz_src(lane2), nk, wave, wm, wn, lane2, p.A2.ld,
+                                  nk & 1, chained);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 lds_barrier();
             }
