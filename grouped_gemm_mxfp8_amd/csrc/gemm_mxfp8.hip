@@ -1020,9 +1020,9 @@ struct LeanLoads {
         for (int u = 0; u < 8; ++u)
             aoffl[u] = (uint32_t)((lean_arow(wave, u) + dma_row) * lda + dma_chunk * 16);
     }
-    template <int u>
+    template <int u, bool LIVE = false>     // LIVE: ks is known to be < nk
     __device__ __forceinline__ void load(int st, int ks) const {
-        const bool live = ks < nk;
+        const bool live = LIVE || ks < nk;
         const uint32_t k0 = (uint32_t)ks * BK;
         auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
         if constexpr (u < 8) {
@@ -1053,6 +1053,10 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
     const int b0 = uni(base);
     const LeanLoads<NJ> L(o, lda, uni((int)lds_addr(&sm)), wave, lane, nk);
     auto dma_u = [&](auto uc, int st, int ks) { L.template load<decltype(uc)::value>(st, ks); };
+    // the loads of a step known to be inside the K range
+    auto dma_live = [&](auto uc, int st, int ks) {
+        L.template load<decltype(uc)::value, true>(st, ks);
+    };
     v8i af[4], bfr[NJ];
     int asc[4], bsc[NJ];
     // row i (0..7) of the wave into register slot i & 3
@@ -1090,7 +1094,7 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
     }
     static_for<4>([&](auto ic) { read_a(ic, b0); });
     static_for<NJ>([&](auto jc) { read_b(jc, b0); });
-    for (int ks = 0; ks < nk; ++ks) {
+    auto step = [&](int ks, auto ld) {
         const int cur = (b0 + ks) & 1, nxt = cur ^ 1;
         lds_barrier();                                  // S1: B, R0 and B scales of cur are free
         // pass A: rows 0..3; in the last column row i + 4 replaces row i
@@ -1100,7 +1104,7 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, 4 + s % 4>{}, cur);
             constexpr int u = SC::a_at(s);
-            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            if constexpr (u >= 0) ld(std::integral_constant<int, u>{}, cur, ks + 2);
             __builtin_amdgcn_sched_barrier(0);
         });
         wait_vmcnt<SC::kNA>();
@@ -1114,10 +1118,13 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
             if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
             if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, s % 4>{}, nxt);
             constexpr int u = SC::b_at(s);
-            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, cur, ks + 2);
+            if constexpr (u >= 0) ld(std::integral_constant<int, u>{}, cur, ks + 2);
             __builtin_amdgcn_sched_barrier(0);
         });
-    }
+    };
+    int ks = 0;
+    for (; ks + 2 < nk; ++ks) step(ks, dma_live);
+    for (; ks < nk; ++ks) step(ks, dma_u);
 }
 
 // Position of one tile (or split-tail chunk) of a launch.
