@@ -756,25 +756,30 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
     // block q of row r (pinned on the device by per-block scale probes).
     v8i af[8], bfr[NJ];
     int asc[8], bsc[NJ];
+    // Per-lane byte offsets of the lane's first fragment row (row i adds
+    // i * 16 rows, a constant): the reads of one stage then share one base
+    // per kind and differ only in their immediate offsets.
+    const int a_row0 = wm * 128 + r16, b_row0 = wn * (NJ * 16) + r16;
+    const int a_lo = a_row0 * BK + ((q ^ swz) << 4), a_hi = a_row0 * BK + (((q + 4) ^ swz) << 4);
+    const int b_lo = b_row0 * BK + ((q ^ swz) << 4), b_hi = b_row0 * BK + (((q + 4) ^ swz) << 4);
+    const int a_s = a_row0 * 4 + q, b_s = b_row0 * 4 + q;
     auto read_a = [&](auto ic, int st) {
         constexpr int i = decltype(ic)::value;
-        const int row = wm * 128 + i * 16 + r16;
-        const uint8_t* base = &sm.a[st][row * BK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        const uint8_t* stg = sm.a[st];
+        const uint4 lo = *reinterpret_cast<const uint4*>(stg + a_lo + i * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(stg + a_hi + i * 16 * BK);
         af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        asc[i] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
+        asc[i] = (reinterpret_cast<const uint8_t*>(sm.as[st]) + a_s)[i * 16 * 4];
     };
     auto read_b = [&](auto jc, int st) {
         constexpr int j = decltype(jc)::value;
-        const int row = wn * (NJ * 16) + j * 16 + r16;
-        const uint8_t* base = &sm.b[st][row * BK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        const uint8_t* stg = sm.b[st];
+        const uint4 lo = *reinterpret_cast<const uint4*>(stg + b_lo + j * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(stg + b_hi + j * 16 * BK);
         bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
+        bsc[j] = (reinterpret_cast<const uint8_t*>(sm.bs[st]) + b_s)[j * 16 * 4];
     };
     auto mfma = [&](auto ic, auto jc) {
         constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
@@ -896,25 +901,28 @@ __device__ __forceinline__ void tile_gemm_chain(v4f (&acc)[8][8], GemmSmem& sm, 
 
     v8i af[8], bfr[NJ];
     int asc[8], bsc[NJ];
+    // per-lane offsets of the first fragment row, as in tile_gemm
+    const int a_row0 = wm * 128 + r16, b_row0 = wn * (NJ * 16) + r16;
+    const int a_lo = a_row0 * BK + ((q ^ swz) << 4), a_hi = a_row0 * BK + (((q + 4) ^ swz) << 4);
+    const int b_lo = b_row0 * BK + ((q ^ swz) << 4), b_hi = b_row0 * BK + (((q + 4) ^ swz) << 4);
+    const int a_s = a_row0 * 4 + q, b_s = b_row0 * 4 + q;
     auto read_a = [&](auto ic, int st) {
         constexpr int i = decltype(ic)::value;
-        const int row = wm * 128 + i * 16 + r16;
-        const uint8_t* b = &sm.a[st][row * BK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(b + ((q ^ swz) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(b + (((q + 4) ^ swz) << 4));
+        const uint8_t* stg = sm.a[st];
+        const uint4 lo = *reinterpret_cast<const uint4*>(stg + a_lo + i * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(stg + a_hi + i * 16 * BK);
         af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        asc[i] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
+        asc[i] = (reinterpret_cast<const uint8_t*>(sm.as[st]) + a_s)[i * 16 * 4];
     };
     auto read_b = [&](auto jc, int st) {
         constexpr int j = decltype(jc)::value;
-        const int row = wn * (NJ * 16) + j * 16 + r16;
-        const uint8_t* b = &sm.b[st][row * BK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(b + ((q ^ swz) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(b + (((q + 4) ^ swz) << 4));
+        const uint8_t* stg = sm.b[st];
+        const uint4 lo = *reinterpret_cast<const uint4*>(stg + b_lo + j * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(stg + b_hi + j * 16 * BK);
         bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
+        bsc[j] = (reinterpret_cast<const uint8_t*>(sm.bs[st]) + b_s)[j * 16 * 4];
     };
     auto mfma = [&](auto ic, auto jc) {
         constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
@@ -1059,26 +1067,29 @@ __device__ __forceinline__ void tile_gemm_lean(v4f (&acc)[8][NJ], GemmSmem& sm, 
     };
     v8i af[4], bfr[NJ];
     int asc[4], bsc[NJ];
+    // per-lane offsets of the first fragment row, as in tile_gemm
+    const int a_row0 = wm * 128 + r16, b_row0 = wn * (NJ * 16) + r16;
+    const int a_lo = a_row0 * BK + ((q ^ swz) << 4), a_hi = a_row0 * BK + (((q + 4) ^ swz) << 4);
+    const int b_lo = b_row0 * BK + ((q ^ swz) << 4), b_hi = b_row0 * BK + (((q + 4) ^ swz) << 4);
+    const int a_s = a_row0 * 4 + q, b_s = b_row0 * 4 + q;
     // row i (0..7) of the wave into register slot i & 3
     auto read_a = [&](auto ic, int st) {
         constexpr int i = decltype(ic)::value;
-        const int row = wm * 128 + i * 16 + r16;
-        const uint8_t* base = &sm.a[st][row * BK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        const uint8_t* stg = sm.a[st];
+        const uint4 lo = *reinterpret_cast<const uint4*>(stg + a_lo + i * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(stg + a_hi + i * 16 * BK);
         af[i & 3] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        asc[i & 3] = reinterpret_cast<const uint8_t*>(sm.as[st])[row * 4 + q];
+        asc[i & 3] = (reinterpret_cast<const uint8_t*>(sm.as[st]) + a_s)[i * 16 * 4];
     };
     auto read_b = [&](auto jc, int st) {
         constexpr int j = decltype(jc)::value;
-        const int row = wn * (NJ * 16) + j * 16 + r16;
-        const uint8_t* base = &sm.b[st][row * BK];
-        const uint4 lo = *reinterpret_cast<const uint4*>(base + ((q ^ swz) << 4));
-        const uint4 hi = *reinterpret_cast<const uint4*>(base + (((q + 4) ^ swz) << 4));
+        const uint8_t* stg = sm.b[st];
+        const uint4 lo = *reinterpret_cast<const uint4*>(stg + b_lo + j * 16 * BK);
+        const uint4 hi = *reinterpret_cast<const uint4*>(stg + b_hi + j * 16 * BK);
         bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        bsc[j] = reinterpret_cast<const uint8_t*>(sm.bs[st])[row * 4 + q];
+        bsc[j] = (reinterpret_cast<const uint8_t*>(sm.bs[st]) + b_s)[j * 16 * 4];
     };
     auto mfma = [&](auto ic, auto jc) {     // ic: wave row 0..7 (register slot ic & 3)
         constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
