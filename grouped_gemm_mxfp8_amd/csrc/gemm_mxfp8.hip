@@ -1488,10 +1488,17 @@ mx_gemm_kernel(GemmProblem p) {
             // recomputed [a | b].
             v4f dacc[8][4];
             if constexpr (EPI == Epi::kDSwigluR) {
+                // each block its own zero: one zero shared by all of them (as
+                // the compiler would make it) keeps the loop-carried blocks
+                // from getting their own registers, and the dz loop then
+                // moves accumulators around every step
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                    for (int j = 0; j < 4; ++j) {
+                        dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                        asm volatile("" : "+a"(dacc[i][j]));
+                    }
                 int lane2 = lane_id;
                 asm volatile("" : "+v"(lane2));
                 tile_gemm_lean<4>(dacc, sm, dz_src(lane2), nk, wave, wm, wn, lane2, p.A2.ld,
