@@ -107,6 +107,29 @@ def test_mxfp8_linear_small(dev, counts, K, N):
     assert_parity(to64(ys), ref_s)
 
 
+@pytest.mark.parametrize("K", [128, 256, 384])
+def test_mxfp8_linear_chained_tiles(dev, K):
+    """More tiles than workgroups (273 M-tiles x 2 N-tiles = 546 tiles on 256
+    workgroups), so each workgroup runs a chain of tiles whose last K steps
+    fetch the next tile's first ones; K = 128, 256, 384 are 1, 2 and 3 K
+    steps (a chain link needs two)."""
+    counts = [40000, 37, 0, 29000, 5]
+    x, w, off_np = _mx_case(dev, counts, K, 512, seed=K, outliers=True)
+    off = torch.from_numpy(off_np).to(dev)
+    xq = gm.mxfp8_quantize(x.to(dev), rowwise=True)["row"]
+    wq = gm.mxfp8_quantize(w.to(dev), rowwise=True)["row"]
+    r = torch.rand(x.shape[0], generator=torch.Generator().manual_seed(2)).to(dev)
+    y = gm.grouped_linear_fwd(xq, off, wq)
+    ys = gm.grouped_linear_fwd(xq, off, wq, row_scale=r)
+    torch.cuda.synchronize()
+    stage = O.grouped_linear(deq(xq), deq(wq), off_np)
+    assert_parity(to64(y), stage, rel=4e-3, row=3e-2)
+    assert_parity(to64(ys), stage * r.cpu().numpy().astype(np.float64)[:, None],
+                  rel=4e-3, row=3e-2)
+    ref = O.grouped_linear_mxfp8(to64(x), to64(w), off_np)
+    assert_parity(to64(y), ref)
+
+
 def test_mxfp8_linear_full_workload(dev):
     """T=8192 top-2 (M=16384), E=8, K=1024, N=2816 with 1% outliers, the
     launch bench.py times for this workload."""

@@ -240,6 +240,9 @@ MODES = [pytest.param(False, id="recompute"), pytest.param(True, id="save_h")]
     ([300, 0, 257, 143], 256, 384),          # F/256 not integral: masked dz tiles (save-h)
     ([1, 33, 0, 250, 95, 0, 129, 6], 512, 256),
     ([600, 600], 384, 128),
+    # 17 M-tiles x 16 F-tiles = 272 tiles: two per workgroup for some; K = H = 128
+    # is one K step (the recompute backward's dz GEMM then runs its own prologue)
+    ([2000, 1500, 700], 128, 2048),
 ])
 def test_mlp_small(dev, counts, H, F, save_h):
     run_case(dev, small_case(counts, H, F, seed=H + F), save_h=save_h)
