@@ -1544,23 +1544,17 @@ mx_gemm_kernel(GemmProblem p) {
                         float gu[2][2][4], uu[2][2][4], z[2][2][4];
                         pick_unit<2 * jp>(acc, ip, gu);
                         pick_unit<2 * jp + 4>(acc, ip, uu);
-                        // Rows past the expert's valid rows are selected to 0 (h
-                        // and z): the padded rows take part in the token-axis
-                        // blocks, and rows past M read never-written scale bytes
-                        // (the tiled layout pads rows to 32), so their
-                        // accumulators may be anything, NaN included.
+                        // Rows past the expert's valid rows (they take part in
+                        // the token-axis blocks) hold exact zeros: their codes
+                        // read as zero through the range checks and their scales
+                        // are finite (the quantizer writes the tiled layout's
+                        // padding rows), and their routing weights are zero.
 #pragma unroll
                         for (int ii = 0; ii < 2; ++ii) {
                             const int i = 2 * ip + ii;
-                            const bool rv = i * 16 + r16 < rows_valid_w;
 #pragma unroll
                             for (int jj = 0; jj < 2; ++jj) {
                                 const int j = 2 * jp + jj;
-#pragma unroll
-                                for (int v = 0; v < 4; ++v) {
-                                    gu[ii][jj][v] = rv ? gu[ii][jj][v] : 0.f;
-                                    uu[ii][jj][v] = rv ? uu[ii][jj][v] : 0.f;
-                                }
                                 if (p.h && rows_pad_w > 0) {
                                     const uint2 g2 = pack4_bf16(gu[ii][jj]), u2 = pack4_bf16(uu[ii][jj]);
                                     store_nt(h_block(p.h, prow + i * 16, cw + j * 16, F, lane),
@@ -1743,20 +1737,18 @@ mx_gemm_kernel(GemmProblem p) {
                         pick_unit_stashed<2 * jp>(acc, ip, ga, stash, lane);
                         pick_unit_stashed<2 * jp + 4>(acc, ip, ua, stash, lane);
                         pick_unit<2 * jp>(dacc, ip, dzu);
-                        // Rows past the expert's valid rows are selected to 0 (a,
-                        // b and dz): rows past M read never-written scale bytes,
-                        // so their accumulators may be anything, NaN included,
-                        // and the padded rows take part in the token-axis blocks.
+                        // Rows past the expert's valid rows (they take part in
+                        // the token-axis blocks) hold exact zeros in a, b and dz,
+                        // as in the forward, and zero routing weights.
 #pragma unroll
                         for (int ii = 0; ii < 2; ++ii) {
-                            const bool rv = (2 * ip + ii) * 16 + r16 < rows_valid_w;
 #pragma unroll
                             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                                 for (int v = 0; v < 4; ++v) {
-                                    const float av = rv ? ga[ii][jj][v] : 0.f;
-                                    const float bv = rv ? ua[ii][jj][v] : 0.f;
-                                    const float dz = rv ? dzu[ii][jj][v] : 0.f;
+                                    const float av = ga[ii][jj][v];
+                                    const float bv = ua[ii][jj][v];
+                                    const float dz = dzu[ii][jj][v];
                                     float sg;
                                     const float sl_ = silu_sig(av, sg);
                                     drs[ii] += dz * (sl_ * bv);

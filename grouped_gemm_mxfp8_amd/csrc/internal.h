@@ -17,10 +17,12 @@ constexpr int kMaxGroups = 1024;   // largest expert count the kernels accept
 //    consecutive rows form one 128-byte line, so a K step of a 256-row tile
 //    reads 8 lines instead of 256:
 //      byte ((r / 32) * (Kp / 128) + kb / 4) * 128 + (r % 32) * 4 + kb % 4,
-//    Kp % 128 == 0, rows padded to a multiple of 32.  The scale bytes of the
-//    padding rows are never written: GEMM rows that read them are not stored,
-//    and the fused epilogues select those rows to zero before any reduction
-//    across rows.
+//    Kp % 128 == 0, rows padded to a multiple of 32.  The tile quantizer
+//    writes code 0 (2^-127) into the padding rows' scale bytes, so that the
+//    fused GEMMs, whose token-axis outputs take in rows past the last valid
+//    one, accumulate exact zeros for them (their codes read as zero through
+//    the range checks); other kernels' padding scale bytes are not written,
+//    and the GEMM rows that read them are not stored.
 __host__ __device__ inline int64_t tiled_scale_offset(int64_t r, int64_t kb, int64_t Kp) {
     return ((r >> 5) * (Kp >> 7) + (kb >> 2)) * 128 + (r & 31) * 4 + (kb & 3);
 }

@@ -296,6 +296,14 @@ quant_tiles128_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
     const int t = threadIdx.x;
     const int c16 = t & 15, rg = t >> 4;
     const int64_t col0 = (int64_t)blockIdx.x * 128;
+    // The tiled scale layout pads the rows to a multiple of 32: the first row
+    // tile of each column tile writes code 0 (2^-127, a finite scale) into the
+    // padding rows R .. of its four K blocks, so that a GEMM tile reading
+    // rows past R (their codes read as zero through the range checks)
+    // accumulates exact zeros there.
+    // (one batch only: batched copies continue in the next batch's rows)
+    if (tiled && rc && gridDim.z == 1 && blockIdx.y == 0 && t < (int)((32 - (R & 31)) & 31))
+        *reinterpret_cast<uint32_t*>(rs + tiled_scale_offset(R + t, col0 / 32, C)) = 0u;
     const int64_t ccol = col0 + c16 * 8;              // this lane's 8 columns (all < C)
     const __amdgpu_buffer_rsrc_t xr = gather
         ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0,
