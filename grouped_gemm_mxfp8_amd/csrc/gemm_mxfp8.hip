@@ -117,29 +117,52 @@ __device__ __forceinline__ uint32_t stage_lds(uint32_t smb, int st, int off) {
 }
 
 // Global -> LDS load of 16 (or 4) bytes per lane: lane l's bytes land at LDS
-// address lds + 16*l (4*l).  Issued through inline asm so that the compiler
-// does not track it: the kernel waits for these loads itself with vmcnt.
-// M0 carries the LDS base (declared clobbered: no other instruction in these
-// kernels reads M0); one wait state separates the M0 write from the load.
+// address lds + OFF + 16*l (4*l).  Issued through inline asm so that the
+// compiler does not track it: the kernel waits for these loads itself with
+// vmcnt.  M0 carries the LDS address (declared clobbered: no other
+// instruction in these kernels reads M0); one wait state separates the M0
+// write from the load.  OFF, a constant, is added into M0 by the same scalar
+// instruction that writes it, so that the loads of one stage share one base
+// register instead of each keeping its own address live in a scalar register.
+template <uint32_t OFF = 0>
 __device__ __forceinline__ void dma_b128(const v4i& rsrc, uint32_t lds, uint32_t voff,
                                          uint32_t soff) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
-        :
-        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
+    if constexpr (OFF == 0)
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen lds"
+            :
+            : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+            : "memory", "m0");
+    else
+        asm volatile(
+            "s_add_u32 m0, %0, %4\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen lds"
+            :
+            : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF)
+            : "memory", "m0", "scc");
 }
+template <uint32_t OFF = 0>
 __device__ __forceinline__ void dma_b32(const v4i& rsrc, uint32_t lds, uint32_t voff,
                                         uint32_t soff) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dword %1, %2, %3 offen lds"
-        :
-        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
-        : "memory", "m0");
+    if constexpr (OFF == 0)
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dword %1, %2, %3 offen lds"
+            :
+            : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+            : "memory", "m0");
+    else
+        asm volatile(
+            "s_add_u32 m0, %0, %4\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dword %1, %2, %3 offen lds"
+            :
+            : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF)
+            : "memory", "m0", "scc");
 }
 
 // Compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>),
@@ -168,6 +191,16 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
     return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The lane index, computed where it is used: a volatile computation is not
+// hoisted, so no per-lane value has to stay live across the tile loops (where
+// it would take a register, or a scratch slot whose reload waits with vmcnt
+// for every store and load in flight).
+__device__ __forceinline__ int lane_now() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
 }
 
 __device__ __forceinline__ float silu_sig(float a, float& sg) {
@@ -534,22 +567,48 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // gs: the tile's per-group output scale; rs: the wave's 128 routing weights
 // in LDS (rows wm*128 ..), or null.  Nothing here reads global memory: a
 // global load would wait (vmcnt) for every store and load in flight.
+// part (a chunk of a split tail tile): the fp32 accumulators go instead, as
+// they are, to the wave's blocks of a partial tile there (block (i, j) at
+// byte (i * 8 + j) * 1024, lane l's 16 bytes at 16 l).  Both outputs share
+// one pass over the row blocks, so the accumulators are read one way only.
 template <int NJ>
-__device__ __forceinline__ void store_tile_bf16_regs(const v4f (&acc)[8][NJ], const GemmProblem& p,
+__device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][NJ], const GemmProblem& p,
                                                      int g, int64_t m0, int64_t mvalid, int64_t n0,
                                                      int wm, int wn, int lane, float gs,
-                                                     const float* rs) {
+                                                     const float* rs, uint8_t* part = nullptr) {
     const int r16 = lane & 15, q = lane >> 4;
     const bool lo8 = r16 < 8;
     const int64_t rwave = m0 + wm * 128;
     const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
     uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (p.kgroup ? (int64_t)g * p.c_gstride : 0);
     const int64_t cw = n0 + wn * (NJ * 16);
+    // addresses: a wave-uniform base plus one 32-bit per-lane byte offset (the
+    // lane's row r16 & 7 and its 16-byte chunk of line 0); rows, the second
+    // half of a block and further lines only move the uniform base
+    uint8_t* const Cw = reinterpret_cast<uint8_t*>(C + rwave * p.ldc + cw);
+    const uint32_t ldb = (uint32_t)p.ldc * 2u;
+    const int chunk0 = (lo8 ? 0 : 4) + 2 * (q & 1) + (q >> 1);
+    const uint32_t loff = (uint32_t)(r16 & 7) * ldb + (uint32_t)chunk0 * 16u;
     auto ror8 = [](uint32_t v) {
         return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
     };
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+        // four waves keep the accumulators in AGPRs: pinned there at each row
+        // block, the block is moved to VGPRs only when it is converted (else
+        // the compiler may move the whole tile up front and spill)
+        if constexpr (NJ == 8) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
+        }
+        if (part) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                *reinterpret_cast<v4f*>(part + (int64_t)(i * 8 + j) * 1024 + (uint32_t)lane * 16u) =
+                    acc[i][j];
+            __builtin_amdgcn_sched_barrier(0);
+            continue;
+        }
         const float sc = rs ? rs[i * 16 + r16] * gs : gs;
         const int rl1 = i * 16 + (r16 & 7), rl2 = rl1 + 8;
 #pragma unroll
@@ -579,17 +638,19 @@ __device__ __forceinline__ void store_tile_bf16_regs(const v4f (&acc)[8][NJ], co
                 s1[v] = lo8 ? d[0][v] : rv[v];
                 s2[v] = lo8 ? rv[v] : d[1][v];
             }
-            const int jp = 2 * c + (lo8 ? 0 : 1);
-            const int chunk = (2 * jp + (q & 1)) * 2 + (q >> 1);
+            const int chunk = chunk0 + 8 * c;
             if (cw + chunk * 8 < p.N) {
+                uint8_t* const b1 = Cw + (int64_t)(i * 16) * ldb + c * 128;
                 if (rl1 < rows_valid_w)
-                    store_nt(C + (rwave + rl1) * p.ldc + cw + chunk * 8,
-                             make_uint4(s1[0], s1[1], s1[2], s1[3]));
+                    store_nt(b1 + loff, make_uint4(s1[0], s1[1], s1[2], s1[3]));
                 if (rl2 < rows_valid_w)
-                    store_nt(C + (rwave + rl2) * p.ldc + cw + chunk * 8,
-                             make_uint4(s2[0], s2[1], s2[2], s2[3]));
+                    store_nt(b1 + (int64_t)8 * ldb + loff, make_uint4(s2[0], s2[1], s2[2], s2[3]));
             }
         }
+        // one row block at a time: the scheduler would otherwise read ahead
+        // the accumulators of later blocks into registers the kernel has not
+        // got (and spill them, the reload then waiting for every store)
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -738,10 +799,10 @@ __device__ __forceinline__ void tile_gemm(v4f (&acc)[8][NJ], GemmSmem& sm, const
         const uint32_t k0 = (uint32_t)ks * BK;
         auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
         if constexpr (u < 8) {
-            dma_b128(rng(o.ra), stage_lds<kPartA>(smb, st, (wave * 8 + u) * 1024), o.aoff[u], k0);
+            dma_b128<u * 1024>(rng(o.ra), stage_lds<kPartA>(smb, st, wave * 8 * 1024), o.aoff[u], k0);
         } else if constexpr (u < 8 + NJ) {
-            dma_b128(rng(o.rb), stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024),
-                     o.boff[u - 8], k0);
+            dma_b128<(u - 8) * 1024>(rng(o.rb), stage_lds<kPartB>(smb, st, wave * NJ * 1024),
+                                     o.boff[u - 8], k0);
         } else if constexpr (u == 8 + NJ) {
             dma_b32(rng(o.sa.rsrc), stage_lds<kPartAs>(smb, st, wave * 64 * 4), o.sa.voff,
                     o.sa.s0 + ks * o.sa.sstep);
@@ -895,10 +956,10 @@ __device__ __forceinline__ void tile_gemm_chain(v4f (&acc)[8][8], GemmSmem& sm, 
         const uint32_t k0 = (uint32_t)ks * BK;
         auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
         if constexpr (u < 8) {
-            dma_b128(rng(src.ra), stage_lds<kPartA>(smb, st, (wave * 8 + u) * 1024), o.aoff[u], k0);
+            dma_b128<u * 1024>(rng(src.ra), stage_lds<kPartA>(smb, st, wave * 8 * 1024), o.aoff[u], k0);
         } else if constexpr (u < 8 + NJ) {
-            dma_b128(rng(src.rb), stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024),
-                     o.boff[u - 8], k0);
+            dma_b128<(u - 8) * 1024>(rng(src.rb), stage_lds<kPartB>(smb, st, wave * NJ * 1024),
+                                     o.boff[u - 8], k0);
         } else if constexpr (u == 8 + NJ) {
             dma_b32(rng(src.sar), stage_lds<kPartAs>(smb, st, wave * 64 * 4), src.sav,
                     src.sa0 + ks * o.sa.sstep);
@@ -1015,6 +1076,7 @@ __device__ __forceinline__ int a_group_row8(int wave, int u) {
     return (wave >> 2) * 128 + (wave & 3) * 16 + (u & 1) * 8 + (u >> 1) * 64;
 }
 
+template <bool UNIT>
 __device__ __forceinline__ TileSrc8 tile_src8(const MxOperand& A, const MxOperand& B, int64_t m0,
                                               int64_t mvalid, int64_t brow0, int64_t bvalid,
                                               int64_t klo, int64_t K, int wave, int lane) {
@@ -1030,8 +1092,8 @@ __device__ __forceinline__ TileSrc8 tile_src8(const MxOperand& A, const MxOperan
         o.boff[j] = (uint32_t)(((wave * 4 + j) * 8 + dma_row) * ldb + dma_chunk * 16);
     }
     const int lrow = (wave & 3) * 64 + lane;
-    o.sc = wave < 4 ? scale_src<true>(A.scales, lda, A.tiled, m0, mvalid, lrow, klo, K)
-                    : scale_src<true>(B.scales, ldb, B.tiled, brow0, bvalid, lrow, klo, K);
+    o.sc = wave < 4 ? scale_src<UNIT>(A.scales, lda, A.tiled, m0, mvalid, lrow, klo, K)
+                    : scale_src<UNIT>(B.scales, ldb, B.tiled, brow0, bvalid, lrow, klo, K);
     return o;
 }
 
@@ -1083,11 +1145,11 @@ __device__ __forceinline__ void tile_gemm_chain8(v4f (&acc)[8][4], GemmSmem& sm,
         const uint32_t k0 = (uint32_t)ks * BK;
         auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
         if constexpr (u < 4) {
-            dma_b128(rng(src.ra), stage_lds<kPartA>(smb, st, a_group_row8(wave, u) * BK), o.aoff[u],
-                     k0);
+            dma_b128<(uint32_t)(((u & 1) * 8 + (u >> 1) * 64) * BK)>(
+                rng(src.ra), stage_lds<kPartA>(smb, st, a_group_row8(wave, 0) * BK), o.aoff[u], k0);
         } else if constexpr (u < 8) {
-            dma_b128(rng(src.rb), stage_lds<kPartB>(smb, st, (wave * 4 + (u - 4)) * 1024),
-                     o.boff[u - 4], k0);
+            dma_b128<(u - 4) * 1024>(rng(src.rb), stage_lds<kPartB>(smb, st, wave * 4 * 1024),
+                                     o.boff[u - 4], k0);
         } else {
             dma_b32(rng(src.sr), sc_lds + (uint32_t)st * (uint32_t)sizeof(GemmSmem::as[0]), src.sv,
                     src.s0 + ks * o.sc.sstep);
@@ -1201,6 +1263,8 @@ template <> struct LeanSched<4> {   // 256 x 128 tile: 14 loads, 32 MFMAs per wa
     }
 };
 
+// lean_arow(w, u) = lean_arow_base(w) + (u >= 4 ? 64 : 0) + 8 * (u & 3)
+__device__ __forceinline__ constexpr int lean_arow_base(int w) { return w < 2 ? 32 * w : 64 + 32 * w; }
 __device__ __forceinline__ constexpr int lean_arow(int w, int u) {
     return ((u >= 4) ? 64 : 0) + ((4 * w + (u & 3)) < 8 ? 8 * (4 * w + (u & 3))
                                                        : 128 + 8 * (4 * w + (u & 3) - 8));
@@ -1230,10 +1294,11 @@ struct LeanLoads {
         const uint32_t k0 = (uint32_t)ks * BK;
         auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
         if constexpr (u < 8) {
-            dma_b128(rng(o.ra), stage_lds<kPartA>(smb, st, lean_arow(wave, u) * BK), aoffl[u], k0);
+            dma_b128<(uint32_t)(((u >= 4 ? 64 : 0) + 8 * (u & 3)) * BK)>(
+                rng(o.ra), stage_lds<kPartA>(smb, st, lean_arow_base(wave) * BK), aoffl[u], k0);
         } else if constexpr (u < 8 + NJ) {
-            dma_b128(rng(o.rb), stage_lds<kPartB>(smb, st, (wave * NJ + (u - 8)) * 1024),
-                     o.boff[u - 8], k0);
+            dma_b128<(u - 8) * 1024>(rng(o.rb), stage_lds<kPartB>(smb, st, wave * NJ * 1024),
+                                     o.boff[u - 8], k0);
         } else if constexpr (u == 8 + NJ) {
             dma_b32(rng(o.sb.rsrc), stage_lds<kPartBs>(smb, st, wave * 64 * 4), o.sb.voff,
                     o.sb.s0 + ks * o.sb.sstep);
@@ -1343,10 +1408,15 @@ struct TileLoc {
 // SPLIT (plain store, row-grouped only): the tail-split schedule below.
 // NW: waves per workgroup, 4 (one per SIMD) or 8 (two per SIMD, plain store
 // only).
-template <Epi EPI, bool SPLIT = false, int NW = 4>
+// TILED (plain store only): both operands carry block scales in the K-step
+// tiled layout, checked on the host; the tile sources then test neither for
+// missing scales nor for the layout (runtime flags the plain kernel would
+// otherwise keep live across its tile loop, at the cost of spilled registers).
+template <Epi EPI, bool SPLIT = false, int NW = 4, bool TILED = false>
 __global__ void __launch_bounds__(NW * 64, 1)
 mx_gemm_kernel(GemmProblem p) {
     static_assert(NW == 4 || (NW == 8 && EPI == Epi::kStoreBf16), "eight waves: plain tiles only");
+    static_assert(!TILED || EPI == Epi::kStoreBf16, "TILED: plain tiles only");
     constexpr int kThreads = NW * 64;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Slot<EPI>::kSmem];
     GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem);
@@ -1552,13 +1622,20 @@ mx_gemm_kernel(GemmProblem p) {
                 const bool has_next = wnext < items;
                 // per-lane offsets from an opaque copy of the lane index, so
                 // that they are not kept live through the epilogue
-                int lane = lane_id;
-                asm volatile("" : "+v"(lane));
+                int lane = lane_now();
                 const int nk = (int)(L.K / BK);
                 auto src_of = [&](const TileLoc& T) {
                     const int64_t bg = kgroup ? 0 : (int64_t)T.g * p.B.gstride;
-                    return tile_src<true, 8>(p.A, p.B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0,
-                                             T.klo, T.K, brow_plain, wave, lane);
+                    if constexpr (TILED) {
+                        MxOperand A = p.A, B = p.B;
+                        A.tiled = true;
+                        B.tiled = true;
+                        return tile_src<false, 8>(A, B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0,
+                                                  T.klo, T.K, brow_plain, wave, lane);
+                    } else {
+                        return tile_src<true, 8>(p.A, p.B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0,
+                                                 T.klo, T.K, brow_plain, wave, lane);
+                    }
                 };
                 // this wave's routing weights (its 128 rows; rows past the
                 // tile read as 0) into LDS; the main loop's waits cover the
@@ -1577,16 +1654,28 @@ mx_gemm_kernel(GemmProblem p) {
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
                     for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                // the next tile's position, found once (while this tile's
+                // last K steps run) and kept for the next iteration
+                TileLoc Ln{};
+                bool have_ln = false;
                 if constexpr (NW == 8) {
                     auto src8_of = [&](const TileLoc& T) {
                         const int64_t bg = kgroup ? 0 : (int64_t)T.g * p.B.gstride;
-                        return tile_src8(p.A, p.B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0, T.klo,
+                        if constexpr (TILED) {
+                            MxOperand A = p.A, B = p.B;
+                            A.tiled = true;
+                            B.tiled = true;
+                            return tile_src8<false>(A, B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0,
+                                                    T.klo, T.K, wave, lane);
+                        }
+                        return tile_src8<true>(p.A, p.B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0, T.klo,
                                          T.K, wave, lane);
                     };
                     const TileSrc8 o = src8_of(L);
                     auto next_src = [&]() -> TileNext8 {
                         if (!has_next) return tile_next8(o, 0);
-                        const TileLoc Ln = locate(wnext);
+                        Ln = locate(wnext);
+                        have_ln = true;
                         return tile_next8(src8_of(Ln), (int)(Ln.K / BK));
                     };
                     tile_gemm_chain8(acc, sm, o, next_src, nk, base, pre, wave, wm, wn, lane);
@@ -1594,32 +1683,30 @@ mx_gemm_kernel(GemmProblem p) {
                     const TileSrc o = src_of(L);
                     auto next_src = [&]() -> TileNext {
                         if (!has_next) return tile_next(o, 0);
-                        const TileLoc Ln = locate(wnext);
+                        Ln = locate(wnext);
+                        have_ln = true;
                         return tile_next(src_of(Ln), (int)(Ln.K / BK));
                     };
                     tile_gemm_chain(acc, sm, o, next_src, nk, base, pre, wave, wm, wn, lane);
                 }
-                if (!SPLIT || L.chunk < 0) {
-                    if (use_rs && nk == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    store_tile_bf16_regs<NJ>(acc, p, L.g, L.m0, L.mvalid, L.n0, wm, wn, lane,
-                                             has_gs ? s_gs[L.g] : 1.0f,
-                                             use_rs ? &s_rsw[wave * 128] : nullptr);
-                } else {
-                    // a chunk of a split tail tile: fp32 partial tile to the
-                    // workspace in the four-wave block order (block (i, j) of
-                    // wave (wm, wn4) holds rows wm*128 + i*16 .., columns
-                    // wn4*128 + j*16 ..); chunk 0 also records the tile's
-                    // coordinates
-                    float* part = split_part(p.split_ws, w - full);
+                // a chunk of a split tail tile leaves an fp32 partial tile in
+                // the workspace, in the four-wave block order (block (i, j)
+                // of wave (wm, wn4) holds rows wm*128 + i*16 .., columns
+                // wn4*128 + j*16 ..); chunk 0 also records the tile's
+                // coordinates
+                uint8_t* part = nullptr;
+                if (SPLIT && L.chunk >= 0) {
                     const int w4 = NW == 8 ? wm * 2 + (wn >> 1) : wave;
                     const int j4 = NW == 8 ? (wn & 1) * 4 : 0;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-#pragma unroll
-                        for (int j = 0; j < NJ; ++j)
-                            *reinterpret_cast<v4f*>(
-                                part + ((w4 * 64 + i * 8 + j4 + j) * 64 + lane) * 4) = acc[i][j];
-                    if (L.chunk == 0 && tid == 0) {
+                    part = reinterpret_cast<uint8_t*>(split_part(p.split_ws, w - full)) +
+                           (int64_t)(w4 * 64 + j4) * 1024;
+                }
+                if (use_rs && nk == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                store_tile_bf16_regs<NJ>(acc, p, L.g, L.m0, L.mvalid, L.n0, wm, wn, lane,
+                                         has_gs ? s_gs[L.g] : 1.0f,
+                                         use_rs ? &s_rsw[wave * 128] : nullptr, part);
+                if (SPLIT && L.chunk >= 0) {
+                    if (L.chunk == 0 && wave == 0 && lane == 0) {
                         int64_t* meta = reinterpret_cast<SplitHdr*>(p.split_ws)->meta[(w - full) / S];
                         meta[0] = L.g;
                         meta[1] = L.m0;
@@ -1629,9 +1716,9 @@ mx_gemm_kernel(GemmProblem p) {
                 }
                 if (!has_next) break;
                 pre = nk >= 2;               // tile_gemm_chain switched to the next tile
-                base = pre ? (base + nk) & 1 : 0;
+                base = uni(pre ? (base + nk) & 1 : 0);
                 w = wnext;
-                L = locate(w);
+                L = have_ln ? Ln : locate(w);
             }
         }
         // no load may still be landing in LDS when the workgroup ends
@@ -1643,8 +1730,7 @@ mx_gemm_kernel(GemmProblem p) {
             // Per-lane offsets are derived per tile from an opaque copy of the
             // lane index: hoisted out of the tile loop they would stay live
             // through the epilogue, which needs every register it can get.
-            int lane = lane_id;
-            asm volatile("" : "+v"(lane));
+            int lane = lane_now();
             const int r16 = lane & 15, q = lane >> 4;
             const int swz = r16 & 7;
             const TileLoc L = locate(w);
@@ -1692,8 +1778,7 @@ mx_gemm_kernel(GemmProblem p) {
                                                      brow_gu, wave, lane);
                 const uint32_t smb = uni((int)lds_addr(&sm));
                 auto make_tail = [&]() {
-                    int lane3 = lane_id;
-                    asm volatile("" : "+v"(lane3));
+                    int lane3 = lane_now();
                     const LeanLoads<4> L(dz_src(lane3), p.A2.ld, smb, wave, lane3, nk);
                     return [L, smb, wave](auto uc, int st, int kn) {
                         constexpr int u = decltype(uc)::value;
@@ -1742,8 +1827,7 @@ mx_gemm_kernel(GemmProblem p) {
                         dacc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
                         asm volatile("" : "+a"(dacc[i][j]));
                     }
-                int lane2 = lane_id;
-                asm volatile("" : "+v"(lane2));
+                int lane2 = lane_now();
                 tile_gemm_lean<4>(dacc, sm, dz_src(lane2), nk, wave, wm, wn, lane2, p.A2.ld,
                                   nk & 1, chained);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1773,8 +1857,7 @@ mx_gemm_kernel(GemmProblem p) {
                     // lane index in every slice: hoisted out of the tile loop they
                     // would stay live through the main loop and crowd out the
                     // accumulators.
-                    int lane = lane_id;
-                    asm volatile("" : "+v"(lane));
+                    int lane = lane_now();
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2];
 #pragma unroll
@@ -1858,8 +1941,7 @@ mx_gemm_kernel(GemmProblem p) {
                     // lane index in every slice: hoisted out of the tile loop they
                     // would stay live through the main loop and crowd out the
                     // accumulators.
-                    int lane = lane_id;
-                    asm volatile("" : "+v"(lane));
+                    int lane = lane_now();
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2], drs[2];
 #pragma unroll
@@ -1964,8 +2046,7 @@ mx_gemm_kernel(GemmProblem p) {
 #pragma nounroll
                 for (int ip = 0; ip < 4; ++ip) {
                     // lane-derived values re-derived per slice (see the forward)
-                    int lane = lane_id;
-                    asm volatile("" : "+v"(lane));
+                    int lane = lane_now();
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2], drs[2];
 #pragma unroll
@@ -2078,19 +2159,27 @@ hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s) {
     switch (epi) {
         case Epi::kStoreBf16: {
             const bool split = p.split_ws && !p.kgroup;
-            if (!p.kgroup && p.K <= kEightWaveMaxK) {
-                if (split)
-                    hipLaunchKernelGGL((mx_gemm_kernel<Epi::kStoreBf16, true, 8>), dim3(grid),
-                                       dim3(8 * 64), 0, s, p);
-                else
-                    hipLaunchKernelGGL((mx_gemm_kernel<Epi::kStoreBf16, false, 8>), dim3(grid),
-                                       dim3(8 * 64), 0, s, p);
-            } else if (split) {
-                hipLaunchKernelGGL((mx_gemm_kernel<Epi::kStoreBf16, true>), dim3(grid),
-                                   dim3(NTHREADS), 0, s, p);
+            const bool tiled = p.A.scales && p.B.scales && p.A.tiled && p.B.tiled;
+            const bool eight = !p.kgroup && p.K <= kEightWaveMaxK;
+            auto go = [&](auto kern, int threads) {
+                hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, p);
+            };
+            if (eight) {
+                if (tiled) {
+                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 8, true>, 8 * 64);
+                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 8, true>, 8 * 64);
+                } else {
+                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 8, false>, 8 * 64);
+                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 8, false>, 8 * 64);
+                }
             } else {
-                hipLaunchKernelGGL((mx_gemm_kernel<Epi::kStoreBf16>), dim3(grid), dim3(NTHREADS), 0,
-                                   s, p);
+                if (tiled) {
+                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 4, true>, NTHREADS);
+                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 4, true>, NTHREADS);
+                } else {
+                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 4, false>, NTHREADS);
+                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 4, false>, NTHREADS);
+                }
             }
             break;
         }
