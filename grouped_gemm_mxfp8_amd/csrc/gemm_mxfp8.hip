@@ -40,10 +40,6 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 128, NTHREADS = 256;
 constexpr int BAND = 8;
-// Plain-store launches over short K run on eight waves, the others on four:
-// the eight-wave epilogue is shorter (half the stores per wave) but its main
-// loop a little slower, so it pays only when tiles are short.
-constexpr int64_t kEightWaveMaxK = 1024;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, dword format
 
 struct GemmSmem {
@@ -563,7 +559,6 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // + (r16 & 7), with lanes r16 < 8 on the jp = 2c half of the line and lanes
 // r16 >= 8 on the other.  (Stored as the pairs left the swap, each
 // instruction would write half lines, and the output would cost more.)
-// NJ: the wave's 16-column blocks (8 on four waves, 4 on eight), NJ / 4 lines.
 // gs: the tile's per-group output scale; rs: the wave's 128 routing weights
 // in LDS (rows wm*128 ..), or null.  Nothing here reads global memory: a
 // global load would wait (vmcnt) for every store and load in flight.
@@ -571,8 +566,7 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // they are, to the wave's blocks of a partial tile there (block (i, j) at
 // byte (i * 8 + j) * 1024, lane l's 16 bytes at 16 l).  Both outputs share
 // one pass over the row blocks, so the accumulators are read one way only.
-template <int NJ>
-__device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][NJ], const GemmProblem& p,
+__device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][8], const GemmProblem& p,
                                                      int g, int64_t m0, int64_t mvalid, int64_t n0,
                                                      int wm, int wn, int lane, float gs,
                                                      const float* rs, uint8_t* part = nullptr) {
@@ -581,7 +575,7 @@ __device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][NJ], const Ge
     const int64_t rwave = m0 + wm * 128;
     const int rows_valid_w = (int)min((int64_t)128, max((int64_t)0, mvalid - wm * 128));
     uint16_t* C = reinterpret_cast<uint16_t*>(p.C) + (p.kgroup ? (int64_t)g * p.c_gstride : 0);
-    const int64_t cw = n0 + wn * (NJ * 16);
+    const int64_t cw = n0 + wn * 128;
     // addresses: a wave-uniform base plus one 32-bit per-lane byte offset (the
     // lane's row r16 & 7 and its 16-byte chunk of line 0); rows, the second
     // half of a block and further lines only move the uniform base
@@ -594,16 +588,14 @@ __device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][NJ], const Ge
     };
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        // four waves keep the accumulators in AGPRs: pinned there at each row
-        // block, the block is moved to VGPRs only when it is converted (else
-        // the compiler may move the whole tile up front and spill)
-        if constexpr (NJ == 8) {
+        // the accumulators live in AGPRs: pinned there at each row block, the
+        // block moves to VGPRs only when it is converted (else the compiler
+        // may move the whole tile up front and spill)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
-        }
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
         if (part) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j)
+            for (int j = 0; j < 8; ++j)
                 *reinterpret_cast<v4f*>(part + (int64_t)(i * 8 + j) * 1024 + (uint32_t)lane * 16u) =
                     acc[i][j];
             __builtin_amdgcn_sched_barrier(0);
@@ -612,7 +604,7 @@ __device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][NJ], const Ge
         const float sc = rs ? rs[i * 16 + r16] * gs : gs;
         const int rl1 = i * 16 + (r16 & 7), rl2 = rl1 + 8;
 #pragma unroll
-        for (int c = 0; c < NJ / 4; ++c) {
+        for (int c = 0; c < 2; ++c) {
             uint32_t d[2][4];                       // jp = 2c + h, after the swap
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -741,8 +733,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
     else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else static_assert(N < 0, "add the wait count");
 }
 
@@ -1045,194 +1035,6 @@ __device__ __forceinline__ void tile_gemm_chain(v4f (&acc)[8][8], GemmSmem& sm, 
     }
 }
 
-// ---- plain tiles on eight waves ----------------------------------------------
-// The plain kernel runs the same 256 x 256 tile on 8 waves, two per SIMD:
-// wave (wm = wave >> 2, wn = wave & 3) owns tile rows wm*128 .. +128 and B
-// rows wn*64 .. +64, acc[8][4] (128 registers), so two waves share one
-// SIMD's 512 registers.  With one wave per SIMD, a load or LDS read that
-// cannot issue also holds up that SIMD's next MFMA; with two, the other wave
-// issues its MFMAs meanwhile (a main-loop model of the two layouts on the
-// MI355X: 3.4 against 2.8 PFLOP/s).
-//
-// Registers: the wave keeps 4 A fragments (rows 0..3 of its 8, then rows
-// 4..7 in the same registers) and its 4 B fragments, as in tile_gemm_lean,
-// so the stage regions that hold the A rows 4..7 of every wave (tile rows
-// 64..127 and 192..255, region R1) and the A scales are read during pass A
-// and may only be reloaded after S2.  Each wave issues 9 loads per K step:
-//   u = 0, 1   A rows of region R0 (tile rows 0..63, 128..191)   pass A
-//   u = 2, 3   A rows of region R1                              pass B
-//   u = 4..7   B rows: groups of 8 rows wave*4 + u - 4         pass A
-//   u = 8      scales: A rows (wave & 3) * 64 .. +64 (waves 0..3) or those
-//              of B (waves 4..7)                                pass B
-// A load u of wave w covers the 8 tile rows from
-//   (w >> 2) * 128 + (w & 3) * 16 + (u & 1) * 8 + (u >> 1) * 64.
-struct TileSrc8 {
-    v4i ra, rb;
-    ScaleSrc sc;                 // A scales (waves 0..3) or B scales (4..7)
-    uint32_t aoff[4], boff[4];
-};
-
-__device__ __forceinline__ int a_group_row8(int wave, int u) {
-    return (wave >> 2) * 128 + (wave & 3) * 16 + (u & 1) * 8 + (u >> 1) * 64;
-}
-
-template <bool UNIT>
-__device__ __forceinline__ TileSrc8 tile_src8(const MxOperand& A, const MxOperand& B, int64_t m0,
-                                              int64_t mvalid, int64_t brow0, int64_t bvalid,
-                                              int64_t klo, int64_t K, int wave, int lane) {
-    TileSrc8 o;
-    const int64_t lda = A.ld, ldb = B.ld;
-    o.ra = make_rsrc(A.codes + m0 * lda + klo, (mvalid - 1) * lda + K);
-    o.rb = make_rsrc(B.codes + brow0 * ldb + klo, (bvalid - 1) * ldb + K);
-    const int dma_row = lane >> 3;
-    const int dma_chunk = (lane & 7) ^ (dma_row & 7);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        o.aoff[j] = (uint32_t)((a_group_row8(wave, j) + dma_row) * lda + dma_chunk * 16);
-        o.boff[j] = (uint32_t)(((wave * 4 + j) * 8 + dma_row) * ldb + dma_chunk * 16);
-    }
-    const int lrow = (wave & 3) * 64 + lane;
-    o.sc = wave < 4 ? scale_src<UNIT>(A.scales, lda, A.tiled, m0, mvalid, lrow, klo, K)
-                    : scale_src<UNIT>(B.scales, ldb, B.tiled, brow0, bvalid, lrow, klo, K);
-    return o;
-}
-
-struct TileNext8 {
-    v4i ra, rb, sr;
-    uint32_t sv, s0;
-    int nk;                      // K steps (0: no next tile)
-};
-__device__ __forceinline__ TileNext8 tile_next8(const TileSrc8& o, int nk) {
-    return TileNext8{uni4(o.ra), uni4(o.rb), uni4(o.sc.rsrc), o.sc.voff,
-                     (uint32_t)uni((int)o.sc.s0), uni(nk)};
-}
-
-// Slots of the loads over the 16 MFMA slots of each pass.
-struct Sched8 {
-    static constexpr int kLoads = 9, kNA = 6;
-    static constexpr int a_at(int s) {
-        return s == 0 ? 0 : s == 3 ? 4 : s == 5 ? 1 : s == 8 ? 5 : s == 10 ? 6 : s == 13 ? 7 : -1;
-    }
-    static constexpr int b_at(int s) { return s == 1 ? 2 : s == 5 ? 3 : s == 9 ? 8 : -1; }
-};
-static_assert(offsetof(GemmSmem, bs) == offsetof(GemmSmem, as) + sizeof(GemmSmem::as),
-              "B scales follow the A scales");
-
-// tile_gemm_chain on eight waves: the same two-stage pipeline, chaining and
-// waits.  Per step, pass A runs A rows 0..3 over the 4 columns and, in the
-// last column, reads row i + 4 of the current step into row i's registers
-// once row i's last MFMA has issued; pass B runs rows 4..7 and reads the
-// next step's B column j after its last MFMA and row i (0..3) after row
-// i + 4's.
-template <class NextSrc>
-__device__ __forceinline__ void tile_gemm_chain8(v4f (&acc)[8][4], GemmSmem& sm,
-                                                 const TileSrc8& o, NextSrc next_src, int nk,
-                                                 int base, bool pre, int wave, int wm, int wn,
-                                                 int lane) {
-    using SC = Sched8;
-    constexpr int NJ = 4;
-    const int r16 = lane & 15, q = lane >> 4;
-    const int swz = r16 & 7;
-    const int b0 = uni(base);
-    const uint32_t smb = uni((int)lds_addr(&sm));
-    // this wave's 256 bytes of the A or B scale area of stage 0
-    const uint32_t sc_lds = smb + (uint32_t)offsetof(GemmSmem, as) +
-                            (uint32_t)(wave >> 2) * (uint32_t)sizeof(GemmSmem::as) +
-                            (uint32_t)(wave & 3) * 256u;
-    auto dma_u = [&](auto uc, auto livec, const TileNext8& src, int st, int ks) {
-        constexpr int u = decltype(uc)::value;
-        const bool live = decltype(livec)::value || ks < src.nk;
-        const uint32_t k0 = (uint32_t)ks * BK;
-        auto rng = [&](const v4i& r) { return live ? r : v4i{r.x, r.y, 0, r.w}; };
-        if constexpr (u < 4) {
-            dma_b128<(uint32_t)(((u & 1) * 8 + (u >> 1) * 64) * BK)>(
-                rng(src.ra), stage_lds<kPartA>(smb, st, a_group_row8(wave, 0) * BK), o.aoff[u], k0);
-        } else if constexpr (u < 8) {
-            dma_b128<(u - 4) * 1024>(rng(src.rb), stage_lds<kPartB>(smb, st, wave * 4 * 1024),
-                                     o.boff[u - 4], k0);
-        } else {
-            dma_b32(rng(src.sr), sc_lds + (uint32_t)st * (uint32_t)sizeof(GemmSmem::as[0]), src.sv,
-                    src.s0 + ks * o.sc.sstep);
-        }
-    };
-
-    // af[i] holds A row i (pass A) or i + 4 (pass B) of the wave's 8
-    v8i af[4], bfr[NJ];
-    int asc[4], bsc[NJ];
-    const int a_row0 = wm * 128 + r16, b_row0 = wn * (NJ * 16) + r16;
-    const int a_lo = a_row0 * BK + ((q ^ swz) << 4), a_hi = a_row0 * BK + (((q + 4) ^ swz) << 4);
-    const int b_lo = b_row0 * BK + ((q ^ swz) << 4), b_hi = b_row0 * BK + (((q + 4) ^ swz) << 4);
-    const int a_s = a_row0 * 4 + q, b_s = b_row0 * 4 + q;
-    // A row r (0..7) of stage st into the registers of row r & 3
-    auto read_a = [&](auto rc, int st) {
-        constexpr int r = decltype(rc)::value, i = r & 3;
-        const uint8_t* stg = sm.a[st];
-        const uint4 lo = *reinterpret_cast<const uint4*>(stg + a_lo + r * 16 * BK);
-        const uint4 hi = *reinterpret_cast<const uint4*>(stg + a_hi + r * 16 * BK);
-        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        asc[i] = (reinterpret_cast<const uint8_t*>(sm.as[st]) + a_s)[r * 16 * 4];
-    };
-    auto read_b = [&](auto jc, int st) {
-        constexpr int j = decltype(jc)::value;
-        const uint8_t* stg = sm.b[st];
-        const uint4 lo = *reinterpret_cast<const uint4*>(stg + b_lo + j * 16 * BK);
-        const uint4 hi = *reinterpret_cast<const uint4*>(stg + b_hi + j * 16 * BK);
-        bfr[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        bsc[j] = (reinterpret_cast<const uint8_t*>(sm.bs[st]) + b_s)[j * 16 * 4];
-    };
-    // MFMA of A row r (registers r & 3) with B column j
-    auto mfma = [&](auto rc, auto jc) {
-        constexpr int r = decltype(rc)::value, i = r & 3, j = decltype(jc)::value;
-        acc[r][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bfr[j], af[i], acc[r][j], 0, 0, 0, bsc[j], 0, asc[i]);
-    };
-    auto step = [&](int ks, auto livec, const TileNext8& src, int kl) {
-        const int cur = (b0 + ks) & 1, nxt = cur ^ 1;
-        lds_barrier();                                  // S1: R0, B and B scales of cur free
-        static_for<4 * NJ>([&](auto sc) {
-            constexpr int s = decltype(sc)::value, r = s % 4, j = s / 4;
-            mfma(std::integral_constant<int, r>{}, std::integral_constant<int, j>{});
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (j == NJ - 1) read_a(std::integral_constant<int, r + 4>{}, cur);
-            constexpr int u = SC::a_at(s);
-            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, livec, src, cur, kl);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        wait_vmcnt<SC::kNA>();
-        lds_barrier();                                  // S2: stage nxt complete; R1 of cur read
-        static_for<4 * NJ>([&](auto sc) {
-            constexpr int s = decltype(sc)::value, r = 4 + s % 4, j = s / 4;
-            mfma(std::integral_constant<int, r>{}, std::integral_constant<int, j>{});
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (s % 4 == 3) read_b(std::integral_constant<int, j>{}, nxt);
-            if constexpr (j == NJ - 1) read_a(std::integral_constant<int, r - 4>{}, nxt);
-            constexpr int u = SC::b_at(s);
-            if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, livec, src, cur, kl);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-
-    const TileNext8 own = tile_next8(o, nk);
-    if (!pre) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();                                  // no load in flight, stages free
-        static_for<SC::kLoads>([&](auto uc) { dma_u(uc, std::false_type{}, own, b0, 0); });
-        static_for<SC::kLoads>([&](auto uc) { dma_u(uc, std::false_type{}, own, b0 ^ 1, 1); });
-        wait_vmcnt<SC::kLoads>();
-        lds_barrier();
-    }
-    static_for<4>([&](auto rc) { read_a(rc, b0); });
-    static_for<NJ>([&](auto jc) { read_b(jc, b0); });
-    int ks = 0;
-    for (; ks + 2 < nk; ++ks) step(ks, std::true_type{}, own, ks + 2);
-    if (ks < nk) {
-        const TileNext8 nx = next_src();
-        for (; ks < nk; ++ks) step(ks, std::false_type{}, nx, ks + 2 - nk);
-    }
-}
-
 // tile_gemm with only four A fragments in registers (rows 0..3 of the wave's
 // eight, then rows 4..7 in the same registers), for a tile GEMM that runs
 // while other accumulators stay live.  Changes to the schedule of tile_gemm:
@@ -1412,12 +1214,11 @@ struct TileLoc {
 // tiled layout, checked on the host; the tile sources then test neither for
 // missing scales nor for the layout (runtime flags the plain kernel would
 // otherwise keep live across its tile loop, at the cost of spilled registers).
-template <Epi EPI, bool SPLIT = false, int NW = 4, bool TILED = false>
-__global__ void __launch_bounds__(NW * 64, 1)
+template <Epi EPI, bool SPLIT = false, bool TILED = false>
+__global__ void __launch_bounds__(NTHREADS, 1)
 mx_gemm_kernel(GemmProblem p) {
-    static_assert(NW == 4 || (NW == 8 && EPI == Epi::kStoreBf16), "eight waves: plain tiles only");
     static_assert(!TILED || EPI == Epi::kStoreBf16, "TILED: plain tiles only");
-    constexpr int kThreads = NW * 64;
+    constexpr int kThreads = NTHREADS;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Slot<EPI>::kSmem];
     GemmSmem& sm = *reinterpret_cast<GemmSmem*>(smem);
     __shared__ int s_prefix[kMaxGroups + 1];
@@ -1432,7 +1233,7 @@ mx_gemm_kernel(GemmProblem p) {
     // likewise its per-group output scales (per-tensor FP8 operands) and
     // each wave's routing weights of its 128 tile rows, for the epilogue
     __shared__ float s_gs[kOffsLds ? kMaxGroups : 1];
-    __shared__ float s_rsw[kOffsLds ? NW * 128 : 1];
+    __shared__ float s_rsw[kOffsLds ? 4 * 128 : 1];
     const bool has_gs = p.gsa || p.gsb;
     // the fused epilogues read the tile's routing weights from LDS: a global
     // load in the epilogue would wait (vmcnt) for the output stores in flight
@@ -1442,7 +1243,7 @@ mx_gemm_kernel(GemmProblem p) {
     const int tid = threadIdx.x;
     const int lane_id = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = NW == 8 ? wave >> 2 : wave >> 1, wn = NW == 8 ? wave & 3 : wave & 1;
+    const int wm = wave >> 1, wn = wave & 1;
     const int G = p.G;
 
     // output columns per tile: the gate-up tile pairs 128 gate with 128 up
@@ -1648,61 +1449,34 @@ mx_gemm_kernel(GemmProblem p) {
                     dma_b32(rr, la, (uint32_t)lane * 4u, 0u);
                     dma_b32(rr, la + 256u, (uint32_t)lane * 4u + 256u, 0u);
                 }
-                constexpr int NJ = NW == 8 ? 4 : 8;
-                v4f acc[8][NJ];
+                v4f acc[8][8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
                 // the next tile's position, found once (while this tile's
                 // last K steps run) and kept for the next iteration
                 TileLoc Ln{};
                 bool have_ln = false;
-                if constexpr (NW == 8) {
-                    auto src8_of = [&](const TileLoc& T) {
-                        const int64_t bg = kgroup ? 0 : (int64_t)T.g * p.B.gstride;
-                        if constexpr (TILED) {
-                            MxOperand A = p.A, B = p.B;
-                            A.tiled = true;
-                            B.tiled = true;
-                            return tile_src8<false>(A, B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0,
-                                                    T.klo, T.K, wave, lane);
-                        }
-                        return tile_src8<true>(p.A, p.B, T.m0, T.mvalid, bg + T.n0, p.N - T.n0, T.klo,
-                                         T.K, wave, lane);
-                    };
-                    const TileSrc8 o = src8_of(L);
-                    auto next_src = [&]() -> TileNext8 {
-                        if (!has_next) return tile_next8(o, 0);
-                        Ln = locate(wnext);
-                        have_ln = true;
-                        return tile_next8(src8_of(Ln), (int)(Ln.K / BK));
-                    };
-                    tile_gemm_chain8(acc, sm, o, next_src, nk, base, pre, wave, wm, wn, lane);
-                } else {
-                    const TileSrc o = src_of(L);
-                    auto next_src = [&]() -> TileNext {
-                        if (!has_next) return tile_next(o, 0);
-                        Ln = locate(wnext);
-                        have_ln = true;
-                        return tile_next(src_of(Ln), (int)(Ln.K / BK));
-                    };
-                    tile_gemm_chain(acc, sm, o, next_src, nk, base, pre, wave, wm, wn, lane);
-                }
+                const TileSrc o = src_of(L);
+                auto next_src = [&]() -> TileNext {
+                    if (!has_next) return tile_next(o, 0);
+                    Ln = locate(wnext);
+                    have_ln = true;
+                    return tile_next(src_of(Ln), (int)(Ln.K / BK));
+                };
+                tile_gemm_chain(acc, sm, o, next_src, nk, base, pre, wave, wm, wn, lane);
                 // a chunk of a split tail tile leaves an fp32 partial tile in
                 // the workspace, in the four-wave block order (block (i, j)
                 // of wave (wm, wn4) holds rows wm*128 + i*16 .., columns
                 // wn4*128 + j*16 ..); chunk 0 also records the tile's
                 // coordinates
                 uint8_t* part = nullptr;
-                if (SPLIT && L.chunk >= 0) {
-                    const int w4 = NW == 8 ? wm * 2 + (wn >> 1) : wave;
-                    const int j4 = NW == 8 ? (wn & 1) * 4 : 0;
+                if (SPLIT && L.chunk >= 0)
                     part = reinterpret_cast<uint8_t*>(split_part(p.split_ws, w - full)) +
-                           (int64_t)(w4 * 64 + j4) * 1024;
-                }
+                           (int64_t)wave * 64 * 1024;
                 if (use_rs && nk == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                store_tile_bf16_regs<NJ>(acc, p, L.g, L.m0, L.mvalid, L.n0, wm, wn, lane,
+                store_tile_bf16_regs(acc, p, L.g, L.m0, L.mvalid, L.n0, wm, wn, lane,
                                          has_gs ? s_gs[L.g] : 1.0f,
                                          use_rs ? &s_rsw[wave * 128] : nullptr, part);
                 if (SPLIT && L.chunk >= 0) {
@@ -2160,26 +1934,15 @@ hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s) {
         case Epi::kStoreBf16: {
             const bool split = p.split_ws && !p.kgroup;
             const bool tiled = p.A.scales && p.B.scales && p.A.tiled && p.B.tiled;
-            const bool eight = !p.kgroup && p.K <= kEightWaveMaxK;
-            auto go = [&](auto kern, int threads) {
-                hipLaunchKernelGGL(kern, dim3(grid), dim3(threads), 0, s, p);
+            auto go = [&](auto kern) {
+                hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), 0, s, p);
             };
-            if (eight) {
-                if (tiled) {
-                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 8, true>, 8 * 64);
-                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 8, true>, 8 * 64);
-                } else {
-                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 8, false>, 8 * 64);
-                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 8, false>, 8 * 64);
-                }
+            if (tiled) {
+                if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, true>);
+                else go(mx_gemm_kernel<Epi::kStoreBf16, false, true>);
             } else {
-                if (tiled) {
-                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 4, true>, NTHREADS);
-                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 4, true>, NTHREADS);
-                } else {
-                    if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, 4, false>, NTHREADS);
-                    else go(mx_gemm_kernel<Epi::kStoreBf16, false, 4, false>, NTHREADS);
-                }
+                if (split) go(mx_gemm_kernel<Epi::kStoreBf16, true, false>);
+                else go(mx_gemm_kernel<Epi::kStoreBf16, false, false>);
             }
             break;
         }
