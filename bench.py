@@ -193,11 +193,12 @@ def roofline(agg):
 def cpu_baseline(seed, T, M, E, H, F):
     """The FP64 oracle (as it is) on a bounded sample of the same workload.
 
-    Sample: one expert, full H=4096, a slice of Fs=1024 of the F=14336
+    Sample: one expert, full H=4096, a slice of Fs=2048 of the F=14336
     intermediate units (gate and up rows and the matching W2 columns), run on
-    n=512 and n=1024 rows.  The oracle's time is linear in rows and in F, with
-    a per-expert part (weight quantization) and a per-row part; the two runs
-    give both, and the whole step is extrapolated as
+    n=1024 and n=2048 rows (some 10-20 s of host time on 16 cores).  The
+    oracle's time is linear in rows and in F, with a per-expert part (weight
+    quantization) and a per-row part; the two runs give both, and the whole
+    step is extrapolated as
         (F/Fs) * (E * per_expert + M * per_row).
     """
     import numpy as np
@@ -219,7 +220,7 @@ def cpu_baseline(seed, T, M, E, H, F):
             threads = 1
     except Exception:
         threads = 1
-    Fs, n = 1024, 512
+    Fs, n = 2048, 1024
     g = torch.Generator().manual_seed(seed)
     bf = lambda *s, std=1.0: (torch.randn(*s, generator=g) * std).to(torch.bfloat16).double().numpy()
     X, dY = bf(2 * n, H), bf(2 * n, H)
