@@ -428,6 +428,49 @@ mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
                     "quant_tiles");
 }
 
+// K not a multiple of the GEMM's K step (128) but of the MX block (32): the
+// operands are copied into rows of Kp = K rounded up to 128, the codes past K
+// set to 0 and (with block scales) their scales to 2^0, so the padding adds
+// exact zeros.  The copies live in one device allocation, made and freed in
+// stream order around the GEMM.
+struct PaddedOperands {
+    uint8_t* buf = nullptr;
+    const uint8_t *x = nullptr, *xs = nullptr, *w = nullptr, *ws = nullptr;
+    hipStream_t s = nullptr;
+    ~PaddedOperands() {
+        if (buf) (void)hipFreeAsync(buf, s);
+    }
+};
+static int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+static mx_status pad_operands(const char* fn, const uint8_t* x, const uint8_t* x_scales, int64_t M,
+                              const uint8_t* w, const uint8_t* w_scales, int64_t EN, int64_t K,
+                              int64_t Kp, hipStream_t s, PaddedOperands& out) {
+    const bool scaled = x_scales != nullptr;
+    const int64_t xb = round_up(M * Kp, 256), wb = round_up(EN * Kp, 256);
+    const int64_t xsb = scaled ? round_up(M * (Kp / 32), 256) : 0;
+    const int64_t wsb = scaled ? round_up(EN * (Kp / 32), 256) : 0;
+    out.s = s;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&out.buf), (size_t)(xb + wb + xsb + wsb), s);
+    if (e != hipSuccess) {
+        out.buf = nullptr;
+        return fail(MX_ERR_LAUNCH, "%s: padded copies (K %% 128 != 0): %s", fn, hipGetErrorString(e));
+    }
+    uint8_t* xp = out.buf;
+    uint8_t* wp = xp + xb;
+    uint8_t* xsp = wp + wb;
+    uint8_t* wsp = xsp + xsb;
+    e = mx::launch_pad_rows(x, M, K, xp, Kp, 0, s);
+    if (e == hipSuccess) e = mx::launch_pad_rows(w, EN, K, wp, Kp, 0, s);
+    if (scaled && e == hipSuccess) e = mx::launch_pad_rows(x_scales, M, K / 32, xsp, Kp / 32, 127, s);
+    if (scaled && e == hipSuccess) e = mx::launch_pad_rows(w_scales, EN, K / 32, wsp, Kp / 32, 127, s);
+    if (e != hipSuccess) return launched(e, "pad_rows");
+    out.x = xp;
+    out.w = wp;
+    out.xs = scaled ? xsp : nullptr;
+    out.ws = scaled ? wsp : nullptr;
+    return MX_OK;
+}
+
 mx_status grouped_linear_fwd(int32_t dtype, const void* x, const uint8_t* x_scales,
                              const int64_t* d_offsets, int32_t E, int64_t M,
                              const void* w, const uint8_t* w_scales, int64_t N,
@@ -466,18 +509,28 @@ mx_status grouped_linear_fwd(int32_t dtype, const void* x, const uint8_t* x_scal
         return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: unknown dtype %d", dtype);
     if (!x_scales || !w_scales)
         return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd: MXFP8 needs x_scales and w_scales");
-    if (K % 128 || N % 32)
-        return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd: MXFP8 needs K %% 128 == 0 and N %% 32 == 0");
-    if (N * K > kI32Max || 256 * K > kI32Max)
+    if (K % 32 || N % 32)
+        return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd: MXFP8 needs K %% 32 == 0 and N %% 32 == 0");
+    const int64_t Kp = round_up(K, 128);
+    if (N * Kp > kI32Max || 256 * Kp > kI32Max)
         return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd: operand too large");
     if (M == 0) return ok();
+    PaddedOperands pad;
+    const uint8_t *xa = static_cast<const uint8_t*>(x), *xsa = x_scales;
+    const uint8_t *wa = static_cast<const uint8_t*>(w), *wsa = w_scales;
+    if (Kp != K) {
+        const mx_status ps = pad_operands("grouped_linear_fwd", xa, xsa, M, wa, wsa, (int64_t)E * N,
+                                          K, Kp, s, pad);
+        if (ps != MX_OK) return ps;
+        xa = pad.x; xsa = pad.xs; wa = pad.w; wsa = pad.ws;
+    }
     mx::GemmProblem p{};
     p.kgroup = false;
     p.offs = d_offsets;
     p.G = E;
-    p.M = M; p.N = N; p.K = K;
-    p.A = mx::MxOperand{static_cast<const uint8_t*>(x), x_scales, K, 0};
-    p.B = mx::MxOperand{static_cast<const uint8_t*>(w), w_scales, K, N};
+    p.M = M; p.N = N; p.K = Kp;
+    p.A = mx::MxOperand{xa, xsa, Kp, 0};
+    p.B = mx::MxOperand{wa, wsa, Kp, N};
     p.C = y; p.ldc = N; p.c_gstride = 0;
     p.rscale = d_row_scale;
     return launched(gemm(p, mx::Epi::kStoreBf16, 2.0 * M * N * K, s), "mx_gemm");
@@ -536,23 +589,32 @@ mx_status grouped_linear_fwd_fp8(const uint8_t* x, const float* d_x_scale_inv,
                     (long long)M, (long long)N, (long long)K);
     if (!aligned(x, 16) || !aligned(w, 16))
         return fail(MX_ERR_INVALID_ARG, "grouped_linear_fwd_fp8: x and w must be 16-byte aligned");
-    if (K % 128 || N % 32)
+    if (K % 32 || N % 32)
         return fail(MX_ERR_UNSUPPORTED,
-                    "grouped_linear_fwd_fp8: needs K %% 128 == 0 and N %% 32 == 0");
-    if (N * K > kI32Max || 256 * K > kI32Max)
+                    "grouped_linear_fwd_fp8: needs K %% 32 == 0 and N %% 32 == 0");
+    const int64_t Kp = round_up(K, 128);
+    if (N * Kp > kI32Max || 256 * Kp > kI32Max)
         return fail(MX_ERR_UNSUPPORTED, "grouped_linear_fwd_fp8: operand too large");
     {
         const mx_status cs = check_device_offsets("grouped_linear_fwd_fp8", d_offsets, E, M, true, s);
         if (cs != MX_OK) return cs;
     }
     if (M == 0) return ok();
+    PaddedOperands pad;
+    const uint8_t *xa = x, *wa = w;
+    if (Kp != K) {
+        const mx_status ps = pad_operands("grouped_linear_fwd_fp8", x, nullptr, M, w, nullptr,
+                                          (int64_t)E * N, K, Kp, s, pad);
+        if (ps != MX_OK) return ps;
+        xa = pad.x; wa = pad.w;
+    }
     mx::GemmProblem p{};
     p.kgroup = false;
     p.offs = d_offsets;
     p.G = E;
-    p.M = M; p.N = N; p.K = K;
-    p.A = mx::MxOperand{x, nullptr, K, 0};           // no block scales: one per group
-    p.B = mx::MxOperand{w, nullptr, K, N};
+    p.M = M; p.N = N; p.K = Kp;
+    p.A = mx::MxOperand{xa, nullptr, Kp, 0};         // no block scales: one per group
+    p.B = mx::MxOperand{wa, nullptr, Kp, N};
     p.C = y; p.ldc = N; p.c_gstride = 0;
     p.rscale = d_row_scale;
     p.gsa = d_x_scale_inv;

@@ -38,6 +38,10 @@ hipError_t launch_padded_offsets(const int64_t* offs, int G, int64_t* poff,
 // scales, C % 128 == 0).
 hipError_t launch_quant_rows(const uint16_t* x, int64_t rows, int64_t C,
                              uint8_t* codes, uint8_t* scales, bool tiled, hipStream_t s);
+// Copy rows of n bytes into rows of np bytes (np >= n), the bytes past n set
+// to fill; 16-byte aligned src and dst.
+hipError_t launch_pad_rows(const uint8_t* src, int64_t rows, int64_t n, uint8_t* dst, int64_t np,
+                           uint8_t fill, hipStream_t s);
 // Tile pass: rowwise (optional) and columnwise (optional) copies of
 // x[batch][R][C].  Grouped mode (offs != nullptr, batch == 1) needs poff
 // already computed; row_bound is the padded-length bound (multiple of 128).

@@ -400,6 +400,27 @@ quant_tiles128_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
     }
 }
 
+// Row padding: rows of n bytes (stride n) become rows of np bytes (stride np),
+// bytes n .. np - 1 set to fill.  One thread per 16 output bytes: one 16-byte
+// copy where both strides are multiples of 16 and the chunk lies within the
+// source row, else byte by byte (scale rows, the chunk at the seam).
+__global__ void __launch_bounds__(256) pad_rows_kernel(const uint8_t* __restrict__ src,
+                                                       int64_t rows, int64_t n,
+                                                       uint8_t* __restrict__ dst, int64_t np,
+                                                       uint32_t fill) {
+    const int64_t chunks = (np + 15) / 16;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * chunks) return;
+    const int64_t row = i / chunks, c = (i - row * chunks) * 16;
+    const uint8_t* sr = src + row * n;
+    uint8_t* dr = dst + row * np + c;
+    if (n % 16 == 0 && np % 16 == 0 && c + 16 <= n) {
+        *reinterpret_cast<uint4*>(dr) = *reinterpret_cast<const uint4*>(sr + c);
+        return;
+    }
+    for (int b = 0; b < 16 && c + b < np; ++b) dr[b] = c + b < n ? sr[c + b] : (uint8_t)fill;
+}
+
 }  // namespace
 
 hipError_t launch_padded_offsets(const int64_t* offs, int G, int64_t* poff,
@@ -437,6 +458,15 @@ hipError_t launch_quant_tiles(const uint16_t* x, int64_t batch, int64_t R,
     dim3 grid((unsigned)((C + 63) / 64), (unsigned)ytiles, (unsigned)batch);
     hipLaunchKernelGGL(quant_tiles_kernel, grid, dim3(256), 0, s, x, R, C, offs,
                        poff, G, rc, rs, cc, cs, ld, tiled, gather, src_rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_rows(const uint8_t* src, int64_t rows, int64_t n, uint8_t* dst, int64_t np,
+                           uint8_t fill, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    const int64_t threads = rows * ((np + 15) / 16);
+    hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       src, rows, n, dst, np, (uint32_t)fill);
     return hipGetLastError();
 }
 

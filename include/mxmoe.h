@@ -135,7 +135,12 @@ mx_status mxfp8_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
  *   dtype MX_DTYPE_MXFP8: x = E4M3 codes [M][K] with x_scales [M][K/32];
  *                         w = codes [E][N][K] with w_scales [E][N][K/32]
  *                         (rowwise copies from mxfp8_quantize).
- *                         K % 128 == 0, N % 32 == 0.
+ *                         K % 32 == 0, N % 32 == 0.  K % 128 != 0 runs
+ *                         through zero-padded copies of both operands to K
+ *                         rounded up to 128 (codes 0, scales 2^0 past K),
+ *                         in one device allocation made with hipMallocAsync
+ *                         on `stream` and freed after the GEMM (a failed
+ *                         allocation returns MX_ERR_LAUNCH).
  *   d_row_scale  fp32 [M] routing weight applied to each output row, or NULL.
  *   y            bf16 [M][N].
  */
@@ -167,7 +172,8 @@ mx_status grouped_linear_fwd(int32_t dtype, const void* x,
  *                        * w_scale_inv[e]  (times r[row] if given)
  *   x codes [M][K], w codes [E][N][K] (from fp8_tensor_quantize, x with the
  *   same offsets, w as E matrices), scale_inv fp32 [E] each (device), y bf16
- *   [M][N].  fp32 accumulation.  K % 128 == 0, N % 32 == 0.
+ *   [M][N].  fp32 accumulation.  K % 32 == 0, N % 32 == 0 (K % 128 != 0:
+ *   padded copies as for grouped_linear_fwd).
  */
 mx_status fp8_tensor_quantize(const void* x, int64_t batch, int64_t R, int64_t C,
                               const int64_t* d_offsets, int32_t G, uint8_t* codes,

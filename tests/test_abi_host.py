@@ -148,9 +148,10 @@ def test_grouped_linear_rejects_bad_arguments(mxlib):
     assert f(0, FAKE, FAKE, FAKE, 4, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
     # bf16 K not a multiple of 32
     assert f(0, FAKE, None, FAKE, 4, 512, FAKE, None, 256, 100, None, FAKE, None) == MX_ERR_UNSUPPORTED
-    # MXFP8 without scales, K not a multiple of 128
+    # MXFP8 without scales; MXFP8 with K or N not a multiple of the 32-element block
     assert f(1, FAKE, None, FAKE, 4, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
-    assert f(1, FAKE, FAKE, FAKE, 4, 512, FAKE, FAKE, 256, 96, None, FAKE, None) == MX_ERR_UNSUPPORTED
+    assert f(1, FAKE, FAKE, FAKE, 4, 512, FAKE, FAKE, 256, 100, None, FAKE, None) == MX_ERR_UNSUPPORTED
+    assert f(1, FAKE, FAKE, FAKE, 4, 512, FAKE, FAKE, 250, 128, None, FAKE, None) == MX_ERR_UNSUPPORTED
     # E out of range, negative M
     assert f(0, FAKE, None, FAKE, 0, 512, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG
     assert f(0, FAKE, None, FAKE, 4, -1, FAKE, None, 256, 128, None, FAKE, None) == MX_ERR_INVALID_ARG

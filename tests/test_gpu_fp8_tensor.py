@@ -102,6 +102,8 @@ def gemm_case(rng, counts, K, N, row_scale):
 @pytest.mark.parametrize("counts,K,N,row_scale", [
     ([300, 0, 17, 129, 1, 553], 256, 96, False), ([700, 300], 512, 320, True),
     ([1], 128, 32, False), ([257, 0, 0, 1000], 1024, 64, True),
+    # K not a multiple of 128 (zero-padded copies)
+    ([300, 17, 0, 44], 160, 96, True), ([513], 992, 64, False),
 ])
 def test_grouped_linear_fp8_matches_oracle(dev, counts, K, N, row_scale):
     rng = np.random.default_rng(sum(counts) + K + N)

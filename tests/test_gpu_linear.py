@@ -87,6 +87,10 @@ def _mx_case(dev, counts, K, N, seed, outliers=False):
     ([300, 0, 17, 511], 256, 320),           # ragged M tails, an empty expert, N tail
     ([0, 0, 1, 0], 384, 64),                 # a single row
     ([1000, 2000, 3], 512, 544),
+    # K not a multiple of the 128-wide K step: zero-padded copies
+    ([300, 0, 17, 511], 96, 320),
+    ([1000, 5, 700], 544, 256),
+    ([64, 129], 1056, 64),
 ])
 def test_mxfp8_linear_small(dev, counts, K, N):
     x, w, off_np = _mx_case(dev, counts, K, N, seed=K + N, outliers=True)
