@@ -1421,8 +1421,8 @@ mx_gemm_kernel(GemmProblem p) {
             for (;;) {
                 const int wnext = w + grid;
                 const bool has_next = wnext < items;
-                // per-lane offsets from an opaque copy of the lane index, so
-                // that they are not kept live through the epilogue
+                // per-lane offsets from the lane index computed here, so that
+                // they are not kept live through the epilogue
                 int lane = lane_now();
                 const int nk = (int)(L.K / BK);
                 auto src_of = [&](const TileLoc& T) {
@@ -1501,9 +1501,9 @@ mx_gemm_kernel(GemmProblem p) {
         for (int t0 = 0; t0 < items; t0 += grid) {
             const int w = t0 + slot;
             if (w >= items) break;
-            // Per-lane offsets are derived per tile from an opaque copy of the
-            // lane index: hoisted out of the tile loop they would stay live
-            // through the epilogue, which needs every register it can get.
+            // Per-lane offsets are derived per tile from the lane index computed
+            // here: hoisted out of the tile loop they would stay live through
+            // the epilogue, which needs every register it can get.
             int lane = lane_now();
             const int r16 = lane & 15, q = lane >> 4;
             const int swz = r16 & 7;
@@ -1627,10 +1627,9 @@ mx_gemm_kernel(GemmProblem p) {
                 uint8_t* st = smem + wave * Slot<EPI>::kBytes;
 #pragma nounroll
                 for (int ip = 0; ip < 4; ++ip) {
-                    // Lane-derived values are re-derived from an opaque copy of the
-                    // lane index in every slice: hoisted out of the tile loop they
-                    // would stay live through the main loop and crowd out the
-                    // accumulators.
+                    // Lane-derived values are re-derived from the lane index in
+                    // every slice: hoisted out of the tile loop they would stay
+                    // live through the main loop and crowd out the accumulators.
                     int lane = lane_now();
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2];
@@ -1711,10 +1710,9 @@ mx_gemm_kernel(GemmProblem p) {
                 static_for<4>([&](auto jpc) { dma_unit(0, jpc, lane); });
 #pragma nounroll
                 for (int ip = 0; ip < 4; ++ip) {
-                    // Lane-derived values are re-derived from an opaque copy of the
-                    // lane index in every slice: hoisted out of the tile loop they
-                    // would stay live through the main loop and crowd out the
-                    // accumulators.
+                    // Lane-derived values are re-derived from the lane index in
+                    // every slice: hoisted out of the tile loop they would stay
+                    // live through the main loop and crowd out the accumulators.
                     int lane = lane_now();
                     const int r16 = lane & 15, q = lane >> 4;
                     float rr[2], drs[2];
