@@ -31,8 +31,10 @@
  * Conventions shared by every entry point
  *   - All pointers named d_* and every tensor pointer are DEVICE pointers on
  *     the current HIP device.  Sizes are host scalars.  The library never
- *     allocates, frees or synchronises: every call enqueues kernels on
- *     `stream` and returns.  The caller owns every buffer.
+ *     synchronises: every call enqueues kernels on `stream` and returns.  The
+ *     caller owns every buffer; the library allocates only the zero-padded
+ *     operand copies of a GroupedLinear call whose K is not a multiple of 128
+ *     (stream-ordered, freed on `stream` after its GEMM).
  *   - Rows are token-sorted: expert e owns rows [off[e], off[e+1]) of every
  *     [M, *] tensor; d_offsets is int64 [E+1] with off[0] = 0, off[E] = M,
  *     non-decreasing (not checked on the device).  Experts may be empty.
