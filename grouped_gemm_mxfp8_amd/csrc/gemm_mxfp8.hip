@@ -236,14 +236,16 @@ __device__ __forceinline__ float sum4q(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// (Quad permutes and row rotations with full row and bank masks give every lane
+// a source, so the plain DPP move needs no old value to start from.)
 // 4 x 4 byte transpose across the 4 lanes that share (lane >> 2): lane u
 // holds bytes B[u][0..3] and receives B[0..3][u].  Two rounds: swap 16-bit
 // halves with lane u^2, then bytes with lane u^1 (DPP quad permutes + v_perm).
 __device__ __forceinline__ uint32_t transpose4x4_bytes(uint32_t x, int u) {
-    const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
     const uint32_t t = (u & 2) ? __builtin_amdgcn_perm(y, x, 0x03020706u)
                                : __builtin_amdgcn_perm(y, x, 0x05040100u);
-    const uint32_t w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0xB1, 0xF, 0xF, false);
+    const uint32_t w = (uint32_t)__builtin_amdgcn_mov_dpp((int)t, 0xB1, 0xF, 0xF, false);
     return (u & 1) ? __builtin_amdgcn_perm(w, t, 0x03070105u)
                    : __builtin_amdgcn_perm(w, t, 0x06020400u);
 }
@@ -359,15 +361,17 @@ __device__ __forceinline__ void quant_unit(const float (&u)[2][2][4], int lc, in
         uint32_t scv[4];
         // column v's two rows (ii = 0, 1) share its scale: one scaled
         // conversion per column, byte pairs (ii0, ii1) regrouped by row below
-        uint32_t pr[2] = {0u, 0u};
+        // (the even column's conversion writes the low half, the odd one's the
+        // high half, so the even one starts from any bits: its input's)
+        uint32_t pr[2];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             uint32_t m = max(abs_bits(u[0][jj][v]), abs_bits(u[1][jj][v]));
             m = max16(m);
             scv[v] = scale_code_from_amax_bits(m);
-            pr[v >> 1] = e4m3x2_scaled(pr[v >> 1], u[0][jj][v], u[1][jj][v],
-                                       e4m3_limit_from_code(scv[v]), scale_from_code(scv[v]),
-                                       (v & 1) != 0);
+            pr[v >> 1] = e4m3x2_scaled((v & 1) ? pr[v >> 1] : __float_as_uint(u[0][jj][v]),
+                                       u[0][jj][v], u[1][jj][v], e4m3_limit_from_code(scv[v]),
+                                       scale_from_code(scv[v]), (v & 1) != 0);
         }
         // pr[0] = [v0 of ii0, v0 of ii1, v1 of ii0, v1 of ii1], pr[1] likewise
         // for v2, v3; row ii's dword holds its v0..v3
@@ -584,7 +588,7 @@ __device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][8], const Gem
     const int chunk0 = (lo8 ? 0 : 4) + 2 * (q & 1) + (q >> 1);
     const uint32_t loff = (uint32_t)(r16 & 7) * ldb + (uint32_t)chunk0 * 16u;
     auto ror8 = [](uint32_t v) {
-        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);
     };
 #pragma unroll
     for (int i = 0; i < 8; ++i) {

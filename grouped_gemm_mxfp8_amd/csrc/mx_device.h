@@ -95,10 +95,14 @@ __device__ __forceinline__ uint32_t e4m3x2_scaled(uint32_t old, float a, float b
                        : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale, false);
     return __builtin_bit_cast(uint32_t, r);
 }
-// Four values of one block: bytes a, b, c, d.
+// Four values of one block: bytes a, b, c, d.  The first conversion writes
+// the low half and the second the high half, so the first one's other half
+// may be anything: a's own bits, whose register the conversion can then
+// write in place (a zero there would cost a register copy per dword).
 __device__ __forceinline__ uint32_t e4m3x4_scaled(float a, float b, float c, float d, float lim,
                                                   float scale) {
-    return e4m3x2_scaled(e4m3x2_scaled(0u, a, b, lim, scale, false), c, d, lim, scale, true);
+    return e4m3x2_scaled(e4m3x2_scaled(__float_as_uint(a), a, b, lim, scale, false), c, d, lim,
+                         scale, true);
 }
 
 // Streaming stores: the output is read by a later kernel, never again by
