@@ -570,6 +570,10 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 // they are, to the wave's blocks of a partial tile there (block (i, j) at
 // byte (i * 8 + j) * 1024, lane l's 16 bytes at 16 l).  Both outputs share
 // one pass over the row blocks, so the accumulators are read one way only.
+// SCALED: the accumulators are multiplied by gs (and the row's rs) before
+// the conversion; otherwise gs and rs are not read (the kernel variant for
+// launches without output scales).
+template <bool SCALED>
 __device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][8], const GemmProblem& p,
                                                      int g, int64_t m0, int64_t mvalid, int64_t n0,
                                                      int wm, int wn, int lane, float gs,
@@ -587,66 +591,75 @@ __device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][8], const Gem
     const uint32_t ldb = (uint32_t)p.ldc * 2u;
     const int chunk0 = (lo8 ? 0 : 4) + 2 * (q & 1) + (q >> 1);
     const uint32_t loff = (uint32_t)(r16 & 7) * ldb + (uint32_t)chunk0 * 16u;
-    auto ror8 = [](uint32_t v) {
-        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);
+    // The rotation by 8 lanes of the rows' second halves, written only where
+    // it lands: into the lanes r16 >= 8 (banks 2, 3) of s1, which start as
+    // d0, and into the lanes r16 < 8 (banks 0, 1) of s2, which start as d1:
+    // s1 = lo8 ? d0 : d1 of lane r16 ^ 8, s2 = lo8 ? d0 of lane r16 ^ 8 : d1.
+    auto into_hi = [](uint32_t old, uint32_t v) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, 0x128, 0xf, 0xc, false);
     };
+    auto into_lo = [](uint32_t old, uint32_t v) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, 0x128, 0xf, 0x3, false);
+    };
+    {
+        constexpr bool kScaled = SCALED;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        // the accumulators live in AGPRs: pinned there at each row block, the
-        // block moves to VGPRs only when it is converted (else the compiler
-        // may move the whole tile up front and spill)
+        for (int i = 0; i < 8; ++i) {
+            // the accumulators live in AGPRs: pinned there at each row block, the
+            // block moves to VGPRs only when it is converted (else the compiler
+            // may move the whole tile up front and spill)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
-        if (part) {
+            for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+            if (part) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<v4f*>(part + (int64_t)(i * 8 + j) * 1024 + (uint32_t)lane * 16u) =
-                    acc[i][j];
-            __builtin_amdgcn_sched_barrier(0);
-            continue;
-        }
-        const float sc = rs ? rs[i * 16 + r16] * gs : gs;
-        const int rl1 = i * 16 + (r16 & 7), rl2 = rl1 + 8;
+                for (int j = 0; j < 8; ++j)
+                    *reinterpret_cast<v4f*>(part + (int64_t)(i * 8 + j) * 1024 + (uint32_t)lane * 16u) =
+                        acc[i][j];
+                __builtin_amdgcn_sched_barrier(0);
+                continue;
+            }
+            const float sc = kScaled ? (rs ? rs[i * 16 + r16] * gs : gs) : 1.0f;
+            const int rl1 = i * 16 + (r16 & 7), rl2 = rl1 + 8;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            uint32_t d[2][4];                       // jp = 2c + h, after the swap
+            for (int c = 0; c < 2; ++c) {
+                uint32_t d[2][4];                       // jp = 2c + h, after the swap
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int jp = 2 * c + h;
-                float va[4], vb[4];
+                for (int h = 0; h < 2; ++h) {
+                    const int jp = 2 * c + h;
+                    float va[4], vb[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        va[v] = kScaled ? acc[i][2 * jp][v] * sc : acc[i][2 * jp][v];
+                        vb[v] = kScaled ? acc[i][2 * jp + 1][v] * sc : acc[i][2 * jp + 1][v];
+                    }
+                    const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
+                    const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+                    const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+                    d[h][0] = x[0];
+                    d[h][1] = y[0];
+                    d[h][2] = x[1];
+                    d[h][3] = y[1];
+                }
+                uint32_t s1[4], s2[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    va[v] = acc[i][2 * jp][v] * sc;
-                    vb[v] = acc[i][2 * jp + 1][v] * sc;
+                    s1[v] = into_hi(d[0][v], d[1][v]);
+                    s2[v] = into_lo(d[1][v], d[0][v]);
                 }
-                const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
-                const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
-                const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
-                d[h][0] = x[0];
-                d[h][1] = y[0];
-                d[h][2] = x[1];
-                d[h][3] = y[1];
+                const int chunk = chunk0 + 8 * c;
+                if (cw + chunk * 8 < p.N) {
+                    uint8_t* const b1 = Cw + (int64_t)(i * 16) * ldb + c * 128;
+                    if (rl1 < rows_valid_w)
+                        store_nt(b1 + loff, make_uint4(s1[0], s1[1], s1[2], s1[3]));
+                    if (rl2 < rows_valid_w)
+                        store_nt(b1 + (int64_t)8 * ldb + loff, make_uint4(s2[0], s2[1], s2[2], s2[3]));
+                }
             }
-            uint32_t rv[4], s1[4], s2[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                rv[v] = ror8(lo8 ? d[1][v] : d[0][v]);
-                s1[v] = lo8 ? d[0][v] : rv[v];
-                s2[v] = lo8 ? rv[v] : d[1][v];
-            }
-            const int chunk = chunk0 + 8 * c;
-            if (cw + chunk * 8 < p.N) {
-                uint8_t* const b1 = Cw + (int64_t)(i * 16) * ldb + c * 128;
-                if (rl1 < rows_valid_w)
-                    store_nt(b1 + loff, make_uint4(s1[0], s1[1], s1[2], s1[3]));
-                if (rl2 < rows_valid_w)
-                    store_nt(b1 + (int64_t)8 * ldb + loff, make_uint4(s2[0], s2[1], s2[2], s2[3]));
-            }
+            // one row block at a time: the scheduler would otherwise read ahead
+            // the accumulators of later blocks into registers the kernel has not
+            // got (and spill them, the reload then waiting for every store)
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // one row block at a time: the scheduler would otherwise read ahead
-        // the accumulators of later blocks into registers the kernel has not
-        // got (and spill them, the reload then waiting for every store)
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -988,18 +1001,21 @@ __device__ __forceinline__ void tile_gemm_chain(v4f (&acc)[8][8], GemmSmem& sm, 
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         bsc[j] = (reinterpret_cast<const uint8_t*>(sm.bs[st]) + b_s)[j * 16 * 4];
     };
-    auto mfma = [&](auto ic, auto jc) {
+    // FIRST: the tile's first K step, whose MFMAs take a zero accumulator
+    // input instead of acc (no per-tile zeroing of the 256 accumulators)
+    auto mfma = [&](auto ic, auto jc, auto firstc) {
         constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            bfr[j], af[i], acc[i][j], 0, 0, 0, bsc[j], 0, asc[i]);
+            bfr[j], af[i], decltype(firstc)::value ? v4f{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0,
+            bsc[j], 0, asc[i]);
     };
     // one K step: the MFMAs of step ks, the loads of step kl of src
-    auto step = [&](int ks, auto livec, const TileNext& src, int kl) {
+    auto step = [&](int ks, auto livec, const TileNext& src, int kl, auto firstc) {
         const int cur = (b0 + ks) & 1, nxt = cur ^ 1;
         lds_barrier();                                  // S1: stage cur is free
         static_for<4 * NJ>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
-            mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{});
+            mfma(std::integral_constant<int, s % 4>{}, std::integral_constant<int, s / 4>{}, firstc);
             __builtin_amdgcn_sched_barrier(0);
             constexpr int u = SC::a_at(s);
             if constexpr (u >= 0) dma_u(std::integral_constant<int, u>{}, livec, src, cur, kl);
@@ -1009,7 +1025,7 @@ __device__ __forceinline__ void tile_gemm_chain(v4f (&acc)[8][8], GemmSmem& sm, 
         lds_barrier();                                  // S2: stage nxt complete
         static_for<4 * NJ>([&](auto sc) {
             constexpr int s = decltype(sc)::value, j = s / 4, i = 4 + s % 4;
-            mfma(std::integral_constant<int, i>{}, std::integral_constant<int, j>{});
+            mfma(std::integral_constant<int, i>{}, std::integral_constant<int, j>{}, firstc);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (s < 4) read_a(std::integral_constant<int, s>{}, nxt);
             if constexpr (s >= 4 * NJ - 4) read_a(std::integral_constant<int, i>{}, nxt);
@@ -1031,11 +1047,23 @@ __device__ __forceinline__ void tile_gemm_chain(v4f (&acc)[8][8], GemmSmem& sm, 
     }
     static_for<8>([&](auto ic) { read_a(ic, b0); });
     static_for<NJ>([&](auto jc) { read_b(jc, b0); });
+    // Step 0 starts the accumulation from zero when it is followed by two
+    // or more steps (its loads then stay within the tile); a tile of one or
+    // two K steps (or none) zeroes acc first and runs every step as usual.
     int ks = 0;
-    for (; ks + 2 < nk; ++ks) step(ks, std::true_type{}, own, ks + 2);
+    if (nk >= 3) {
+        step(0, std::true_type{}, own, 2, std::true_type{});
+        ks = 1;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    for (; ks + 2 < nk; ++ks) step(ks, std::true_type{}, own, ks + 2, std::false_type{});
     if (ks < nk) {
         const TileNext nx = next_src();
-        for (; ks < nk; ++ks) step(ks, std::false_type{}, nx, ks + 2 - nk);
+        for (; ks < nk; ++ks) step(ks, std::false_type{}, nx, ks + 2 - nk, std::false_type{});
     }
 }
 
@@ -1215,9 +1243,11 @@ struct TileLoc {
 // NW: waves per workgroup, 4 (one per SIMD) or 8 (two per SIMD, plain store
 // only).
 // TILED (plain store only): both operands carry block scales in the K-step
-// tiled layout, checked on the host; the tile sources then test neither for
-// missing scales nor for the layout (runtime flags the plain kernel would
-// otherwise keep live across its tile loop, at the cost of spilled registers).
+// tiled layout and the output has no row scale and no group factors, checked
+// on the host; the tile sources then test neither for missing scales nor for
+// the layout (runtime flags the plain kernel would otherwise keep live across
+// its tile loop, at the cost of spilled registers), and the epilogue converts
+// the accumulators without a multiply.
 template <Epi EPI, bool SPLIT = false, bool TILED = false>
 __global__ void __launch_bounds__(NTHREADS, 1)
 mx_gemm_kernel(GemmProblem p) {
@@ -1445,7 +1475,7 @@ mx_gemm_kernel(GemmProblem p) {
                 // this wave's routing weights (its 128 rows; rows past the
                 // tile read as 0) into LDS; the main loop's waits cover the
                 // loads (every step waits for all but its own newest loads)
-                const bool use_rs = p.rscale && (!SPLIT || L.chunk < 0);
+                const bool use_rs = !TILED && p.rscale && (!SPLIT || L.chunk < 0);
                 if (use_rs) {
                     const int64_t nrw = min((int64_t)128, max((int64_t)0, L.mvalid - wm * 128));
                     const v4i rr = make_rsrc(p.rscale + L.m0 + wm * 128, nrw * 4);
@@ -1453,11 +1483,7 @@ mx_gemm_kernel(GemmProblem p) {
                     dma_b32(rr, la, (uint32_t)lane * 4u, 0u);
                     dma_b32(rr, la + 256u, (uint32_t)lane * 4u + 256u, 0u);
                 }
-                v4f acc[8][8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                v4f acc[8][8];    // written by tile_gemm_chain's first step
                 // the next tile's position, found once (while this tile's
                 // last K steps run) and kept for the next iteration
                 TileLoc Ln{};
@@ -1480,7 +1506,7 @@ mx_gemm_kernel(GemmProblem p) {
                     part = reinterpret_cast<uint8_t*>(split_part(p.split_ws, w - full)) +
                            (int64_t)wave * 64 * 1024;
                 if (use_rs && nk == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                store_tile_bf16_regs(acc, p, L.g, L.m0, L.mvalid, L.n0, wm, wn, lane,
+                store_tile_bf16_regs<!TILED>(acc, p, L.g, L.m0, L.mvalid, L.n0, wm, wn, lane,
                                          has_gs ? s_gs[L.g] : 1.0f,
                                          use_rs ? &s_rsw[wave * 128] : nullptr, part);
                 if (SPLIT && L.chunk >= 0) {
@@ -1935,7 +1961,8 @@ hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s) {
     switch (epi) {
         case Epi::kStoreBf16: {
             const bool split = p.split_ws && !p.kgroup;
-            const bool tiled = p.A.scales && p.B.scales && p.A.tiled && p.B.tiled;
+            const bool tiled = p.A.scales && p.B.scales && p.A.tiled && p.B.tiled && !p.rscale &&
+                               !p.gsa && !p.gsb;
             auto go = [&](auto kern) {
                 hipLaunchKernelGGL(kern, dim3(grid), dim3(NTHREADS), 0, s, p);
             };
