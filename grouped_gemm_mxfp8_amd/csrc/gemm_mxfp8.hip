@@ -1239,9 +1239,8 @@ struct TileLoc {
     int64_t m0, mvalid, n0, klo, K;
 };
 
+// One workgroup of four waves (one per SIMD) per CU, persistent over tiles.
 // SPLIT (plain store, row-grouped only): the tail-split schedule below.
-// NW: waves per workgroup, 4 (one per SIMD) or 8 (two per SIMD, plain store
-// only).
 // TILED (plain store only): both operands carry block scales in the K-step
 // tiled layout and the output has no row scale and no group factors, checked
 // on the host; the tile sources then test neither for missing scales nor for
