@@ -876,7 +876,7 @@ mx_status grouped_mlp_bwd_ex(const void* dy, const int64_t* d_offsets, int32_t E
         p.qc = wb + W.dhc; p.qcs = wb + W.dhc_s; p.ldqc = d.Mp;
         p.qtiled = true;
         p.poff = poff;
-        p.drp = reinterpret_cast<float*>(wb + W.drp); p.lddrp = nparts;
+        p.drp = reinterpret_cast<float*>(wb + W.drp); p.lddrp = M;   // part-major partials
         const mx::MxOperand dyr{wb + W.dyr, wb + W.dyr_s, H, 0, true};
         const mx::MxOperand w2c{cb + C.w2c, cb + C.w2c_s, H, F, true};
         if (sh) {

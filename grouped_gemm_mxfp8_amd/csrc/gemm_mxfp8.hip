@@ -1810,7 +1810,7 @@ mx_gemm_kernel(GemmProblem p) {
                     for (int ii = 0; ii < 2; ++ii) {
                         const float sum = sum4q(drs[ii]);
                         const int rl = (2 * ip + ii) * 16 + r16;
-                        if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                        if (q == 0 && rl < rows_valid_w) p.drp[(int64_t)part * p.lddrp + rwave + rl] = sum;
                     }
                     // the wave's 128 columns are all below F or all at or past it
                     lds_wait();
@@ -1889,7 +1889,7 @@ mx_gemm_kernel(GemmProblem p) {
                     for (int ii = 0; ii < 2; ++ii) {
                         const float sum = sum4q(drs[ii]);
                         const int rl = (2 * ip + ii) * 16 + r16;
-                        if (q == 0 && rl < rows_valid_w) p.drp[(rwave + rl) * p.lddrp + part] = sum;
+                        if (q == 0 && rl < rows_valid_w) p.drp[(int64_t)part * p.lddrp + rwave + rl] = sum;
                     }
                     lds_wait();
                     flush_rows<128, false>(st, d, rwave, ip, rows_valid_w, lane);
@@ -1904,13 +1904,16 @@ mx_gemm_kernel(GemmProblem p) {
     }
 }
 
+// The partials are part-major ([nparts][M]), so each part's loads are
+// coalesced across the rows of a wave; the sum runs over j in ascending order.
 __global__ void __launch_bounds__(256)
 dr_reduce_kernel(const float* __restrict__ drp, int64_t M, int64_t nparts,
                  float* __restrict__ dr) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= M) return;
     float s = 0.f;
-    for (int64_t j = 0; j < nparts; ++j) s += drp[i * nparts + j];
+#pragma unroll 32
+    for (int64_t j = 0; j < nparts; ++j) s += drp[j * M + i];
     dr[i] = s;
 }
 

@@ -96,7 +96,7 @@ struct GemmProblem {
     uint8_t* qc; uint8_t* qcs; int64_t ldqc;   // columnwise MXFP8 output
     bool qtiled;                // fused outputs: K-step tiled scales
     const int64_t* poff;        // padded token offsets of the column copy
-    float* drp; int64_t lddrp;  // kDSwiglu(R): dr partials [M][lddrp]
+    float* drp; int64_t lddrp;  // kDSwiglu(R): dr partials, part j of row i at drp[j * lddrp + i]
     const float* gsa;           // kStoreBf16: per-group factors of A and of B
     const float* gsb;           //   (scale_inv of per-tensor FP8), or nullptr
     uint8_t* split_ws;          // kStoreBf16, row-grouped: tail-split workspace
@@ -122,7 +122,7 @@ constexpr size_t kSplitWsBytes = kSplitHdrBytes + (size_t)kSplitItems * 256 * 25
 hipError_t launch_mx_gemm(const GemmProblem& p, Epi epi, hipStream_t s);
 hipError_t launch_split_fixup(const GemmProblem& p, hipStream_t s);
 
-// Sum of dr partials: dr[i] = sum_j drp[i][j], j ascending.
+// Sum of dr partials: dr[i] = sum_j drp[j * M + i], j ascending.
 hipError_t launch_dr_reduce(const float* drp, int64_t M, int64_t nparts,
                             float* dr, hipStream_t s);
 
