@@ -601,65 +601,62 @@ __device__ __forceinline__ void store_tile_bf16_regs(v4f (&acc)[8][8], const Gem
     auto into_lo = [](uint32_t old, uint32_t v) {
         return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, 0x128, 0xf, 0x3, false);
     };
-    {
-        constexpr bool kScaled = SCALED;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            // the accumulators live in AGPRs: pinned there at each row block, the
-            // block moves to VGPRs only when it is converted (else the compiler
-            // may move the whole tile up front and spill)
+    for (int i = 0; i < 8; ++i) {
+        // the accumulators live in AGPRs: pinned there at each row block, the
+        // block moves to VGPRs only when it is converted (else the compiler
+        // may move the whole tile up front and spill)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
-            if (part) {
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+        if (part) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    *reinterpret_cast<v4f*>(part + (int64_t)(i * 8 + j) * 1024 + (uint32_t)lane * 16u) =
-                        acc[i][j];
-                __builtin_amdgcn_sched_barrier(0);
-                continue;
-            }
-            const float sc = kScaled ? (rs ? rs[i * 16 + r16] * gs : gs) : 1.0f;
-            const int rl1 = i * 16 + (r16 & 7), rl2 = rl1 + 8;
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<v4f*>(part + (int64_t)(i * 8 + j) * 1024 + (uint32_t)lane * 16u) =
+                    acc[i][j];
+            __builtin_amdgcn_sched_barrier(0);
+            continue;
+        }
+        const float sc = SCALED ? (rs ? rs[i * 16 + r16] * gs : gs) : 1.0f;
+        const int rl1 = i * 16 + (r16 & 7), rl2 = rl1 + 8;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                uint32_t d[2][4];                       // jp = 2c + h, after the swap
+        for (int c = 0; c < 2; ++c) {
+            uint32_t d[2][4];                       // jp = 2c + h, after the swap
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int jp = 2 * c + h;
-                    float va[4], vb[4];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        va[v] = kScaled ? acc[i][2 * jp][v] * sc : acc[i][2 * jp][v];
-                        vb[v] = kScaled ? acc[i][2 * jp + 1][v] * sc : acc[i][2 * jp + 1][v];
-                    }
-                    const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
-                    const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
-                    const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
-                    d[h][0] = x[0];
-                    d[h][1] = y[0];
-                    d[h][2] = x[1];
-                    d[h][3] = y[1];
-                }
-                uint32_t s1[4], s2[4];
+            for (int h = 0; h < 2; ++h) {
+                const int jp = 2 * c + h;
+                float va[4], vb[4];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    s1[v] = into_hi(d[0][v], d[1][v]);
-                    s2[v] = into_lo(d[1][v], d[0][v]);
+                    va[v] = SCALED ? acc[i][2 * jp][v] * sc : acc[i][2 * jp][v];
+                    vb[v] = SCALED ? acc[i][2 * jp + 1][v] * sc : acc[i][2 * jp + 1][v];
                 }
-                const int chunk = chunk0 + 8 * c;
-                if (cw + chunk * 8 < p.N) {
-                    uint8_t* const b1 = Cw + (int64_t)(i * 16) * ldb + c * 128;
-                    if (rl1 < rows_valid_w)
-                        store_nt(b1 + loff, make_uint4(s1[0], s1[1], s1[2], s1[3]));
-                    if (rl2 < rows_valid_w)
-                        store_nt(b1 + (int64_t)8 * ldb + loff, make_uint4(s2[0], s2[1], s2[2], s2[3]));
-                }
+                const uint2 a = pack4_bf16(va), b = pack4_bf16(vb);
+                const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+                const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+                d[h][0] = x[0];
+                d[h][1] = y[0];
+                d[h][2] = x[1];
+                d[h][3] = y[1];
             }
-            // one row block at a time: the scheduler would otherwise read ahead
-            // the accumulators of later blocks into registers the kernel has not
-            // got (and spill them, the reload then waiting for every store)
-            __builtin_amdgcn_sched_barrier(0);
+            uint32_t s1[4], s2[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                s1[v] = into_hi(d[0][v], d[1][v]);
+                s2[v] = into_lo(d[1][v], d[0][v]);
+            }
+            const int chunk = chunk0 + 8 * c;
+            if (cw + chunk * 8 < p.N) {
+                uint8_t* const b1 = Cw + (int64_t)(i * 16) * ldb + c * 128;
+                if (rl1 < rows_valid_w)
+                    store_nt(b1 + loff, make_uint4(s1[0], s1[1], s1[2], s1[3]));
+                if (rl2 < rows_valid_w)
+                    store_nt(b1 + (int64_t)8 * ldb + loff, make_uint4(s2[0], s2[1], s2[2], s2[3]));
+            }
         }
+        // one row block at a time: the scheduler would otherwise read ahead
+        // the accumulators of later blocks into registers the kernel has not
+        // got (and spill them, the reload then waiting for every store)
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

@@ -132,7 +132,7 @@ __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(v2u16, a),
                                                                   __builtin_bit_cast(v2u16, b)));
 }
-// Largest magnitude of the 2n bf16 values in w[0 .. n), as a 15-bit pattern.
+// Largest magnitude of the 2N bf16 values in w[0 .. N), as a 15-bit pattern.
 template <int N>
 __device__ __forceinline__ uint32_t bf16_amax(const uint32_t* w) {
     uint32_t m = w[0] & 0x7fff7fffu;
