@@ -39,6 +39,7 @@ K=1024, N=2816) in MXFP8 and in per-tensor FP8, and the tiny BF16 workload
 launch per expert, not in the step either.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --headline-only [--workload fine_grained_64e]   (profiler runs)
 """
 from __future__ import annotations
 
@@ -67,6 +68,10 @@ def parse():
     ap.add_argument("--headline-only", action="store_true",
                     help="time the headline step only (and its launch-record pass): no side "
                          "figures, for short profiler runs")
+    ap.add_argument("--workload", default="mixtral_fwd_bwd",
+                    choices=["mixtral_fwd_bwd", "fine_grained_64e"],
+                    help="with --headline-only: the step's workload (the headline is the "
+                         "Mixtral shape; the 64-expert workload is there for profiler runs)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many "
                          "MiB (read + write), the reference dispatch that scales "
@@ -175,7 +180,7 @@ def measured_traffic(kernel):
     return None if ent is None else int(round(ent["bytes"]))
 
 
-def roofline(agg):
+def roofline(agg, with_traffic=True):
     name, a = max(agg.items(), key=lambda kv: kv[1]["ms"])
     sec = a["ms"] / 1e3
     if a["unit"] == 0:
@@ -185,7 +190,8 @@ def roofline(agg):
         achieved = a["work"] / sec / 1e9
         peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
     return {"kernel": name, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 4), "traffic": measured_traffic(name),
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(name) if with_traffic else None,
             "traffic_unit": "HBM bytes per launch",
             "launches": a["launches"], "avg_launch_ms": round(a["ms"] / a["launches"], 4)}
 
@@ -509,7 +515,10 @@ def main():
     dev = torch.device("cuda:0")
     print(f"[bench] device {torch.cuda.get_device_name(dev)}; building inputs", file=sys.stderr,
           flush=True)
-    case = make_mlp_case("mixtral_fwd_bwd", seed=args.seed, device=dev)
+    if args.workload != "mixtral_fwd_bwd" and not args.headline_only:
+        print(json.dumps({"error": "--workload other than the headline's needs --headline-only"}))
+        return 2
+    case = make_mlp_case(args.workload, seed=args.seed, device=dev)
     M, H, F, E, T = case.M, case.H, case.F, case.E, case.T
     x, w1, w2, r, off, dy = case.X, case.W1, case.W2, case.r, case.offsets, case.dY
     # workspaces large enough for both modes
@@ -551,13 +560,16 @@ def main():
                 for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["ms"])}
 
     if args.headline_only:
-        out = {"metric": "GroupedMLP fwd+bwd tokens/s & TFLOP/s (MXFP8), Mixtral-8x7B expert shape",
+        shape = ("Mixtral-8x7B expert shape" if args.workload == "mixtral_fwd_bwd" else
+                 "64-expert long-sequence workload (T=32768 top-8, H=2048, F=1408)")
+        out = {"metric": "GroupedMLP fwd+bwd tokens/s & TFLOP/s (MXFP8), " + shape,
                "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
                "steps": args.steps, "warmup": args.warmup,
                "ms_per_step": round(elapsed / args.steps * 1e3, 4), "gpu_ms_per_step": stats,
                "tflops": round(flops_step * args.steps / elapsed / 1e12, 2),
-               "roofline": roofline(agg), "kernels": kernels_of(agg, args.steps),
-               "note": "headline only (--headline-only)"}
+               "roofline": roofline(agg, args.workload == "mixtral_fwd_bwd"),
+               "kernels": kernels_of(agg, args.steps),
+               "note": "headline only (--headline-only), workload " + args.workload}
         print(json.dumps(out), flush=True)
         return 0
 
